@@ -1,0 +1,158 @@
+/*
+ * libssd -- Mamba-2 SSD (state-space duality) chunked selective-scan forward on AMD Instinct
+ * MI355X (gfx950). C ABI: plain pointers and sizes only.
+ *
+ * The operation (per batch b and head h, state S of shape [P, N]):
+ *     S_t    = exp(dt[t,h] * A[h]) * S_{t-1} + dt[t,h] * outer(x[t,h,:], B[t,g(h),:])
+ *     y[t,h] = S_t @ C[t,g(h),:] + D[h] * x[t,h,:]
+ * with S_{-1} = initial_state (zeros when NULL), final_state = S_{L-1}, and g(h) = h / (H / G).
+ * This is the selective state-space step of "Why SSM and linear-RNN FLOPs do not convert into GPU
+ * FLOPs" (first paragraph) with one decay shared by every state entry of a head, in the Mamba-2
+ * SSD form. It is evaluated with the chunked algorithm ("nitter.gq/da_be19" thread, post 5/6):
+ * the sequence is cut into chunks of `chunk_size` tokens; inside a chunk the quadratic masked form
+ * (C B^T masked by the decay) is used, across chunks a linear recurrence over chunk states; the
+ * stages are the per-chunk cumulative decay, the state entering each chunk, and the outputs
+ * ("Mamba-2 in NVIDIA cuTile: Faster Forward Kernels and What the Benchmark Means", section
+ * "Why Mamba-2 is a useful kernel example").
+ *
+ * Layouts: every tensor is dense, row-major (last index fastest), in device memory:
+ *     x, y            [batch, seqlen, nheads, headdim]     io dtype (fp32 or bf16)
+ *     dt              [batch, seqlen, nheads]              fp32, the final positive step sizes
+ *     A, D            [nheads]                             fp32 (A <= 0 is the decay regime)
+ *     B, C            [batch, seqlen, ngroups, dstate]     io dtype
+ *     initial_state,
+ *     final_state     [batch, nheads, headdim, dstate]     fp32
+ *
+ * Ownership: the caller owns every buffer; the library keeps no pointer after a call returns.
+ * Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null stream):
+ * device faults surface at the caller's next synchronisation. Workspace (unfused path, and the
+ * segment states of the fused path) is allocated stream-ordered on `stream` and released the same
+ * way.
+ *
+ * Errors: every argument check runs on the host before any HIP call; on failure nothing is
+ * launched and nothing is written. Status codes are never thrown across the ABI.
+ *
+ * Precision (bf16 io): x, B, C are converted exactly to fp16 for the matrix cores; operands that
+ * carry fp32 values (the masked C B^T block, the chunk states fed to the readout) are rounded to
+ * fp16 once, and the chunk-state operand is split into fp16 high + low parts. All accumulation is
+ * fp32; y is rounded once to bf16 (nearest-even). Inputs must stay within fp16 range
+ * (|v| < 65504). fp32 io uses fp32 matrix-core instructions throughout.
+ * Results are bitwise reproducible run to run on one GPU (fixed reduction order, no atomics on
+ * data).
+ */
+#ifndef LIBSSD_SSD_H
+#define LIBSSD_SSD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, nheads % ngroups != 0,
+                                     misaligned pointer, overlapping output, bad enum value */
+    SSD_ERR_UNSUPPORTED = 2,      /* valid request outside what the kernels implement: chunk_size
+                                     not a power of two in [16, 256], headdim or dstate not a
+                                     multiple of 16 or above 256, sizes beyond 32-bit indexing */
+    SSD_ERR_NO_DEVICE = 3,        /* no HIP device visible */
+    SSD_ERR_OUT_OF_MEMORY = 4,    /* workspace allocation failed */
+    SSD_ERR_HIP = 5               /* a HIP call or kernel launch failed */
+} ssd_status;
+
+typedef enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype; /* dtype of x, B, C, y */
+
+typedef struct {
+    int64_t batch, seqlen, nheads, headdim, dstate, ngroups;
+    int32_t io_dtype; /* ssd_dtype */
+    int32_t reserved; /* must be 0 */
+} ssd_problem;
+
+typedef enum {
+    SSD_VARIANT_AUTO = 0,
+    SSD_VARIANT_UNFUSED = 1, /* cumsum, C B^T, chunk states, state passing, chunk scan: five
+                                kernels, intermediates in workspace */
+    SSD_VARIANT_FUSED = 2    /* intra-chunk C B^T block kept in registers; states carried on chip
+                                through runs of chunks, exchanged only at run boundaries */
+} ssd_variant;
+
+typedef enum {
+    SSD_PRECISION_AUTO = 0, /* fp16 operands with the chunk-state operand split hi + lo (bf16 io),
+                               fp32 (fp32 io) */
+    SSD_PRECISION_FP16 = 1, /* bf16 io: every fp32-carrying operand rounded once to fp16 */
+    SSD_PRECISION_FP32 = 3  /* fp32 matrix-core instructions for every contraction */
+} ssd_precision;
+
+typedef struct {
+    int32_t variant;    /* ssd_variant */
+    int32_t precision;  /* ssd_precision */
+    int32_t run_chunks; /* fused variant: chunks per run (state carried on chip through a run);
+                           0 = chosen from the problem size; must be >= 0 */
+} ssd_options;
+
+/* Full forward. initial_state may be NULL (zeros); final_state may be NULL (not written).
+ * Alignment: every pointer 16-byte aligned. y must not overlap any input; final_state must not
+ * overlap initial_state or any other argument. chunk_size: power of two in [16, 256]; the last
+ * chunk may be shorter. */
+ssd_status ssd_forward(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                       const void* B, const void* C, const float* D, int64_t chunk_size,
+                       const float* initial_state, void* y, float* final_state, void* stream);
+
+/* Same, with explicit variant / precision (opts may be NULL = auto). */
+ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                          const void* B, const void* C, const float* D, int64_t chunk_size,
+                          const float* initial_state, void* y, float* final_state, void* stream,
+                          const ssd_options* opts);
+
+/* ---- Stages of the unfused path, exposed so each can be checked on its own. -----------------
+ * nc = ceil(seqlen / chunk_size), Q = chunk_size. Workspace layouts (fp32, row-major):
+ *     Acs      [batch, nheads, nc, Q]   inclusive cumulative sum of dt*A inside each chunk; past
+ *                                       the end of a ragged last chunk it repeats the last value
+ *     dtc      [batch, nheads, nc, Q]   dt regrouped per (head, chunk); 0 past the end
+ *     CB       [batch, nc, ngroups, Q, Q]  C_i . B_j; only 16x16 blocks on or below the block
+ *                                       diagonal are written, and in them only j <= i is
+ *                                       meaningful
+ *     states   [batch, nc, nheads, headdim, dstate]  each chunk's own end state (zero entry state)
+ *     h_in     [batch, nc, nheads, headdim, dstate]  state entering each chunk
+ */
+
+/* Stage 1 (per-chunk cumulative decay): writes Acs and dtc. */
+ssd_status ssd_chunk_cumsum(const ssd_problem* prob, const float* dt, const float* A,
+                            int64_t chunk_size, float* Acs, float* dtc, void* stream);
+
+/* Stage 2 (C B^T inside each chunk, shared by the heads of a group): writes CB. */
+ssd_status ssd_bmm_chunk(const ssd_problem* prob, const void* B, const void* C,
+                         int64_t chunk_size, float* CB, void* stream);
+
+/* Stage 3 (each chunk's own end state): states = sum_j exp(Acs_last - Acs_j) dt_j x_j B_j^T. */
+ssd_status ssd_chunk_state(const ssd_problem* prob, const void* x, const void* B,
+                           const float* Acs, const float* dtc, int64_t chunk_size,
+                           float* states, void* stream, const ssd_options* opts);
+
+/* Stage 4 (state entering each chunk): h_in[0] = initial_state (or 0),
+ * h_in[c+1] = exp(Acs_last[c]) h_in[c] + states[c]; final_state = h_in[nc] (may be NULL). */
+ssd_status ssd_state_passing(const ssd_problem* prob, const float* states, const float* Acs,
+                             int64_t chunk_size, const float* initial_state, float* h_in,
+                             float* final_state, void* stream);
+
+/* Stage 5 (outputs): y = (CB * exp(Acs_i - Acs_j) * dt_j, j <= i) x + exp(Acs_i) C_i h_in^T
+ * + D x. */
+ssd_status ssd_chunk_scan(const ssd_problem* prob, const void* x, const void* C, const float* CB,
+                          const float* Acs, const float* dtc, const float* h_in, const float* D,
+                          int64_t chunk_size, void* y, void* stream, const ssd_options* opts);
+
+/* Bytes of each unfused workspace tensor, in the order Acs, dtc, CB, states, h_in. */
+ssd_status ssd_workspace_sizes(const ssd_problem* prob, int64_t chunk_size, int64_t sizes[5]);
+
+/* Static text for a status code. */
+const char* ssd_status_string(ssd_status status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSSD_SSD_H */

@@ -1,0 +1,374 @@
+// libssd C ABI: argument checks, workspace, and the sequence of kernel launches.
+// Every check runs on the host before the first HIP call, so invalid requests return without
+// touching the device (and the checks work on machines without a GPU).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/ssd.h"
+#include "ssd_launch.h"
+
+namespace {
+
+using ssd::Dims;
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Shape checks shared by every entry point.
+ssd_status check_problem(const ssd_problem* p, int64_t chunk_size) {
+  if (!p) return SSD_ERR_INVALID_ARGUMENT;
+  if (p->batch <= 0 || p->seqlen <= 0 || p->nheads <= 0 || p->headdim <= 0 || p->dstate <= 0 ||
+      p->ngroups <= 0)
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (p->nheads % p->ngroups != 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (p->io_dtype != SSD_DTYPE_F32 && p->io_dtype != SSD_DTYPE_BF16)
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (p->reserved != 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (chunk_size <= 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (!pow2(chunk_size) || chunk_size < 16 || chunk_size > 256) return SSD_ERR_UNSUPPORTED;
+  if (p->headdim % 16 || p->headdim > 256 || p->dstate % 16 || p->dstate > 256)
+    return SSD_ERR_UNSUPPORTED;
+  // Every tensor (inputs, outputs, workspace) must be indexable with 31-bit element counts
+  // inside one (batch) slice and 63-bit overall; keep whole tensors below 2^31 elements.
+  const int64_t nc = (p->seqlen + chunk_size - 1) / chunk_size;
+  const double big = static_cast<double>(kMaxIndex);
+  const double x_el = double(p->batch) * p->seqlen * p->nheads * p->headdim;
+  const double bc_el = double(p->batch) * p->seqlen * p->ngroups * p->dstate;
+  const double st_el = double(p->batch) * nc * p->nheads * p->headdim * p->dstate;
+  const double cb_el = double(p->batch) * nc * p->ngroups * chunk_size * chunk_size;
+  if (x_el > big || bc_el > big || st_el > big || cb_el > big) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+Dims make_dims(const ssd_problem* p, int64_t Q) {
+  Dims d;
+  d.Bt = (int)p->batch;
+  d.L = (int)p->seqlen;
+  d.H = (int)p->nheads;
+  d.P = (int)p->headdim;
+  d.N = (int)p->dstate;
+  d.G = (int)p->ngroups;
+  d.Q = (int)Q;
+  d.nc = (int)((p->seqlen + Q - 1) / Q);
+  return d;
+}
+
+int64_t io_bytes(const ssd_problem* p) { return p->io_dtype == SSD_DTYPE_BF16 ? 2 : 4; }
+
+struct Sizes {
+  int64_t x, dt, hd, bc, state;  // bytes of x/y, dt, A/D, B/C, initial/final state
+};
+
+Sizes sizes_of(const ssd_problem* p) {
+  Sizes s;
+  const int64_t e = io_bytes(p);
+  s.x = p->batch * p->seqlen * p->nheads * p->headdim * e;
+  s.dt = p->batch * p->seqlen * p->nheads * 4;
+  s.hd = p->nheads * 4;
+  s.bc = p->batch * p->seqlen * p->ngroups * p->dstate * e;
+  s.state = p->batch * p->nheads * p->headdim * p->dstate * 4;
+  return s;
+}
+
+ssd_status check_options(const ssd_options* o) {
+  if (!o) return SSD_OK;
+  if (o->variant < SSD_VARIANT_AUTO || o->variant > SSD_VARIANT_FUSED)
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (o->precision != SSD_PRECISION_AUTO && o->precision != SSD_PRECISION_FP16 &&
+      o->precision != SSD_PRECISION_FP32)
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (o->run_chunks < 0) return SSD_ERR_INVALID_ARGUMENT;
+  return SSD_OK;
+}
+
+ssd_status device_ready() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return SSD_ERR_NO_DEVICE;
+  return SSD_OK;
+}
+
+ssd_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return SSD_OK;
+  if (e == hipErrorOutOfMemory) return SSD_ERR_OUT_OF_MEMORY;
+  return SSD_ERR_HIP;
+}
+
+ssd_status check_forward_args(const ssd_problem* prob, const void* x, const float* dt,
+                              const float* A, const void* B, const void* C, const float* D,
+                              int64_t chunk_size, const float* h0, void* y, float* fin) {
+  ssd_status st = check_problem(prob, chunk_size);
+  if (st != SSD_OK) return st;
+  if (!x || !dt || !A || !B || !C || !D || !y) return SSD_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x, dt, A, B, C, D, h0, y, fin};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return SSD_ERR_INVALID_ARGUMENT;
+  const Sizes s = sizes_of(prob);
+  const Range ry = range_of(y, s.x);
+  const Range inputs[] = {range_of(x, s.x),  range_of(dt, s.dt), range_of(A, s.hd),
+                          range_of(B, s.bc), range_of(C, s.bc),  range_of(D, s.hd)};
+  for (const Range& r : inputs)
+    if (overlap(ry, r)) return SSD_ERR_INVALID_ARGUMENT;
+  if (h0 && overlap(ry, range_of(h0, s.state))) return SSD_ERR_INVALID_ARGUMENT;
+  if (fin) {
+    const Range rf = range_of(fin, s.state);
+    if (overlap(rf, ry)) return SSD_ERR_INVALID_ARGUMENT;
+    for (const Range& r : inputs)
+      if (overlap(rf, r)) return SSD_ERR_INVALID_ARGUMENT;
+    if (h0 && overlap(rf, range_of(h0, s.state))) return SSD_ERR_INVALID_ARGUMENT;
+  }
+  return SSD_OK;
+}
+
+struct Workspace {
+  float *Acs, *dtc, *CB, *states, *h_in;
+};
+
+void workspace_sizes(const Dims& d, int64_t out[5]) {
+  const int64_t aq = (int64_t)d.Bt * d.H * d.nc * d.Q * 4;
+  out[0] = aq;
+  out[1] = aq;
+  out[2] = (int64_t)d.Bt * d.nc * d.G * d.Q * d.Q * 4;
+  out[3] = (int64_t)d.Bt * d.nc * d.H * d.P * d.N * 4;
+  out[4] = out[3];
+}
+
+int resolve_precision(int io, int prec) {
+  if (io == ssd::kIoF32) return ssd::kPrecFp32;
+  return prec;  // auto, fp16 or fp32 for bf16 io
+}
+
+ssd_status run_unfused(const ssd_problem* prob, const Dims& d, int prec, const void* x,
+                       const float* dt, const float* A, const void* B, const void* C,
+                       const float* D, const float* h0, void* y, float* fin, hipStream_t s) {
+  int64_t sz[5];
+  workspace_sizes(d, sz);
+  int64_t total = 0, off[5];
+  for (int i = 0; i < 5; ++i) {
+    off[i] = total;
+    total += (sz[i] + 255) & ~int64_t(255);
+  }
+  void* base = nullptr;
+  hipError_t e = hipMallocAsync(&base, (size_t)total, s);
+  if (e != hipSuccess) return SSD_ERR_OUT_OF_MEMORY;
+  char* b = static_cast<char*>(base);
+  Workspace w{reinterpret_cast<float*>(b + off[0]), reinterpret_cast<float*>(b + off[1]),
+              reinterpret_cast<float*>(b + off[2]), reinterpret_cast<float*>(b + off[3]),
+              reinterpret_cast<float*>(b + off[4])};
+  const int io = prob->io_dtype;
+  e = ssd::launch_chunk_cumsum(d, dt, A, w.Acs, w.dtc, s);
+  if (e == hipSuccess) e = ssd::launch_bmm_chunk(d, io, B, C, w.CB, s);
+  if (e == hipSuccess) e = ssd::launch_chunk_state(d, io, prec, x, B, w.Acs, w.dtc, w.states, s);
+  if (e == hipSuccess) e = ssd::launch_state_passing(d, w.states, w.Acs, h0, w.h_in, fin, s);
+  if (e == hipSuccess)
+    e = ssd::launch_chunk_scan(d, io, prec, x, C, w.CB, w.Acs, w.dtc, w.h_in, D, y, s);
+  hipError_t ef = hipFreeAsync(base, s);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(ef);
+}
+
+// Runs of S chunks: enough (batch, head, run) blocks to fill the chip (about 1024), as few run
+// boundaries as that allows (each boundary costs one fp32 state write and read).
+void choose_runs(const Dims& d, int requested, int* S, int* nr) {
+  if (requested > 0) {
+    *S = requested < d.nc ? requested : d.nc;
+    *nr = (d.nc + *S - 1) / *S;
+    return;
+  }
+  const int units = d.Bt * d.H;
+  int want = (1024 + units - 1) / units;
+  if (want > d.nc) want = d.nc;
+  if (want < 1) want = 1;
+  *S = (d.nc + want - 1) / want;
+  *nr = (d.nc + *S - 1) / *S;
+}
+
+ssd_status run_fused(const Dims& d, int run_chunks, const void* x, const float* dt, const float* A,
+                     const void* B, const void* C, const float* D, const float* h0, void* y,
+                     float* fin, hipStream_t s) {
+  int S = 1, nr = 1;
+  choose_runs(d, run_chunks, &S, &nr);
+  const int64_t st_bytes = (int64_t)d.Bt * nr * d.H * d.P * d.N * 4;
+  const int64_t ld_bytes = (int64_t)d.Bt * d.H * nr * 4;
+  const int64_t a = (st_bytes + 255) & ~int64_t(255);
+  const int64_t total = 2 * a + ((ld_bytes + 255) & ~int64_t(255));
+  void* base = nullptr;
+  if (hipMallocAsync(&base, (size_t)total, s) != hipSuccess) return SSD_ERR_OUT_OF_MEMORY;
+  char* b = static_cast<char*>(base);
+  float* states = reinterpret_cast<float*>(b);
+  float* h_run = reinterpret_cast<float*>(b + a);
+  float* logdecay = reinterpret_cast<float*>(b + 2 * a);
+  hipError_t e = ssd::launch_run_state(d, x, B, dt, A, S * d.Q, nr, states, logdecay, s);
+  if (e == hipSuccess)
+    e = ssd::launch_chain_passing(d, nr, states, logdecay, nr, 1, h0, h_run, fin, s);
+  if (e == hipSuccess) e = ssd::launch_fused_scan(d, x, B, C, dt, A, D, h_run, y, S, nr, s);
+  hipError_t ef = hipFreeAsync(base, s);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(ef);
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                          const void* B, const void* C, const float* D, int64_t chunk_size,
+                          const float* initial_state, void* y, float* final_state, void* stream,
+                          const ssd_options* opts) {
+  ssd_status st = check_forward_args(prob, x, dt, A, B, C, D, chunk_size, initial_state, y,
+                                     final_state);
+  if (st != SSD_OK) return st;
+  st = check_options(opts);
+  if (st != SSD_OK) return st;
+  st = device_ready();
+  if (st != SSD_OK) return st;
+  const Dims d = make_dims(prob, chunk_size);
+  const int prec = resolve_precision(prob->io_dtype, opts ? opts->precision : 0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int variant = opts ? opts->variant : SSD_VARIANT_AUTO;
+  // The fused kernels cover bf16 io with fp16 operands (chained run states split hi + lo) for
+  // headdim 64 / dstate 64, 128 and headdim 128 / dstate 128, 256.
+  const bool fusable = prob->io_dtype == SSD_DTYPE_BF16 && prec != ssd::kPrecFp32 &&
+                       ssd::fused_supported(d);
+  if (variant == SSD_VARIANT_FUSED && !fusable) return SSD_ERR_UNSUPPORTED;
+  if (variant != SSD_VARIANT_UNFUSED && fusable)
+    return run_fused(d, opts ? opts->run_chunks : 0, x, dt, A, B, C, D, initial_state, y,
+                     final_state, s);
+  return run_unfused(prob, d, prec, x, dt, A, B, C, D, initial_state, y, final_state, s);
+}
+
+ssd_status ssd_forward(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                       const void* B, const void* C, const float* D, int64_t chunk_size,
+                       const float* initial_state, void* y, float* final_state, void* stream) {
+  return ssd_forward_ex(prob, x, dt, A, B, C, D, chunk_size, initial_state, y, final_state,
+                        stream, nullptr);
+}
+
+ssd_status ssd_workspace_sizes(const ssd_problem* prob, int64_t chunk_size, int64_t sizes[5]) {
+  ssd_status st = check_problem(prob, chunk_size);
+  if (st != SSD_OK) return st;
+  if (!sizes) return SSD_ERR_INVALID_ARGUMENT;
+  workspace_sizes(make_dims(prob, chunk_size), sizes);
+  return SSD_OK;
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_problem* prob, const float* dt, const float* A,
+                            int64_t chunk_size, float* Acs, float* dtc, void* stream) {
+  ssd_status st = check_problem(prob, chunk_size);
+  if (st != SSD_OK) return st;
+  if (!dt || !A || !Acs || !dtc) return SSD_ERR_INVALID_ARGUMENT;
+  const Dims d = make_dims(prob, chunk_size);
+  int64_t ws[5];
+  workspace_sizes(d, ws);
+  const Sizes s = sizes_of(prob);
+  const Range ra = range_of(Acs, ws[0]), rd = range_of(dtc, ws[1]);
+  if (overlap(ra, rd) || overlap(ra, range_of(dt, s.dt)) || overlap(rd, range_of(dt, s.dt)))
+    return SSD_ERR_INVALID_ARGUMENT;
+  st = device_ready();
+  if (st != SSD_OK) return st;
+  return from_hip(ssd::launch_chunk_cumsum(d, dt, A, Acs, dtc, static_cast<hipStream_t>(stream)));
+}
+
+ssd_status ssd_bmm_chunk(const ssd_problem* prob, const void* B, const void* C,
+                         int64_t chunk_size, float* CB, void* stream) {
+  ssd_status st = check_problem(prob, chunk_size);
+  if (st != SSD_OK) return st;
+  if (!B || !C || !CB || !aligned16(B) || !aligned16(C) || !aligned16(CB))
+    return SSD_ERR_INVALID_ARGUMENT;
+  st = device_ready();
+  if (st != SSD_OK) return st;
+  const Dims d = make_dims(prob, chunk_size);
+  return from_hip(
+      ssd::launch_bmm_chunk(d, prob->io_dtype, B, C, CB, static_cast<hipStream_t>(stream)));
+}
+
+ssd_status ssd_chunk_state(const ssd_problem* prob, const void* x, const void* B,
+                           const float* Acs, const float* dtc, int64_t chunk_size, float* states,
+                           void* stream, const ssd_options* opts) {
+  ssd_status st = check_problem(prob, chunk_size);
+  if (st != SSD_OK) return st;
+  st = check_options(opts);
+  if (st != SSD_OK) return st;
+  if (!x || !B || !Acs || !dtc || !states || !aligned16(x) || !aligned16(B) ||
+      !aligned16(states))
+    return SSD_ERR_INVALID_ARGUMENT;
+  st = device_ready();
+  if (st != SSD_OK) return st;
+  const Dims d = make_dims(prob, chunk_size);
+  const int prec = resolve_precision(prob->io_dtype, opts ? opts->precision : 0);
+  return from_hip(ssd::launch_chunk_state(d, prob->io_dtype, prec, x, B, Acs, dtc, states,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+ssd_status ssd_state_passing(const ssd_problem* prob, const float* states, const float* Acs,
+                             int64_t chunk_size, const float* initial_state, float* h_in,
+                             float* final_state, void* stream) {
+  ssd_status st = check_problem(prob, chunk_size);
+  if (st != SSD_OK) return st;
+  if (!states || !Acs || !h_in) return SSD_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {states, h_in, initial_state, final_state};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return SSD_ERR_INVALID_ARGUMENT;
+  const Dims d = make_dims(prob, chunk_size);
+  int64_t ws[5];
+  workspace_sizes(d, ws);
+  if (overlap(range_of(states, ws[3]), range_of(h_in, ws[4]))) return SSD_ERR_INVALID_ARGUMENT;
+  st = device_ready();
+  if (st != SSD_OK) return st;
+  return from_hip(ssd::launch_state_passing(d, states, Acs, initial_state, h_in, final_state,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+ssd_status ssd_chunk_scan(const ssd_problem* prob, const void* x, const void* C, const float* CB,
+                          const float* Acs, const float* dtc, const float* h_in, const float* D,
+                          int64_t chunk_size, void* y, void* stream, const ssd_options* opts) {
+  ssd_status st = check_problem(prob, chunk_size);
+  if (st != SSD_OK) return st;
+  st = check_options(opts);
+  if (st != SSD_OK) return st;
+  if (!x || !C || !CB || !Acs || !dtc || !h_in || !D || !y) return SSD_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x, C, CB, h_in, y};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return SSD_ERR_INVALID_ARGUMENT;
+  const Sizes s = sizes_of(prob);
+  if (overlap(range_of(y, s.x), range_of(x, s.x)) || overlap(range_of(y, s.x), range_of(C, s.bc)))
+    return SSD_ERR_INVALID_ARGUMENT;
+  st = device_ready();
+  if (st != SSD_OK) return st;
+  const Dims d = make_dims(prob, chunk_size);
+  const int prec = resolve_precision(prob->io_dtype, opts ? opts->precision : 0);
+  return from_hip(ssd::launch_chunk_scan(d, prob->io_dtype, prec, x, C, CB, Acs, dtc, h_in, D,
+                                         y, static_cast<hipStream_t>(stream)));
+}
+
+const char* ssd_status_string(ssd_status status) {
+  switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SSD_ERR_UNSUPPORTED: return "unsupported problem";
+    case SSD_ERR_NO_DEVICE: return "no HIP device";
+    case SSD_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case SSD_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int ssd_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Kernel launchers of libssd (library-internal). Every launcher assumes the host checks of
+// ssd_api.cpp have passed: positive sizes, nheads % ngroups == 0, chunk size a power of two in
+// [16, 256], headdim and dstate multiples of 16 up to 256, 16-byte aligned pointers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct Dims {
+  int Bt, L, H, P, N, G, Q, nc;
+};
+
+constexpr int kIoF32 = 0, kIoBf16 = 1;
+constexpr int kPrecAuto = 0, kPrecFp16 = 1, kPrecFp32 = 3;
+
+hipError_t launch_chunk_cumsum(const Dims& d, const float* dt, const float* A, float* Acs,
+                               float* dtc, hipStream_t s);
+hipError_t launch_bmm_chunk(const Dims& d, int io, const void* B, const void* C, float* CB,
+                            hipStream_t s);
+hipError_t launch_chunk_state(const Dims& d, int io, int prec, const void* x, const void* B,
+                              const float* Acs, const float* dtc, float* states, hipStream_t s);
+hipError_t launch_state_passing(const Dims& d, const float* states, const float* Acs,
+                                const float* h0, float* h_in, float* fin, hipStream_t s);
+hipError_t launch_chain_passing(const Dims& d, int nsteps, const float* states,
+                                const float* logdecay, int64_t ld_bh, int64_t ld_step,
+                                const float* h0, float* h_in, float* fin, hipStream_t s);
+hipError_t launch_chunk_scan(const Dims& d, int io, int prec, const void* x, const void* C,
+                             const float* CB, const float* Acs, const float* dtc,
+                             const float* h_in, const float* D, void* y, hipStream_t s);
+
+
+// fused path (bf16 io)
+bool fused_supported(const Dims& d);
+hipError_t launch_run_state(const Dims& d, const void* x, const void* B, const float* dt,
+                            const float* A, int run_len, int nr, float* states, float* logdecay,
+                            hipStream_t s);
+hipError_t launch_fused_scan(const Dims& d, const void* x, const void* B, const void* C,
+                             const float* dt, const float* A, const float* D,
+                             const float* h_run, void* y, int S, int nr, hipStream_t s);
+
+}  // namespace ssd

@@ -1,0 +1,235 @@
+"""Python binding of libssd (ctypes). Argument marshalling only: every step of the forward runs
+in the library's HIP kernels; torch provides device memory and the current stream.
+
+The library must have been built (``python -m mamba_ssd_chunked_cumsum_amd.build``); there is no
+fallback: a missing or unloadable library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB
+
+SSD_OK, SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED = 0, 1, 2
+SSD_ERR_NO_DEVICE, SSD_ERR_OUT_OF_MEMORY, SSD_ERR_HIP = 3, 4, 5
+
+VARIANTS = {"auto": 0, "unfused": 1, "fused": 2}
+PRECISIONS = {"auto": 0, "fp16": 1, "fp32": 3}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+# Symbols include/ssd.h declares.
+EXPORTS = ("ssd_forward", "ssd_forward_ex", "ssd_chunk_cumsum", "ssd_bmm_chunk",
+           "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_workspace_sizes",
+           "ssd_status_string", "ssd_version")
+
+
+class SSDProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class SSDOptions(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("precision", ctypes.c_int32),
+                ("run_chunks", ctypes.c_int32)]
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load():
+    """Load libssd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"libssd is not built ({LIB} missing): run "
+                           "`python -m mamba_ssd_chunked_cumsum_amd.build`")
+    lib = ctypes.CDLL(LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    P = ctypes.POINTER(SSDProblem)
+    O = ctypes.POINTER(SSDOptions)
+    sig = {
+        "ssd_forward": [P, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp],
+        "ssd_forward_ex": [P, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, O],
+        "ssd_chunk_cumsum": [P, vp, vp, i64, vp, vp, vp],
+        "ssd_bmm_chunk": [P, vp, vp, i64, vp, vp],
+        "ssd_chunk_state": [P, vp, vp, vp, vp, i64, vp, vp, O],
+        "ssd_state_passing": [P, vp, vp, i64, vp, vp, vp, vp],
+        "ssd_chunk_scan": [P, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, O],
+        "ssd_workspace_sizes": [P, i64, ctypes.POINTER(ctypes.c_int64)],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.ssd_status_string.argtypes = [ctypes.c_int]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().ssd_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load().ssd_version())
+
+
+def _check(status: int, where: str):
+    if status != SSD_OK:
+        raise SSDError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def problem(batch, seqlen, nheads, headdim, dstate, ngroups, io_dtype) -> SSDProblem:
+    return SSDProblem(batch, seqlen, nheads, headdim, dstate, ngroups, io_dtype, 0)
+
+
+def _problem_from(x, B) -> SSDProblem:
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [batch, seqlen, nheads, headdim], B/C [batch, seqlen, "
+                         "ngroups, dstate]")
+    if x.dtype not in DTYPES:
+        raise ValueError(f"unsupported io dtype {x.dtype}")
+    Bt, L, H, P = x.shape
+    return problem(Bt, L, H, P, B.shape[3], B.shape[2], DTYPES[x.dtype])
+
+
+def _require(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _options(variant, precision, run_chunks=0):
+    return SSDOptions(VARIANTS[variant], PRECISIONS[precision], int(run_chunks))
+
+
+def forward(x, dt, A, B, C, D, chunk_size, initial_state=None, *, variant="auto",
+            precision="auto", run_chunks=0, want_final=True, out=None, final_out=None):
+    """SSD chunked forward. Returns (y, final_state) (final_state None if not wanted)."""
+    dev = x.device
+    _require(x, "x", device=dev)
+    for n, t in (("B", B), ("C", C)):
+        _require(t, n, x.dtype, dev)
+    for n, t in (("dt", dt), ("A", A), ("D", D), ("initial_state", initial_state)):
+        _require(t, n, torch.float32, dev)
+    prob = _problem_from(x, B)
+    y = out if out is not None else torch.empty_like(x)
+    _require(y, "out", x.dtype, dev)
+    fin = None
+    if want_final:
+        fin = final_out if final_out is not None else torch.empty(
+            (x.shape[0], x.shape[2], x.shape[3], B.shape[3]), dtype=torch.float32, device=dev)
+        _require(fin, "final_out", torch.float32, dev)
+    opts = _options(variant, precision, run_chunks)
+    st = load().ssd_forward_ex(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                               _ptr(D), int(chunk_size), _ptr(initial_state), _ptr(y), _ptr(fin),
+                               _stream(x), ctypes.byref(opts))
+    _check(st, "ssd_forward_ex")
+    return y, fin
+
+
+# ---- stages of the unfused path ------------------------------------------------------------------
+
+def workspace_sizes(prob: SSDProblem, chunk_size: int):
+    out = (ctypes.c_int64 * 5)()
+    _check(load().ssd_workspace_sizes(ctypes.byref(prob), int(chunk_size), out),
+           "ssd_workspace_sizes")
+    return list(out)
+
+
+def _nc(L, Q):
+    return -(-L // Q)
+
+
+def chunk_cumsum(dt, A, chunk_size, *, headdim=16, dstate=16, ngroups=1):
+    Bt, L, H = dt.shape
+    _require(dt, "dt", torch.float32)
+    _require(A, "A", torch.float32, dt.device)
+    prob = problem(Bt, L, H, headdim, dstate, ngroups, 0)
+    nc = _nc(L, chunk_size)
+    Acs = torch.empty((Bt, H, nc, chunk_size), dtype=torch.float32, device=dt.device)
+    dtc = torch.empty_like(Acs)
+    _check(load().ssd_chunk_cumsum(ctypes.byref(prob), _ptr(dt), _ptr(A), int(chunk_size),
+                                   _ptr(Acs), _ptr(dtc), _stream(dt)), "ssd_chunk_cumsum")
+    return Acs, dtc
+
+
+def bmm_chunk(B, C, chunk_size, *, nheads=None, headdim=16):
+    Bt, L, G, N = B.shape
+    _require(B, "B")
+    _require(C, "C", B.dtype, B.device)
+    prob = problem(Bt, L, nheads or G, headdim, N, G, DTYPES[B.dtype])
+    nc = _nc(L, chunk_size)
+    CB = torch.zeros((Bt, nc, G, chunk_size, chunk_size), dtype=torch.float32, device=B.device)
+    _check(load().ssd_bmm_chunk(ctypes.byref(prob), _ptr(B), _ptr(C), int(chunk_size), _ptr(CB),
+                                _stream(B)), "ssd_bmm_chunk")
+    return CB
+
+
+def chunk_state(x, B, Acs, dtc, chunk_size, *, precision="auto"):
+    _require(x, "x")
+    _require(B, "B", x.dtype, x.device)
+    prob = _problem_from(x, B)
+    Bt, L, H, P = x.shape
+    N = B.shape[3]
+    st = torch.empty((Bt, _nc(L, chunk_size), H, P, N), dtype=torch.float32, device=x.device)
+    opts = _options("unfused", precision)
+    _check(load().ssd_chunk_state(ctypes.byref(prob), _ptr(x), _ptr(B), _ptr(Acs), _ptr(dtc),
+                                  int(chunk_size), _ptr(st), _stream(x), ctypes.byref(opts)),
+           "ssd_chunk_state")
+    return st
+
+
+def state_passing(states, Acs, chunk_size, initial_state=None, *, seqlen, ngroups=1,
+                  want_final=True):
+    Bt, nc, H, P, N = states.shape
+    prob = problem(Bt, seqlen, H, P, N, ngroups, 0)
+    h_in = torch.empty_like(states)
+    fin = torch.empty((Bt, H, P, N), dtype=torch.float32, device=states.device) \
+        if want_final else None
+    _check(load().ssd_state_passing(ctypes.byref(prob), _ptr(states), _ptr(Acs), int(chunk_size),
+                                    _ptr(initial_state), _ptr(h_in), _ptr(fin),
+                                    _stream(states)), "ssd_state_passing")
+    return h_in, fin
+
+
+def chunk_scan(x, C, CB, Acs, dtc, h_in, D, chunk_size, *, precision="auto"):
+    _require(x, "x")
+    _require(C, "C", x.dtype, x.device)
+    prob = _problem_from(x, C)
+    y = torch.empty_like(x)
+    opts = _options("unfused", precision)
+    _check(load().ssd_chunk_scan(ctypes.byref(prob), _ptr(x), _ptr(C), _ptr(CB), _ptr(Acs),
+                                 _ptr(dtc), _ptr(h_in), _ptr(D), int(chunk_size), _ptr(y),
+                                 _stream(x), ctypes.byref(opts)), "ssd_chunk_scan")
+    return y

@@ -1,0 +1,175 @@
+"""Each unfused stage on the GPU against the float64 chunked oracle's intermediates.
+
+A stage under test gets its inputs from the oracle where they are intermediates (so one stage's
+error does not leak into the next); its output is compared with the oracle's value for the same
+intermediate.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from mamba_ssd_chunked_cumsum_amd import libssd, synth
+from oracle import ssd_chunked
+
+from gpu_util import DEV, note, to_device
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    # (name, shape) -- ragged tails, several chunk sizes, groups, both io dtypes
+    ("f32_q64", synth.SSDShape("t", 1, 256, 2, 16, 16, 1, 64, io="f32")),
+    ("f32_ragged_q32", synth.SSDShape("t", 2, 77, 4, 32, 32, 2, 32, io="f32", init_state=True)),
+    ("bf16_q64", synth.SSDShape("t", 2, 200, 4, 64, 128, 1, 64)),
+    ("bf16_q16_g2", synth.SSDShape("t", 1, 90, 4, 32, 48, 2, 16)),
+    ("bf16_q256_ragged", synth.SSDShape("t", 1, 300, 3, 64, 64, 1, 256, init_state=True)),
+    ("bf16_q128_wide", synth.SSDShape("t", 1, 160, 2, 128, 256, 2, 128)),
+]
+
+
+def _inputs(shape, seed=31):
+    inp = synth.make_inputs(shape, seed=seed)
+    y, f, it = ssd_chunked(**inp, chunk_size=shape.chunk_size)
+    return inp, y, f, it
+
+
+def _valid_mask(shape):
+    """[nc, Q] mask of positions inside the sequence."""
+    nc, Q = shape.nchunks, shape.chunk_size
+    pos = np.arange(nc)[:, None] * Q + np.arange(Q)[None, :]
+    return pos < shape.seqlen
+
+
+@pytest.mark.parametrize("name,shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_chunk_cumsum(name, shape):
+    inp, _, _, it = _inputs(shape)
+    d = to_device(inp, shape.io)
+    note(f"chunk_cumsum {name}")
+    Acs, dtc = libssd.chunk_cumsum(d["dt"], d["A"], shape.chunk_size)
+    torch.cuda.synchronize()
+    Acs, dtc = Acs.cpu().numpy(), dtc.cpu().numpy()
+    ref = it["Acs"]
+    m = _valid_mask(shape)[None, None]
+    m = np.broadcast_to(m, ref.shape)
+    err = np.abs(Acs - ref)[m] / (1.0 + np.abs(ref)[m])
+    assert err.max() <= 2e-5, err.max()
+    # past a ragged end the cumulative sum repeats its last value
+    qlast = shape.seqlen - (shape.nchunks - 1) * shape.chunk_size
+    tail = Acs[:, :, -1, qlast:]
+    assert np.array_equal(tail, np.broadcast_to(Acs[:, :, -1, qlast - 1:qlast], tail.shape))
+    # dtc is dt regrouped per (head, chunk), exactly, with zeros past the end
+    Q = shape.chunk_size
+    pad = np.zeros((shape.batch, shape.nchunks * Q, shape.nheads), np.float32)
+    pad[:, : shape.seqlen] = inp["dt"]
+    want = pad.reshape(shape.batch, shape.nchunks, Q, shape.nheads).transpose(0, 3, 1, 2)
+    assert np.array_equal(dtc, want)
+
+
+@pytest.mark.parametrize("name,shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_bmm_chunk(name, shape):
+    inp, _, _, it = _inputs(shape)
+    d = to_device(inp, shape.io)
+    note(f"bmm_chunk {name}")
+    CB = libssd.bmm_chunk(d["B"], d["C"], shape.chunk_size, nheads=shape.nheads,
+                          headdim=shape.headdim)
+    torch.cuda.synchronize()
+    CB = CB.cpu().numpy().astype(np.float64)
+    ref = it["CB"]
+    Q = shape.chunk_size
+    tri = np.tril(np.ones((Q, Q), bool))
+    m = _valid_mask(shape)
+    # exact products, fp32 accumulation of N terms: |error| <= N 2^-24 sum_n |C_n B_n|
+    Bp = np.abs(np.pad(inp["B"], ((0, 0), (0, shape.nchunks * Q - shape.seqlen), (0, 0), (0, 0))))
+    Cp = np.abs(np.pad(inp["C"], ((0, 0), (0, shape.nchunks * Q - shape.seqlen), (0, 0), (0, 0))))
+    for c in range(shape.nchunks):
+        mm = tri & m[c][:, None] & m[c][None, :]
+        absdot = np.einsum("bign,bjgn->bgij", Cp[:, c * Q:(c + 1) * Q].astype(np.float64),
+                           Bp[:, c * Q:(c + 1) * Q].astype(np.float64))
+        diff = np.abs(CB[:, c][..., mm] - ref[:, c][..., mm])
+        bound = shape.dstate * 2.0 ** -24 * absdot[..., mm]
+        assert np.all(diff <= bound), (diff - bound).max()
+
+
+@pytest.mark.parametrize("precision,op_unit", [("auto", 2.0 ** -22), ("fp16", 2.0 ** -11),
+                                                ("fp32", 0.0)])
+@pytest.mark.parametrize("name,shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_chunk_state(name, shape, precision, op_unit):
+    if shape.io == "f32" and precision != "auto":
+        pytest.skip("fp32 io always runs fp32")
+    inp, _, _, it = _inputs(shape)
+    d = to_device(inp, shape.io)
+    Acs = torch.from_numpy(it["Acs"].astype(np.float32)).to(DEV)
+    Q = shape.chunk_size
+    pad = np.zeros((shape.batch, shape.nchunks * Q, shape.nheads), np.float32)
+    pad[:, : shape.seqlen] = inp["dt"]
+    dtc = torch.from_numpy(np.ascontiguousarray(
+        pad.reshape(shape.batch, shape.nchunks, Q, shape.nheads).transpose(0, 3, 1, 2))).to(DEV)
+    note(f"chunk_state {name} {precision}")
+    st = libssd.chunk_state(d["x"], d["B"], Acs, dtc, Q, precision=precision)
+    torch.cuda.synchronize()
+    st = st.cpu().numpy().astype(np.float64)
+    ref = it["states"]
+    # Elementwise bound from the arithmetic: each term w_j x_j B_j carries the rounding of the
+    # state operand (op_unit: fp16 2^-11, fp16 hi+lo 2^-22, fp32 exact), the error of its weight
+    # exp(Acs_last - Acs_j) formed from fp32 cumulative sums (two roundings of |Acs| <= amax,
+    # plus the exponential's own few ulps), and fp32 accumulation over the chunk (Q 2^-24).
+    amax = np.abs(it["Acs"]).max()
+    eps = op_unit + (Q + 8 + 4 * amax) * 2.0 ** -24
+    L, Lp = shape.seqlen, shape.nchunks * Q
+    xp = np.pad(inp["x"], ((0, 0), (0, Lp - L), (0, 0), (0, 0))).astype(np.float64)
+    Bp = np.pad(inp["B"], ((0, 0), (0, Lp - L), (0, 0), (0, 0))).astype(np.float64)
+    acs = it["Acs"]                                              # [Bt, H, nc, Q]
+    w = np.exp(acs[..., -1:] - acs) * dtc.cpu().numpy()          # [Bt, H, nc, Q]
+    grp = np.arange(shape.nheads) // (shape.nheads // shape.ngroups)
+    xr = np.abs(xp.reshape(shape.batch, shape.nchunks, Q, shape.nheads, shape.headdim))
+    br = np.abs(Bp.reshape(shape.batch, shape.nchunks, Q, shape.ngroups, shape.dstate))[:, :, :, grp]
+    absdot = np.einsum("bhcj,bcjhp,bcjhn->bchpn", w, xr, br)
+    bound = eps * absdot + 1e-30
+    excess = np.abs(st - ref) - bound
+    assert np.all(excess <= 0), (excess.max(), eps)
+
+
+@pytest.mark.parametrize("name,shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_state_passing(name, shape):
+    inp, _, f, it = _inputs(shape)
+    states = torch.from_numpy(it["states"].astype(np.float32)).to(DEV)
+    Acs = torch.from_numpy(it["Acs"].astype(np.float32)).to(DEV)
+    h0 = None if inp["initial_state"] is None else torch.from_numpy(inp["initial_state"]).to(DEV)
+    note(f"state_passing {name}")
+    h_in, fin = libssd.state_passing(states, Acs, shape.chunk_size, h0, seqlen=shape.seqlen,
+                                     ngroups=shape.ngroups)
+    torch.cuda.synchronize()
+    ref = it["h_in"]
+    h_in = h_in.cpu().numpy().astype(np.float64)
+    scale = np.sqrt(np.mean(ref ** 2)) + 1e-30
+    assert np.abs(h_in - ref[:, :-1]).max() / scale <= 1e-5
+    assert np.abs(fin.cpu().numpy() - f).max() / scale <= 1e-5
+    # without a final_state buffer nothing else changes
+    h2, none = libssd.state_passing(states, Acs, shape.chunk_size, h0, seqlen=shape.seqlen,
+                                    ngroups=shape.ngroups, want_final=False)
+    torch.cuda.synchronize()
+    assert none is None and np.array_equal(h2.cpu().numpy(), h_in.astype(np.float32))
+
+
+@pytest.mark.parametrize("precision", ["auto", "fp32"])
+@pytest.mark.parametrize("name,shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_chunk_scan(name, shape, precision):
+    from oracle import metrics
+    if shape.io == "f32" and precision != "auto":
+        pytest.skip("fp32 io always runs fp32")
+    inp, y_ref, _, it = _inputs(shape)
+    d = to_device(inp, shape.io)
+    Q = shape.chunk_size
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+    pad = np.zeros((shape.batch, shape.nchunks * Q, shape.nheads), np.float32)
+    pad[:, : shape.seqlen] = inp["dt"]
+    dtc = pad.reshape(shape.batch, shape.nchunks, Q, shape.nheads).transpose(0, 3, 1, 2)
+    note(f"chunk_scan {name} {precision}")
+    y = libssd.chunk_scan(d["x"], d["C"], f32(it["CB"]), f32(it["Acs"]), f32(dtc),
+                          f32(it["h_in"][:, :-1]), d["D"], Q, precision=precision)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy().astype(np.float64)
+    if shape.io == "f32":
+        assert metrics.rel_floored(y, y_ref) <= 1e-4
+    else:
+        assert metrics.rms_r1(y, y_ref) <= (2e-2 if precision == "auto" else 1e-3)
