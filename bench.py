@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSD chunked forward (libssd) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config 2] [--variant auto]
+
+One step is one full forward (every kernel of the path) over the workload's synthetic inputs,
+which are resident in HBM before timing starts. Before every step a 2 GiB buffer is written so no
+input is left in the 256 MB last-level cache or the L2s (cold-cache timing); each forward, and each
+kernel inside it, is timed with HIP events on the stream it runs on. The timed loop is bracketed
+by device synchronisations.
+
+Prints ONE JSON line: tokens/s, ms per step, the roofline of the dominant kernel (algorithmic
+bytes per launch over its measured duration, against MI355X's 8 TB/s), the whole forward's
+roofline fraction, and the CPU oracle's throughput on the same workload (with the parity of the
+GPU result on the units the oracle computed).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2516.6  # dense fp16/bf16 matrix cores
+FP32_PEAK_TFLOPS = 157.3
+METRIC = "SSD fwd tokens/s + % of MI355X HBM/MFMA roofline, L=8K H=80 P=64 N=128"
+
+
+def algorithmic(shape, with_initial_state: bool):
+    """Algorithmic bytes and flops of one forward (what the method must move and compute).
+
+    bytes/token = H P (s_x + s_y) + 2 G N s_io + 4 H  (+ states in/out: 4 H P N per batch)
+    flops/token = G (Q+1) N [C B^T, causal] + H (Q+1) P [masked intra product]
+                  + 2 H P N [chunk state] + 2 H P N [inter readout] + 2 H P N / Q [passing]
+    Returns per-token stream bytes, whole-forward bytes, and flops.
+    """
+    s_io = 2 if shape.io == "bf16" else 4
+    H, P, N, G, Q = shape.nheads, shape.headdim, shape.dstate, shape.ngroups, shape.chunk_size
+    tokens = shape.batch * shape.seqlen
+    stream_per_token = H * P * 2 * s_io + 2 * G * N * s_io + 4 * H
+    states = shape.batch * H * P * N * 4 * (2 if with_initial_state else 1)
+    flops_per_token = G * (Q + 1) * N + H * (Q + 1) * P + 4 * H * P * N + 2 * H * P * N / Q
+    return {
+        "stream_bytes_per_token": stream_per_token,
+        "bytes": stream_per_token * tokens + states,
+        "flops": flops_per_token * tokens,
+        "tokens": tokens,
+    }
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mamba_ssd_chunked_cumsum_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, launches_bytes: float):
+    """HBM bytes per launch from committed counter runs, if they were taken on these sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, shape, y_gpu, f_gpu, max_seconds: float):
+    """The C oracle (float64 recurrence, OpenMP over heads) timed on the host cores, on the whole
+    workload or, when that would exceed max_seconds, on a spread sample of (batch, head) units.
+    Also scores the GPU output on the units computed."""
+    import numpy as np
+    from oracle import metrics, native
+
+    n_units = shape.batch * shape.nheads
+    per_unit_probe = max(1, min(n_units, 4))
+    probe = list(range(per_unit_probe))
+    t = time.perf_counter()
+    native.forward(**inp, units=probe)
+    t_probe = (time.perf_counter() - t) / per_unit_probe
+    k = n_units if t_probe * n_units <= max_seconds else max(8, int(max_seconds / t_probe))
+    k = min(k, n_units)
+    units = list(range(n_units)) if k == n_units else sorted(
+        set(int(round(i * (n_units - 1) / (k - 1))) for i in range(k)))
+    threads = native.max_threads()
+    t = time.perf_counter()
+    y_ref, f_ref = native.forward(**inp, units=units)
+    elapsed = time.perf_counter() - t
+    tokens_per_s = shape.seqlen * len(units) / shape.nheads / elapsed
+    bs = [u // shape.nheads for u in units]
+    hs = [u % shape.nheads for u in units]
+    yg = np.stack([y_gpu[b, :, h] for b, h in zip(bs, hs)])
+    yr = np.stack([y_ref[b, :, h] for b, h in zip(bs, hs)])
+    fg = np.stack([f_gpu[b, h] for b, h in zip(bs, hs)])
+    fr = np.stack([f_ref[b, h] for b, h in zip(bs, hs)])
+    rep = metrics.parity_report(yg, yr, fg, fr, shape.io)
+    sample = ("whole workload" if len(units) == n_units else
+              f"{len(units)} of {n_units} (batch, head) units, all {shape.seqlen} tokens each")
+    return {
+        "value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": f"{sample}; float64 C recurrence, {elapsed:.2f} s",
+    }, rep
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload index (0..4)")
+    ap.add_argument("--variant", default="auto", choices=["auto", "fused", "unfused"])
+    ap.add_argument("--run-chunks", type=int, default=0)
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush before steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=30.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (a known-size kernel for "
+                         "scaling hardware byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: libssd runs the SSD forward on one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mamba_ssd_chunked_cumsum_amd as ssd
+    from mamba_ssd_chunked_cumsum_amd import libssd, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    shape = synth.CONFIGS[args.config]
+    inp = synth.make_inputs(shape, cfg_index=args.config)
+    io = torch.bfloat16 if shape.io == "bf16" else torch.float32
+    d = {}
+    for k, v in inp.items():
+        if v is None:
+            d[k] = None
+            continue
+        t = torch.from_numpy(v).to(dev)
+        d[k] = t.to(io) if k in ("x", "B", "C") else t
+    y = torch.empty_like(d["x"])
+    fin = torch.empty((shape.batch, shape.nheads, shape.headdim, shape.dstate),
+                      dtype=torch.float32, device=dev)
+
+    def step(timer=None):
+        ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], shape.chunk_size,
+                    d["initial_state"], variant=args.variant, run_chunks=args.run_chunks,
+                    out=y, final_out=fin, timer=timer)
+
+    # correctness run first, then the CPU oracle leg on the same inputs
+    step()
+    torch.cuda.synchronize()
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        y64 = y.float().cpu().numpy().astype(np.float64)
+        f64 = fin.cpu().numpy().astype(np.float64)
+        cpu, parity = cpu_baseline(inp, shape, y64, f64, args.cpu_seconds)
+        del y64, f64
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        step()
+    flush = None if args.no_flush else torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    timers = [libssd.KernelTimer() for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(k & 0xFF)
+        starts[k].record()
+        step(timers[k])
+        ends[k].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+
+    step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    per_kernel = {}
+    for tm in timers:
+        for name, ms in tm.times_ms().items():
+            per_kernel.setdefault(name, []).append(ms)
+    kernel_ms = {k: float(np.mean(v)) for k, v in per_kernel.items()}
+    ms_per_step = float(np.mean(step_ms))
+    alg = algorithmic(shape, d["initial_state"] is not None)
+    tokens = alg["tokens"]
+    value = tokens / (ms_per_step / 1e3)
+
+    dominant = max(kernel_ms, key=kernel_ms.get)
+    # Algorithmic bytes of the dominant kernel: the fused scan (or the unfused chunk scan) streams
+    # every input token's x, B, C, dt and writes y -- the per-token stream figure times the
+    # tokens of one launch. Other kernels are charged the same figure only if they dominate.
+    kb = alg["stream_bytes_per_token"] * tokens
+    achieved = kb / (kernel_ms[dominant] / 1e3) / 1e9
+    traffic = measured_traffic(dominant, shape.name, kb)
+    t_roof = max(alg["bytes"] / (HBM_PEAK_GBS * 1e9),
+                 alg["flops"] / ((MFMA_F16_PEAK_TFLOPS if shape.io == "bf16"
+                                  else FP32_PEAK_TFLOPS) * 1e12))
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if shape.io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": shape.name, "batch": shape.batch, "seqlen": shape.seqlen,
+            "nheads": shape.nheads, "headdim": shape.headdim, "dstate": shape.dstate,
+            "ngroups": shape.ngroups, "chunk_size": shape.chunk_size,
+            "variant": args.variant, "cache_flush": flush is not None,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,
+            "kernel_ms": kernel_ms[dominant],
+        },
+        "forward_roofline": {
+            "bytes": alg["bytes"], "flops": alg["flops"], "t_roofline_us": t_roof * 1e6,
+            "frac": t_roof / (ms_per_step / 1e3),
+            "gbs": alg["bytes"] / (ms_per_step / 1e3) / 1e9,
+            "tflops": alg["flops"] / (ms_per_step / 1e3) / 1e12,
+        },
+        "kernel_ms": kernel_ms,
+        "step_ms_min": float(np.min(step_ms)),
+        "wall_s_timed_loop": wall,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -89,6 +89,14 @@ typedef struct {
     int32_t precision;  /* ssd_precision */
     int32_t run_chunks; /* fused variant: chunks per run (state carried on chip through a run);
                            0 = chosen from the problem size; must be >= 0 */
+    int32_t n_events;   /* capacity of `events`; 0 = no timing events */
+    void** events;      /* optional hipEvent_t[n_events], created by the caller: events[0] is
+                           recorded on `stream` before the first kernel and events[k] after the
+                           k-th kernel, so the caller can time each kernel. Needs n_events >=
+                           kernels + 1 (6 covers every variant), else SSD_ERR_INVALID_ARGUMENT. */
+    int32_t* n_kernels; /* optional out: number of kernels the call launched (fused 3: run
+                           states, state passing over runs, fused scan; unfused 5: cumsum,
+                           C B^T, chunk states, state passing, chunk scan) */
 } ssd_options;
 
 /* Full forward. initial_state may be NULL (zeros); final_state may be NULL (not written).

@@ -95,6 +95,8 @@ ssd_status check_options(const ssd_options* o) {
       o->precision != SSD_PRECISION_FP32)
     return SSD_ERR_INVALID_ARGUMENT;
   if (o->run_chunks < 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (o->n_events < 0 || (o->n_events > 0 && !o->events)) return SSD_ERR_INVALID_ARGUMENT;
+  if (o->n_events > 0 && o->n_events < 6) return SSD_ERR_INVALID_ARGUMENT;
   return SSD_OK;
 }
 
@@ -136,6 +138,16 @@ ssd_status check_forward_args(const ssd_problem* prob, const void* x, const floa
   return SSD_OK;
 }
 
+// Optional timing events around each kernel (caller-owned hipEvent_t's).
+struct Timer {
+  void** ev = nullptr;
+  int n = 0, k = 0;
+  hipError_t mark(hipStream_t s) {
+    if (!ev || k >= n) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(ev[k++]), s);
+  }
+};
+
 struct Workspace {
   float *Acs, *dtc, *CB, *states, *h_in;
 };
@@ -156,7 +168,8 @@ int resolve_precision(int io, int prec) {
 
 ssd_status run_unfused(const ssd_problem* prob, const Dims& d, int prec, const void* x,
                        const float* dt, const float* A, const void* B, const void* C,
-                       const float* D, const float* h0, void* y, float* fin, hipStream_t s) {
+                       const float* D, const float* h0, void* y, float* fin, hipStream_t s,
+                       Timer& t) {
   int64_t sz[5];
   workspace_sizes(d, sz);
   int64_t total = 0, off[5];
@@ -172,12 +185,18 @@ ssd_status run_unfused(const ssd_problem* prob, const Dims& d, int prec, const v
               reinterpret_cast<float*>(b + off[2]), reinterpret_cast<float*>(b + off[3]),
               reinterpret_cast<float*>(b + off[4])};
   const int io = prob->io_dtype;
-  e = ssd::launch_chunk_cumsum(d, dt, A, w.Acs, w.dtc, s);
+  e = t.mark(s);
+  if (e == hipSuccess) e = ssd::launch_chunk_cumsum(d, dt, A, w.Acs, w.dtc, s);
+  if (e == hipSuccess) e = t.mark(s);
   if (e == hipSuccess) e = ssd::launch_bmm_chunk(d, io, B, C, w.CB, s);
+  if (e == hipSuccess) e = t.mark(s);
   if (e == hipSuccess) e = ssd::launch_chunk_state(d, io, prec, x, B, w.Acs, w.dtc, w.states, s);
+  if (e == hipSuccess) e = t.mark(s);
   if (e == hipSuccess) e = ssd::launch_state_passing(d, w.states, w.Acs, h0, w.h_in, fin, s);
+  if (e == hipSuccess) e = t.mark(s);
   if (e == hipSuccess)
     e = ssd::launch_chunk_scan(d, io, prec, x, C, w.CB, w.Acs, w.dtc, w.h_in, D, y, s);
+  if (e == hipSuccess) e = t.mark(s);
   hipError_t ef = hipFreeAsync(base, s);
   if (e != hipSuccess) return from_hip(e);
   return from_hip(ef);
@@ -201,7 +220,7 @@ void choose_runs(const Dims& d, int requested, int* S, int* nr) {
 
 ssd_status run_fused(const Dims& d, int run_chunks, const void* x, const float* dt, const float* A,
                      const void* B, const void* C, const float* D, const float* h0, void* y,
-                     float* fin, hipStream_t s) {
+                     float* fin, hipStream_t s, Timer& t) {
   int S = 1, nr = 1;
   choose_runs(d, run_chunks, &S, &nr);
   const int64_t st_bytes = (int64_t)d.Bt * nr * d.H * d.P * d.N * 4;
@@ -214,10 +233,15 @@ ssd_status run_fused(const Dims& d, int run_chunks, const void* x, const float* 
   float* states = reinterpret_cast<float*>(b);
   float* h_run = reinterpret_cast<float*>(b + a);
   float* logdecay = reinterpret_cast<float*>(b + 2 * a);
-  hipError_t e = ssd::launch_run_state(d, x, B, dt, A, S * d.Q, nr, states, logdecay, s);
+  hipError_t e = t.mark(s);
+  if (e == hipSuccess)
+    e = ssd::launch_run_state(d, x, B, dt, A, S * d.Q, nr, states, logdecay, s);
+  if (e == hipSuccess) e = t.mark(s);
   if (e == hipSuccess)
     e = ssd::launch_chain_passing(d, nr, states, logdecay, nr, 1, h0, h_run, fin, s);
+  if (e == hipSuccess) e = t.mark(s);
   if (e == hipSuccess) e = ssd::launch_fused_scan(d, x, B, C, dt, A, D, h_run, y, S, nr, s);
+  if (e == hipSuccess) e = t.mark(s);
   hipError_t ef = hipFreeAsync(base, s);
   if (e != hipSuccess) return from_hip(e);
   return from_hip(ef);
@@ -247,10 +271,17 @@ ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* d
   const bool fusable = prob->io_dtype == SSD_DTYPE_BF16 && prec != ssd::kPrecFp32 &&
                        ssd::fused_supported(d);
   if (variant == SSD_VARIANT_FUSED && !fusable) return SSD_ERR_UNSUPPORTED;
-  if (variant != SSD_VARIANT_UNFUSED && fusable)
+  Timer t;
+  if (opts && opts->n_events > 0) {
+    t.ev = opts->events;
+    t.n = opts->n_events;
+  }
+  const bool fused = variant != SSD_VARIANT_UNFUSED && fusable;
+  if (opts && opts->n_kernels) *opts->n_kernels = fused ? 3 : 5;
+  if (fused)
     return run_fused(d, opts ? opts->run_chunks : 0, x, dt, A, B, C, D, initial_state, y,
-                     final_state, s);
-  return run_unfused(prob, d, prec, x, dt, A, B, C, D, initial_state, y, final_state, s);
+                     final_state, s, t);
+  return run_unfused(prob, d, prec, x, dt, A, B, C, D, initial_state, y, final_state, s, t);
 }
 
 ssd_status ssd_forward(const ssd_problem* prob, const void* x, const float* dt, const float* A,

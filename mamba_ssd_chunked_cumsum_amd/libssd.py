@@ -36,7 +36,14 @@ class SSDProblem(ctypes.Structure):
 
 class SSDOptions(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("precision", ctypes.c_int32),
-                ("run_chunks", ctypes.c_int32)]
+                ("run_chunks", ctypes.c_int32), ("n_events", ctypes.c_int32),
+                ("events", ctypes.POINTER(ctypes.c_void_p)),
+                ("n_kernels", ctypes.POINTER(ctypes.c_int32))]
+
+
+# kernel names, in launch order, for each number of kernels a call reports
+KERNELS = {3: ("run_state", "state_passing", "fused_scan"),
+           5: ("chunk_cumsum", "bmm_chunk", "chunk_state", "state_passing", "chunk_scan")}
 
 
 class SSDError(RuntimeError):
@@ -130,11 +137,33 @@ def _require(t, name, dtype=None, device=None):
 
 
 def _options(variant, precision, run_chunks=0):
-    return SSDOptions(VARIANTS[variant], PRECISIONS[precision], int(run_chunks))
+    return SSDOptions(VARIANTS[variant], PRECISIONS[precision], int(run_chunks), 0, None, None)
+
+
+class KernelTimer:
+    """Six torch.cuda.Event objects handed to the library, which records them on the call's
+    stream around each kernel it launches. After synchronising, `times_ms()` gives each kernel's
+    elapsed time."""
+
+    def __init__(self):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        self._arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in self.events])
+        self.n_kernels = ctypes.c_int32(0)
+
+    def attach(self, opts: SSDOptions):
+        opts.n_events = 6
+        opts.events = ctypes.cast(self._arr, ctypes.POINTER(ctypes.c_void_p))
+        opts.n_kernels = ctypes.pointer(self.n_kernels)
+
+    def times_ms(self) -> dict:
+        n = self.n_kernels.value
+        names = KERNELS[n]
+        return {names[k]: self.events[k].elapsed_time(self.events[k + 1]) for k in range(n)}
 
 
 def forward(x, dt, A, B, C, D, chunk_size, initial_state=None, *, variant="auto",
-            precision="auto", run_chunks=0, want_final=True, out=None, final_out=None):
+            precision="auto", run_chunks=0, want_final=True, out=None, final_out=None,
+            timer: KernelTimer | None = None):
     """SSD chunked forward. Returns (y, final_state) (final_state None if not wanted)."""
     dev = x.device
     _require(x, "x", device=dev)
@@ -151,6 +180,8 @@ def forward(x, dt, A, B, C, D, chunk_size, initial_state=None, *, variant="auto"
             (x.shape[0], x.shape[2], x.shape[3], B.shape[3]), dtype=torch.float32, device=dev)
         _require(fin, "final_out", torch.float32, dev)
     opts = _options(variant, precision, run_chunks)
+    if timer is not None:
+        timer.attach(opts)
     st = load().ssd_forward_ex(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                                _ptr(D), int(chunk_size), _ptr(initial_state), _ptr(y), _ptr(fin),
                                _stream(x), ctypes.byref(opts))

@@ -45,7 +45,7 @@ def test_version_and_status_strings():
 
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(libssd.SSDProblem) == 6 * 8 + 2 * 4
-    assert ctypes.sizeof(libssd.SSDOptions) == 12
+    assert ctypes.sizeof(libssd.SSDOptions) == 32
 
 
 # placeholder device addresses: 16-byte aligned, far apart, never dereferenced
@@ -169,13 +169,24 @@ def test_adjacent_buffers_are_not_aliasing():
 @pytest.mark.parametrize("variant,precision,status", [(0, 0, 3), (1, 1, 3), (1, 3, 3), (3, 0, 1),
                                                       (-1, 0, 1), (0, 2, 1), (0, 9, 1)])
 def test_options(variant, precision, status):
-    assert call_forward(good_problem(), opts=libssd.SSDOptions(variant, precision, 0)) == status
+    assert call_forward(good_problem(),
+                        opts=libssd.SSDOptions(variant, precision, 0, 0, None, None)) == status
 
 
 @no_gpu
 def test_negative_run_chunks_rejected():
-    assert call_forward(good_problem(), opts=libssd.SSDOptions(2, 0, -1)) == 1
-    assert call_forward(good_problem(), opts=libssd.SSDOptions(2, 0, 3)) == 3
+    assert call_forward(good_problem(), opts=libssd.SSDOptions(2, 0, -1, 0, None, None)) == 1
+    assert call_forward(good_problem(), opts=libssd.SSDOptions(2, 0, 3, 0, None, None)) == 3
+
+
+@no_gpu
+def test_event_options_checked():
+    ev = (ctypes.c_void_p * 6)()
+    evp = ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p))
+    assert call_forward(good_problem(), opts=libssd.SSDOptions(0, 0, 0, 6, None, None)) == 1
+    assert call_forward(good_problem(), opts=libssd.SSDOptions(0, 0, 0, 5, evp, None)) == 1
+    assert call_forward(good_problem(), opts=libssd.SSDOptions(0, 0, 0, -1, evp, None)) == 1
+    assert call_forward(good_problem(), opts=libssd.SSDOptions(0, 0, 0, 6, evp, None)) == 3
 
 
 @no_gpu
