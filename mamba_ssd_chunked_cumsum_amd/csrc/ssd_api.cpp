@@ -235,7 +235,7 @@ ssd_status run_fused(const Dims& d, int run_chunks, const void* x, const float* 
   float* logdecay = reinterpret_cast<float*>(b + 2 * a);
   hipError_t e = t.mark(s);
   if (e == hipSuccess)
-    e = ssd::launch_run_state(d, x, B, dt, A, S * d.Q, nr, states, logdecay, s);
+    e = ssd::launch_run_state(d, x, B, dt, A, S, nr, states, logdecay, s);
   if (e == hipSuccess) e = t.mark(s);
   if (e == hipSuccess)
     e = ssd::launch_chain_passing(d, nr, states, logdecay, nr, 1, h0, h_run, fin, s);

@@ -32,8 +32,9 @@ hipError_t launch_chunk_scan(const Dims& d, int io, int prec, const void* x, con
 
 // fused path (bf16 io)
 bool fused_supported(const Dims& d);
+// S = chunks per run, nr = runs per sequence; states [Bt, nr, H, P, N], logdecay [Bt, H, nr]
 hipError_t launch_run_state(const Dims& d, const void* x, const void* B, const float* dt,
-                            const float* A, int run_len, int nr, float* states, float* logdecay,
+                            const float* A, int S, int nr, float* states, float* logdecay,
                             hipStream_t s);
 hipError_t launch_fused_scan(const Dims& d, const void* x, const void* B, const void* C,
                              const float* dt, const float* A, const float* D,

@@ -147,7 +147,12 @@ class KernelTimer:
 
     def __init__(self):
         self.events = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        self._arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in self.events])
+        for e in self.events:       # torch creates the HIP event lazily, at its first record
+            e.record()
+        handles = [e.cuda_event for e in self.events]
+        if not all(handles):
+            raise RuntimeError("could not create timing events")
+        self._arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(h) for h in handles])
         self.n_kernels = ctypes.c_int32(0)
 
     def attach(self, opts: SSDOptions):

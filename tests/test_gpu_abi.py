@@ -47,3 +47,16 @@ def test_binding_rejects_wrong_dtypes():
         ssd.forward(d["x"], d["dt"], d["A"], d["B"].float(), d["C"], d["D"], 64)
     with pytest.raises(ValueError):
         ssd.forward(d["x"].transpose(1, 2), d["dt"], d["A"], d["B"], d["C"], d["D"], 64)
+
+
+def test_kernel_timer_events():
+    """Per-kernel timing events recorded by the library around each kernel."""
+    d = _inputs()
+    note("kernel timer")
+    for variant, n in (("fused", 3), ("unfused", 5)):
+        tm = libssd.KernelTimer()
+        ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 64, variant=variant,
+                    timer=tm)
+        torch.cuda.synchronize()
+        times = tm.times_ms()
+        assert len(times) == n and all(t >= 0 for t in times.values())
