@@ -29,6 +29,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-t
           "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include")]
 
 
+# Per-source extras. The fused kernels keep their matrix-core accumulators in ordinary VGPRs
+# (their VALU work reads the carried state every sub-chunk); AGPRs then hold what does not fit.
+EXTRA = {"ssd_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc() -> str:
     p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(p):
@@ -47,7 +52,7 @@ def build(verbose: bool = False) -> str:
             continue
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *COMMON, *lang, "-c", path, "-o", obj]
+        cmd = [cc, *COMMON, *EXTRA.get(src, []), *lang, "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,

@@ -202,27 +202,26 @@ ssd_status run_unfused(const ssd_problem* prob, const Dims& d, int prec, const v
   return from_hip(ef);
 }
 
-// Runs of S chunks: enough (batch, head, run) blocks to fill the chip (about 1024), as few run
-// boundaries as that allows (each boundary costs one fp32 state write and read).
-void choose_runs(const Dims& d, int requested, int* S, int* nr) {
-  if (requested > 0) {
-    *S = requested < d.nc ? requested : d.nc;
-    *nr = (d.nc + *S - 1) / *S;
-    return;
-  }
-  const int units = d.Bt * d.H;
-  int want = (1024 + units - 1) / units;
-  if (want > d.nc) want = d.nc;
-  if (want < 1) want = 1;
-  *S = (d.nc + want - 1) / want;
-  *nr = (d.nc + *S - 1) / *S;
+// Compute units of the current device (cached per device).
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
 }
 
-ssd_status run_fused(const Dims& d, int run_chunks, const void* x, const float* dt, const float* A,
-                     const void* B, const void* C, const float* D, const float* h0, void* y,
-                     float* fin, hipStream_t s, Timer& t) {
-  int S = 1, nr = 1;
-  choose_runs(d, run_chunks, &S, &nr);
+// Fused forward: F1 run states, F2 chain over runs (state entering each run, final state),
+// F3 fused scan. Runs are run_chunks chunks long when run_chunks > 0, else planned to give about
+// one block per compute unit (each run boundary costs one fp32 state write and read).
+ssd_status run_fused(const Dims& d, const ssd::FusedPlan& fp, const void* x, const float* dt,
+                     const float* A, const void* B, const void* C, const float* D,
+                     const float* h0, void* y, float* fin, hipStream_t s, Timer& t) {
+  const int nr = fp.nr;
   const int64_t st_bytes = (int64_t)d.Bt * nr * d.H * d.P * d.N * 4;
   const int64_t ld_bytes = (int64_t)d.Bt * d.H * nr * 4;
   const int64_t a = (st_bytes + 255) & ~int64_t(255);
@@ -234,13 +233,12 @@ ssd_status run_fused(const Dims& d, int run_chunks, const void* x, const float* 
   float* h_run = reinterpret_cast<float*>(b + a);
   float* logdecay = reinterpret_cast<float*>(b + 2 * a);
   hipError_t e = t.mark(s);
-  if (e == hipSuccess)
-    e = ssd::launch_run_state(d, x, B, dt, A, S, nr, states, logdecay, s);
+  if (e == hipSuccess) e = ssd::launch_run_state(d, fp, x, B, dt, A, states, logdecay, s);
   if (e == hipSuccess) e = t.mark(s);
   if (e == hipSuccess)
     e = ssd::launch_chain_passing(d, nr, states, logdecay, nr, 1, h0, h_run, fin, s);
   if (e == hipSuccess) e = t.mark(s);
-  if (e == hipSuccess) e = ssd::launch_fused_scan(d, x, B, C, dt, A, D, h_run, y, S, nr, s);
+  if (e == hipSuccess) e = ssd::launch_fused_scan(d, fp, x, B, C, dt, A, D, h_run, y, s);
   if (e == hipSuccess) e = t.mark(s);
   hipError_t ef = hipFreeAsync(base, s);
   if (e != hipSuccess) return from_hip(e);
@@ -267,9 +265,12 @@ ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* d
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int variant = opts ? opts->variant : SSD_VARIANT_AUTO;
   // The fused kernels cover bf16 io with fp16 operands (chained run states split hi + lo) for
-  // headdim 64 / dstate 64, 128 and headdim 128 / dstate 128, 256.
+  // headdim 64 or 128 and dstate 64, 128 or 256.
+  ssd::FusedPlan fp{};
+  const int64_t run_tokens = opts && opts->run_chunks > 0 ? (int64_t)opts->run_chunks * chunk_size : 0;
   const bool fusable = prob->io_dtype == SSD_DTYPE_BF16 && prec != ssd::kPrecFp32 &&
-                       ssd::fused_supported(d);
+                       ssd::fused_plan(d, (int)(run_tokens < (1 << 30) ? run_tokens : (1 << 30)),
+                                       compute_units(), &fp);
   if (variant == SSD_VARIANT_FUSED && !fusable) return SSD_ERR_UNSUPPORTED;
   Timer t;
   if (opts && opts->n_events > 0) {
@@ -279,8 +280,7 @@ ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* d
   const bool fused = variant != SSD_VARIANT_UNFUSED && fusable;
   if (opts && opts->n_kernels) *opts->n_kernels = fused ? 3 : 5;
   if (fused)
-    return run_fused(d, opts ? opts->run_chunks : 0, x, dt, A, B, C, D, initial_state, y,
-                     final_state, s, t);
+    return run_fused(d, fp, x, dt, A, B, C, D, initial_state, y, final_state, s, t);
   return run_unfused(prob, d, prec, x, dt, A, B, C, D, initial_state, y, final_state, s, t);
 }
 

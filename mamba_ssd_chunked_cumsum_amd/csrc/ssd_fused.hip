@@ -1,92 +1,60 @@
-// Fused SSD chunked forward (bf16 io): the intra-chunk C B^T block lives only in registers, and
-// the state is carried on chip through a run of consecutive chunks.
+// Fused SSD chunked forward (bf16 io).
 //
 // The chunked algorithm ("nitter.gq/da_be19" thread, post 5/6; stage order as in "Mamba-2 in
 // NVIDIA cuTile: Faster Forward Kernels and What the Benchmark Means", section "Why Mamba-2 is a
-// useful kernel example") needs, for every chunk, the state entering it. A chunk's fp32 state
-// (P x N) is as large as or larger than its bf16 x tile (Q x P) for the usual shapes, so
-// materialising it per chunk would double the HBM traffic. Here the sequence of each (batch,
-// head) is cut into runs of S chunks:
+// useful kernel example") needs the state entering every chunk. A (batch, head)'s fp32 state
+// (P x N) is as large as its bf16 x tile of 256 tokens, so materialising one per chunk would
+// double the HBM traffic. Here each sequence is cut into a few runs of consecutive tokens (about
+// one block per compute unit in total):
 //
 //   F1 k_run_state    each run's own end state (zero entry state) and total log-decay
-//   F2 k_state_pass   (shared with the unfused path) state entering each run; final state
-//   F3 k_fused_scan   per run: for each chunk, cumulative decay, C B^T, the masked intra-chunk
-//                     product, the inter-chunk readout from the carried state, the skip term,
-//                     and the carried-state update -- all on chip; only y leaves the kernel.
+//   F2 k_state_pass   (shared with the unfused path) the state entering each run; final state
+//   F3 k_fused_scan   per run, sub-chunk by sub-chunk: cumulative decay, C B^T, the masked
+//                     intra-sub-chunk product, the readout of the carried state, the skip term
+//                     and the state update, all on chip; only y leaves the kernel.
 //
-// Only run-boundary states touch memory (1/S of the per-chunk volume).
+// Inside F1/F3 the run is walked in sub-chunks of T tokens (64, or 32 when N = 256), whatever the
+// caller's chunk length: the exact result does not depend on where the sequence is cut (the
+// chunk length cancels out of the recurrence), so the kernel picks the cut that suits the chip's
+// registers and LDS. The caller's chunk length still fixes the stage entry points' outputs.
 //
-// Both kernels handle HB heads of one B/C group per block (so B and C are loaded, and C B^T is
-// computed, once for HB heads) with NW = 4 * HB (P = 64) or 8 (P = 128) waves: wave w carries the
-// state tiles of head w / (NW / HB), p-tile w % (NW / HB), all n-tiles. Tokens are staged through
-// LDS in slabs of SL, double-buffered: the next slab's global loads are issued into registers
-// before the current slab is computed. LDS tiles keep the natural row-major layout ([token][p],
-// [token][n]); matrix-core fragments whose K index is the token are read with the gfx950
-// transposing LDS load (ds_read_b64_tr_b16), so no transposed copy is ever made.
+// Work split (one 256-thread block per compute unit, one wave per SIMD): a wave owns one head's
+// p-slice of PS columns (PS * N <= 8192, so its fp32 state is at most 128 registers per lane) and
+// keeps that state in registers across the whole run. The HPB heads of a block belong to one B/C
+// group, so B and C are staged, and C B^T is computed, once per block and shared.
+//
+// Staging: x, B and C tiles are copied global -> LDS by the gfx950 LDS DMA (global_load_lds
+// dwordx4), which needs no registers, so a whole sub-chunk is in flight while the previous one is
+// computed (F3: two stages, F1: three). The DMA writes each wave instruction's 64 pieces of 16
+// bytes contiguously; the swizzle (16-byte piece c of row t stored at position c ^ (t & 7)) is
+// applied by choosing which global piece each lane fetches. B and C are converted to fp16 in
+// place after arrival; x stays raw bf16 (the skip term D x uses it exactly) and is converted while
+// its fragments are built. Fragments whose K index is the token are read with the gfx950
+// transposing LDS load (ds_read_b64_tr_b16).
+//
+// Matrix-core operand precision: x, B, C enter as exact fp16 copies of the bf16 inputs (inputs
+// are assumed to lie in fp16's range); the decay-masked C B^T block, the carried state (for the
+// readout) and the decay-weighted x (for the state update) are rounded to fp16; F1 splits the
+// weighted x into fp16 high and low parts (two passes), so the run states that are chained over
+// the sequence carry near-fp32 accuracy. All accumulation is fp32.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
-// ---- fragment helpers -----------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Transposing LDS read: within each 16-lane group, lane i receives, in slot q, the (i % 4)-th of
-// the four 16-bit values addressed by lane 4q + i / 4.
-__device__ __forceinline__ f16x4 lds_tr4(const f16* p) {
-  const s16x4 v =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(f16x4, v);
-}
-
-// K fragment of a 16-column tile (columns c0..c0+15, lane -> column c0 + lane % 16) of a
-// row-major LDS tile whose rows are the K index: slot s of lane group g holds row r0 + 8 g + s
-// (the standard K order of the 16x16x32 operands).
-__device__ __forceinline__ f16x8 frag_k(const f16* base, int ld, int r0, int c0, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const f16* p = base + (r0 + 8 * g + (j >> 2)) * ld + c0 + 4 * (j & 3);
-  const f16x4 a = lds_tr4(p), b = lds_tr4(p + 4 * ld);
-  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// Same, in the order of a 16x16 accumulator pair: slots 0-3 hold rows r0 + 4 g + s, slots 4-7
-// rows r0 + 16 + 4 g + s (g = lane group) -- the rows the two C B^T accumulators of a 32-token K
-// step give each lane.
-__device__ __forceinline__ f16x8 frag_k_acc(const f16* base, int ld, int r0, int c0, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const f16* p = base + (r0 + 4 * g + (j >> 2)) * ld + c0 + 4 * (j & 3);
-  const f16x4 a = lds_tr4(p), b = lds_tr4(p + 16 * ld);
-  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// two fp32 -> two fp16, round to nearest even (one v_cvt_pk_f16_f32)
-__device__ __forceinline__ f16x2 cvt_f16x2(float a, float b) {
+// ---- small helpers ------------------------------------------------------------------------------
+__device__ __forceinline__ f16x2 cvt_f16x2(float a, float b) {  // v_cvt_pk_f16_f32, RNE
   return __builtin_convertvector(f32x2{a, b}, f16x2);
 }
-// two fp32 -> two bf16 bit patterns packed in 32 bits, round to nearest even
-// (one v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {  // v_cvt_pk_bf16_f32, RNE
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
-
-// 8 bf16 (one 16-byte piece) -> 8 fp16 (exact for values in fp16's normal range)
-__device__ __forceinline__ f16x8 bf16x8_to_f16x8(uint4 r) {
-  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-  f16x8 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2 h = cvt_f16x2(__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xffff0000u));
-    o[2 * i] = h[0];
-    o[2 * i + 1] = h[1];
-  }
-  return o;
-}
-
-// 8 fp32 -> 8 fp16
 __device__ __forceinline__ f16x8 cvt_f16x8(const float (&v)[8]) {
   f16x8 o;
 #pragma unroll
@@ -97,621 +65,616 @@ __device__ __forceinline__ f16x8 cvt_f16x8(const float (&v)[8]) {
   }
   return o;
 }
+// 8 bf16 (one 16-byte piece) -> 8 fp16 (exact in fp16's normal range)
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 r) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = __builtin_bit_cast(
+        uint32_t, cvt_f16x2(__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xffff0000u)));
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+// two packed bf16 (one 32-bit word) -> two floats
+__device__ __forceinline__ void bf16x2_to_f32(uint32_t w, float& lo, float& hi) {
+  lo = __uint_as_float(w << 16);
+  hi = __uint_as_float(w & 0xffff0000u);
+}
 
-template <int P_, int N_, int HB_, int NW_, int SL_, int MT_>
-struct Cfg {
-  static constexpr int P = P_, N = N_, HB = HB_, NW = NW_, SL = SL_;
-  static constexpr int NT = NW * 64;
-  static constexpr int NP = P / 16, NN = N / 16, NK = N / 32;
-  static constexpr int WPH = NW / HB;   // waves per head for the state tiles
-  static_assert(WPH % NP == 0, "whole waves per (head, p-tile)");
-  static constexpr int WPP = WPH / NP;  // waves per (head, p-tile)
-  static_assert(NN % WPP == 0, "n-tiles split evenly over a (head, p-tile)'s waves");
-  static constexpr int TS = NN / WPP;   // carried-state tiles per wave
-  static_assert(SL % 32 == 0 && SL <= 64, "slab of whole 32-token K steps, one wave of tokens");
-  static_assert(HB == 1 || HB == 2, "one or two heads per block");
-  static constexpr int MAXI = MT_;      // 16-row output tiles per wave (Q <= 16 NW MT)
-  static constexpr int LDX = P + 8, LDB = N + 8, LDH = N + 8;
-  static constexpr int LDY = HB * P + 4;  // floats per row of a wave's 8-row output tile
-  static constexpr int XS = HB * SL * LDX, BS = SL * LDB;   // halfs per stage
-  static constexpr int XPIECES = HB * SL * P / 8, PIECES = XPIECES + SL * N / 8;
-  static constexpr int PPT = (PIECES + NT - 1) / NT;       // 16-byte pieces per thread
-  // h^T (fp16) and, later in each chunk, the waves' fp32 output tiles share one region (halfs)
-  static constexpr int HREG = HB * P * LDH > NW * 8 * LDY * 2 ? HB * P * LDH : NW * 8 * LDY * 2;
+// Byte offset of 16-byte piece c of row t in a swizzled staged tile with rows of ROW bytes.
+template <int ROW>
+__device__ __forceinline__ int swz(int t, int c) {
+  return t * ROW + ((c ^ (t & 7)) << 4);
+}
+
+// One LDS DMA instruction: lane l copies 16 bytes from g to lds + 16 l (lds wave-uniform).
+__device__ __forceinline__ void dma16(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
+                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+}
+// Wait until all of this wave's vector memory operations (DMA included) have completed.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// ... all but the most recent n (n < 16); loads complete in issue order.
+template <int n>
+__device__ __forceinline__ void wait_vm_but() {
+  static_assert(n >= 0 && n < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | n);
+}
+
+// Transposing LDS read: lane i of each 16-lane group receives, in slot q, the (i % 4)-th of the
+// four 16-bit values addressed by lane 4 q + i / 4.
+__device__ __forceinline__ s16x4 tr4(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// K fragment of a staged swizzled tile whose rows are the K index (tokens): lane (g, j) gets
+// column col0 + j and rows r0 + 8 g + 0..7 as eight 16-bit values (raw bits).
+template <int ROW>
+__device__ __forceinline__ s16x8 frag_tr(const char* tile, int r0, int col0, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const int t = r0 + 8 * g + (j >> 2);
+  const int c = (col0 >> 3) + ((j & 3) >> 1);
+  const int half = (j & 1) << 3;
+  const s16x4 lo = tr4(tile + swz<ROW>(t, c) + half);
+  const s16x4 hi = tr4(tile + swz<ROW>(t + 4, c) + half);
+  return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ---- configuration ----------------------------------------------------------------------------
+template <int P_, int N_>
+struct Fz {
+  static constexpr int P = P_, N = N_;
+  static constexpr int T = N >= 256 ? 32 : 64;  // tokens per sub-chunk
+  static constexpr int NW = 4, NT = 256;
+  static constexpr int PS0 = 8192 / N < P ? 8192 / N : P;
+  static constexpr int PS = PS0 < 64 ? PS0 : 64;  // p columns per wave
+  static constexpr int WPH = P / PS, HPB = NW / WPH;  // waves per head, heads per block
+  static constexpr int NPT = PS / 16, NNT = N / 16, NKN = N / 32, NIT = T / 16, NJS = T / 32;
+  static constexpr int ROW_N = N * 2, ROW_P = P * 2;  // staged row bytes
+  static constexpr int BC_BYTES = T * ROW_N, X_BYTES = HPB * T * ROW_P;
+  static constexpr int BC_NI = BC_BYTES / 1024;       // DMA instructions per B (or C) tile
+  static constexpr int SCAN_STAGE = 2 * BC_BYTES + X_BYTES, RUN_STAGE = BC_BYTES + X_BYTES;
+  static constexpr int SCAN_NI = SCAN_STAGE / 1024, RUN_NI = RUN_STAGE / 1024;
+  static constexpr int LDCB = T + 4;                  // floats per C B^T row
+  static constexpr int CB_BYTES = T * LDCB * 4;
+  static constexpr int WA_BYTES = NW * 3 * T * 4;     // per-wave acs, dt, w
+  static constexpr int NSCAN = 2, NRUN = 3;           // stages
+  static constexpr int SCAN_LDS = NSCAN * SCAN_STAGE + CB_BYTES + WA_BYTES;
+  static constexpr int RUN_LDS = NRUN * RUN_STAGE + WA_BYTES;
+  static_assert(P % PS == 0 && NW % WPH == 0, "whole waves per head");
+  static_assert(N / 8 >= 8 && P / 8 >= 8, "swizzle needs 8 pieces per row");
+  static_assert(BC_BYTES % 1024 == 0 && X_BYTES % 1024 == 0, "whole DMA instructions");
+  static_assert(BC_NI % NW == 0 && SCAN_NI % NW == 0 && RUN_NI % NW == 0, "even DMA split");
+  static_assert(SCAN_LDS <= 160 * 1024 && RUN_LDS <= 160 * 1024, "LDS budget");
 };
 
-// Global -> registers for one slab: x of the HB heads and B, token rows [j0, j0 + SL) of the
-// chunk starting at t0 (q valid rows; later rows are zeros).
+// Block / wave coordinates shared by F1 and F3. Grid (nr, G * head-blocks per group, batch).
+struct Coord {
+  int b, r, grp, hbase, hlast;  // block: batch, run, group, first head, last head of the group
+  int wave, lane, g, c16;       // wave, lane, lane group, lane % 16
+  int h, p0;                    // this wave's head and first p column
+  bool active;                  // this wave's head exists
+};
+
 template <class K>
-__device__ __forceinline__ void slab_load(uint4 (&v)[K::PPT], const u16* x, const u16* Bm,
-                                          const Dims& d, int b, int h0, int g, int t0, int q,
-                                          int j0) {
-  // Rows past the end of the chunk read row j0 instead (always inside the sequence) and are
-  // zeroed afterwards, so the loads carry no branches and can all be in flight together.
+__device__ __forceinline__ Coord coords(const Dims& d) {
+  Coord c;
+  const int hpg = d.H / d.G, hbg = (hpg + K::HPB - 1) / K::HPB;
+  c.r = blockIdx.x;
+  c.b = blockIdx.z;
+  c.grp = blockIdx.y / hbg;
+  const int first = (blockIdx.y % hbg) * K::HPB;
+  c.hbase = c.grp * hpg + first;
+  c.hlast = c.grp * hpg + hpg - 1;
+  c.wave = threadIdx.x >> 6;
+  c.lane = threadIdx.x & 63;
+  c.g = c.lane >> 4;
+  c.c16 = c.lane & 15;
+  const int hh = c.wave / K::WPH;
+  c.active = first + hh < hpg;
+  c.h = c.active ? c.hbase + hh : c.hlast;
+  c.p0 = (c.wave % K::WPH) * K::PS;
+  return c;
+}
+
+// Issue one stage's DMA: [B][C if WITH_C][x of the block's heads], tokens tok0 .. tok0 + T - 1.
+// In the last, partial sub-chunk rows past the sequence end re-read its last row; heads past the
+// group re-read its last head (their results are never used).
+template <class K, bool WITH_C, bool FULL>
+__device__ __forceinline__ void issue_stage_(char* st, const u16* x, const u16* Bm, const u16* Cm,
+                                             const Dims& d, const Coord& c, int tok0) {
+  constexpr int NBC = (WITH_C ? 2 : 1) * K::BC_NI;
+  constexpr int NI = WITH_C ? K::SCAN_NI : K::RUN_NI;
+  constexpr int PPR_N = K::N / 8, PPR_P = K::P / 8;
+  constexpr int RPI_N = 64 / PPR_N, RPI_P = 64 / PPR_P;
+  const uint32_t ldbc = (uint32_t)d.G * K::N * 2, ldx = (uint32_t)d.H * K::P * 2;  // row bytes
+  const char* bbase = reinterpret_cast<const char*>(Bm) +
+                      (((int64_t)c.b * d.L + tok0) * d.G + c.grp) * (K::N * 2);
+  const char* cbase = reinterpret_cast<const char*>(Cm) +
+                      (((int64_t)c.b * d.L + tok0) * d.G + c.grp) * (K::N * 2);
+  const char* xbase = reinterpret_cast<const char*>(x) +
+                      (((int64_t)c.b * d.L + tok0) * d.H + c.hbase) * (K::P * 2);
+  const int last = d.L - 1 - tok0;  // last valid row of the sub-chunk
 #pragma unroll
-  for (int k = 0; k < K::PPT; ++k) {
-    const int e = threadIdx.x + k * K::NT;
-    if (k * K::NT >= K::PIECES) break;  // whole iteration past the slab (compile-time)
-    const bool isx = e < K::XPIECES;
-    const int e2 = isx ? e : e - K::XPIECES;
-    const int j = isx ? e / (K::HB * K::P / 8) : e2 / (K::N / 8);
-    const bool valid = (e < K::PIECES) && (j0 + j < q);
-    const int jr = valid ? j : 0;
-    const u16* src =
-        isx ? x + (((int64_t)b * d.L + t0 + j0 + jr) * d.H + h0) * K::P + (e % (K::HB * K::P / 8)) * 8
-            : Bm + (((int64_t)b * d.L + t0 + j0 + jr) * d.G + g) * K::N + (e2 % (K::N / 8)) * 8;
-    const uint4 val = *reinterpret_cast<const uint4*>(src);
-    v[k] = valid ? val : make_uint4(0u, 0u, 0u, 0u);
+  for (int k0 = 0; k0 < NI; k0 += K::NW) {
+    const int k = k0 + c.wave;
+    const char* src;
+    if (k0 < NBC) {  // B or C (NBC and BC_NI are multiples of NW: uniform per k0)
+      const bool isC = WITH_C && k0 >= K::BC_NI;
+      const int kk = isC ? k - K::BC_NI : k;
+      const int t = kk * RPI_N + c.lane / PPR_N, cp = c.lane % PPR_N;
+      const int row = FULL ? t : min(t, last);
+      src = (isC ? cbase : bbase) + (int64_t)row * ldbc + ((cp ^ (t & 7)) << 4);
+    } else {
+      const int kk = k - NBC;
+      const int hh = kk / (K::T / RPI_P), kr = kk % (K::T / RPI_P);
+      const int hoff = min(hh, c.hlast - c.hbase) * (K::P * 2);
+      const int t = kr * RPI_P + c.lane / PPR_P, cp = c.lane % PPR_P;
+      const int row = FULL ? t : min(t, last);
+      src = xbase + hoff + (int64_t)row * ldx + ((cp ^ (t & 7)) << 4);
+    }
+    dma16(src, st + k * 1024);
   }
 }
 
-// Registers -> LDS stage (converted to fp16).
-template <class K>
-__device__ __forceinline__ void slab_store(const uint4 (&v)[K::PPT], f16* Xs, f16* Bs) {
+template <class K, bool WITH_C>
+__device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* Bm, const u16* Cm,
+                                            const Dims& d, const Coord& c, int tok0) {
+  if (tok0 + K::T <= d.L)
+    issue_stage_<K, WITH_C, true>(st, x, Bm, Cm, d, c, tok0);
+  else
+    issue_stage_<K, WITH_C, false>(st, x, Bm, Cm, d, c, tok0);
+}
+
+// Convert this wave's own DMA'd B (and C) pieces of a stage from bf16 to fp16 in place.
+template <class K, bool WITH_C>
+__device__ __forceinline__ void convert_stage(char* st, const Coord& c) {
+  constexpr int NBC = (WITH_C ? 2 : 1) * K::BC_NI;
 #pragma unroll
-  for (int k = 0; k < K::PPT; ++k) {
-    const int e = threadIdx.x + k * K::NT;
-    if (e < K::XPIECES) {
-      const int j = e / (K::HB * K::P / 8), rem = e % (K::HB * K::P / 8);
-      const int hh = rem / (K::P / 8), c8 = rem % (K::P / 8);
-      *reinterpret_cast<f16x8*>(Xs + (hh * K::SL + j) * K::LDX + c8 * 8) = bf16x8_to_f16x8(v[k]);
-    } else if (e < K::PIECES) {
-      const int e2 = e - K::XPIECES;
-      const int j = e2 / (K::N / 8), c8 = e2 % (K::N / 8);
-      *reinterpret_cast<f16x8*>(Bs + j * K::LDB + c8 * 8) = bf16x8_to_f16x8(v[k]);
-    }
+  for (int k0 = 0; k0 < NBC; k0 += K::NW) {
+    uint4* p = reinterpret_cast<uint4*>(st + (k0 + c.wave) * 1024 + c.lane * 16);
+    *p = bf16x8_to_f16x8(*p);
   }
+}
+
+// dt of this wave's head for the tokens of a sub-chunk (lane l: token tok0 + l), 0 past the end.
+template <class K>
+__device__ __forceinline__ float load_dt(const float* dt, const Dims& d, const Coord& c,
+                                         int tok0) {
+  const int t = tok0 + c.lane;
+  const float v = dt[((int64_t)c.b * d.L + min(t, d.L - 1)) * d.H + c.h];
+  return (c.lane < K::T && t < d.L && c.active) ? v : 0.f;
+}
+
+// Per-sub-chunk decay bookkeeping of one wave (lane l = token l): inclusive cumulative log-decay
+// acs, dt, and state weights w = exp(acs_end - acs) dt into the wave's LDS arrays. Returns acs_end.
+template <class K>
+__device__ __forceinline__ float decay_terms(float dv, float a_h, float* wa, const Coord& c) {
+  const float acs = wave_inclusive_scan(a_h * dv);
+  const float acs_end = __shfl(acs, K::T - 1, kWave);
+  if (c.lane < K::T) {
+    wa[c.lane] = acs;
+    wa[K::T + c.lane] = dv;
+    wa[2 * K::T + c.lane] = __expf(acs_end - acs) * dv;
+  }
+  return acs_end;
+}
+
+// x K fragment of p columns col0 .. col0 + 15: raw bf16 -> 8 floats (tokens 32 js + 8 g + 0..7).
+template <class K>
+__device__ __forceinline__ void x_frag(const char* xt, int js, int col0, int lane, float (&v)[8]) {
+  const s16x8 r = frag_tr<K::ROW_P>(xt, 32 * js, col0, lane);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = __uint_as_float((uint32_t)(uint16_t)r[e] << 16);
+}
+
+// B^T K fragment (rows n = col0 .. col0 + 15, K = tokens) of a converted fp16 B tile.
+template <class K>
+__device__ __forceinline__ f16x8 b_frag(const char* Bh, int js, int col0, int lane) {
+  return __builtin_bit_cast(f16x8, frag_tr<K::ROW_N>(Bh, 32 * js, col0, lane));
 }
 
 // ---- F1: run states -------------------------------------------------------------------------
 // state_r = sum_{t in run} exp(sum_{k in (t, end]} dt_k A) dt_t x_t B_t^T (zero entry state) and
-// logdecay_r = sum_{t in run} dt_t A. Grid (nr, H / HB, batch). Slabs are taken from the run end
-// backwards so the weights are suffix sums (accurate where they matter most, near the end).
-// The state operand w_t x_t is split into fp16 high and low parts (two matrix-core passes) so the
-// chained run states keep near-fp32 accuracy.
+// logdecay_r = sum_{t in run} dt_t A. Walked forwards: per sub-chunk, S <- exp(acs_end) S +
+// B^T (w x), the weighted x split into fp16 high and low parts.
 template <class K>
-__global__ __launch_bounds__(K::NT) void k_run_state(const u16* __restrict__ x,
-                                                     const u16* __restrict__ Bm,
-                                                     const float* __restrict__ dt,
-                                                     const float* __restrict__ Av,
-                                                     float* __restrict__ states,
-                                                     float* __restrict__ logdecay, Dims d,
-                                                     int run_len, int nr) {
+__global__ __launch_bounds__(256, 1) void k_run_state(const u16* __restrict__ x,
+                                                      const u16* __restrict__ Bm,
+                                                      const float* __restrict__ dt,
+                                                      const float* __restrict__ Av,
+                                                      float* __restrict__ states,
+                                                      float* __restrict__ logdecay, Dims d,
+                                                      int RS, int nr) {
   using M = Mma<f16>;
-  constexpr int SL = K::SL;
-  __shared__ __align__(16) f16 Xs[2][K::XS];
-  __shared__ __align__(16) f16 Bs[2][K::BS];
-  __shared__ __align__(16) float w[2][K::HB][SL];
+  __shared__ __align__(1024) char smem[K::RUN_LDS];
+  const Coord c = coords<K>(d);
+  constexpr int T = K::T;
+  const int nsub = (d.L + T - 1) / T;
+  const int s_begin = c.r * RS, s_end = min(nsub, s_begin + RS);
+  if (s_begin >= s_end) return;
+  float* wa = reinterpret_cast<float*>(smem + K::NRUN * K::RUN_STAGE) + c.wave * 3 * T;
+  const int xoff = K::BC_BYTES + (c.wave / K::WPH) * (T * K::ROW_P);
+  const float a_h = Av[c.h];
 
-  const int r = blockIdx.x, h0 = blockIdx.y * K::HB, b = blockIdx.z;
-  const int g = h0 / (d.H / d.G);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kg = lane >> 4, col = lane & 15;
-  const int sh = wave / K::WPH, spt = (wave % K::WPH) % K::NP;
-  const int sn0 = ((wave % K::WPH) / K::NP) * K::TS;  // first n-tile carried by this wave
-  const int t_begin = r * run_len, t_end = min(d.L, t_begin + run_len);
-  const int nslab = (t_end - t_begin + SL - 1) / SL;
-  // waves 0..HB-1 compute the weights of their head; lane l < SL holds token s0 + l
-  const float a_h = wave < K::HB ? Av[h0 + wave] : 0.f;
-  float carry = 0.f;  // sum of dt A over the tokens after the current slab (waves < HB)
-
-  f32x4 S[K::TS];
+  f32x4 S[K::NNT][K::NPT];
 #pragma unroll
-  for (int k = 0; k < K::TS; ++k) S[k] = zero4();
-
-  // weights of one slab from its dt (one value per lane), then move the carry past the slab
-  auto weights = [&](float dtv, int stg) {
-    if (wave < K::HB) {
-      const float a = dtv * a_h;
-      float v = a;  // suffix sum over lanes >= l within the slab
+  for (int nt = 0; nt < K::NNT; ++nt)
 #pragma unroll
-      for (int off = 1; off < SL; off <<= 1) {
-        const float o = __shfl_down(v, off, kWave);
-        if (lane + off < SL) v += o;
+    for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] = zero4();
+  float logsum = 0.f;
+
+  // prologue: stages of the first two sub-chunks, dt of the first
+  issue_stage<K, false>(smem, x, Bm, nullptr, d, c, s_begin * T);
+  if (s_begin + 1 < s_end)
+    issue_stage<K, false>(smem + K::RUN_STAGE, x, Bm, nullptr, d, c, (s_begin + 1) * T);
+  float dt_next = load_dt<K>(dt, d, c, s_begin * T);
+
+  for (int s = s_begin; s < s_end; ++s) {
+    const int cur = (s - s_begin) % K::NRUN;
+    char* st = smem + cur * K::RUN_STAGE;
+    const float dv = dt_next;
+    // this stage's DMA done; the next stage's (issued after it) may still be in flight
+    if (s + 1 < s_end)
+      wait_vm_but<K::RUN_NI / K::NW>();
+    else
+      wait_vm_all();
+    convert_stage<K, false>(st, c);
+    __syncthreads();  // stage visible to all waves; every wave is done with sub-chunk s - 1
+    if (s + 2 < s_end)
+      issue_stage<K, false>(smem + ((cur + 2) % K::NRUN) * K::RUN_STAGE, x, Bm, nullptr, d, c,
+                            (s + 2) * T);
+    if (s + 1 < s_end) dt_next = load_dt<K>(dt, d, c, (s + 1) * T);
+    const float acs_end = decay_terms<K>(dv, a_h, wa, c);
+    logsum += acs_end;
+    const float dec = __expf(acs_end);
+#pragma unroll
+    for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] *= dec;
+#pragma unroll
+    for (int js = 0; js < K::NJS; ++js) {
+      const float4 w0 = *reinterpret_cast<const float4*>(wa + 2 * T + 32 * js + 8 * c.g);
+      const float4 w1 = *reinterpret_cast<const float4*>(wa + 2 * T + 32 * js + 8 * c.g + 4);
+      const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      f16x8 xhi[K::NPT], xlo[K::NPT];
+#pragma unroll
+      for (int pt = 0; pt < K::NPT; ++pt) {
+        float v[8], lo[8];
+        x_frag<K>(st + xoff, js, c.p0 + 16 * pt, c.lane, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= wj[e];
+        xhi[pt] = cvt_f16x8(v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = v[e] - (float)xhi[pt][e];
+        xlo[pt] = cvt_f16x8(lo);
       }
-      float after = __shfl_down(v, 1, kWave);  // sum over lanes > l
-      if (lane + 1 >= SL) after = 0.f;
-      if (lane < SL) w[stg][wave][lane] = __expf(carry + after) * dtv;
-      carry += __shfl(v, 0, kWave);
-    }
-  };
-  auto load_dt = [&](int s0) -> float {
-    float v = 0.f;
-    if (wave < K::HB && lane < SL && s0 + lane < t_end)
-      v = dt[((int64_t)b * d.L + s0 + lane) * d.H + h0 + wave];
-    return v;
-  };
-
-  uint4 pre[K::PPT];
-  int stage = 0;
-  {
-    const int s0 = t_begin + (nslab - 1) * SL;
-    slab_load<K>(pre, x, Bm, d, b, h0, g, s0, t_end - s0, 0);
-    const float dtv = load_dt(s0);
-    slab_store<K>(pre, Xs[0], Bs[0]);
-    weights(dtv, 0);
-  }
-  __syncthreads();
-  for (int s = nslab - 1; s >= 0; --s) {
-    const bool next = s > 0;
-    float dtn = 0.f;
-    if (next) {
-      const int s0 = t_begin + (s - 1) * SL;
-      slab_load<K>(pre, x, Bm, d, b, h0, g, s0, t_end - s0, 0);
-      dtn = load_dt(s0);
-    }
-    const f16* X = Xs[stage] + sh * SL * K::LDX;
-    const f16* Bt = Bs[stage];
-    const float* ws = w[stage][sh];
 #pragma unroll
-    for (int ks = 0; ks < SL / 32; ++ks) {
-      const f16x8 xv = frag_k(X, K::LDX, ks * 32, spt * 16, lane);
-      const float4 w0 = *reinterpret_cast<const float4*>(ws + ks * 32 + 8 * kg);
-      const float4 w1 = *reinterpret_cast<const float4*>(ws + ks * 32 + 8 * kg + 4);
-      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      float val[8], rem[8];
+      for (int nt = 0; nt < K::NNT; ++nt) {
+        const f16x8 bt = b_frag<K>(st, js, 16 * nt, c.lane);
 #pragma unroll
-      for (int qq = 0; qq < 8; ++qq) val[qq] = (float)xv[qq] * wv[qq];
-      const f16x8 hi = cvt_f16x8(val);
-#pragma unroll
-      for (int qq = 0; qq < 8; ++qq) rem[qq] = val[qq] - (float)hi[qq];  // exact in fp32
-      const f16x8 lo = cvt_f16x8(rem);
-#pragma unroll
-      for (int k = 0; k < K::TS; ++k) {
-        const f16x8 bf = frag_k(Bt, K::LDB, ks * 32, (sn0 + k) * 16, lane);
-        S[k] = M::mma(bf, hi, S[k]);
-        S[k] = M::mma(bf, lo, S[k]);
+        for (int pt = 0; pt < K::NPT; ++pt) {
+          S[nt][pt] = M::mma(bt, xhi[pt], S[nt][pt]);
+          S[nt][pt] = M::mma(bt, xlo[pt], S[nt][pt]);
+        }
       }
     }
-    if (next) {
-      slab_store<K>(pre, Xs[stage ^ 1], Bs[stage ^ 1]);
-      weights(dtn, stage ^ 1);
-    }
-    __syncthreads();
-    stage ^= 1;
   }
-  if (wave < K::HB && lane == 0) logdecay[((int64_t)b * d.H + h0 + wave) * nr + r] = carry;
-  // S^T tile (n rows, p columns): lane holds p = spt*16 + col, n = nt*16 + 4 kg + rr
-  float* out = states + (((int64_t)b * nr + r) * d.H + h0 + sh) * (int64_t)(K::P * K::N);
+  if (!c.active) return;
+  float* so = states + (((int64_t)c.b * nr + c.r) * d.H + c.h) * (int64_t)(K::P * K::N) +
+              (int64_t)c.p0 * K::N;
 #pragma unroll
-  for (int k = 0; k < K::TS; ++k)
-    *reinterpret_cast<float4*>(out + (spt * 16 + col) * K::N + (sn0 + k) * 16 + 4 * kg) =
-        make_float4(S[k][0], S[k][1], S[k][2], S[k][3]);
+  for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+    for (int pt = 0; pt < K::NPT; ++pt) {
+      const f32x4 v = S[nt][pt];
+      *reinterpret_cast<float4*>(so + (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g) =
+          make_float4(v[0], v[1], v[2], v[3]);
+    }
+  if (c.lane == 0 && c.p0 == 0) logdecay[((int64_t)c.b * d.H + c.h) * nr + c.r] = logsum;
 }
 
-// ---- F3: fused chunk scan over a run ------------------------------------------------------------
-// Grid (nr, H / HB, batch). Wave w owns MAXI 16-row output tiles of each chunk (for all HB heads
-// and all P columns), chosen so every wave has the same causal work (tiles w, 2 NW - 1 - w, ...),
-// and carries the state tiles of its (head, p-tile).
-//
-// Per chunk: C rows of the wave's tiles are loaded once into registers (the B operand of
-// (C B^T)^T and the A operand of the readout share one fragment layout); waves 0..HB-1 form, for
-// their head, the cumulative decay acs, dt, the state weights w_j = exp(acs_last - acs_j) dt_j and
-// the column factors cf_j = exp(acs_e - acs_j) dt_j (e = last token of j's 32-token K step); the
-// carried state is written to LDS in fp16 as h^T [p][n]; the readout y_i = exp(acs_i) C_i . h
-// starts the output accumulators. Then, per slab, for each 32-token K step the two 16x16 blocks
-// of (C B^T)^T are computed into registers and turned, lane by lane, into the A fragment
-//   M[i][j] = CB[i][j] exp(acs_i - acs_j) dt_j   (0 for j > i)
-// of each head -- the Q x Q block never leaves registers. Below the diagonal this is formed as
-// CB[i][j] * exp(acs_i - acs_e) * cf_j: both factors are <= 1 and the exponential is per row, not
-// per element; the one K step holding the tile's diagonal uses the direct form and the mask. The
-// fragment's K slots follow the accumulator layout (j = jb + 4 kg + r, jb + 16 + 4 kg + r), and x
-// is read from LDS in the same order. The carried state decays by exp(acs_last) and accumulates
-// B^T (w x) (skipped after the run's last chunk: the next run's entry state comes from F1/F2).
-// Finally y = accumulator + D x is rounded once to bf16 and written as whole rows.
+// Store the bf16 y tile that F3 left in the x tile of a stage: this wave's p-slice of its head,
+// rows tok0 .. tok0 + T - 1 (rows past the sequence end skipped), 16 bytes per lane.
 template <class K>
-__device__ __forceinline__ int row_tile(int wave, int m) {
-  // m-th 16-row tile of a wave: w, 2 NW - 1 - w, 2 NW + w, 4 NW - 1 - w, ...
-  return (m & 1) ? K::NW * (m + 1) - 1 - wave : K::NW * m + wave;
+__device__ __forceinline__ void store_y(const char* xt, u16* y, const Dims& d, const Coord& c,
+                                        int tok0) {
+  if (!c.active) return;
+  constexpr int PPR = K::PS / 8;  // pieces per row of the wave's slice
+  constexpr int PIECES = K::T * PPR;
+  static_assert(PIECES % 64 == 0, "whole store rounds");
+  u16* yb = y + (((int64_t)c.b * d.L + tok0) * d.H + c.h) * K::P;
+  const int64_t ld = (int64_t)d.H * K::P;
+  const int nrow = d.L - tok0;  // valid rows
+#pragma unroll
+  for (int k = 0; k < PIECES / 64; ++k) {
+    const int e = k * 64 + c.lane;
+    const int t = e / PPR, cp = (c.p0 >> 3) + e % PPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(xt + swz<K::ROW_P>(t, cp));
+    if (nrow >= K::T || t < nrow) *reinterpret_cast<uint4*>(yb + t * ld + (cp << 3)) = v;
+  }
 }
 
+// ---- F3: fused scan -----------------------------------------------------------------------------
+// Per sub-chunk (tokens i, j), with acs the inclusive cumulative log-decay from its start:
+//   y_i = sum_{j <= i} (C_i . B_j) exp(acs_i - acs_j) dt_j x_j + exp(acs_i) C_i . S + D x_i
+//   S  <- exp(acs_end) S + sum_j exp(acs_end - acs_j) dt_j x_j B_j^T
+// Each wave computes y^T for its p-slice (rows p, columns i), so every accumulator lane holds
+// four consecutive p of one token: the readout's A operand comes straight from the state
+// accumulators (K index n in accumulator order), and y leaves in 8-byte row pieces.
 template <class K>
-__global__ __launch_bounds__(K::NT) void k_fused_scan(
+__global__ __launch_bounds__(256, 1) void k_fused_scan(
     const u16* __restrict__ x, const u16* __restrict__ Bm, const u16* __restrict__ Cm,
     const float* __restrict__ dt, const float* __restrict__ Av, const float* __restrict__ Dv,
-    const float* __restrict__ h_run, u16* __restrict__ y, Dims d, int S, int nr) {
+    const float* __restrict__ h_run, u16* __restrict__ y, Dims d, int RS, int nr) {
   using M = Mma<f16>;
-  constexpr int SL = K::SL, HB = K::HB, NP = K::NP, NK = K::NK, MAXI = K::MAXI;
-  __shared__ __align__(16) f16 Xs[2][K::XS];
-  __shared__ __align__(16) f16 Bs[2][K::BS];
-  __shared__ __align__(16) f16 hreg[K::HREG];  // h^T [HB][P][LDH], then per-wave y tiles
-  __shared__ __align__(16) float acs[HB][256];
-  __shared__ __align__(16) float dts[HB][256];
-  __shared__ __align__(16) float wts[HB][256];
-  __shared__ __align__(16) float cfs[HB][256];
+  __shared__ __align__(1024) char smem[K::SCAN_LDS];
+  const Coord c = coords<K>(d);
+  constexpr int T = K::T, NPT = K::NPT, NIT = K::NIT;
+  const int nsub = (d.L + T - 1) / T;
+  const int s_begin = c.r * RS, s_end = min(nsub, s_begin + RS);
+  if (s_begin >= s_end) return;
+  float* cbs = reinterpret_cast<float*>(smem + K::NSCAN * K::SCAN_STAGE);
+  float* wa = reinterpret_cast<float*>(smem + K::NSCAN * K::SCAN_STAGE + K::CB_BYTES) +
+              c.wave * 3 * T;
+  const int xoff = 2 * K::BC_BYTES + (c.wave / K::WPH) * (T * K::ROW_P);
+  const float a_h = Av[c.h], d_h = Dv[c.h];
 
-  const int r = blockIdx.x, h0 = blockIdx.y * HB, b = blockIdx.z;
-  const int g = h0 / (d.H / d.G);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = lane & 15, kg = lane >> 4;
-  const int Q = d.Q, nti = Q / 16;
-  const int sh = wave / K::WPH, spt = (wave % K::WPH) % K::NP;
-  const int sn0 = ((wave % K::WPH) / K::NP) * K::TS;  // first n-tile carried by this wave
-  const int c_begin = r * S, c_end = min(d.nc, c_begin + S);
-  float Dh[HB];
-#pragma unroll
-  for (int hh = 0; hh < HB; ++hh) Dh[hh] = Dv[h0 + hh];
-  const float a_h = wave < HB ? Av[h0 + wave] : 0.f;
-  // entries past Q are read (as zeros) when Q is shorter than a K step or a slab
-  for (int i = threadIdx.x; i < 256; i += K::NT) {
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) acs[hh][i] = dts[hh][i] = wts[hh][i] = cfs[hh][i] = 0.f;
-  }
-
-  // carried state (S^T tiles): lane holds p = spt*16 + col, n = nt*16 + 4 kg + rr
-  f32x4 Sacc[K::TS];
+  // carried state S^T tiles (rows n, columns p): lane holds p = p0 + 16 pt + c16,
+  // n = 16 nt + 4 g + 0..3
+  f32x4 S[K::NNT][NPT];
   {
-    const float* hr = h_run + (((int64_t)b * nr + r) * d.H + h0 + sh) * (int64_t)(K::P * K::N);
+    const float* hr = h_run + (((int64_t)c.b * nr + c.r) * d.H + c.h) * (int64_t)(K::P * K::N) +
+                      (int64_t)c.p0 * K::N;
 #pragma unroll
-    for (int k = 0; k < K::TS; ++k) {
-      const float4 v = *reinterpret_cast<const float4*>(hr + (spt * 16 + col) * K::N +
-                                                        (sn0 + k) * 16 + 4 * kg);
-      Sacc[k] = f32x4{v.x, v.y, v.z, v.w};
-    }
+    for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) {
+        const float4 v =
+            *reinterpret_cast<const float4*>(hr + (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g);
+        S[nt][pt] = f32x4{v.x, v.y, v.z, v.w};
+      }
   }
 
-  uint4 pre[K::PPT];
-  int stage = 0;
-  {
-    const int t0 = c_begin * Q;
-    slab_load<K>(pre, x, Bm, d, b, h0, g, t0, min(Q, d.L - t0), 0);
-    slab_store<K>(pre, Xs[0], Bs[0]);
+  issue_stage<K, true>(smem, x, Bm, Cm, d, c, s_begin * T);
+  float dt_next = load_dt<K>(dt, d, c, s_begin * T);
+  int ytok = -1;  // first token of the sub-chunk whose y waits in the previous stage's x tile
+
+  for (int s = s_begin; s < s_end; ++s) {
+    const int cur = (s - s_begin) & 1;
+    char* st = smem + cur * K::SCAN_STAGE;
+    const char* Bh = st;
+    const char* Ch = st + K::BC_BYTES;
+    const char* xt = st + xoff;
+    const float dv = dt_next;
+    wait_vm_all();  // this stage's DMA, the dt load, and the y stores of the previous round
+    if (ytok >= 0) store_y<K>(smem + (cur ^ 1) * K::SCAN_STAGE + xoff, y, d, c, ytok);
+    convert_stage<K, true>(st, c);
+    __syncthreads();  // stage visible; every wave is done with sub-chunk s - 1 (CB, stage cur^1)
+    if (s + 1 < s_end) {
+      issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, d, c, (s + 1) * T);
+      dt_next = load_dt<K>(dt, d, c, (s + 1) * T);
+    }
+    // C B^T lower-triangle tiles of the sub-chunk, shared by the block's heads: tile q (row-major
+    // over the lower triangle) goes to wave q % NW
+    constexpr int NTILE = NIT * (NIT + 1) / 2;
+#pragma unroll
+    for (int q0 = 0; q0 < NTILE; q0 += K::NW) {
+      const int q = q0 + c.wave;
+      if (q < NTILE) {
+        int it = 0;
+        while ((it + 1) * (it + 2) / 2 <= q) ++it;
+        const int jt = q - it * (it + 1) / 2;
+        f32x4 acc = zero4();
+        const int i = 16 * it + c.c16, j = 16 * jt + c.c16;
+#pragma unroll
+        for (int kn = 0; kn < K::NKN; ++kn) {
+          const f16x8 a = *reinterpret_cast<const f16x8*>(Ch + swz<K::ROW_N>(i, 4 * kn + c.g));
+          const f16x8 bb = *reinterpret_cast<const f16x8*>(Bh + swz<K::ROW_N>(j, 4 * kn + c.g));
+          acc = M::mma(a, bb, acc);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) cbs[(16 * it + 4 * c.g + rr) * K::LDCB + j] = acc[rr];
+      }
+    }
+    const float acs_end = decay_terms<K>(dv, a_h, wa, c);
+    __syncthreads();  // C B^T tiles visible
+    if (!c.active) continue;
+
+    // readout of the carried state: Y^T = S C^T (K index n in accumulator order)
+    f32x4 Y[NPT][NIT];
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) Y[pt][it] = zero4();
+#pragma unroll
+    for (int kn = 0; kn < K::NKN; ++kn) {
+      f16x8 sa[NPT];
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) {
+        const float v[8] = {S[2 * kn][pt][0],     S[2 * kn][pt][1],     S[2 * kn][pt][2],
+                            S[2 * kn][pt][3],     S[2 * kn + 1][pt][0], S[2 * kn + 1][pt][1],
+                            S[2 * kn + 1][pt][2], S[2 * kn + 1][pt][3]};
+        sa[pt] = cvt_f16x8(v);
+      }
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int i = 16 * it + c.c16;
+        const int half = (c.g & 1) << 3;
+        const uint2 lo = *reinterpret_cast<const uint2*>(
+            Ch + swz<K::ROW_N>(i, 4 * kn + (c.g >> 1)) + half);
+        const uint2 hi = *reinterpret_cast<const uint2*>(
+            Ch + swz<K::ROW_N>(i, 4 * kn + 2 + (c.g >> 1)) + half);
+        const f16x8 cf = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(sa[pt], cf, Y[pt][it]);
+      }
+    }
+    float acs_i[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      acs_i[it] = wa[16 * it + c.c16];
+      const float e = __expf(acs_i[it]);
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) Y[pt][it] *= e;
+    }
+
+    // state decay (the readout above used the entry state)
+    const float dec = __expf(acs_end);
+#pragma unroll
+    for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) S[nt][pt] *= dec;
+
+#pragma unroll
+    for (int js = 0; js < K::NJS; ++js) {
+      const int j0 = 32 * js + 8 * c.g;
+      const float4 a0 = *reinterpret_cast<const float4*>(wa + j0);
+      const float4 a1 = *reinterpret_cast<const float4*>(wa + j0 + 4);
+      const float4 d0 = *reinterpret_cast<const float4*>(wa + T + j0);
+      const float4 d1 = *reinterpret_cast<const float4*>(wa + T + j0 + 4);
+      const float4 w0 = *reinterpret_cast<const float4*>(wa + 2 * T + j0);
+      const float4 w1 = *reinterpret_cast<const float4*>(wa + 2 * T + j0 + 4);
+      const float acj[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float dtj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      f16x8 xh[NPT], xs[NPT];
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) {
+        float v[8];
+        x_frag<K>(xt, js, c.p0 + 16 * pt, c.lane, v);
+        xh[pt] = cvt_f16x8(v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= wj[e];
+        xs[pt] = cvt_f16x8(v);
+      }
+      // intra-sub-chunk product: Y^T += x^T M^T, M_ij = CB_ij exp(acs_i - acs_j) dt_j (j <= i)
+#pragma unroll
+      for (int it = 2 * js; it < NIT; ++it) {
+        const int i = 16 * it + c.c16;
+        const float4 c0 = *reinterpret_cast<const float4*>(cbs + i * K::LDCB + j0);
+        const float4 c1 = *reinterpret_cast<const float4*>(cbs + i * K::LDCB + j0 + 4);
+        const float cb[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        float m[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = cb[e] * __expf(fminf(acs_i[it] - acj[e], 0.f)) * dtj[e];
+          m[e] = (j0 + e <= i) ? v : 0.f;
+        }
+        const f16x8 mf = cvt_f16x8(m);
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(xh[pt], mf, Y[pt][it]);
+      }
+      // state update: S^T += B^T (w x)
+#pragma unroll
+      for (int nt = 0; nt < K::NNT; ++nt) {
+        const f16x8 bt = b_frag<K>(Bh, js, 16 * nt, c.lane);
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) S[nt][pt] = M::mma(bt, xs[pt], S[nt][pt]);
+      }
+    }
+
+    // y = Y + D x (x exact from the raw bf16 tile), written over x in the stage (each lane
+    // overwrites exactly the x values it read); stored to memory after the next wait
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int i = 16 * it + c.c16;
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) {
+        const int col = c.p0 + 16 * pt + 4 * c.g;
+        uint2* xp = reinterpret_cast<uint2*>(st + xoff + swz<K::ROW_P>(i, col >> 3) +
+                                             ((col & 7) << 1));
+        const uint2 xr = *xp;
+        float x0, x1, x2, x3;
+        bf16x2_to_f32(xr.x, x0, x1);
+        bf16x2_to_f32(xr.y, x2, x3);
+        const f32x4 v = Y[pt][it];
+        *xp = make_uint2(cvt_bf16x2(v[0] + d_h * x0, v[1] + d_h * x1),
+                         cvt_bf16x2(v[2] + d_h * x2, v[3] + d_h * x3));
+      }
+    }
+    ytok = s * T;
   }
-
-  for (int c = c_begin; c < c_end; ++c) {
-    const int t0 = c * Q, q = min(Q, d.L - t0);
-    const bool carry = (c + 1) < c_end;
-    const int nslab = (q + SL - 1) / SL;
-    // C rows of this wave's tiles (zero past the end of the sequence)
-    f16x8 Cf[MAXI][NK];
-#pragma unroll
-    for (int m = 0; m < MAXI; ++m) {
-      const int ti = row_tile<K>(wave, m);
-      const int i = ti * 16 + col;
-      const bool valid = ti < nti && i < q;
-      const u16* crow = Cm + (((int64_t)b * d.L + t0 + (valid ? i : 0)) * d.G + g) * K::N;
-#pragma unroll
-      for (int kn = 0; kn < NK; ++kn) {
-        const uint4 v = *reinterpret_cast<const uint4*>(crow + kn * 32 + 8 * kg);
-        Cf[m][kn] = bf16x8_to_f16x8(valid ? v : make_uint4(0u, 0u, 0u, 0u));
-      }
-    }
-    __syncthreads();  // previous chunk's y tiles (aliasing h^T) and slab buffers are done
-    if (wave < HB) {
-      const int E = Q >= 64 ? Q / 64 : 1;
-      float loc[4], dv[4];
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = lane * E + e;
-        float v = 0.f;
-        if (e < E && i < q) v = dt[((int64_t)b * d.L + t0 + i) * d.H + h0 + wave];
-        dv[e] = v;
-        s += v * a_h;
-        loc[e] = s;
-      }
-      const float incl = wave_inclusive_scan(s);
-      float excl = __shfl_up(incl, 1, kWave);
-      if (lane == 0) excl = 0.f;
-      const int eq = (q - 1) % E;
-      float mine = excl + loc[0], mylast = excl + loc[0];
-#pragma unroll
-      for (int e = 1; e < 4; ++e) {
-        if (e == eq) mine = excl + loc[e];
-        if (e == E - 1) mylast = excl + loc[e];
-      }
-      const float vlast = __shfl(mine, (q - 1) / E, kWave);
-      if (lane * E + E - 1 >= q) mylast = vlast;
-      // cumulative decay at the last token of this lane's 32-token K step (a lane's E tokens
-      // never straddle two K steps); meaningful for Q >= 32
-      const float aend = __shfl(mylast, ((lane * E) | 31) / E, kWave);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = lane * E + e;
-        if (e < E && i < Q) {
-          const float a = (i < q) ? excl + loc[e] : vlast;
-          acs[wave][i] = a;
-          dts[wave][i] = dv[e];
-          wts[wave][i] = (i < q) ? __expf(vlast - a) * dv[e] : 0.f;
-          cfs[wave][i] = (i < q) ? __expf(aend - a) * dv[e] : 0.f;
-        }
-      }
-    }
-    {  // carried state -> h^T (fp16) for the readout
-      f16* ht = hreg + (sh * K::P + spt * 16 + col) * K::LDH;
-#pragma unroll
-      for (int k = 0; k < K::TS; ++k) {
-        const f16x2 lo = cvt_f16x2(Sacc[k][0], Sacc[k][1]);
-        const f16x2 hi = cvt_f16x2(Sacc[k][2], Sacc[k][3]);
-        *reinterpret_cast<f16x4*>(ht + (sn0 + k) * 16 + 4 * kg) = f16x4{lo[0], lo[1], hi[0], hi[1]};
-      }
-    }
-    __syncthreads();
-
-    // readout of the state entering this chunk
-    f32x4 Y[MAXI][HB][NP];
-    float acs_i[MAXI][HB];
-#pragma unroll
-    for (int m = 0; m < MAXI; ++m) {
-      const int ti = row_tile<K>(wave, m);
-#pragma unroll
-      for (int hh = 0; hh < HB; ++hh) {
-        acs_i[m][hh] = ti < nti ? acs[hh][ti * 16 + col] : 0.f;
-#pragma unroll
-        for (int pt = 0; pt < NP; ++pt) Y[m][hh][pt] = zero4();
-      }
-      if (ti >= nti) continue;
-#pragma unroll
-      for (int hh = 0; hh < HB; ++hh) {
-#pragma unroll
-        for (int kn = 0; kn < NK; ++kn) {
-#pragma unroll
-          for (int pt = 0; pt < NP; ++pt)
-            Y[m][hh][pt] = M::mma(
-                Cf[m][kn], M::lds(hreg + (hh * K::P + pt * 16 + col) * K::LDH + kn * 32 + 8 * kg),
-                Y[m][hh][pt]);
-        }
-        const float4 ar = *reinterpret_cast<const float4*>(&acs[hh][ti * 16 + 4 * kg]);
-        const float e4[4] = {__expf(ar.x), __expf(ar.y), __expf(ar.z), __expf(ar.w)};
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-          for (int pt = 0; pt < NP; ++pt) Y[m][hh][pt][rr] *= e4[rr];
-      }
-    }
-    if (carry) {
-      const float dec = __expf(acs[sh][Q - 1]);
-#pragma unroll
-      for (int k = 0; k < K::TS; ++k) Sacc[k] *= dec;
-    }
-
-    for (int s = 0; s < nslab; ++s) {
-      const int j0 = s * SL;
-      const bool more = (s + 1 < nslab) || (c + 1 < c_end);
-      if (more) {
-        if (s + 1 < nslab) {
-          slab_load<K>(pre, x, Bm, d, b, h0, g, t0, q, j0 + SL);
-        } else {
-          const int t1 = t0 + Q;
-          slab_load<K>(pre, x, Bm, d, b, h0, g, t1, min(Q, d.L - t1), 0);
-        }
-      }
-      const f16* Xst = Xs[stage];
-      const f16* Bst = Bs[stage];
-      // intra-chunk masked product
-#pragma unroll
-      for (int ks = 0; ks < SL / 32; ++ks) {
-        const int jb = j0 + ks * 32;  // chunk-local first token of this K step
-        bool act[MAXI];
-        bool any = false;
-#pragma unroll
-        for (int m = 0; m < MAXI; ++m) {
-          const int ti = row_tile<K>(wave, m);
-          act[m] = (ti < nti) && (ti * 16 + 15 >= jb);
-          any |= act[m];
-        }
-        if (!any) continue;
-        // (C B^T)^T for both 16-token halves of the K step and every active row tile; the B
-        // fragments are loaded once and shared by the tiles. Both halves are always formed: the
-        // second is wasted (and masked) only in the K step holding an even tile's diagonal.
-        f32x4 c0[MAXI], c1[MAXI];
-        {
-          f16x8 b0[NK], b1[NK];
-          const f16* brow = Bst + (ks * 32 + col) * K::LDB + 8 * kg;
-#pragma unroll
-          for (int kn = 0; kn < NK; ++kn) {
-            b0[kn] = M::lds(brow + kn * 32);
-            b1[kn] = M::lds(brow + 16 * K::LDB + kn * 32);
-          }
-#pragma unroll
-          for (int m = 0; m < MAXI; ++m) {
-            c0[m] = zero4();
-            c1[m] = zero4();
-            if (!act[m]) continue;
-#pragma unroll
-            for (int kn = 0; kn < NK; ++kn) {
-              c0[m] = M::mma(b0[kn], Cf[m][kn], c0[m]);
-              c1[m] = M::mma(b1[kn], Cf[m][kn], c1[m]);
-            }
-          }
-        }
-        const int ja = jb + 4 * kg;  // this lane's K slots: ja + rr and ja + 16 + rr
-#pragma unroll
-        for (int hh = 0; hh < HB; ++hh) {
-          f16x8 xf[NP];
-#pragma unroll
-          for (int pt = 0; pt < NP; ++pt)
-            xf[pt] = frag_k_acc(Xst + hh * SL * K::LDX, K::LDX, ks * 32, pt * 16, lane);
-          const float aend = acs[hh][jb + 31];
-          const float4 f0 = *reinterpret_cast<const float4*>(&cfs[hh][ja]);
-          const float4 f1 = *reinterpret_cast<const float4*>(&cfs[hh][ja + 16]);
-          const float cf[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-#pragma unroll
-          for (int m = 0; m < MAXI; ++m) {
-            if (!act[m]) continue;
-            const int ti = row_tile<K>(wave, m);
-            const int i = ti * 16 + col;
-            float v[8];
-            if (ti * 16 >= jb + 32) {  // strictly below the diagonal: factorized decay
-              const float rf = __expf(acs_i[m][hh] - aend);
-#pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                v[rr] = c0[m][rr] * rf * cf[rr];
-                v[4 + rr] = c1[m][rr] * rf * cf[4 + rr];
-              }
-            } else {  // the K step holding this tile's diagonal: direct form and causal mask
-              const float4 a0 = *reinterpret_cast<const float4*>(&acs[hh][ja]);
-              const float4 a1 = *reinterpret_cast<const float4*>(&acs[hh][ja + 16]);
-              const float4 d0 = *reinterpret_cast<const float4*>(&dts[hh][ja]);
-              const float4 d1 = *reinterpret_cast<const float4*>(&dts[hh][ja + 16]);
-              const float aj[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-              const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                const float e0 = c0[m][rr] * __expf(acs_i[m][hh] - aj[rr]) * dj[rr];
-                const float e1 = c1[m][rr] * __expf(acs_i[m][hh] - aj[4 + rr]) * dj[4 + rr];
-                v[rr] = (ja + rr <= i) ? e0 : 0.f;
-                v[4 + rr] = (ja + 16 + rr <= i) ? e1 : 0.f;
-              }
-            }
-            const f16x8 mf = cvt_f16x8(v);
-#pragma unroll
-            for (int pt = 0; pt < NP; ++pt) Y[m][hh][pt] = M::mma(mf, xf[pt], Y[m][hh][pt]);
-          }
-        }
-      }
-      // carried-state update with this slab
-      if (carry) {
-        const f16* X = Xst + sh * SL * K::LDX;
-#pragma unroll
-        for (int ks = 0; ks < SL / 32; ++ks) {
-          const f16x8 xv = frag_k(X, K::LDX, ks * 32, spt * 16, lane);
-          const float4 w0 = *reinterpret_cast<const float4*>(&wts[sh][j0 + ks * 32 + 8 * kg]);
-          const float4 w1 = *reinterpret_cast<const float4*>(&wts[sh][j0 + ks * 32 + 8 * kg + 4]);
-          const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-          float val[8];
-#pragma unroll
-          for (int qq = 0; qq < 8; ++qq) val[qq] = (float)xv[qq] * wv[qq];
-          const f16x8 wf = cvt_f16x8(val);
-#pragma unroll
-          for (int k = 0; k < K::TS; ++k)
-            Sacc[k] = M::mma(frag_k(Bst, K::LDB, ks * 32, (sn0 + k) * 16, lane), wf, Sacc[k]);
-        }
-      }
-      if (more) slab_store<K>(pre, Xs[stage ^ 1], Bs[stage ^ 1]);
-      __syncthreads();
-      stage ^= 1;
-    }
-
-    // y = accumulator + D x, rounded once to bf16. Each wave moves its 16-row tiles through an
-    // fp32 LDS tile (8 rows at a time) so that y is written, and x read back exactly (bf16) for
-    // the skip term, as whole 16-byte pieces of rows.
-    float* yt = reinterpret_cast<float*>(hreg) + wave * 8 * K::LDY;
-    constexpr int RP = HB * K::P / 8;  // 16-byte (8-value) pieces per row
-#pragma unroll
-    for (int m = 0; m < MAXI; ++m) {
-      const int ti = row_tile<K>(wave, m);
-      if (ti >= nti) continue;
-      // x for the skip term of this tile, loaded up front (rows past the end read row 0)
-      constexpr int PPL = (8 * RP + 63) / 64;  // pieces per lane per half
-      uint4 xr[2][PPL];
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int k = 0; k < PPL; ++k) {
-          const int e = lane + 64 * k;
-          const int row = e / RP, c8 = e % RP;
-          const int i = ti * 16 + 8 * half + row;
-          const int ir = (e < 8 * RP && i < q) ? i : 0;
-          xr[half][k] = *reinterpret_cast<const uint4*>(
-              x + (((int64_t)b * d.L + t0 + ir) * d.H + h0) * K::P + c8 * 8);
-        }
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if ((kg >> 1) == half) {  // lanes holding rows 8*half .. 8*half + 7
-#pragma unroll
-          for (int hh = 0; hh < HB; ++hh)
-#pragma unroll
-            for (int pt = 0; pt < NP; ++pt)
-#pragma unroll
-              for (int rr = 0; rr < 4; ++rr)
-                yt[(4 * (kg & 1) + rr) * K::LDY + hh * K::P + pt * 16 + col] = Y[m][hh][pt][rr];
-        }
-#pragma unroll
-        for (int k = 0; k < PPL; ++k) {
-          const int e = lane + 64 * k;
-          const int row = e / RP, c8 = e % RP;
-          const int i = ti * 16 + 8 * half + row;
-          if (e < 8 * RP && i < q) {
-            const int64_t off = (((int64_t)b * d.L + t0 + i) * d.H + h0) * K::P + c8 * 8;
-            const float dh = (c8 * 8 < K::P) ? Dh[0] : Dh[HB - 1];  // HB <= 2
-            const uint4 xw = xr[half][k];
-            const uint32_t xwv[4] = {xw.x, xw.y, xw.z, xw.w};
-            float xv[8];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              xv[2 * t] = __uint_as_float(xwv[t] << 16);
-              xv[2 * t + 1] = __uint_as_float(xwv[t] & 0xffff0000u);
-            }
-            const float4 lo = *reinterpret_cast<const float4*>(yt + row * K::LDY + c8 * 8);
-            const float4 hi = *reinterpret_cast<const float4*>(yt + row * K::LDY + c8 * 8 + 4);
-            const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            uint32_t packed[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              packed[k] = cvt_bf16x2(v[2 * k] + dh * xv[2 * k], v[2 * k + 1] + dh * xv[2 * k + 1]);
-            *reinterpret_cast<uint4*>(y + off) =
-                make_uint4(packed[0], packed[1], packed[2], packed[3]);
-          }
-        }
-      }
-    }
+  if (ytok >= 0) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's y tile writes have landed
+    store_y<K>(smem + ((s_end - 1 - s_begin) & 1) * K::SCAN_STAGE + xoff, y, d, c, ytok);
   }
 }
 
 // ---- launchers ----------------------------------------------------------------------------------
-// One head per block, 8 waves; MT 16-row output tiles per wave: 2 for Q = 256, 1 for Q <= 128.
-template <int P, int N, int SL>
-using CfgQ256 = Cfg<P, N, 1, 8, SL, 2>;
-template <int P, int N, int SL>
-using CfgQ128 = Cfg<P, N, 1, 8, SL, 1>;
-
-bool fused_supported(const Dims& d) {
-  return (d.P == 64 && (d.N == 64 || d.N == 128)) || (d.P == 128 && (d.N == 128 || d.N == 256));
+template <class K>
+static void plan_for(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
+  fp->T = K::T;
+  fp->nsub = (d.L + K::T - 1) / K::T;
+  const int hpg = d.H / d.G;
+  fp->head_blocks = d.G * ((hpg + K::HPB - 1) / K::HPB);
+  const int units = d.Bt * fp->head_blocks;
+  int RS;
+  if (run_tokens > 0) {
+    RS = (run_tokens + K::T - 1) / K::T;
+  } else {
+    int want = n_cu / units;  // runs per sequence: about one block per compute unit
+    if (want < 1) want = 1;
+    RS = (fp->nsub + want - 1) / want;
+  }
+  if (RS < 1) RS = 1;
+  if (RS > fp->nsub) RS = fp->nsub;
+  fp->RS = RS;
+  fp->nr = (fp->nsub + RS - 1) / RS;
 }
 
 template <class K>
-static hipError_t launch_phase(int phase, const Dims& d, const void* x, const void* B,
-                               const void* C, const float* dt, const float* A, const float* D,
-                               int S, int nr, float* states, float* logdecay,
-                               const float* h_run, void* y, hipStream_t s) {
-  dim3 grid(nr, d.H / K::HB, d.Bt);
+static hipError_t launch_k(int phase, const Dims& d, const FusedPlan& fp, const void* x,
+                           const void* B, const void* C, const float* dt, const float* A,
+                           const float* D, float* states, float* logdecay, const float* h_run,
+                           void* y, hipStream_t s) {
+  dim3 grid(fp.nr, fp.head_blocks, d.Bt);
   if (phase == 0)
     hipLaunchKernelGGL(k_run_state<K>, grid, dim3(K::NT), 0, s, (const u16*)x, (const u16*)B, dt,
-                       A, states, logdecay, d, S * d.Q, nr);
+                       A, states, logdecay, d, fp.RS, fp.nr);
   else
     hipLaunchKernelGGL(k_fused_scan<K>, grid, dim3(K::NT), 0, s, (const u16*)x, (const u16*)B,
-                       (const u16*)C, dt, A, D, h_run, (u16*)y, d, S, nr);
+                       (const u16*)C, dt, A, D, h_run, (u16*)y, d, fp.RS, fp.nr);
   return hipGetLastError();
 }
 
-template <int P, int N, int SL>
-static hipError_t dispatch_q(int phase, const Dims& d, const void* x, const void* B, const void* C,
-                             const float* dt, const float* A, const float* D, int S, int nr,
-                             float* states, float* logdecay, const float* h_run, void* y,
-                             hipStream_t s) {
-  if (d.Q > 128)
-    return launch_phase<CfgQ256<P, N, SL>>(phase, d, x, B, C, dt, A, D, S, nr, states, logdecay,
-                                           h_run, y, s);
-  return launch_phase<CfgQ128<P, N, SL>>(phase, d, x, B, C, dt, A, D, S, nr, states, logdecay,
-                                         h_run, y, s);
+#define SSD_FUSED_SHAPES(X) X(64, 64) X(64, 128) X(64, 256) X(128, 64) X(128, 128) X(128, 256)
+
+bool fused_plan(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
+#define SSD_PLAN(P_, N_)                              \
+  if (d.P == P_ && d.N == N_) {                       \
+    plan_for<Fz<P_, N_>>(d, run_tokens, n_cu, fp);    \
+    return true;                                      \
+  }
+  SSD_FUSED_SHAPES(SSD_PLAN)
+#undef SSD_PLAN
+  return false;
 }
 
-static hipError_t dispatch(int phase, const Dims& d, const void* x, const void* B, const void* C,
-                           const float* dt, const float* A, const float* D, int S, int nr,
-                           float* states, float* logdecay, const float* h_run, void* y,
-                           hipStream_t s) {
-#define SSD_PHASE(P, N, SL) \
-  dispatch_q<P, N, SL>(phase, d, x, B, C, dt, A, D, S, nr, states, logdecay, h_run, y, s)
-  if (d.P == 64 && d.N == 128) return SSD_PHASE(64, 128, 64);
-  if (d.P == 64 && d.N == 64) return SSD_PHASE(64, 64, 64);
-  if (d.P == 128 && d.N == 128) return SSD_PHASE(128, 128, 64);
-  if (d.P == 128 && d.N == 256) return SSD_PHASE(128, 256, 32);
-#undef SSD_PHASE
+static hipError_t dispatch(int phase, const Dims& d, const FusedPlan& fp, const void* x,
+                           const void* B, const void* C, const float* dt, const float* A,
+                           const float* D, float* states, float* logdecay, const float* h_run,
+                           void* y, hipStream_t s) {
+#define SSD_LAUNCH(P_, N_)                                                                    \
+  if (d.P == P_ && d.N == N_)                                                                 \
+    return launch_k<Fz<P_, N_>>(phase, d, fp, x, B, C, dt, A, D, states, logdecay, h_run, y, \
+                                s);
+  SSD_FUSED_SHAPES(SSD_LAUNCH)
+#undef SSD_LAUNCH
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_run_state(const Dims& d, const void* x, const void* B, const float* dt,
-                            const float* A, int S, int nr, float* states, float* logdecay,
+hipError_t launch_run_state(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
+                            const float* dt, const float* A, float* states, float* logdecay,
                             hipStream_t s) {
-  return dispatch(0, d, x, B, nullptr, dt, A, nullptr, S, nr, states, logdecay, nullptr, nullptr,
-                  s);
+  return dispatch(0, d, fp, x, B, nullptr, dt, A, nullptr, states, logdecay, nullptr, nullptr, s);
 }
 
-hipError_t launch_fused_scan(const Dims& d, const void* x, const void* B, const void* C,
-                             const float* dt, const float* A, const float* D,
-                             const float* h_run, void* y, int S, int nr, hipStream_t s) {
-  return dispatch(1, d, x, B, C, dt, A, D, S, nr, nullptr, nullptr, h_run, y, s);
+hipError_t launch_fused_scan(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
+                             const void* C, const float* dt, const float* A, const float* D,
+                             const float* h_run, void* y, hipStream_t s) {
+  return dispatch(1, d, fp, x, B, C, dt, A, D, nullptr, nullptr, h_run, y, s);
 }
 
 }  // namespace ssd

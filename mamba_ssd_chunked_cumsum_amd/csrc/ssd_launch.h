@@ -31,13 +31,21 @@ hipError_t launch_chunk_scan(const Dims& d, int io, int prec, const void* x, con
 
 
 // fused path (bf16 io)
-bool fused_supported(const Dims& d);
-// S = chunks per run, nr = runs per sequence; states [Bt, nr, H, P, N], logdecay [Bt, H, nr]
-hipError_t launch_run_state(const Dims& d, const void* x, const void* B, const float* dt,
-                            const float* A, int S, int nr, float* states, float* logdecay,
+// Sub-chunk walk of one fused forward: T tokens per sub-chunk, nsub sub-chunks per sequence, runs
+// of RS sub-chunks (nr runs), head_blocks blocks per (batch, run).
+struct FusedPlan {
+  int T, nsub, RS, nr, head_blocks;
+};
+// False when the fused kernels do not cover (P, N). run_tokens > 0 asks for runs of at least that
+// many tokens; 0 lets the plan aim at about one block per compute unit (n_cu of them).
+bool fused_plan(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp);
+// states [Bt, nr, H, P, N] (each run's end state from a zero entry state), logdecay [Bt, H, nr]
+hipError_t launch_run_state(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
+                            const float* dt, const float* A, float* states, float* logdecay,
                             hipStream_t s);
-hipError_t launch_fused_scan(const Dims& d, const void* x, const void* B, const void* C,
-                             const float* dt, const float* A, const float* D,
-                             const float* h_run, void* y, int S, int nr, hipStream_t s);
+// h_run [Bt, nr, H, P, N]: the state entering each run
+hipError_t launch_fused_scan(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
+                             const void* C, const float* dt, const float* A, const float* D,
+                             const float* h_run, void* y, hipStream_t s);
 
 }  // namespace ssd
