@@ -48,6 +48,12 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Scheduling fence: keeps the compiler from hoisting one step's LDS reads (and the registers they
+// hold) above the previous step.
+#define SSD_SB() __builtin_amdgcn_sched_barrier(0)
+
 // ---- small helpers ------------------------------------------------------------------------------
 __device__ __forceinline__ f16x2 cvt_f16x2(float a, float b) {  // v_cvt_pk_f16_f32, RNE
   return __builtin_convertvector(f32x2{a, b}, f16x2);
@@ -122,13 +128,13 @@ __device__ __forceinline__ s16x8 frag_tr(const char* tile, int r0, int col0, int
 }
 
 // ---- configuration ----------------------------------------------------------------------------
-template <int P_, int N_>
+template <int P_, int N_, int NW_ = 4, int PSMAX_ = 64>
 struct Fz {
   static constexpr int P = P_, N = N_;
   static constexpr int T = N >= 256 ? 32 : 64;  // tokens per sub-chunk
-  static constexpr int NW = 4, NT = 256;
+  static constexpr int NW = NW_, NT = 64 * NW_;
   static constexpr int PS0 = 8192 / N < P ? 8192 / N : P;
-  static constexpr int PS = PS0 < 64 ? PS0 : 64;  // p columns per wave
+  static constexpr int PS = PS0 < PSMAX_ ? PS0 : PSMAX_;  // p columns per wave
   static constexpr int WPH = P / PS, HPB = NW / WPH;  // waves per head, heads per block
   static constexpr int NPT = PS / 16, NNT = N / 16, NKN = N / 32, NIT = T / 16, NJS = T / 32;
   static constexpr int ROW_N = N * 2, ROW_P = P * 2;  // staged row bytes
@@ -138,7 +144,8 @@ struct Fz {
   static constexpr int SCAN_NI = SCAN_STAGE / 1024, RUN_NI = RUN_STAGE / 1024;
   static constexpr int LDCB = T + 4;                  // floats per C B^T row
   static constexpr int CB_BYTES = T * LDCB * 4;
-  static constexpr int WA_BYTES = NW * 3 * T * 4;     // per-wave acs, dt, w
+  static constexpr int NWA = 4;                       // per-wave token arrays
+  static constexpr int WA_BYTES = NW * NWA * T * 4;   // acs2, dt, w, cf
   static constexpr int NSCAN = 2, NRUN = 3;           // stages
   static constexpr int SCAN_LDS = NSCAN * SCAN_STAGE + CB_BYTES + WA_BYTES;
   static constexpr int RUN_LDS = NRUN * RUN_STAGE + WA_BYTES;
@@ -167,7 +174,7 @@ __device__ __forceinline__ Coord coords(const Dims& d) {
   const int first = (blockIdx.y % hbg) * K::HPB;
   c.hbase = c.grp * hpg + first;
   c.hlast = c.grp * hpg + hpg - 1;
-  c.wave = threadIdx.x >> 6;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar registers
   c.lane = threadIdx.x & 63;
   c.g = c.lane >> 4;
   c.c16 = c.lane & 15;
@@ -178,53 +185,107 @@ __device__ __forceinline__ Coord coords(const Dims& d) {
   return c;
 }
 
+// Per-lane byte offsets of the DMA pieces of a full sub-chunk. Instruction kk of a region with
+// PPR 16-byte pieces per row covers rows kk * RPI .. + RPI - 1 (RPI = 64 / PPR); lane l fetches
+// piece (l % PPR) ^ (t & 7) of row t = kk * RPI + l / PPR. Since RPI * kk mod 8 cycles with period
+// NPAT = 8 / RPI, the lane part of the address takes NPAT values; the rest is wave-uniform.
+template <int PPR>
+struct DmaPat {
+  static constexpr int RPI = 64 / PPR, NPAT = RPI >= 8 ? 1 : 8 / RPI;
+  uint32_t off[NPAT];
+  __device__ __forceinline__ void init(int lane, uint32_t ld) {
+#pragma unroll
+    for (int q = 0; q < NPAT; ++q) {
+      const int r = lane / PPR, t7 = (q * RPI + r) & 7;
+      off[q] = (uint32_t)r * ld + (uint32_t)(((lane % PPR) ^ t7) << 4);
+    }
+  }
+  __device__ __forceinline__ uint32_t at(int kk) const {
+    uint32_t o = off[0];
+#pragma unroll
+    for (int q = 1; q < NPAT; ++q)
+      if (kk % NPAT == q) o = off[q];
+    return o;
+  }
+};
+
+template <class K>
+struct DmaLanes {
+  DmaPat<K::N / 8> bc;
+  DmaPat<K::P / 8> x;
+  __device__ __forceinline__ void init(const Dims& d, int lane) {
+    bc.init(lane, (uint32_t)d.G * K::N * 2);
+    x.init(lane, (uint32_t)d.H * K::P * 2);
+  }
+};
+
+// Re-derive the lane coordinates through an opaque copy at the top of every sub-chunk, so that the
+// compiler recomputes lane-dependent addresses and masks where they are used instead of hoisting
+// all of them out of the loop (which costs more registers than the loop body has).
+__device__ __forceinline__ void refresh_lane(Coord& c) {
+  asm volatile("" : "+v"(c.lane));
+  c.g = c.lane >> 4;
+  c.c16 = c.lane & 15;
+}
+
 // Issue one stage's DMA: [B][C if WITH_C][x of the block's heads], tokens tok0 .. tok0 + T - 1.
 // In the last, partial sub-chunk rows past the sequence end re-read its last row; heads past the
 // group re-read its last head (their results are never used).
-template <class K, bool WITH_C, bool FULL>
-__device__ __forceinline__ void issue_stage_(char* st, const u16* x, const u16* Bm, const u16* Cm,
-                                             const Dims& d, const Coord& c, int tok0) {
+template <class K, bool WITH_C>
+__device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* Bm, const u16* Cm,
+                                            const Dims& d, const Coord& c, const DmaLanes<K>& dl,
+                                            int tok0) {
   constexpr int NBC = (WITH_C ? 2 : 1) * K::BC_NI;
   constexpr int NI = WITH_C ? K::SCAN_NI : K::RUN_NI;
   constexpr int PPR_N = K::N / 8, PPR_P = K::P / 8;
   constexpr int RPI_N = 64 / PPR_N, RPI_P = 64 / PPR_P;
-  const uint32_t ldbc = (uint32_t)d.G * K::N * 2, ldx = (uint32_t)d.H * K::P * 2;  // row bytes
+  const int64_t ldbc = (int64_t)d.G * K::N * 2, ldx = (int64_t)d.H * K::P * 2;  // row bytes
   const char* bbase = reinterpret_cast<const char*>(Bm) +
                       (((int64_t)c.b * d.L + tok0) * d.G + c.grp) * (K::N * 2);
   const char* cbase = reinterpret_cast<const char*>(Cm) +
                       (((int64_t)c.b * d.L + tok0) * d.G + c.grp) * (K::N * 2);
   const char* xbase = reinterpret_cast<const char*>(x) +
                       (((int64_t)c.b * d.L + tok0) * d.H + c.hbase) * (K::P * 2);
-  const int last = d.L - 1 - tok0;  // last valid row of the sub-chunk
+  if (tok0 + K::T <= d.L) {
 #pragma unroll
-  for (int k0 = 0; k0 < NI; k0 += K::NW) {
-    const int k = k0 + c.wave;
-    const char* src;
-    if (k0 < NBC) {  // B or C (NBC and BC_NI are multiples of NW: uniform per k0)
-      const bool isC = WITH_C && k0 >= K::BC_NI;
-      const int kk = isC ? k - K::BC_NI : k;
-      const int t = kk * RPI_N + c.lane / PPR_N, cp = c.lane % PPR_N;
-      const int row = FULL ? t : min(t, last);
-      src = (isC ? cbase : bbase) + (int64_t)row * ldbc + ((cp ^ (t & 7)) << 4);
-    } else {
-      const int kk = k - NBC;
-      const int hh = kk / (K::T / RPI_P), kr = kk % (K::T / RPI_P);
-      const int hoff = min(hh, c.hlast - c.hbase) * (K::P * 2);
-      const int t = kr * RPI_P + c.lane / PPR_P, cp = c.lane % PPR_P;
-      const int row = FULL ? t : min(t, last);
-      src = xbase + hoff + (int64_t)row * ldx + ((cp ^ (t & 7)) << 4);
+    for (int k0 = 0; k0 < NI; k0 += K::NW) {
+      const int k = k0 + c.wave;
+      if (k0 < NBC) {  // B or C (NBC and BC_NI are multiples of NW: uniform per k0)
+        const bool isC = WITH_C && k0 >= K::BC_NI;
+        const int kk = isC ? k - K::BC_NI : k;
+        // one 32-bit lane offset on top of the uniform sub-chunk base (keeps the per-instruction
+        // part out of the scalar registers)
+        const uint32_t o = dl.bc.at(kk) + (uint32_t)(kk * RPI_N) * (uint32_t)ldbc;
+        dma16((isC ? cbase : bbase) + o, st + k * 1024);
+      } else {
+        const int kk = k - NBC;
+        const int hh = kk / (K::T / RPI_P), kr = kk % (K::T / RPI_P);
+        const int hoff = min(hh, c.hlast - c.hbase) * (K::P * 2);
+        const uint32_t o = (uint32_t)hoff + dl.x.at(kr) + (uint32_t)(kr * RPI_P) * (uint32_t)ldx;
+        dma16(xbase + o, st + k * 1024);
+      }
     }
-    dma16(src, st + k * 1024);
+  } else {
+    const int last = d.L - 1 - tok0;  // last valid row of the sub-chunk
+#pragma unroll
+    for (int k0 = 0; k0 < NI; k0 += K::NW) {
+      const int k = k0 + c.wave;
+      const char* src;
+      if (k0 < NBC) {
+        const bool isC = WITH_C && k0 >= K::BC_NI;
+        const int kk = isC ? k - K::BC_NI : k;
+        const int t = kk * RPI_N + c.lane / PPR_N, cp = c.lane % PPR_N;
+        src = (isC ? cbase : bbase) + (int64_t)min(t, last) * ldbc + ((cp ^ (t & 7)) << 4);
+      } else {
+        const int kk = k - NBC;
+        const int hh = kk / (K::T / RPI_P), kr = kk % (K::T / RPI_P);
+        const int hoff = min(hh, c.hlast - c.hbase) * (K::P * 2);
+        const int t = kr * RPI_P + c.lane / PPR_P, cp = c.lane % PPR_P;
+        src = xbase + hoff + (int64_t)min(t, last) * ldx + ((cp ^ (t & 7)) << 4);
+      }
+      dma16(src, st + k * 1024);
+    }
   }
-}
-
-template <class K, bool WITH_C>
-__device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* Bm, const u16* Cm,
-                                            const Dims& d, const Coord& c, int tok0) {
-  if (tok0 + K::T <= d.L)
-    issue_stage_<K, WITH_C, true>(st, x, Bm, Cm, d, c, tok0);
-  else
-    issue_stage_<K, WITH_C, false>(st, x, Bm, Cm, d, c, tok0);
 }
 
 // Convert this wave's own DMA'd B (and C) pieces of a stage from bf16 to fp16 in place.
@@ -247,16 +308,22 @@ __device__ __forceinline__ float load_dt(const float* dt, const Dims& d, const C
   return (c.lane < K::T && t < d.L && c.active) ? v : 0.f;
 }
 
-// Per-sub-chunk decay bookkeeping of one wave (lane l = token l): inclusive cumulative log-decay
-// acs, dt, and state weights w = exp(acs_end - acs) dt into the wave's LDS arrays. Returns acs_end.
+// Per-sub-chunk decay bookkeeping of one wave (lane l = token l, acs = inclusive cumulative
+// log-decay from the sub-chunk start). Into the wave's LDS arrays:
+//   acs2 = acs log2(e);  dt;  w = exp(acs_end - acs) dt (state weights);
+//   cf = exp(acs_e - acs) dt, e the last token of the token's 16-row block (column factor of the
+//   off-diagonal blocks of the decay mask; both of its factors are <= 1).
+// Returns acs_end.
 template <class K>
 __device__ __forceinline__ float decay_terms(float dv, float a_h, float* wa, const Coord& c) {
   const float acs = wave_inclusive_scan(a_h * dv);
   const float acs_end = __shfl(acs, K::T - 1, kWave);
+  const float acs_blk = __shfl(acs, c.lane | 15, kWave);
   if (c.lane < K::T) {
-    wa[c.lane] = acs;
+    wa[c.lane] = acs * kLog2e;
     wa[K::T + c.lane] = dv;
     wa[2 * K::T + c.lane] = __expf(acs_end - acs) * dv;
+    wa[3 * K::T + c.lane] = __expf(acs_blk - acs) * dv;
   }
   return acs_end;
 }
@@ -280,7 +347,7 @@ __device__ __forceinline__ f16x8 b_frag(const char* Bh, int js, int col0, int la
 // logdecay_r = sum_{t in run} dt_t A. Walked forwards: per sub-chunk, S <- exp(acs_end) S +
 // B^T (w x), the weighted x split into fp16 high and low parts.
 template <class K>
-__global__ __launch_bounds__(256, 1) void k_run_state(const u16* __restrict__ x,
+__global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ x,
                                                       const u16* __restrict__ Bm,
                                                       const float* __restrict__ dt,
                                                       const float* __restrict__ Av,
@@ -289,12 +356,14 @@ __global__ __launch_bounds__(256, 1) void k_run_state(const u16* __restrict__ x,
                                                       int RS, int nr) {
   using M = Mma<f16>;
   __shared__ __align__(1024) char smem[K::RUN_LDS];
-  const Coord c = coords<K>(d);
+  Coord c = coords<K>(d);
+  DmaLanes<K> dl;
+  dl.init(d, c.lane);
   constexpr int T = K::T;
   const int nsub = (d.L + T - 1) / T;
   const int s_begin = c.r * RS, s_end = min(nsub, s_begin + RS);
   if (s_begin >= s_end) return;
-  float* wa = reinterpret_cast<float*>(smem + K::NRUN * K::RUN_STAGE) + c.wave * 3 * T;
+  float* wa = reinterpret_cast<float*>(smem + K::NRUN * K::RUN_STAGE) + c.wave * K::NWA * T;
   const int xoff = K::BC_BYTES + (c.wave / K::WPH) * (T * K::ROW_P);
   const float a_h = Av[c.h];
 
@@ -306,9 +375,9 @@ __global__ __launch_bounds__(256, 1) void k_run_state(const u16* __restrict__ x,
   float logsum = 0.f;
 
   // prologue: stages of the first two sub-chunks, dt of the first
-  issue_stage<K, false>(smem, x, Bm, nullptr, d, c, s_begin * T);
+  issue_stage<K, false>(smem, x, Bm, nullptr, d, c, dl, s_begin * T);
   if (s_begin + 1 < s_end)
-    issue_stage<K, false>(smem + K::RUN_STAGE, x, Bm, nullptr, d, c, (s_begin + 1) * T);
+    issue_stage<K, false>(smem + K::RUN_STAGE, x, Bm, nullptr, d, c, dl, (s_begin + 1) * T);
   float dt_next = load_dt<K>(dt, d, c, s_begin * T);
 
   for (int s = s_begin; s < s_end; ++s) {
@@ -323,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void k_run_state(const u16* __restrict__ x,
     convert_stage<K, false>(st, c);
     __syncthreads();  // stage visible to all waves; every wave is done with sub-chunk s - 1
     if (s + 2 < s_end)
-      issue_stage<K, false>(smem + ((cur + 2) % K::NRUN) * K::RUN_STAGE, x, Bm, nullptr, d, c,
+      issue_stage<K, false>(smem + ((cur + 2) % K::NRUN) * K::RUN_STAGE, x, Bm, nullptr, d, c, dl,
                             (s + 2) * T);
     if (s + 1 < s_end) dt_next = load_dt<K>(dt, d, c, (s + 1) * T);
     const float acs_end = decay_terms<K>(dv, a_h, wa, c);
@@ -376,23 +445,27 @@ __global__ __launch_bounds__(256, 1) void k_run_state(const u16* __restrict__ x,
 }
 
 // Store the bf16 y tile that F3 left in the x tile of a stage: this wave's p-slice of its head,
-// rows tok0 .. tok0 + T - 1 (rows past the sequence end skipped), 16 bytes per lane.
+// rows tok0 .. tok0 + T - 1 (rows past the sequence end skipped), 16 bytes per lane. Round k
+// covers rows k * RPR .. + RPR - 1; the lane parts of the LDS and global addresses do not depend
+// on k (RPR is a multiple of 8, so the swizzle pattern repeats).
 template <class K>
 __device__ __forceinline__ void store_y(const char* xt, u16* y, const Dims& d, const Coord& c,
                                         int tok0) {
   if (!c.active) return;
   constexpr int PPR = K::PS / 8;  // pieces per row of the wave's slice
-  constexpr int PIECES = K::T * PPR;
-  static_assert(PIECES % 64 == 0, "whole store rounds");
-  u16* yb = y + (((int64_t)c.b * d.L + tok0) * d.H + c.h) * K::P;
-  const int64_t ld = (int64_t)d.H * K::P;
+  constexpr int RPR = 64 / PPR;   // rows per round
+  constexpr int ROUNDS = K::T / RPR;
+  static_assert(RPR % 8 == 0 && K::T % RPR == 0, "whole store rounds");
+  const int r = c.lane / PPR, cp = (c.p0 >> 3) + c.lane % PPR;
+  const int64_t ld = (int64_t)d.H * K::P;  // y row stride (elements)
+  u16* yb = y + (((int64_t)c.b * d.L + tok0) * d.H + c.h) * K::P + (cp << 3) + r * ld;
+  const char* xl = xt + r * K::ROW_P + ((cp ^ (r & 7)) << 4);
   const int nrow = d.L - tok0;  // valid rows
 #pragma unroll
-  for (int k = 0; k < PIECES / 64; ++k) {
-    const int e = k * 64 + c.lane;
-    const int t = e / PPR, cp = (c.p0 >> 3) + e % PPR;
-    const uint4 v = *reinterpret_cast<const uint4*>(xt + swz<K::ROW_P>(t, cp));
-    if (nrow >= K::T || t < nrow) *reinterpret_cast<uint4*>(yb + t * ld + (cp << 3)) = v;
+  for (int k = 0; k < ROUNDS; ++k) {
+    const uint4 v = *reinterpret_cast<const uint4*>(xl + k * RPR * K::ROW_P);
+    if (nrow >= K::T || k * RPR + r < nrow)
+      *reinterpret_cast<uint4*>(yb + (int64_t)(k * RPR) * ld) = v;
   }
 }
 
@@ -404,20 +477,22 @@ __device__ __forceinline__ void store_y(const char* xt, u16* y, const Dims& d, c
 // four consecutive p of one token: the readout's A operand comes straight from the state
 // accumulators (K index n in accumulator order), and y leaves in 8-byte row pieces.
 template <class K>
-__global__ __launch_bounds__(256, 1) void k_fused_scan(
+__global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     const u16* __restrict__ x, const u16* __restrict__ Bm, const u16* __restrict__ Cm,
     const float* __restrict__ dt, const float* __restrict__ Av, const float* __restrict__ Dv,
     const float* __restrict__ h_run, u16* __restrict__ y, Dims d, int RS, int nr) {
   using M = Mma<f16>;
   __shared__ __align__(1024) char smem[K::SCAN_LDS];
-  const Coord c = coords<K>(d);
+  Coord c = coords<K>(d);
+  DmaLanes<K> dl;
+  dl.init(d, c.lane);
   constexpr int T = K::T, NPT = K::NPT, NIT = K::NIT;
   const int nsub = (d.L + T - 1) / T;
   const int s_begin = c.r * RS, s_end = min(nsub, s_begin + RS);
   if (s_begin >= s_end) return;
   float* cbs = reinterpret_cast<float*>(smem + K::NSCAN * K::SCAN_STAGE);
   float* wa = reinterpret_cast<float*>(smem + K::NSCAN * K::SCAN_STAGE + K::CB_BYTES) +
-              c.wave * 3 * T;
+              c.wave * K::NWA * T;
   const int xoff = 2 * K::BC_BYTES + (c.wave / K::WPH) * (T * K::ROW_P);
   const float a_h = Av[c.h], d_h = Dv[c.h];
 
@@ -437,11 +512,12 @@ __global__ __launch_bounds__(256, 1) void k_fused_scan(
       }
   }
 
-  issue_stage<K, true>(smem, x, Bm, Cm, d, c, s_begin * T);
+  issue_stage<K, true>(smem, x, Bm, Cm, d, c, dl, s_begin * T);
   float dt_next = load_dt<K>(dt, d, c, s_begin * T);
   int ytok = -1;  // first token of the sub-chunk whose y waits in the previous stage's x tile
 
   for (int s = s_begin; s < s_end; ++s) {
+    refresh_lane(c);
     const int cur = (s - s_begin) & 1;
     char* st = smem + cur * K::SCAN_STAGE;
     const char* Bh = st;
@@ -453,7 +529,7 @@ __global__ __launch_bounds__(256, 1) void k_fused_scan(
     convert_stage<K, true>(st, c);
     __syncthreads();  // stage visible; every wave is done with sub-chunk s - 1 (CB, stage cur^1)
     if (s + 1 < s_end) {
-      issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, d, c, (s + 1) * T);
+      issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, d, c, dl, (s + 1) * T);
       dt_next = load_dt<K>(dt, d, c, (s + 1) * T);
     }
     // C B^T lower-triangle tiles of the sub-chunk, shared by the block's heads: tile q (row-major
@@ -511,14 +587,15 @@ __global__ __launch_bounds__(256, 1) void k_fused_scan(
         for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(sa[pt], cf, Y[pt][it]);
       }
     }
-    float acs_i[NIT];
+    float acs2_i[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      acs_i[it] = wa[16 * it + c.c16];
-      const float e = __expf(acs_i[it]);
+      acs2_i[it] = wa[16 * it + c.c16];
+      const float e = __builtin_amdgcn_exp2f(acs2_i[it]);
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) Y[pt][it] *= e;
     }
+    SSD_SB();
 
     // state decay (the readout above used the entry state)
     const float dec = __expf(acs_end);
@@ -529,27 +606,23 @@ __global__ __launch_bounds__(256, 1) void k_fused_scan(
 
 #pragma unroll
     for (int js = 0; js < K::NJS; ++js) {
-      const int j0 = 32 * js + 8 * c.g;
-      const float4 a0 = *reinterpret_cast<const float4*>(wa + j0);
-      const float4 a1 = *reinterpret_cast<const float4*>(wa + j0 + 4);
-      const float4 d0 = *reinterpret_cast<const float4*>(wa + T + j0);
-      const float4 d1 = *reinterpret_cast<const float4*>(wa + T + j0 + 4);
-      const float4 w0 = *reinterpret_cast<const float4*>(wa + 2 * T + j0);
-      const float4 w1 = *reinterpret_cast<const float4*>(wa + 2 * T + j0 + 4);
-      const float acj[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      const float dtj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-      const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      const int j0 = 32 * js + 8 * c.g;  // this lane's 8 tokens of the K step
       f16x8 xh[NPT], xs[NPT];
+      {
+        const float4 w0 = *reinterpret_cast<const float4*>(wa + 2 * T + j0);
+        const float4 w1 = *reinterpret_cast<const float4*>(wa + 2 * T + j0 + 4);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const f16x8 w16 = cvt_f16x8(wv);
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) {
-        float v[8];
-        x_frag<K>(xt, js, c.p0 + 16 * pt, c.lane, v);
-        xh[pt] = cvt_f16x8(v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= wj[e];
-        xs[pt] = cvt_f16x8(v);
+        for (int pt = 0; pt < NPT; ++pt) {
+          float v[8];
+          x_frag<K>(xt, js, c.p0 + 16 * pt, c.lane, v);
+          xh[pt] = cvt_f16x8(v);
+          xs[pt] = xh[pt] * w16;  // packed fp16 multiply
+        }
       }
-      // intra-sub-chunk product: Y^T += x^T M^T, M_ij = CB_ij exp(acs_i - acs_j) dt_j (j <= i)
+      // intra-sub-chunk product: Y^T += x^T M^T, M_ij = CB_ij exp(acs_i - acs_j) dt_j (j <= i),
+      // plus D on the diagonal (the skip term D x_i rides along with the diagonal block)
 #pragma unroll
       for (int it = 2 * js; it < NIT; ++it) {
         const int i = 16 * it + c.c16;
@@ -557,15 +630,34 @@ __global__ __launch_bounds__(256, 1) void k_fused_scan(
         const float4 c1 = *reinterpret_cast<const float4*>(cbs + i * K::LDCB + j0 + 4);
         const float cb[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
         float m[8];
+        if (2 * js + 1 < it) {
+          // both 16-token blocks of the K step lie before token tile it: factor the decay
+          // through the end of the lane's block, exp(acs_i - acs_e) * [exp(acs_e - acs_j) dt_j]
+          const int e = 32 * js + 16 * (c.g >> 1) + 15;
+          const float r = __builtin_amdgcn_exp2f(acs2_i[it] - wa[e]);
+          const float4 f0 = *reinterpret_cast<const float4*>(wa + 3 * T + j0);
+          const float4 f1 = *reinterpret_cast<const float4*>(wa + 3 * T + j0 + 4);
+          const float cf[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = cb[e] * __expf(fminf(acs_i[it] - acj[e], 0.f)) * dtj[e];
-          m[e] = (j0 + e <= i) ? v : 0.f;
+          for (int q = 0; q < 8; ++q) m[q] = cb[q] * cf[q] * r;
+        } else {
+          const float4 a0 = *reinterpret_cast<const float4*>(wa + j0);
+          const float4 a1 = *reinterpret_cast<const float4*>(wa + j0 + 4);
+          const float4 d0 = *reinterpret_cast<const float4*>(wa + T + j0);
+          const float4 d1 = *reinterpret_cast<const float4*>(wa + T + j0 + 4);
+          const float acj[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+          const float dtj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float v = cb[q] * __builtin_amdgcn_exp2f(fminf(acs2_i[it] - acj[q], 0.f)) * dtj[q];
+            m[q] = (j0 + q < i) ? v : ((j0 + q == i) ? v + d_h : 0.f);
+          }
         }
         const f16x8 mf = cvt_f16x8(m);
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(xh[pt], mf, Y[pt][it]);
       }
+      SSD_SB();
       // state update: S^T += B^T (w x)
 #pragma unroll
       for (int nt = 0; nt < K::NNT; ++nt) {
@@ -573,25 +665,20 @@ __global__ __launch_bounds__(256, 1) void k_fused_scan(
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) S[nt][pt] = M::mma(bt, xs[pt], S[nt][pt]);
       }
+      SSD_SB();
     }
 
-    // y = Y + D x (x exact from the raw bf16 tile), written over x in the stage (each lane
-    // overwrites exactly the x values it read); stored to memory after the next wait
+    // y = Y, written over x in the stage (each lane's 8-byte pieces are its own and x is no
+    // longer needed); stored to memory after the next wait
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int i = 16 * it + c.c16;
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
         const int col = c.p0 + 16 * pt + 4 * c.g;
-        uint2* xp = reinterpret_cast<uint2*>(st + xoff + swz<K::ROW_P>(i, col >> 3) +
-                                             ((col & 7) << 1));
-        const uint2 xr = *xp;
-        float x0, x1, x2, x3;
-        bf16x2_to_f32(xr.x, x0, x1);
-        bf16x2_to_f32(xr.y, x2, x3);
         const f32x4 v = Y[pt][it];
-        *xp = make_uint2(cvt_bf16x2(v[0] + d_h * x0, v[1] + d_h * x1),
-                         cvt_bf16x2(v[2] + d_h * x2, v[3] + d_h * x3));
+        *reinterpret_cast<uint2*>(st + xoff + swz<K::ROW_P>(i, col >> 3) + ((col & 7) << 1)) =
+            make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
       }
     }
     ytok = s * T;
@@ -603,18 +690,35 @@ __global__ __launch_bounds__(256, 1) void k_fused_scan(
 }
 
 // ---- launchers ----------------------------------------------------------------------------------
+// Configurations: both kernels run two waves per SIMD (8 waves per block, 32-column slices), so
+// one wave's memory and matrix-core latencies hide behind the other's work and each wave fits in
+// 256 registers. Both walk the same sub-chunks (T depends on N only), so their runs line up.
+#ifndef SSD_F3_NW
+#define SSD_F3_NW 8
+#define SSD_F3_PS 32
+#endif
+template <int P, int N>
+using RunCfg = Fz<P, N, 8, 32>;
+template <int P, int N>
+using ScanCfg = Fz<P, N, SSD_F3_NW, SSD_F3_PS>;
+
 template <class K>
-static void plan_for(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
-  fp->T = K::T;
-  fp->nsub = (d.L + K::T - 1) / K::T;
+static int head_blocks(const Dims& d) {
   const int hpg = d.H / d.G;
-  fp->head_blocks = d.G * ((hpg + K::HPB - 1) / K::HPB);
+  return d.G * ((hpg + K::HPB - 1) / K::HPB);
+}
+
+template <class K3>
+static void plan_for(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
+  fp->T = K3::T;
+  fp->nsub = (d.L + K3::T - 1) / K3::T;
+  fp->head_blocks = head_blocks<K3>(d);
   const int units = d.Bt * fp->head_blocks;
   int RS;
   if (run_tokens > 0) {
-    RS = (run_tokens + K::T - 1) / K::T;
+    RS = (run_tokens + K3::T - 1) / K3::T;
   } else {
-    int want = n_cu / units;  // runs per sequence: about one block per compute unit
+    int want = n_cu / units;  // runs per sequence: about one scan block per compute unit
     if (want < 1) want = 1;
     RS = (fp->nsub + want - 1) / want;
   }
@@ -624,28 +728,32 @@ static void plan_for(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
   fp->nr = (fp->nsub + RS - 1) / RS;
 }
 
-template <class K>
+template <class K1, class K3>
 static hipError_t launch_k(int phase, const Dims& d, const FusedPlan& fp, const void* x,
                            const void* B, const void* C, const float* dt, const float* A,
                            const float* D, float* states, float* logdecay, const float* h_run,
                            void* y, hipStream_t s) {
-  dim3 grid(fp.nr, fp.head_blocks, d.Bt);
+  static_assert(K1::T == K3::T, "F1 and F3 walk the same sub-chunks");
   if (phase == 0)
-    hipLaunchKernelGGL(k_run_state<K>, grid, dim3(K::NT), 0, s, (const u16*)x, (const u16*)B, dt,
-                       A, states, logdecay, d, fp.RS, fp.nr);
+    hipLaunchKernelGGL(k_run_state<K1>, dim3(fp.nr, head_blocks<K1>(d), d.Bt), dim3(K1::NT), 0,
+                       s, (const u16*)x, (const u16*)B, dt, A, states, logdecay, d, fp.RS,
+                       fp.nr);
   else
-    hipLaunchKernelGGL(k_fused_scan<K>, grid, dim3(K::NT), 0, s, (const u16*)x, (const u16*)B,
-                       (const u16*)C, dt, A, D, h_run, (u16*)y, d, fp.RS, fp.nr);
+    hipLaunchKernelGGL(k_fused_scan<K3>, dim3(fp.nr, head_blocks<K3>(d), d.Bt), dim3(K3::NT), 0,
+                       s, (const u16*)x, (const u16*)B, (const u16*)C, dt, A, D, h_run, (u16*)y,
+                       d, fp.RS, fp.nr);
   return hipGetLastError();
 }
 
+#ifndef SSD_FUSED_SHAPES
 #define SSD_FUSED_SHAPES(X) X(64, 64) X(64, 128) X(64, 256) X(128, 64) X(128, 128) X(128, 256)
+#endif
 
 bool fused_plan(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
-#define SSD_PLAN(P_, N_)                              \
-  if (d.P == P_ && d.N == N_) {                       \
-    plan_for<Fz<P_, N_>>(d, run_tokens, n_cu, fp);    \
-    return true;                                      \
+#define SSD_PLAN(P_, N_)                                   \
+  if (d.P == P_ && d.N == N_) {                            \
+    plan_for<ScanCfg<P_, N_>>(d, run_tokens, n_cu, fp);    \
+    return true;                                           \
   }
   SSD_FUSED_SHAPES(SSD_PLAN)
 #undef SSD_PLAN
@@ -656,10 +764,10 @@ static hipError_t dispatch(int phase, const Dims& d, const FusedPlan& fp, const 
                            const void* B, const void* C, const float* dt, const float* A,
                            const float* D, float* states, float* logdecay, const float* h_run,
                            void* y, hipStream_t s) {
-#define SSD_LAUNCH(P_, N_)                                                                    \
-  if (d.P == P_ && d.N == N_)                                                                 \
-    return launch_k<Fz<P_, N_>>(phase, d, fp, x, B, C, dt, A, D, states, logdecay, h_run, y, \
-                                s);
+#define SSD_LAUNCH(P_, N_)                                                                  \
+  if (d.P == P_ && d.N == N_)                                                               \
+    return launch_k<RunCfg<P_, N_>, ScanCfg<P_, N_>>(phase, d, fp, x, B, C, dt, A, D, states, \
+                                                     logdecay, h_run, y, s);
   SSD_FUSED_SHAPES(SSD_LAUNCH)
 #undef SSD_LAUNCH
   return hipErrorInvalidValue;
