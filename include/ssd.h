@@ -73,8 +73,16 @@ typedef enum {
     SSD_VARIANT_AUTO = 0,
     SSD_VARIANT_UNFUSED = 1, /* cumsum, C B^T, chunk states, state passing, chunk scan: five
                                 kernels, intermediates in workspace */
-    SSD_VARIANT_FUSED = 2    /* intra-chunk C B^T block kept in registers; states carried on chip
-                                through runs of chunks, exchanged only at run boundaries */
+    SSD_VARIANT_FUSED = 2    /* bf16 io, headdim 64 or 128, dstate 64, 128 or 256: three kernels
+                                (run states, state passing over runs, fused scan). The sequence is
+                                cut into runs (about one block per compute unit); inside a run
+                                the state stays on chip and each sub-chunk of 64 tokens (32 when
+                                dstate is 256) gets its C B^T block, decay mask, readout and
+                                state update without leaving the compute unit. The exact result
+                                does not depend on the chunk length, so chunk_size only sets
+                                the run length when run_chunks is given. Assumes A <= 0 and
+                                dt >= 0 (decays at most 1); D enters through the fp16 diagonal
+                                of the masked block (exact for D = 1) */
 } ssd_variant;
 
 typedef enum {
@@ -87,8 +95,9 @@ typedef enum {
 typedef struct {
     int32_t variant;    /* ssd_variant */
     int32_t precision;  /* ssd_precision */
-    int32_t run_chunks; /* fused variant: chunks per run (state carried on chip through a run);
-                           0 = chosen from the problem size; must be >= 0 */
+    int32_t run_chunks; /* fused variant: runs of run_chunks * chunk_size tokens (rounded up to
+                           the kernels' sub-chunk); 0 = chosen from the problem size and the
+                           device's compute units; must be >= 0 */
     int32_t n_events;   /* capacity of `events`; 0 = no timing events */
     void** events;      /* optional hipEvent_t[n_events], created by the caller: events[0] is
                            recorded on `stream` before the first kernel and events[k] after the

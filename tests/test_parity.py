@@ -18,7 +18,7 @@ from gpu_util import as64, check_shape, note, run_gpu, score, to_device
 pytestmark = pytest.mark.gpu
 
 VARIANTS = ["unfused", "fused"]
-FUSED_SHAPES = {(64, 64), (64, 128), (128, 128), (128, 256)}   # (headdim, dstate)
+FUSED_SHAPES = {(p, n) for p in (64, 128) for n in (64, 128, 256)}   # (headdim, dstate)
 
 
 def skip_unfusable(shape, variant, precision="auto"):
@@ -57,6 +57,11 @@ EDGE = [
     synth.SSDShape("p128n128_q128", 1, 640, 4, 128, 128, 2, 128, init_state=True),
     synth.SSDShape("p128n256_q128_ragged", 2, 500, 2, 128, 256, 2, 128, random_d=True),
     synth.SSDShape("p128n256_q32", 1, 333, 2, 128, 256, 1, 32),
+    synth.SSDShape("p64n256_heads5", 1, 300, 5, 64, 256, 1, 64, init_state=True),
+    synth.SSDShape("p128n64_g3", 2, 200, 6, 128, 64, 3, 32, random_d=True),
+    # head counts that leave part of a fused block idle, and groups of one head
+    synth.SSDShape("p64n128_heads7", 1, 390, 7, 64, 128, 1, 64),
+    synth.SSDShape("p64n128_g6", 1, 150, 6, 64, 128, 6, 128, init_state=True),
 ]
 
 
