@@ -4,15 +4,21 @@
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config 2] [--variant auto]
 
 One step is one full forward (every kernel of the path) over the workload's synthetic inputs,
-which are resident in HBM before timing starts. Before every step a 2 GiB buffer is written so no
-input is left in the 256 MB last-level cache or the L2s (cold-cache timing); each forward, and each
-kernel inside it, is timed with HIP events on the stream it runs on. The timed loop is bracketed
-by device synchronisations.
+which are resident in HBM before timing starts. Before every step a read-only sweep over 2 GiB of
+clean memory leaves no input in the 256 MB Infinity Cache or the L2s (cold-cache timing); each
+forward, and each kernel inside it, is timed with HIP events on the stream it runs on. The timed
+loop is bracketed by device synchronisations.
 
 Prints ONE JSON line: tokens/s, ms per step, the roofline of the dominant kernel (algorithmic
 bytes per launch over its measured duration, against MI355X's 8 TB/s), the whole forward's
 roofline fraction, and the CPU oracle's throughput on the same workload (with the parity of the
 GPU result on the units the oracle computed).
+
+    python bench.py --summarize-profiles DIR
+
+turns rocprofv3 output under DIR (a kernel-trace run and one FETCH_SIZE and one WRITE_SIZE counter
+run, each with --copy-calibration, plus DIR/bench.json from a plain bench run) into the text
+summaries under profiles/ and the traffic record the bench line reports; see PROFILE_COMMANDS.
 """
 
 from __future__ import annotations
@@ -114,6 +120,110 @@ def cpu_baseline(inp, shape, y_gpu, f_gpu, max_seconds: float):
     }, rep
 
 
+PROFILE_COMMANDS = [
+    "python3 bench.py --steps 20 --warmup 3 > DIR/bench.json",
+    "rocprofv3 --kernel-trace --stats -d DIR/prof_kt -o kt --output-format csv -- "
+    "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE -d DIR/prof_fetch -o fetch --output-format csv -- "
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --copy-calibration",
+    "rocprofv3 --pmc WRITE_SIZE -d DIR/prof_write -o write --output-format csv -- "
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --copy-calibration",
+    "python3 bench.py --summarize-profiles DIR",
+]
+
+
+def _short_kernel(name: str):
+    import re
+    m = re.search(r"ssd::k_(\w+)", name)
+    if m:
+        return m.group(1)
+    if "copyBuffer" in name:
+        return "copy"
+    return None
+
+
+def _csv_rows(path):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(path)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_profiles(d: str) -> None:
+    """Write profiles/<kernel>_<workload>.txt and profiles/traffic_<kernel>_<workload>.json from
+    the rocprofv3 runs under d (see PROFILE_COMMANDS)."""
+    with open(os.path.join(d, "bench.json")) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
+    workload = bench["config"]["workload"]
+    stats = {}
+    for r in _csv_rows(os.path.join(d, "prof_kt", "*kernel_stats.csv")):
+        k = _short_kernel(r["Name"])
+        if k and k != "copy":
+            stats[k] = (int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                        float(r["MaxNs"]))
+    counters = {}
+    for sub in ("prof_fetch", "prof_write"):
+        for r in _csv_rows(os.path.join(d, sub, "*counter_collection.csv")):
+            k = _short_kernel(r["Kernel_Name"])
+            if k:
+                counters.setdefault((k, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    # copy calibration: the 1 GiB device-to-device copy reads and writes exactly 2^30 bytes
+    gib = float(1 << 30)
+    cf = max(counters.get(("copy", "FETCH_SIZE"), [0.0]))
+    cw = max(counters.get(("copy", "WRITE_SIZE"), [0.0]))
+    if cf <= 0 or cw <= 0:
+        raise SystemExit("no 1 GiB copy dispatch found in the counter runs (--copy-calibration)")
+    fetch_scale, write_scale = gib / (cf * 1024), gib / (cw * 1024)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    alg_bytes = bench["roofline"]["achieved"] * 1e9 * bench["roofline"]["kernel_ms"] / 1e3
+    lines = [
+        f"rocprofv3 summary: libssd forward kernels, workload {workload} "
+        f"({json.dumps(bench['config'])})",
+        f"kernel sources hash {kernel_source_hash()}",
+        "",
+        "commands (DIR = a scratch output folder; the last runs on any host):",
+        *["  " + c for c in PROFILE_COMMANDS],
+        "",
+        f"copy calibration (1 GiB copy): FETCH_SIZE {cf:.0f} KiB -> x{fetch_scale:.3f}, "
+        f"WRITE_SIZE {cw:.0f} KiB -> x{write_scale:.3f}",
+        "",
+        f"{'kernel':16s}{'calls':>7s}{'avg us':>10s}{'min us':>10s}{'max us':>10s}"
+        f"{'bench us':>10s}{'fetch MB':>11s}{'write MB':>11s}",
+    ]
+    traffic = {}
+    for k, (calls, avg, mn, mx) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
+        fk = counters.get((k, "FETCH_SIZE"))
+        wk = counters.get((k, "WRITE_SIZE"))
+        fb = (sum(fk) / len(fk)) * 1024 * fetch_scale if fk else float("nan")
+        wb = (sum(wk) / len(wk)) * 1024 * write_scale if wk else float("nan")
+        traffic[k] = (fb, wb)
+        bus = bench["kernel_ms"].get(k, float("nan")) * 1e3
+        lines.append(f"{k:16s}{calls:7d}{avg / 1e3:10.1f}{mn / 1e3:10.1f}{mx / 1e3:10.1f}"
+                     f"{bus:10.1f}{fb / 1e6:11.2f}{wb / 1e6:11.2f}")
+    dom = bench["roofline"]["kernel"]
+    fb, wb = traffic.get(dom, (float("nan"), float("nan")))
+    lines += [
+        "",
+        f"dominant kernel {dom}: algorithmic bytes per launch {alg_bytes / 1e6:.2f} MB, "
+        f"measured HBM bytes per launch {(fb + wb) / 1e6:.2f} MB "
+        f"(ratio {(fb + wb) / alg_bytes:.2f})",
+        f"bench line: {bench['ms_per_step'] * 1e3:.1f} us per forward, "
+        f"{bench['value'] / 1e6:.2f} M tokens/s, roofline frac {bench['roofline']['frac']:.3f}",
+    ]
+    with open(os.path.join(ROOT, "profiles", f"{dom}_{workload}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    rec = {"kernel": dom, "workload": workload, "source_hash": kernel_source_hash(),
+           "hbm_bytes_per_launch": fb + wb, "fetch_bytes_per_launch": fb,
+           "write_bytes_per_launch": wb, "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "commands": PROFILE_COMMANDS}
+    with open(os.path.join(ROOT, "profiles", f"traffic_{dom}_{workload}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,10 +237,15 @@ def main():
                          "256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=30.0)
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 output under DIR and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (a known-size kernel for "
                          "scaling hardware byte counters)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

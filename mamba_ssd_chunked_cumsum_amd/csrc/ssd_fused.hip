@@ -26,7 +26,7 @@
 // Staging: x, B and C tiles are copied global -> LDS by the gfx950 LDS DMA (global_load_lds
 // dwordx4), which needs no registers, so a whole sub-chunk is in flight while the previous one is
 // computed (F3: two stages, F1: three). The DMA writes each wave instruction's 64 pieces of 16
-// bytes contiguously; the swizzle (16-byte piece c of row t stored at position c ^ (t & 7)) is
+// bytes contiguously; the swizzle (16-byte piece c of row t stored at position c ^ key(t)) is
 // applied by choosing which global piece each lane fetches. B and C are converted to fp16 in
 // place after arrival; x stays raw bf16 (the skip term D x uses it exactly) and is converted while
 // its fragments are built. Fragments whose K index is the token are read with the gfx950
@@ -52,7 +52,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // Scheduling fence: keeps the compiler from hoisting one step's LDS reads (and the registers they
 // hold) above the previous step.
+#ifdef SSD_SB_ON
 #define SSD_SB() __builtin_amdgcn_sched_barrier(0)
+#else
+#define SSD_SB()
+#endif
 
 // ---- small helpers ------------------------------------------------------------------------------
 __device__ __forceinline__ f16x2 cvt_f16x2(float a, float b) {  // v_cvt_pk_f16_f32, RNE
@@ -87,10 +91,22 @@ __device__ __forceinline__ void bf16x2_to_f32(uint32_t w, float& lo, float& hi) 
   hi = __uint_as_float(w & 0xffff0000u);
 }
 
+// Swizzle of staged tiles: 16-byte piece c of row t is stored at position c ^ key(t), key(t) a
+// permutation of t's low bits chosen so that the fragment reads below touch every LDS bank once:
+// 16 consecutive rows read at one piece (key injective on 16 rows), and the transposing reads of
+// rows {0..3, 8..11} (+4) at a pair of pieces (key >> 1 distinct on those rows; for 128-byte rows,
+// which share a bank line in pairs, distinct within each row parity).
+template <int PPR>
+__device__ __forceinline__ int swz_key(int t) {
+  if (PPR >= 16)  // key bits (t2, t0, t1, t3)
+    return ((t >> 2) & 1) | ((t & 3) << 1) | (((t >> 3) & 1) << 3);
+  return ((t >> 2) & 1) | (((t >> 1) & 1) << 1) | (((t >> 3) & 1) << 2);  // (t2, t1, t3)
+}
+
 // Byte offset of 16-byte piece c of row t in a swizzled staged tile with rows of ROW bytes.
 template <int ROW>
 __device__ __forceinline__ int swz(int t, int c) {
-  return t * ROW + ((c ^ (t & 7)) << 4);
+  return t * ROW + ((c ^ swz_key<ROW / 16>(t)) << 4);
 }
 
 // One LDS DMA instruction: lane l copies 16 bytes from g to lds + 16 l (lds wave-uniform).
@@ -128,10 +144,10 @@ __device__ __forceinline__ s16x8 frag_tr(const char* tile, int r0, int col0, int
 }
 
 // ---- configuration ----------------------------------------------------------------------------
-template <int P_, int N_, int NW_ = 4, int PSMAX_ = 64>
+template <int P_, int N_, int NW_ = 4, int PSMAX_ = 64, int T_ = (N_ >= 256 ? 32 : 64)>
 struct Fz {
   static constexpr int P = P_, N = N_;
-  static constexpr int T = N >= 256 ? 32 : 64;  // tokens per sub-chunk
+  static constexpr int T = T_;  // tokens per sub-chunk
   static constexpr int NW = NW_, NT = 64 * NW_;
   static constexpr int PS0 = 8192 / N < P ? 8192 / N : P;
   static constexpr int PS = PS0 < PSMAX_ ? PS0 : PSMAX_;  // p columns per wave
@@ -152,7 +168,7 @@ struct Fz {
   static_assert(P % PS == 0 && NW % WPH == 0, "whole waves per head");
   static_assert(N / 8 >= 8 && P / 8 >= 8, "swizzle needs 8 pieces per row");
   static_assert(BC_BYTES % 1024 == 0 && X_BYTES % 1024 == 0, "whole DMA instructions");
-  static_assert(BC_NI % NW == 0 && SCAN_NI % NW == 0 && RUN_NI % NW == 0, "even DMA split");
+  static_assert(BC_BYTES >= 1024, "whole DMA instructions");
   static_assert(SCAN_LDS <= 160 * 1024 && RUN_LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -187,17 +203,17 @@ __device__ __forceinline__ Coord coords(const Dims& d) {
 
 // Per-lane byte offsets of the DMA pieces of a full sub-chunk. Instruction kk of a region with
 // PPR 16-byte pieces per row covers rows kk * RPI .. + RPI - 1 (RPI = 64 / PPR); lane l fetches
-// piece (l % PPR) ^ (t & 7) of row t = kk * RPI + l / PPR. Since RPI * kk mod 8 cycles with period
-// NPAT = 8 / RPI, the lane part of the address takes NPAT values; the rest is wave-uniform.
+// piece (l % PPR) ^ key(t) of row t = kk * RPI + l / PPR. The key depends on t mod 16 only, so the
+// lane part of the address takes NPAT = 16 / RPI values; the rest is wave-uniform.
 template <int PPR>
 struct DmaPat {
-  static constexpr int RPI = 64 / PPR, NPAT = RPI >= 8 ? 1 : 8 / RPI;
+  static constexpr int RPI = 64 / PPR, NPAT = RPI >= 16 ? 1 : 16 / RPI;
   uint32_t off[NPAT];
   __device__ __forceinline__ void init(int lane, uint32_t ld) {
 #pragma unroll
     for (int q = 0; q < NPAT; ++q) {
-      const int r = lane / PPR, t7 = (q * RPI + r) & 7;
-      off[q] = (uint32_t)r * ld + (uint32_t)(((lane % PPR) ^ t7) << 4);
+      const int r = lane / PPR, t = q * RPI + r;
+      off[q] = (uint32_t)r * ld + (uint32_t)(((lane % PPR) ^ swz_key<PPR>(t)) << 4);
     }
   }
   __device__ __forceinline__ uint32_t at(int kk) const {
@@ -247,21 +263,26 @@ __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* B
   const char* xbase = reinterpret_cast<const char*>(x) +
                       (((int64_t)c.b * d.L + tok0) * d.H + c.hbase) * (K::P * 2);
   if (tok0 + K::T <= d.L) {
+    // row strides as opaque scalars: their per-instruction multiples are recomputed (scalar ALU)
+    // each call rather than held in scalar registers across the loop
+    uint32_t lb = (uint32_t)ldbc, lx = (uint32_t)ldx;
+    asm volatile("" : "+s"(lb), "+s"(lx));
+    constexpr bool EVEN = NBC % K::NW == 0 && NI % K::NW == 0;
 #pragma unroll
     for (int k0 = 0; k0 < NI; k0 += K::NW) {
-      const int k = k0 + c.wave;
-      if (k0 < NBC) {  // B or C (NBC and BC_NI are multiples of NW: uniform per k0)
-        const bool isC = WITH_C && k0 >= K::BC_NI;
+      const int k = k0 + c.wave;  // wave-uniform
+      if (!EVEN && k >= NI) break;
+      const bool bc = EVEN ? k0 < NBC : k < NBC;
+      if (bc) {  // B or C
+        const bool isC = WITH_C && (EVEN ? k0 >= K::BC_NI : k >= K::BC_NI);
         const int kk = isC ? k - K::BC_NI : k;
-        // one 32-bit lane offset on top of the uniform sub-chunk base (keeps the per-instruction
-        // part out of the scalar registers)
-        const uint32_t o = dl.bc.at(kk) + (uint32_t)(kk * RPI_N) * (uint32_t)ldbc;
+        const uint32_t o = dl.bc.at(kk) + (uint32_t)(kk * RPI_N) * lb;
         dma16((isC ? cbase : bbase) + o, st + k * 1024);
       } else {
         const int kk = k - NBC;
         const int hh = kk / (K::T / RPI_P), kr = kk % (K::T / RPI_P);
         const int hoff = min(hh, c.hlast - c.hbase) * (K::P * 2);
-        const uint32_t o = (uint32_t)hoff + dl.x.at(kr) + (uint32_t)(kr * RPI_P) * (uint32_t)ldx;
+        const uint32_t o = (uint32_t)hoff + dl.x.at(kr) + (uint32_t)(kr * RPI_P) * lx;
         dma16(xbase + o, st + k * 1024);
       }
     }
@@ -270,18 +291,19 @@ __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* B
 #pragma unroll
     for (int k0 = 0; k0 < NI; k0 += K::NW) {
       const int k = k0 + c.wave;
+      if (k >= NI) break;
       const char* src;
-      if (k0 < NBC) {
-        const bool isC = WITH_C && k0 >= K::BC_NI;
+      if (k < NBC) {
+        const bool isC = WITH_C && k >= K::BC_NI;
         const int kk = isC ? k - K::BC_NI : k;
         const int t = kk * RPI_N + c.lane / PPR_N, cp = c.lane % PPR_N;
-        src = (isC ? cbase : bbase) + (int64_t)min(t, last) * ldbc + ((cp ^ (t & 7)) << 4);
+        src = (isC ? cbase : bbase) + (int64_t)min(t, last) * ldbc + ((cp ^ swz_key<PPR_N>(t)) << 4);
       } else {
         const int kk = k - NBC;
         const int hh = kk / (K::T / RPI_P), kr = kk % (K::T / RPI_P);
         const int hoff = min(hh, c.hlast - c.hbase) * (K::P * 2);
         const int t = kr * RPI_P + c.lane / PPR_P, cp = c.lane % PPR_P;
-        src = xbase + hoff + (int64_t)min(t, last) * ldx + ((cp ^ (t & 7)) << 4);
+        src = xbase + hoff + (int64_t)min(t, last) * ldx + ((cp ^ swz_key<PPR_P>(t)) << 4);
       }
       dma16(src, st + k * 1024);
     }
@@ -294,6 +316,7 @@ __device__ __forceinline__ void convert_stage(char* st, const Coord& c) {
   constexpr int NBC = (WITH_C ? 2 : 1) * K::BC_NI;
 #pragma unroll
   for (int k0 = 0; k0 < NBC; k0 += K::NW) {
+    if (k0 + c.wave >= NBC) break;
     uint4* p = reinterpret_cast<uint4*>(st + (k0 + c.wave) * 1024 + c.lane * 16);
     *p = bf16x8_to_f16x8(*p);
   }
@@ -374,27 +397,34 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
     for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] = zero4();
   float logsum = 0.f;
 
-  // prologue: stages of the first two sub-chunks, dt of the first
+  // prologue: dt of the first sub-chunk, stages of the first two. Every dt load is issued before
+  // the DMA of the same round, so waiting for a dt value never waits for a later stage.
+  float dt_next = load_dt<K>(dt, d, c, s_begin * T);
   issue_stage<K, false>(smem, x, Bm, nullptr, d, c, dl, s_begin * T);
   if (s_begin + 1 < s_end)
     issue_stage<K, false>(smem + K::RUN_STAGE, x, Bm, nullptr, d, c, dl, (s_begin + 1) * T);
-  float dt_next = load_dt<K>(dt, d, c, s_begin * T);
+  // DMA instructions this wave issues per stage
+  constexpr int NLO = K::RUN_NI / K::NW;
+  const bool hi = c.wave < K::RUN_NI % K::NW;
 
   for (int s = s_begin; s < s_end; ++s) {
     const int cur = (s - s_begin) % K::NRUN;
     char* st = smem + cur * K::RUN_STAGE;
     const float dv = dt_next;
-    // this stage's DMA done; the next stage's (issued after it) may still be in flight
-    if (s + 1 < s_end)
-      wait_vm_but<K::RUN_NI / K::NW>();
-    else
+    // this stage's DMA done; the next stage's (at least this wave's instructions for it were
+    // issued after this stage's) may still be in flight
+    if (s + 1 >= s_end)
       wait_vm_all();
+    else if (hi)
+      wait_vm_but<NLO + 1>();
+    else
+      wait_vm_but<NLO>();
     convert_stage<K, false>(st, c);
     __syncthreads();  // stage visible to all waves; every wave is done with sub-chunk s - 1
+    if (s + 1 < s_end) dt_next = load_dt<K>(dt, d, c, (s + 1) * T);
     if (s + 2 < s_end)
       issue_stage<K, false>(smem + ((cur + 2) % K::NRUN) * K::RUN_STAGE, x, Bm, nullptr, d, c, dl,
                             (s + 2) * T);
-    if (s + 1 < s_end) dt_next = load_dt<K>(dt, d, c, (s + 1) * T);
     const float acs_end = decay_terms<K>(dv, a_h, wa, c);
     logsum += acs_end;
     const float dec = __expf(acs_end);
@@ -419,6 +449,21 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
         for (int e = 0; e < 8; ++e) lo[e] = v[e] - (float)xhi[pt][e];
         xlo[pt] = cvt_f16x8(lo);
       }
+#ifndef SSD_F1_NO_HOIST
+      // all B^T fragments of the K step first (their LDS latency overlaps), then the high parts
+      // for every tile, then the low parts (no back-to-back dependent matrix-core ops)
+      f16x8 bts[K::NNT];
+#pragma unroll
+      for (int nt = 0; nt < K::NNT; ++nt) bts[nt] = b_frag<K>(st, js, 16 * nt, c.lane);
+#pragma unroll
+      for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] = M::mma(bts[nt], xhi[pt], S[nt][pt]);
+#pragma unroll
+      for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] = M::mma(bts[nt], xlo[pt], S[nt][pt]);
+#else
 #pragma unroll
       for (int nt = 0; nt < K::NNT; ++nt) {
         const f16x8 bt = b_frag<K>(st, js, 16 * nt, c.lane);
@@ -428,6 +473,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
           S[nt][pt] = M::mma(bt, xlo[pt], S[nt][pt]);
         }
       }
+#endif
     }
   }
   if (!c.active) return;
@@ -447,7 +493,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
 // Store the bf16 y tile that F3 left in the x tile of a stage: this wave's p-slice of its head,
 // rows tok0 .. tok0 + T - 1 (rows past the sequence end skipped), 16 bytes per lane. Round k
 // covers rows k * RPR .. + RPR - 1; the lane parts of the LDS and global addresses do not depend
-// on k (RPR is a multiple of 8, so the swizzle pattern repeats).
+// on k (RPR is a multiple of 16, the swizzle key's period).
 template <class K>
 __device__ __forceinline__ void store_y(const char* xt, u16* y, const Dims& d, const Coord& c,
                                         int tok0) {
@@ -455,11 +501,11 @@ __device__ __forceinline__ void store_y(const char* xt, u16* y, const Dims& d, c
   constexpr int PPR = K::PS / 8;  // pieces per row of the wave's slice
   constexpr int RPR = 64 / PPR;   // rows per round
   constexpr int ROUNDS = K::T / RPR;
-  static_assert(RPR % 8 == 0 && K::T % RPR == 0, "whole store rounds");
+  static_assert(RPR % 16 == 0 && K::T % RPR == 0, "whole store rounds (key period 16 rows)");
   const int r = c.lane / PPR, cp = (c.p0 >> 3) + c.lane % PPR;
   const int64_t ld = (int64_t)d.H * K::P;  // y row stride (elements)
   u16* yb = y + (((int64_t)c.b * d.L + tok0) * d.H + c.h) * K::P + (cp << 3) + r * ld;
-  const char* xl = xt + r * K::ROW_P + ((cp ^ (r & 7)) << 4);
+  const char* xl = xt + swz<K::ROW_P>(r, cp);
   const int nrow = d.L - tok0;  // valid rows
 #pragma unroll
   for (int k = 0; k < ROUNDS; ++k) {
@@ -467,6 +513,50 @@ __device__ __forceinline__ void store_y(const char* xt, u16* y, const Dims& d, c
     if (nrow >= K::T || k * RPR + r < nrow)
       *reinterpret_cast<uint4*>(yb + (int64_t)(k * RPR) * ld) = v;
   }
+}
+
+// Lane-constant byte offsets of F3's LDS fragment accesses, relative to the tile they read,
+// computed once per kernel. The swizzle key sees only a row's low 4 bits and a piece's low bits,
+// so the unrolled loop indices it does not see (token-tile rows, high piece bits) enter as
+// immediates on top of these.
+template <class K>
+struct ScanLane {
+  static constexpr int PPR_N = K::N / 8;
+  static constexpr int KP = PPR_N >= 16 ? 4 : 2;   // K steps over n with distinct patterns
+  static constexpr int NP = PPR_N >= 16 ? 8 : 4;   // n tiles with distinct patterns
+  uint32_t cro[KP][2];      // readout C^T fragment: row c16, piece 4 kn + 2 h + g/2, half g&1
+  uint32_t btr[NP][2];      // B^T fragment (transposing read): rows 8 g + j/4 (+4), piece 2 nt + ..
+  uint32_t xtr[K::NPT][2];  // x fragment (transposing read)
+  uint32_t cbr[KP];         // C B^T inputs: row c16, piece 4 kn + g
+  uint32_t epi[K::NPT];     // y write into the x tile: row c16, piece (p0 + 16 pt) / 8 + g/2
+  __device__ __forceinline__ void init(const Coord& c) {
+    const int g = c.g, c16 = c.c16, j = c.lane & 15;
+#pragma unroll
+    for (int b = 0; b < KP; ++b) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        cro[b][h] = swz<K::ROW_N>(c16, 4 * b + 2 * h + (g >> 1)) + ((g & 1) << 3);
+      cbr[b] = swz<K::ROW_N>(c16, 4 * b + g);
+    }
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int t = 8 * g + (j >> 2) + 4 * hi;
+#pragma unroll
+      for (int b = 0; b < NP; ++b) btr[b][hi] = swz<K::ROW_N>(t, 2 * b + ((j & 3) >> 1)) + ((j & 1) << 3);
+#pragma unroll
+      for (int pt = 0; pt < K::NPT; ++pt)
+        xtr[pt][hi] = swz<K::ROW_P>(t, ((c.p0 + 16 * pt) >> 3) + ((j & 3) >> 1)) + ((j & 1) << 3);
+    }
+#pragma unroll
+    for (int pt = 0; pt < K::NPT; ++pt)
+      epi[pt] = swz<K::ROW_P>(c16, ((c.p0 + 16 * pt) >> 3) + (g >> 1)) + ((g & 1) << 3);
+  }
+};
+
+// Two transposing reads at precomputed lane offsets -> one 8-value K fragment.
+__device__ __forceinline__ s16x8 tr8(const char* base, uint32_t lo, uint32_t hi) {
+  const s16x4 a = tr4(base + lo), b = tr4(base + hi);
+  return s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 // ---- F3: fused scan -----------------------------------------------------------------------------
@@ -486,6 +576,9 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
   Coord c = coords<K>(d);
   DmaLanes<K> dl;
   dl.init(d, c.lane);
+  ScanLane<K> sl;
+  sl.init(c);
+  using SL = ScanLane<K>;
   constexpr int T = K::T, NPT = K::NPT, NIT = K::NIT;
   const int nsub = (d.L + T - 1) / T;
   const int s_begin = c.r * RS, s_end = min(nsub, s_begin + RS);
@@ -543,11 +636,14 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
         while ((it + 1) * (it + 2) / 2 <= q) ++it;
         const int jt = q - it * (it + 1) / 2;
         f32x4 acc = zero4();
-        const int i = 16 * it + c.c16, j = 16 * jt + c.c16;
+        const int j = 16 * jt + c.c16;
+        const char* crow = Ch + 16 * it * K::ROW_N;
+        const char* brow = Bh + 16 * jt * K::ROW_N;
 #pragma unroll
         for (int kn = 0; kn < K::NKN; ++kn) {
-          const f16x8 a = *reinterpret_cast<const f16x8*>(Ch + swz<K::ROW_N>(i, 4 * kn + c.g));
-          const f16x8 bb = *reinterpret_cast<const f16x8*>(Bh + swz<K::ROW_N>(j, 4 * kn + c.g));
+          const int o = (kn / SL::KP) * (16 * SL::KP * 4);  // piece bits above the pattern
+          const f16x8 a = *reinterpret_cast<const f16x8*>(crow + sl.cbr[kn % SL::KP] + o);
+          const f16x8 bb = *reinterpret_cast<const f16x8*>(brow + sl.cbr[kn % SL::KP] + o);
           acc = M::mma(a, bb, acc);
         }
 #pragma unroll
@@ -576,12 +672,9 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
       }
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
-        const int i = 16 * it + c.c16;
-        const int half = (c.g & 1) << 3;
-        const uint2 lo = *reinterpret_cast<const uint2*>(
-            Ch + swz<K::ROW_N>(i, 4 * kn + (c.g >> 1)) + half);
-        const uint2 hi = *reinterpret_cast<const uint2*>(
-            Ch + swz<K::ROW_N>(i, 4 * kn + 2 + (c.g >> 1)) + half);
+        const char* crow = Ch + 16 * it * K::ROW_N + (kn / SL::KP) * (16 * SL::KP * 4);
+        const uint2 lo = *reinterpret_cast<const uint2*>(crow + sl.cro[kn % SL::KP][0]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(crow + sl.cro[kn % SL::KP][1]);
         const f16x8 cf = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(sa[pt], cf, Y[pt][it]);
@@ -615,8 +708,10 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
         const f16x8 w16 = cvt_f16x8(wv);
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
+          const s16x8 r = tr8(xt + 32 * js * K::ROW_P, sl.xtr[pt][0], sl.xtr[pt][1]);
           float v[8];
-          x_frag<K>(xt, js, c.p0 + 16 * pt, c.lane, v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = __uint_as_float((uint32_t)(uint16_t)r[e] << 16);
           xh[pt] = cvt_f16x8(v);
           xs[pt] = xh[pt] * w16;  // packed fp16 multiply
         }
@@ -661,7 +756,9 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
       // state update: S^T += B^T (w x)
 #pragma unroll
       for (int nt = 0; nt < K::NNT; ++nt) {
-        const f16x8 bt = b_frag<K>(Bh, js, 16 * nt, c.lane);
+        const char* bb = Bh + 32 * js * K::ROW_N + (nt / SL::NP) * (16 * 2 * SL::NP);
+        const f16x8 bt = __builtin_bit_cast(
+            f16x8, tr8(bb, sl.btr[nt % SL::NP][0], sl.btr[nt % SL::NP][1]));
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) S[nt][pt] = M::mma(bt, xs[pt], S[nt][pt]);
       }
@@ -672,12 +769,10 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     // longer needed); stored to memory after the next wait
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int i = 16 * it + c.c16;
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
-        const int col = c.p0 + 16 * pt + 4 * c.g;
         const f32x4 v = Y[pt][it];
-        *reinterpret_cast<uint2*>(st + xoff + swz<K::ROW_P>(i, col >> 3) + ((col & 7) << 1)) =
+        *reinterpret_cast<uint2*>(st + xoff + 16 * it * K::ROW_P + sl.epi[pt]) =
             make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
       }
     }
@@ -697,10 +792,15 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
 #define SSD_F3_NW 8
 #define SSD_F3_PS 32
 #endif
+#ifdef SSD_TOKENS
+#define SSD_T(N) SSD_TOKENS
+#else
+#define SSD_T(N) ((N) >= 256 ? 32 : 64)
+#endif
 template <int P, int N>
-using RunCfg = Fz<P, N, 8, 32>;
+using RunCfg = Fz<P, N, 8, 32, SSD_T(N)>;
 template <int P, int N>
-using ScanCfg = Fz<P, N, SSD_F3_NW, SSD_F3_PS>;
+using ScanCfg = Fz<P, N, SSD_F3_NW, SSD_F3_PS, SSD_T(N)>;
 
 template <class K>
 static int head_blocks(const Dims& d) {
