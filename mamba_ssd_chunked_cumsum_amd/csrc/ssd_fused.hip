@@ -169,7 +169,6 @@ struct Fz {
   static_assert(N / 8 >= 8 && P / 8 >= 8, "swizzle needs 8 pieces per row");
   static_assert(BC_BYTES % 1024 == 0 && X_BYTES % 1024 == 0, "whole DMA instructions");
   static_assert(BC_BYTES >= 1024, "whole DMA instructions");
-  static_assert(SCAN_LDS <= 160 * 1024 && RUN_LDS <= 160 * 1024, "LDS budget");
 };
 
 // Block / wave coordinates shared by F1 and F3. Grid (nr, G * head-blocks per group, batch).
@@ -267,7 +266,8 @@ __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* B
     // each call rather than held in scalar registers across the loop
     uint32_t lb = (uint32_t)ldbc, lx = (uint32_t)ldx;
     asm volatile("" : "+s"(lb), "+s"(lx));
-    constexpr bool EVEN = NBC % K::NW == 0 && NI % K::NW == 0;
+    // every round of NW instructions lies inside one region: the region tests are compile-time
+    constexpr bool EVEN = K::BC_NI % K::NW == 0 && NI % K::NW == 0;
 #pragma unroll
     for (int k0 = 0; k0 < NI; k0 += K::NW) {
       const int k = k0 + c.wave;  // wave-uniform
@@ -376,14 +376,16 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
                                                       const float* __restrict__ Av,
                                                       float* __restrict__ states,
                                                       float* __restrict__ logdecay, Dims d,
-                                                      int RS, int nr) {
+                                                      int run_len, int nr) {
   using M = Mma<f16>;
+  static_assert(K::RUN_LDS <= 160 * 1024, "LDS budget");
   __shared__ __align__(1024) char smem[K::RUN_LDS];
   Coord c = coords<K>(d);
   DmaLanes<K> dl;
   dl.init(d, c.lane);
   constexpr int T = K::T;
   const int nsub = (d.L + T - 1) / T;
+  const int RS = run_len / T;  // sub-chunks per run (run_len is a multiple of every T)
   const int s_begin = c.r * RS, s_end = min(nsub, s_begin + RS);
   if (s_begin >= s_end) return;
   float* wa = reinterpret_cast<float*>(smem + K::NRUN * K::RUN_STAGE) + c.wave * K::NWA * T;
@@ -492,8 +494,8 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
 
 // Store the bf16 y tile that F3 left in the x tile of a stage: this wave's p-slice of its head,
 // rows tok0 .. tok0 + T - 1 (rows past the sequence end skipped), 16 bytes per lane. Round k
-// covers rows k * RPR .. + RPR - 1; the lane parts of the LDS and global addresses do not depend
-// on k (RPR is a multiple of 16, the swizzle key's period).
+// covers rows k * RPR .. + RPR - 1; the swizzle key repeats every 16 rows, so the LDS lane offset
+// takes 16 / RPR values (at least one).
 template <class K>
 __device__ __forceinline__ void store_y(const char* xt, u16* y, const Dims& d, const Coord& c,
                                         int tok0) {
@@ -501,17 +503,22 @@ __device__ __forceinline__ void store_y(const char* xt, u16* y, const Dims& d, c
   constexpr int PPR = K::PS / 8;  // pieces per row of the wave's slice
   constexpr int RPR = 64 / PPR;   // rows per round
   constexpr int ROUNDS = K::T / RPR;
-  static_assert(RPR % 16 == 0 && K::T % RPR == 0, "whole store rounds (key period 16 rows)");
+  constexpr int NPAT = RPR >= 16 ? 1 : 16 / RPR;
+  static_assert(K::T % RPR == 0 && (RPR % 16 == 0 || 16 % RPR == 0), "whole store rounds");
   const int r = c.lane / PPR, cp = (c.p0 >> 3) + c.lane % PPR;
   const int64_t ld = (int64_t)d.H * K::P;  // y row stride (elements)
   u16* yb = y + (((int64_t)c.b * d.L + tok0) * d.H + c.h) * K::P + (cp << 3) + r * ld;
-  const char* xl = xt + swz<K::ROW_P>(r, cp);
+  int xl[NPAT];
+#pragma unroll
+  for (int q = 0; q < NPAT; ++q) xl[q] = swz<K::ROW_P>(q * RPR + r, cp);
   const int nrow = d.L - tok0;  // valid rows
 #pragma unroll
   for (int k = 0; k < ROUNDS; ++k) {
-    const uint4 v = *reinterpret_cast<const uint4*>(xl + k * RPR * K::ROW_P);
-    if (nrow >= K::T || k * RPR + r < nrow)
-      *reinterpret_cast<uint4*>(yb + (int64_t)(k * RPR) * ld) = v;
+    const int row0 = k * RPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(xt + xl[k % NPAT] + (row0 / (NPAT * RPR)) *
+                                                                          (NPAT * RPR) * K::ROW_P);
+    if (nrow >= K::T || row0 + r < nrow)
+      *reinterpret_cast<uint4*>(yb + (int64_t)row0 * ld) = v;
   }
 }
 
@@ -570,8 +577,9 @@ template <class K>
 __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     const u16* __restrict__ x, const u16* __restrict__ Bm, const u16* __restrict__ Cm,
     const float* __restrict__ dt, const float* __restrict__ Av, const float* __restrict__ Dv,
-    const float* __restrict__ h_run, u16* __restrict__ y, Dims d, int RS, int nr) {
+    const float* __restrict__ h_run, u16* __restrict__ y, Dims d, int run_len, int nr) {
   using M = Mma<f16>;
+  static_assert(K::SCAN_LDS <= 160 * 1024, "LDS budget");
   __shared__ __align__(1024) char smem[K::SCAN_LDS];
   Coord c = coords<K>(d);
   DmaLanes<K> dl;
@@ -581,6 +589,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
   using SL = ScanLane<K>;
   constexpr int T = K::T, NPT = K::NPT, NIT = K::NIT;
   const int nsub = (d.L + T - 1) / T;
+  const int RS = run_len / T;  // sub-chunks per run (run_len is a multiple of every T)
   const int s_begin = c.r * RS, s_end = min(nsub, s_begin + RS);
   if (s_begin >= s_end) return;
   float* cbs = reinterpret_cast<float*>(smem + K::NSCAN * K::SCAN_STAGE);
@@ -620,6 +629,8 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     wait_vm_all();  // this stage's DMA, the dt load, and the y stores of the previous round
     if (ytok >= 0) store_y<K>(smem + (cur ^ 1) * K::SCAN_STAGE + xoff, y, d, c, ytok);
     convert_stage<K, true>(st, c);
+    // this wave's decay bookkeeping needs only its dt: done while other waves finish converting
+    const float acs_end = decay_terms<K>(dv, a_h, wa, c);
     __syncthreads();  // stage visible; every wave is done with sub-chunk s - 1 (CB, stage cur^1)
     if (s + 1 < s_end) {
       issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, d, c, dl, (s + 1) * T);
@@ -650,12 +661,13 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
         for (int rr = 0; rr < 4; ++rr) cbs[(16 * it + 4 * c.g + rr) * K::LDCB + j] = acc[rr];
       }
     }
-    const float acs_end = decay_terms<K>(dv, a_h, wa, c);
-    __syncthreads();  // C B^T tiles visible
-    if (!c.active) continue;
+    // readout of the carried state first: it needs no C B^T, so it absorbs the uneven C B^T
+    // shares before the barrier that publishes the tiles
+    f32x4 Y[NPT][NIT];
+    float acs2_i[NIT];
+    if (c.active) {
 
     // readout of the carried state: Y^T = S C^T (K index n in accumulator order)
-    f32x4 Y[NPT][NIT];
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt)
 #pragma unroll
@@ -680,7 +692,6 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
         for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(sa[pt], cf, Y[pt][it]);
       }
     }
-    float acs2_i[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       acs2_i[it] = wa[16 * it + c.c16];
@@ -688,6 +699,9 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) Y[pt][it] *= e;
     }
+    }
+    __syncthreads();  // C B^T tiles visible
+    if (!c.active) continue;
     SSD_SB();
 
     // state decay (the readout above used the entry state)
@@ -797,10 +811,15 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
 #else
 #define SSD_T(N) ((N) >= 256 ? 32 : 64)
 #endif
+#ifdef SSD_F3_TOK
+#define SSD_F3_T(N) SSD_F3_TOK
+#else
+#define SSD_F3_T(N) SSD_T(N)
+#endif
 template <int P, int N>
 using RunCfg = Fz<P, N, 8, 32, SSD_T(N)>;
 template <int P, int N>
-using ScanCfg = Fz<P, N, SSD_F3_NW, SSD_F3_PS, SSD_T(N)>;
+using ScanCfg = Fz<P, N, SSD_F3_NW, SSD_F3_PS, SSD_F3_T(N)>;
 
 template <class K>
 static int head_blocks(const Dims& d) {
@@ -808,24 +827,25 @@ static int head_blocks(const Dims& d) {
   return d.G * ((hpg + K::HPB - 1) / K::HPB);
 }
 
+// Runs are planned in tokens, as whole multiples of 64 (so of every kernel's sub-chunk).
 template <class K3>
 static void plan_for(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
-  fp->T = K3::T;
-  fp->nsub = (d.L + K3::T - 1) / K3::T;
+  constexpr int U = 64;
+  const int nunit = (d.L + U - 1) / U;
   fp->head_blocks = head_blocks<K3>(d);
   const int units = d.Bt * fp->head_blocks;
-  int RS;
+  int RU;
   if (run_tokens > 0) {
-    RS = (run_tokens + K3::T - 1) / K3::T;
+    RU = (run_tokens + U - 1) / U;
   } else {
     int want = n_cu / units;  // runs per sequence: about one scan block per compute unit
     if (want < 1) want = 1;
-    RS = (fp->nsub + want - 1) / want;
+    RU = (nunit + want - 1) / want;
   }
-  if (RS < 1) RS = 1;
-  if (RS > fp->nsub) RS = fp->nsub;
-  fp->RS = RS;
-  fp->nr = (fp->nsub + RS - 1) / RS;
+  if (RU < 1) RU = 1;
+  if (RU > nunit) RU = nunit;
+  fp->run_len = RU * U;
+  fp->nr = (nunit + RU - 1) / RU;
 }
 
 template <class K1, class K3>
@@ -833,15 +853,15 @@ static hipError_t launch_k(int phase, const Dims& d, const FusedPlan& fp, const 
                            const void* B, const void* C, const float* dt, const float* A,
                            const float* D, float* states, float* logdecay, const float* h_run,
                            void* y, hipStream_t s) {
-  static_assert(K1::T == K3::T, "F1 and F3 walk the same sub-chunks");
+  static_assert(64 % K1::T == 0 && 64 % K3::T == 0, "runs are whole sub-chunks of both kernels");
   if (phase == 0)
     hipLaunchKernelGGL(k_run_state<K1>, dim3(fp.nr, head_blocks<K1>(d), d.Bt), dim3(K1::NT), 0,
-                       s, (const u16*)x, (const u16*)B, dt, A, states, logdecay, d, fp.RS,
+                       s, (const u16*)x, (const u16*)B, dt, A, states, logdecay, d, fp.run_len,
                        fp.nr);
   else
     hipLaunchKernelGGL(k_fused_scan<K3>, dim3(fp.nr, head_blocks<K3>(d), d.Bt), dim3(K3::NT), 0,
                        s, (const u16*)x, (const u16*)B, (const u16*)C, dt, A, D, h_run, (u16*)y,
-                       d, fp.RS, fp.nr);
+                       d, fp.run_len, fp.nr);
   return hipGetLastError();
 }
 

@@ -31,10 +31,10 @@ hipError_t launch_chunk_scan(const Dims& d, int io, int prec, const void* x, con
 
 
 // fused path (bf16 io)
-// Sub-chunk walk of one fused forward: T tokens per sub-chunk, nsub sub-chunks per sequence, runs
-// of RS sub-chunks (nr runs), head_blocks blocks per (batch, run).
+// Run plan of one fused forward: runs of run_len tokens (a multiple of 64), nr runs per sequence,
+// head_blocks fused-scan blocks per (batch, run).
 struct FusedPlan {
-  int T, nsub, RS, nr, head_blocks;
+  int run_len, nr, head_blocks;
 };
 // False when the fused kernels do not cover (P, N). run_tokens > 0 asks for runs of at least that
 // many tokens; 0 lets the plan aim at about one block per compute unit (n_cu of them).
