@@ -109,18 +109,36 @@ __device__ __forceinline__ int swz(int t, int c) {
   return t * ROW + ((c ^ swz_key<ROW / 16>(t)) << 4);
 }
 
-// One LDS DMA instruction: lane l copies 16 bytes from g to lds + 16 l (lds wave-uniform).
-__device__ __forceinline__ void dma16(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
-                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+// LDS DMA (global_load_lds): lane l copies 16 (dma_x4) or 4 (dma_x1) bytes from sbase + voff to
+// LDS address lds + 16 l (4 l); sbase and lds are wave-uniform. Issued as inline assembly so that
+// the compiler neither counts them nor adds its own conservative waits before LDS reads (it
+// treats any such DMA as possibly aliasing every LDS access); the kernels wait for them
+// explicitly (wait_vm_*) and publish the data with a barrier. M0 holds the LDS address; the
+// compiler reserves M0 and sets it right before its own uses, so it holds no live value here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_x4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_x1(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff),
+               "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// 32-bit LDS address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(p);
 }
 // Wait until all of this wave's vector memory operations (DMA included) have completed.
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
-// ... all but the most recent n (n < 16); loads complete in issue order.
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// ... all but the most recent n; loads complete in issue order.
 template <int n>
 __device__ __forceinline__ void wait_vm_but() {
-  static_assert(n >= 0 && n < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0f70 | n);
+  static_assert(n >= 0 && n < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
 }
 
 // Transposing LDS read: lane i of each 16-lane group receives, in slot q, the (i % 4)-th of the
@@ -156,8 +174,12 @@ struct Fz {
   static constexpr int ROW_N = N * 2, ROW_P = P * 2;  // staged row bytes
   static constexpr int BC_BYTES = T * ROW_N, X_BYTES = HPB * T * ROW_P;
   static constexpr int BC_NI = BC_BYTES / 1024;       // DMA instructions per B (or C) tile
-  static constexpr int SCAN_STAGE = 2 * BC_BYTES + X_BYTES, RUN_STAGE = BC_BYTES + X_BYTES;
-  static constexpr int SCAN_NI = SCAN_STAGE / 1024, RUN_NI = RUN_STAGE / 1024;
+  static constexpr int X_NI = X_BYTES / 1024;         // ... per x tile of the block's heads
+  static constexpr int DT_BYTES = NW * 256;           // per wave: dt of its head, 64 tokens
+  // stage: [B][C (scan only)][x of the HPB heads][dt per wave]
+  static constexpr int SCAN_NI = 2 * BC_NI + X_NI, RUN_NI = BC_NI + X_NI;
+  static constexpr int SCAN_DT = SCAN_NI * 1024, RUN_DT = RUN_NI * 1024;  // dt offsets
+  static constexpr int SCAN_STAGE = SCAN_DT + DT_BYTES, RUN_STAGE = RUN_DT + DT_BYTES;
   static constexpr int LDCB = T + 4;                  // floats per C B^T row
   static constexpr int CB_BYTES = T * LDCB * 4;
   static constexpr int NWA = 4;                       // per-wave token arrays
@@ -200,37 +222,33 @@ __device__ __forceinline__ Coord coords(const Dims& d) {
   return c;
 }
 
-// Per-lane byte offsets of the DMA pieces of a full sub-chunk. Instruction kk of a region with
-// PPR 16-byte pieces per row covers rows kk * RPI .. + RPI - 1 (RPI = 64 / PPR); lane l fetches
-// piece (l % PPR) ^ key(t) of row t = kk * RPI + l / PPR. The key depends on t mod 16 only, so the
-// lane part of the address takes NPAT = 16 / RPI values; the rest is wave-uniform.
+// This lane's byte offsets of its DMA pieces, relative to wave-uniform bases. Instruction kk of a
+// region with PPR 16-byte pieces per row covers rows kk * RPI .. + RPI - 1 (RPI = 64 / PPR); lane
+// l fetches piece (l % PPR) ^ key(t) of row t = kk * RPI + l / PPR. The key depends on t mod 16,
+// i.e. on kk mod NPAT = 16 / RPI; a wave's instructions of a region all have kk = wave (mod
+// NPAT) (region starts and the wave count are multiples of NPAT), so one offset per region does.
 template <int PPR>
-struct DmaPat {
+struct DmaGeo {
   static constexpr int RPI = 64 / PPR, NPAT = RPI >= 16 ? 1 : 16 / RPI;
-  uint32_t off[NPAT];
-  __device__ __forceinline__ void init(int lane, uint32_t ld) {
-#pragma unroll
-    for (int q = 0; q < NPAT; ++q) {
-      const int r = lane / PPR, t = q * RPI + r;
-      off[q] = (uint32_t)r * ld + (uint32_t)(((lane % PPR) ^ swz_key<PPR>(t)) << 4);
-    }
-  }
-  __device__ __forceinline__ uint32_t at(int kk) const {
-    uint32_t o = off[0];
-#pragma unroll
-    for (int q = 1; q < NPAT; ++q)
-      if (kk % NPAT == q) o = off[q];
-    return o;
+  static __device__ __forceinline__ uint32_t lane_off(int wave, int lane, uint32_t ld) {
+    const int r = lane / PPR, t = (wave % NPAT) * RPI + r;
+    return (uint32_t)r * ld + (uint32_t)(((lane % PPR) ^ swz_key<PPR>(t)) << 4);
   }
 };
 
 template <class K>
 struct DmaLanes {
-  DmaPat<K::N / 8> bc;
-  DmaPat<K::P / 8> x;
-  __device__ __forceinline__ void init(const Dims& d, int lane) {
-    bc.init(lane, (uint32_t)d.G * K::N * 2);
-    x.init(lane, (uint32_t)d.H * K::P * 2);
+  using GN = DmaGeo<K::N / 8>;
+  using GP = DmaGeo<K::P / 8>;
+  static_assert(K::NW % GN::NPAT == 0 && K::BC_NI % GN::NPAT == 0, "B/C pattern per wave");
+  static_assert(K::NW % GP::NPAT == 0 && (K::T / GP::RPI) % GP::NPAT == 0 &&
+                    K::BC_NI % GP::NPAT == 0,
+                "x pattern per wave");
+  uint32_t bc, x, dt;
+  __device__ __forceinline__ void init(const Dims& d, const Coord& c) {
+    bc = GN::lane_off(c.wave, c.lane, (uint32_t)d.G * K::N * 2);
+    x = GP::lane_off(c.wave, c.lane, (uint32_t)d.H * K::P * 2);
+    dt = (uint32_t)min(c.lane, K::T - 1) * (uint32_t)d.H * 4;
   }
 };
 
@@ -243,24 +261,27 @@ __device__ __forceinline__ void refresh_lane(Coord& c) {
   c.c16 = c.lane & 15;
 }
 
-// Issue one stage's DMA: [B][C if WITH_C][x of the block's heads], tokens tok0 .. tok0 + T - 1.
-// In the last, partial sub-chunk rows past the sequence end re-read its last row; heads past the
-// group re-read its last head (their results are never used).
+// Issue one stage's DMA: [B][C if WITH_C][x of the block's heads], tokens tok0 .. tok0 + T - 1,
+// then one instruction per wave for the dt of its own head. In the last, partial sub-chunk rows
+// past the sequence end re-read its last row; heads past the group re-read its last head (their
+// results are never used). Per wave: NI / NW (+1 for the first NI % NW waves) + 1 instructions.
 template <class K, bool WITH_C>
 __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* Bm, const u16* Cm,
-                                            const Dims& d, const Coord& c, const DmaLanes<K>& dl,
-                                            int tok0) {
+                                            const float* dt, const Dims& d, const Coord& c,
+                                            const DmaLanes<K>& dl, int tok0) {
   constexpr int NBC = (WITH_C ? 2 : 1) * K::BC_NI;
-  constexpr int NI = WITH_C ? K::SCAN_NI : K::RUN_NI;
+  constexpr int NI = NBC + K::X_NI;
   constexpr int PPR_N = K::N / 8, PPR_P = K::P / 8;
   constexpr int RPI_N = 64 / PPR_N, RPI_P = 64 / PPR_P;
+  constexpr int XI = K::T / RPI_P;  // x instructions per head
   const int64_t ldbc = (int64_t)d.G * K::N * 2, ldx = (int64_t)d.H * K::P * 2;  // row bytes
-  const char* bbase = reinterpret_cast<const char*>(Bm) +
-                      (((int64_t)c.b * d.L + tok0) * d.G + c.grp) * (K::N * 2);
-  const char* cbase = reinterpret_cast<const char*>(Cm) +
-                      (((int64_t)c.b * d.L + tok0) * d.G + c.grp) * (K::N * 2);
-  const char* xbase = reinterpret_cast<const char*>(x) +
-                      (((int64_t)c.b * d.L + tok0) * d.H + c.hbase) * (K::P * 2);
+  const int64_t row0 = (int64_t)c.b * d.L + tok0;
+  const char* bbase = reinterpret_cast<const char*>(Bm) + (row0 * d.G + c.grp) * (K::N * 2);
+  const char* cbase = reinterpret_cast<const char*>(Cm) + (row0 * d.G + c.grp) * (K::N * 2);
+  const char* xbase = reinterpret_cast<const char*>(x) + (row0 * d.H + c.hbase) * (K::P * 2);
+  const char* dbase = reinterpret_cast<const char*>(dt) + (row0 * d.H + c.h) * 4;
+  const uint32_t l0 = lds_addr(st);
+  const uint32_t ldt = l0 + NI * 1024 + c.wave * 256;
   if (tok0 + K::T <= d.L) {
     // row strides as opaque scalars: their per-instruction multiples are recomputed (scalar ALU)
     // each call rather than held in scalar registers across the loop
@@ -276,37 +297,39 @@ __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* B
       if (bc) {  // B or C
         const bool isC = WITH_C && (EVEN ? k0 >= K::BC_NI : k >= K::BC_NI);
         const int kk = isC ? k - K::BC_NI : k;
-        const uint32_t o = dl.bc.at(kk) + (uint32_t)(kk * RPI_N) * lb;
-        dma16((isC ? cbase : bbase) + o, st + k * 1024);
+        dma_x4((isC ? cbase : bbase) + (uint32_t)(kk * RPI_N) * lb, dl.bc, l0 + k * 1024);
       } else {
         const int kk = k - NBC;
-        const int hh = kk / (K::T / RPI_P), kr = kk % (K::T / RPI_P);
+        const int hh = kk / XI, kr = kk % XI;
         const int hoff = min(hh, c.hlast - c.hbase) * (K::P * 2);
-        const uint32_t o = (uint32_t)hoff + dl.x.at(kr) + (uint32_t)(kr * RPI_P) * lx;
-        dma16(xbase + o, st + k * 1024);
+        dma_x4(xbase + hoff + (uint32_t)(kr * RPI_P) * lx, dl.x, l0 + k * 1024);
       }
     }
+    dma_x1(dbase, dl.dt, ldt);
   } else {
     const int last = d.L - 1 - tok0;  // last valid row of the sub-chunk
 #pragma unroll
     for (int k0 = 0; k0 < NI; k0 += K::NW) {
       const int k = k0 + c.wave;
       if (k >= NI) break;
-      const char* src;
       if (k < NBC) {
         const bool isC = WITH_C && k >= K::BC_NI;
         const int kk = isC ? k - K::BC_NI : k;
         const int t = kk * RPI_N + c.lane / PPR_N, cp = c.lane % PPR_N;
-        src = (isC ? cbase : bbase) + (int64_t)min(t, last) * ldbc + ((cp ^ swz_key<PPR_N>(t)) << 4);
+        const uint32_t o =
+            (uint32_t)(min(t, last) * ldbc) + (uint32_t)((cp ^ swz_key<PPR_N>(t)) << 4);
+        dma_x4(isC ? cbase : bbase, o, l0 + k * 1024);
       } else {
         const int kk = k - NBC;
-        const int hh = kk / (K::T / RPI_P), kr = kk % (K::T / RPI_P);
+        const int hh = kk / XI, kr = kk % XI;
         const int hoff = min(hh, c.hlast - c.hbase) * (K::P * 2);
         const int t = kr * RPI_P + c.lane / PPR_P, cp = c.lane % PPR_P;
-        src = xbase + hoff + (int64_t)min(t, last) * ldx + ((cp ^ swz_key<PPR_P>(t)) << 4);
+        const uint32_t o = (uint32_t)(hoff + min(t, last) * ldx) +
+                           (uint32_t)((cp ^ swz_key<PPR_P>(t)) << 4);
+        dma_x4(xbase, o, l0 + k * 1024);
       }
-      dma16(src, st + k * 1024);
     }
+    dma_x1(dbase, (uint32_t)min(c.lane, last) * (uint32_t)d.H * 4, ldt);
   }
 }
 
@@ -322,13 +345,13 @@ __device__ __forceinline__ void convert_stage(char* st, const Coord& c) {
   }
 }
 
-// dt of this wave's head for the tokens of a sub-chunk (lane l: token tok0 + l), 0 past the end.
+// dt of this wave's head for the tokens of a staged sub-chunk (lane l: token tok0 + l), 0 past the
+// sequence end; dts is the stage's dt region (this wave's own DMA: readable after its own wait).
 template <class K>
-__device__ __forceinline__ float load_dt(const float* dt, const Dims& d, const Coord& c,
-                                         int tok0) {
-  const int t = tok0 + c.lane;
-  const float v = dt[((int64_t)c.b * d.L + min(t, d.L - 1)) * d.H + c.h];
-  return (c.lane < K::T && t < d.L && c.active) ? v : 0.f;
+__device__ __forceinline__ float stage_dt(const char* dts, const Dims& d, const Coord& c,
+                                          int tok0) {
+  const float v = reinterpret_cast<const float*>(dts + c.wave * 256)[c.lane];
+  return (c.lane < K::T && tok0 + c.lane < d.L && c.active) ? v : 0.f;
 }
 
 // Per-sub-chunk decay bookkeeping of one wave (lane l = token l, acs = inclusive cumulative
@@ -382,7 +405,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
   __shared__ __align__(1024) char smem[K::RUN_LDS];
   Coord c = coords<K>(d);
   DmaLanes<K> dl;
-  dl.init(d, c.lane);
+  dl.init(d, c);
   constexpr int T = K::T;
   const int nsub = (d.L + T - 1) / T;
   const int RS = run_len / T;  // sub-chunks per run (run_len is a multiple of every T)
@@ -399,34 +422,31 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
     for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] = zero4();
   float logsum = 0.f;
 
-  // prologue: dt of the first sub-chunk, stages of the first two. Every dt load is issued before
-  // the DMA of the same round, so waiting for a dt value never waits for a later stage.
-  float dt_next = load_dt<K>(dt, d, c, s_begin * T);
-  issue_stage<K, false>(smem, x, Bm, nullptr, d, c, dl, s_begin * T);
+  // prologue: stages of the first two sub-chunks
+  issue_stage<K, false>(smem, x, Bm, nullptr, dt, d, c, dl, s_begin * T);
   if (s_begin + 1 < s_end)
-    issue_stage<K, false>(smem + K::RUN_STAGE, x, Bm, nullptr, d, c, dl, (s_begin + 1) * T);
-  // DMA instructions this wave issues per stage
-  constexpr int NLO = K::RUN_NI / K::NW;
+    issue_stage<K, false>(smem + K::RUN_STAGE, x, Bm, nullptr, dt, d, c, dl, (s_begin + 1) * T);
+  // DMA instructions this wave issues per stage: NLO or NLO + 1 tile pieces, and its dt
+  constexpr int NLO = K::RUN_NI / K::NW + 1;
   const bool hi = c.wave < K::RUN_NI % K::NW;
 
   for (int s = s_begin; s < s_end; ++s) {
     const int cur = (s - s_begin) % K::NRUN;
     char* st = smem + cur * K::RUN_STAGE;
-    const float dv = dt_next;
-    // this stage's DMA done; the next stage's (at least this wave's instructions for it were
-    // issued after this stage's) may still be in flight
+    // this stage's DMA done; the next stage's (this wave's instructions for it were issued after
+    // this stage's) may still be in flight
     if (s + 1 >= s_end)
       wait_vm_all();
     else if (hi)
       wait_vm_but<NLO + 1>();
     else
       wait_vm_but<NLO>();
+    const float dv = stage_dt<K>(st + K::RUN_DT, d, c, s * T);
     convert_stage<K, false>(st, c);
     __syncthreads();  // stage visible to all waves; every wave is done with sub-chunk s - 1
-    if (s + 1 < s_end) dt_next = load_dt<K>(dt, d, c, (s + 1) * T);
     if (s + 2 < s_end)
-      issue_stage<K, false>(smem + ((cur + 2) % K::NRUN) * K::RUN_STAGE, x, Bm, nullptr, d, c, dl,
-                            (s + 2) * T);
+      issue_stage<K, false>(smem + ((cur + 2) % K::NRUN) * K::RUN_STAGE, x, Bm, nullptr, dt, d, c,
+                            dl, (s + 2) * T);
     const float acs_end = decay_terms<K>(dv, a_h, wa, c);
     logsum += acs_end;
     const float dec = __expf(acs_end);
@@ -583,7 +603,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
   __shared__ __align__(1024) char smem[K::SCAN_LDS];
   Coord c = coords<K>(d);
   DmaLanes<K> dl;
-  dl.init(d, c.lane);
+  dl.init(d, c);
   ScanLane<K> sl;
   sl.init(c);
   using SL = ScanLane<K>;
@@ -612,10 +632,12 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
             *reinterpret_cast<const float4*>(hr + (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g);
         S[nt][pt] = f32x4{v.x, v.y, v.z, v.w};
       }
+    // the compiler's own wait for these loads (it does not see the DMA waits, which are inline
+    // assembly), here rather than at the state's first use inside the loop
+    __builtin_amdgcn_s_waitcnt(0x0f70);
   }
 
-  issue_stage<K, true>(smem, x, Bm, Cm, d, c, dl, s_begin * T);
-  float dt_next = load_dt<K>(dt, d, c, s_begin * T);
+  issue_stage<K, true>(smem, x, Bm, Cm, dt, d, c, dl, s_begin * T);
   int ytok = -1;  // first token of the sub-chunk whose y waits in the previous stage's x tile
 
   for (int s = s_begin; s < s_end; ++s) {
@@ -625,17 +647,15 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     const char* Bh = st;
     const char* Ch = st + K::BC_BYTES;
     const char* xt = st + xoff;
-    const float dv = dt_next;
-    wait_vm_all();  // this stage's DMA, the dt load, and the y stores of the previous round
+    wait_vm_all();  // this stage's DMA and the y stores of the previous round
     if (ytok >= 0) store_y<K>(smem + (cur ^ 1) * K::SCAN_STAGE + xoff, y, d, c, ytok);
+    const float dv = stage_dt<K>(st + K::SCAN_DT, d, c, s * T);
     convert_stage<K, true>(st, c);
     // this wave's decay bookkeeping needs only its dt: done while other waves finish converting
     const float acs_end = decay_terms<K>(dv, a_h, wa, c);
     __syncthreads();  // stage visible; every wave is done with sub-chunk s - 1 (CB, stage cur^1)
-    if (s + 1 < s_end) {
-      issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, d, c, dl, (s + 1) * T);
-      dt_next = load_dt<K>(dt, d, c, (s + 1) * T);
-    }
+    if (s + 1 < s_end)
+      issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, dt, d, c, dl, (s + 1) * T);
     // C B^T lower-triangle tiles of the sub-chunk, shared by the block's heads: tile q (row-major
     // over the lower triangle) goes to wave q % NW
     constexpr int NTILE = NIT * (NIT + 1) / 2;
