@@ -182,8 +182,8 @@ struct Fz {
   static constexpr int SCAN_STAGE = SCAN_DT + DT_BYTES, RUN_STAGE = RUN_DT + DT_BYTES;
   static constexpr int LDCB = T + 4;                  // floats per C B^T row
   static constexpr int CB_BYTES = T * LDCB * 4;
-  static constexpr int NWA = 4;                       // per-wave token arrays
-  static constexpr int WA_BYTES = NW * NWA * T * 4;   // acs2, dt, w, cf
+  static constexpr int NWA = 5;                       // per-wave token arrays
+  static constexpr int WA_BYTES = NW * NWA * T * 4;   // acs2, dt, w, cf, rdiag
   static constexpr int NSCAN = 2, NRUN = 3;           // stages
   static constexpr int SCAN_LDS = NSCAN * SCAN_STAGE + CB_BYTES + WA_BYTES;
   static constexpr int RUN_LDS = NRUN * RUN_STAGE + WA_BYTES;
@@ -354,23 +354,52 @@ __device__ __forceinline__ float stage_dt(const char* dts, const Dims& d, const 
   return (c.lane < K::T && tok0 + c.lane < d.L && c.active) ? v : 0.f;
 }
 
+// DPP lane moves (VALU, no LDS round trip); lanes whose source is outside the pattern read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xf, false));
+}
+// Inclusive prefix sum over the wave's 64 lanes: within rows of 16 by shifts of 1, 2, 4, 8, then
+// row 0's total into row 1 and row 2's into row 3 (row_bcast:15), then rows 0-1's total into rows
+// 2-3 (row_bcast:31).
+__device__ __forceinline__ float wave_scan(float v) {
+  v += dpp_mov<0x111, 0xf>(v);
+  v += dpp_mov<0x112, 0xf>(v);
+  v += dpp_mov<0x114, 0xf>(v);
+  v += dpp_mov<0x118, 0xf>(v);
+  v += dpp_mov<0x142, 0xa>(v);
+  v += dpp_mov<0x143, 0xc>(v);
+  return v;
+}
+// Lane 15 of each row of 16, broadcast to the row (row_newbcast:15).
+__device__ __forceinline__ float row_last(float v) { return dpp_mov<0x15f, 0xf>(v); }
+
 // Per-sub-chunk decay bookkeeping of one wave (lane l = token l, acs = inclusive cumulative
-// log-decay from the sub-chunk start). Into the wave's LDS arrays:
+// log-decay from the sub-chunk start, e(l) the last token of l's 16-token block). Into the wave's
+// LDS arrays:
 //   acs2 = acs log2(e);  dt;  w = exp(acs_end - acs) dt (state weights);
-//   cf = exp(acs_e - acs) dt, e the last token of the token's 16-row block (column factor of the
-//   off-diagonal blocks of the decay mask; both of its factors are <= 1).
-// Returns acs_end.
+//   cf = exp(acs_e - acs) dt (column factor of the decay mask through the end of the token's
+//   block; both of its factors are <= 1);  rdiag = exp(acs - acs_e) >= 1 (its row factor inside
+//   the token's own block).
+// Returns acs_end; *fast tells whether every block's decay span acs - acs_e stays below 2^100 in
+// base 2, so that rdiag and cf stay inside fp32's normal range and the factored diagonal is exact
+// up to rounding.
 template <class K>
-__device__ __forceinline__ float decay_terms(float dv, float a_h, float* wa, const Coord& c) {
-  const float acs = wave_inclusive_scan(a_h * dv);
-  const float acs_end = __shfl(acs, K::T - 1, kWave);
-  const float acs_blk = __shfl(acs, c.lane | 15, kWave);
+__device__ __forceinline__ float decay_terms(float dv, float a_h, float* wa, const Coord& c,
+                                             bool* fast = nullptr) {
+  const float acs = wave_scan(a_h * dv);
+  const float acs_end = __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acs), K::T - 1));
+  const float span = acs - row_last(acs);  // >= 0
   if (c.lane < K::T) {
     wa[c.lane] = acs * kLog2e;
     wa[K::T + c.lane] = dv;
     wa[2 * K::T + c.lane] = __expf(acs_end - acs) * dv;
-    wa[3 * K::T + c.lane] = __expf(acs_blk - acs) * dv;
+    wa[3 * K::T + c.lane] = __expf(-span) * dv;
+    if (fast) wa[4 * K::T + c.lane] = __expf(span);
   }
+  if (fast) *fast = __ballot(span * kLog2e >= 100.f) == 0;
   return acs_end;
 }
 
@@ -652,7 +681,8 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     const float dv = stage_dt<K>(st + K::SCAN_DT, d, c, s * T);
     convert_stage<K, true>(st, c);
     // this wave's decay bookkeeping needs only its dt: done while other waves finish converting
-    const float acs_end = decay_terms<K>(dv, a_h, wa, c);
+    bool fast;
+    const float acs_end = decay_terms<K>(dv, a_h, wa, c, &fast);
     __syncthreads();  // stage visible; every wave is done with sub-chunk s - 1 (CB, stage cur^1)
     if (s + 1 < s_end)
       issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, dt, d, c, dl, (s + 1) * T);
@@ -769,6 +799,23 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
           const float cf[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
           for (int q = 0; q < 8; ++q) m[q] = cb[q] * cf[q] * r;
+        } else if (fast) {
+          // tiles of the diagonal's block row: the lane's 8 tokens lie in row block it (decay
+          // factored through the block's last token, masked), in the block before it (factored
+          // through that block's last token) or after it (masked out)
+          const float4 f0 = *reinterpret_cast<const float4*>(wa + 3 * T + j0);
+          const float4 f1 = *reinterpret_cast<const float4*>(wa + 3 * T + j0 + 4);
+          const float cf[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+          float r = wa[4 * T + i];
+          if (2 * js + 1 == it) {  // lanes g < 2 hold tokens of block 2 js
+            const float rb = __builtin_amdgcn_exp2f(acs2_i[it] - wa[32 * js + 15]);
+            r = c.g < 2 ? rb : r;
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float v = cb[q] * cf[q] * r;
+            m[q] = (j0 + q < i) ? v : ((j0 + q == i) ? v + d_h : 0.f);
+          }
         } else {
           const float4 a0 = *reinterpret_cast<const float4*>(wa + j0);
           const float4 a1 = *reinterpret_cast<const float4*>(wa + j0 + 4);

@@ -71,9 +71,12 @@ def score(y, f, y_ref, f_ref, io, units=None, H=None):
 
 
 def check_shape(shape: synth.SSDShape, seed=None, cfg_index=None, variant="auto",
-                precision="auto", max_units=None, run_chunks=0):
-    """Run one workload on the GPU and the oracle; return the parity report."""
+                precision="auto", max_units=None, run_chunks=0, mutate=None):
+    """Run one workload on the GPU and the oracle; return the parity report. `mutate`, if
+    given, edits the drawn input arrays in place before both sides see them."""
     inp = synth.make_inputs(shape, seed=seed, cfg_index=cfg_index)
+    if mutate is not None:
+        mutate(inp)
     units = None
     if max_units is not None and shape.batch * shape.nheads > max_units:
         units = sample_units(shape.batch, shape.nheads, max_units)

@@ -91,6 +91,30 @@ def test_fused_run_lengths(shape, run_chunks):
     assert rep["pass"], rep
 
 
+def _strong_decay(inp):
+    """Decay far beyond fp32's exponent range inside one 16-token block: head 0 everywhere,
+    head 1 in bursts of 40 tokens, head 2 left as drawn (the fused kernel's factored decay
+    mask must hand such blocks to its direct form)."""
+    dt, A = inp["dt"], inp["A"]
+    A[:3] = -16.0
+    dt[:, :, 0] = 0.5 + dt[:, :, 0]                       # ~8 nats per token
+    L = dt.shape[1]
+    for t0 in range(17, L, 150):
+        dt[:, t0:t0 + 40, 1] = 2.0                        # 32 nats per token
+    dt[:, ::37, 2] = 0.0                                  # no decay at some tokens
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("shape", [
+    synth.SSDShape("strong_p64n128", 2, 700, 3, 64, 128, 1, 64, init_state=True),
+    synth.SSDShape("strong_p128n64_q32", 1, 450, 4, 128, 64, 2, 32),
+], ids=lambda s: s.name)
+def test_strong_decay(shape, variant):
+    skip_unfusable(shape, variant)
+    rep = check_shape(shape, seed=31, variant=variant, mutate=_strong_decay)
+    assert rep["pass"], rep
+
+
 @pytest.mark.parametrize("precision", ["fp16", "fp32"])
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_precision_options(precision, variant):
