@@ -180,12 +180,13 @@ struct Fz {
   static constexpr int SCAN_NI = 2 * BC_NI + X_NI, RUN_NI = BC_NI + X_NI;
   static constexpr int SCAN_DT = SCAN_NI * 1024, RUN_DT = RUN_NI * 1024;  // dt offsets
   static constexpr int SCAN_STAGE = SCAN_DT + DT_BYTES, RUN_STAGE = RUN_DT + DT_BYTES;
-  static constexpr int LDCB = T + 4;                  // floats per C B^T row
-  static constexpr int CB_BYTES = T * LDCB * 4;
+  static constexpr int NMB = NIT * (NIT + 1) / 2;    // lower-triangle 16x16 blocks of M
+  static constexpr int MT_HEAD = NMB * 512;           // a head's fp16 M blocks
   static constexpr int NWA = 5;                       // per-wave token arrays
-  static constexpr int WA_BYTES = NW * NWA * T * 4;   // acs2, dt, w, cf, rdiag
+  static constexpr int WA_BYTES = NW * NWA * T * 4;   // acs2, dt, w, cf, rdiag (F1: per wave)
+  static constexpr int WA_SCAN = HPB * NWA * T * 4;   // F3: per head
   static constexpr int NSCAN = 2, NRUN = 3;           // stages
-  static constexpr int SCAN_LDS = NSCAN * SCAN_STAGE + CB_BYTES + WA_BYTES;
+  static constexpr int SCAN_LDS = NSCAN * SCAN_STAGE + HPB * MT_HEAD + WA_SCAN;
   static constexpr int RUN_LDS = NRUN * RUN_STAGE + WA_BYTES;
   static_assert(P % PS == 0 && NW % WPH == 0, "whole waves per head");
   static_assert(N / 8 >= 8 && P / 8 >= 8, "swizzle needs 8 pieces per row");
@@ -264,11 +265,16 @@ __device__ __forceinline__ void refresh_lane(Coord& c) {
 // Issue one stage's DMA: [B][C if WITH_C][x of the block's heads], tokens tok0 .. tok0 + T - 1,
 // then one instruction per wave for the dt of its own head. In the last, partial sub-chunk rows
 // past the sequence end re-read its last row; heads past the group re-read its last head (their
-// results are never used). Per wave: NI / NW (+1 for the first NI % NW waves) + 1 instructions.
+// results are never used). Per wave: NI / NW (+1 for the first NI % NW waves) + 1 instructions,
+// in rounds of one instruction per wave; only rounds r0 .. r1 - 1 (and the dt instruction if
+// with_dt) are issued here, so that a caller can spread a stage's instructions over its work
+// (a wave stalls when it issues more than the memory pipeline accepts). After full unrolling
+// the round tests are compile-time.
 template <class K, bool WITH_C>
 __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* Bm, const u16* Cm,
                                             const float* dt, const Dims& d, const Coord& c,
-                                            const DmaLanes<K>& dl, int tok0) {
+                                            const DmaLanes<K>& dl, int tok0, int r0 = 0,
+                                            int r1 = 1 << 20, bool with_dt = true) {
   constexpr int NBC = (WITH_C ? 2 : 1) * K::BC_NI;
   constexpr int NI = NBC + K::X_NI;
   constexpr int PPR_N = K::N / 8, PPR_P = K::P / 8;
@@ -291,6 +297,7 @@ __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* B
     constexpr bool EVEN = K::BC_NI % K::NW == 0 && NI % K::NW == 0;
 #pragma unroll
     for (int k0 = 0; k0 < NI; k0 += K::NW) {
+      if (k0 < r0 * K::NW || k0 >= r1 * K::NW) continue;
       const int k = k0 + c.wave;  // wave-uniform
       if (!EVEN && k >= NI) break;
       const bool bc = EVEN ? k0 < NBC : k < NBC;
@@ -305,11 +312,12 @@ __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* B
         dma_x4(xbase + hoff + (uint32_t)(kr * RPI_P) * lx, dl.x, l0 + k * 1024);
       }
     }
-    dma_x1(dbase, dl.dt, ldt);
+    if (with_dt) dma_x1(dbase, dl.dt, ldt);
   } else {
     const int last = d.L - 1 - tok0;  // last valid row of the sub-chunk
 #pragma unroll
     for (int k0 = 0; k0 < NI; k0 += K::NW) {
+      if (k0 < r0 * K::NW || k0 >= r1 * K::NW) continue;
       const int k = k0 + c.wave;
       if (k >= NI) break;
       if (k < NBC) {
@@ -329,7 +337,7 @@ __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* B
         dma_x4(xbase, o, l0 + k * 1024);
       }
     }
-    dma_x1(dbase, (uint32_t)min(c.lane, last) * (uint32_t)d.H * 4, ldt);
+    if (with_dt) dma_x1(dbase, (uint32_t)min(c.lane, last) * (uint32_t)d.H * 4, ldt);
   }
 }
 
@@ -585,8 +593,13 @@ struct ScanLane {
   uint32_t xtr[K::NPT][2];  // x fragment (transposing read)
   uint32_t cbr[KP];         // C B^T inputs: row c16, piece 4 kn + g
   uint32_t epi[K::NPT];     // y write into the x tile: row c16, piece (p0 + 16 pt) / 8 + g/2
+  uint32_t mwr;             // M block write: row c16, columns 4 g .. 4 g + 3
+  uint32_t mrd;             // M fragment read: block + g/2, row c16, columns 8 (g&1) .. + 7
   __device__ __forceinline__ void init(const Coord& c) {
     const int g = c.g, c16 = c.c16, j = c.lane & 15;
+    const int sw = (c16 >> 3) & 1;  // M rows 8..15 of a block hold their two pieces swapped
+    mwr = c16 * 32 + (((g >> 1) ^ sw) << 4) + ((g & 1) << 3);
+    mrd = (g >> 1) * 512 + c16 * 32 + (((g & 1) ^ sw) << 4);
 #pragma unroll
     for (int b = 0; b < KP; ++b) {
 #pragma unroll
@@ -617,11 +630,125 @@ __device__ __forceinline__ s16x8 tr8(const char* base, uint32_t lo, uint32_t hi)
 
 // ---- F3: fused scan -----------------------------------------------------------------------------
 // Per sub-chunk (tokens i, j), with acs the inclusive cumulative log-decay from its start:
-//   y_i = sum_{j <= i} (C_i . B_j) exp(acs_i - acs_j) dt_j x_j + exp(acs_i) C_i . S + D x_i
+//   y_i = sum_{j <= i} M_ij x_j + exp(acs_i) C_i . S,
+//   M_ij = (C_i . B_j) exp(acs_i - acs_j) dt_j (j <= i), plus D on the diagonal (skip term)
 //   S  <- exp(acs_end) S + sum_j exp(acs_end - acs_j) dt_j x_j B_j^T
-// Each wave computes y^T for its p-slice (rows p, columns i), so every accumulator lane holds
-// four consecutive p of one token: the readout's A operand comes straight from the state
-// accumulators (K index n in accumulator order), and y leaves in 8-byte row pieces.
+// A head's waves split the lower-triangle 16x16 blocks of its M, build them straight from the
+// C B^T accumulators and leave them in LDS in fp16. Each wave then computes y^T for its p-slice
+// (rows p, columns i), so every accumulator lane holds four consecutive p of one token: the
+// readout's A operand comes straight from the state accumulators (K index n in accumulator
+// order), and y leaves in 8-byte row pieces.
+
+// Byte offset of M block (row block it, column block jt <= it) in a head's M area.
+__device__ __forceinline__ constexpr int mblk(int it, int jt) {
+  return (it * (it + 1) / 2 + jt) * 512;
+}
+
+// One M block from its C B^T accumulators (transposed: lane (g, c16) holds tokens
+// j = 16 jt + 4 g + rr, rr = 0..3, of row i = 16 it + c16), written to the head's M area in fp16.
+// Blocks below the diagonal factor the decay through the end of column block jt (both factors
+// <= 1); diagonal blocks through the end of their own block (rdiag >= 1, cf <= dt) when the
+// sub-chunk's block spans allow it (fast), else directly.
+template <class K>
+__device__ __forceinline__ void put_m(f32x4 acc, int it, int jt, const float* wa, float d_h,
+                                      bool fast, char* mh, const ScanLane<K>& sl, const Coord& c) {
+  constexpr int T = K::T;
+  const int i = 16 * it + c.c16, jb = 16 * jt + 4 * c.g;
+  const float4 cf = *reinterpret_cast<const float4*>(wa + 3 * T + jb);
+  const float cfv[4] = {cf.x, cf.y, cf.z, cf.w};
+  float m[4];
+  if (jt < it) {
+    const float r = __builtin_amdgcn_exp2f(wa[i] - wa[16 * jt + 15]);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) m[rr] = acc[rr] * cfv[rr] * r;
+  } else if (fast) {
+    const float r = wa[4 * T + i];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float v = acc[rr] * cfv[rr] * r;
+      m[rr] = (jb + rr < i) ? v : ((jb + rr == i) ? v + d_h : 0.f);
+    }
+  } else {
+    const float acs2_i = wa[i];
+    const float4 aj = *reinterpret_cast<const float4*>(wa + jb);
+    const float4 dj = *reinterpret_cast<const float4*>(wa + T + jb);
+    const float ajv[4] = {aj.x, aj.y, aj.z, aj.w}, djv[4] = {dj.x, dj.y, dj.z, dj.w};
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float v = acc[rr] * __builtin_amdgcn_exp2f(fminf(acs2_i - ajv[rr], 0.f)) * djv[rr];
+      m[rr] = (jb + rr < i) ? v : ((jb + rr == i) ? v + d_h : 0.f);
+    }
+  }
+  const f16x2 lo = cvt_f16x2(m[0], m[1]), hi = cvt_f16x2(m[2], m[3]);
+  *reinterpret_cast<uint2*>(mh + mblk(it, jt) + sl.mwr) =
+      make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// C B^T fragment (rows r0 .. r0 + 15 of a converted B or C tile, K step kn over n).
+template <class K>
+__device__ __forceinline__ f16x8 bc_frag(const char* tile, int r0, int kn, const ScanLane<K>& sl) {
+  using SL = ScanLane<K>;
+  return *reinterpret_cast<const f16x8*>(tile + r0 * K::ROW_N + sl.cbr[kn % SL::KP] +
+                                         (kn / SL::KP) * (16 * SL::KP * 4));
+}
+
+// This wave's share of its head's M blocks for the staged sub-chunk.
+// dma(kn) issues the next stage's share for K step kn (0 .. NKN - 1), spread over the work.
+template <class K, class Dma>
+__device__ __forceinline__ void build_m(const char* Bh, const char* Ch, const float* wa, float d_h,
+                                        bool fast, char* mh, const ScanLane<K>& sl,
+                                        const Coord& c, Dma&& dma) {
+  using M = Mma<f16>;
+  constexpr int NIT = K::NIT;
+  const int hw = c.wave % K::WPH;  // wave within the head (wave-uniform)
+  if constexpr (NIT == 4 && K::WPH == 2) {
+    // row blocks {0, 3} or {1, 2}: five blocks each, C fragments of two row blocks and B
+    // fragments of (up to) four column blocks per K step
+    const int ia = hw, ib = 3 - hw;
+    f32x4 a0 = zero4(), a1 = zero4(), b0 = zero4(), b1 = zero4(), b2 = zero4(), b3 = zero4();
+#pragma unroll
+    for (int kn = 0; kn < K::NKN; ++kn) {
+      dma(kn);
+      const f16x8 ca = bc_frag<K>(Ch, 16 * ia, kn, sl), cb = bc_frag<K>(Ch, 16 * ib, kn, sl);
+      f16x8 bf[4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) bf[jt] = bc_frag<K>(Bh, 16 * jt, kn, sl);
+      a0 = M::mma(bf[0], ca, a0);
+      b0 = M::mma(bf[0], cb, b0);
+      b1 = M::mma(bf[1], cb, b1);
+      b2 = M::mma(bf[2], cb, b2);
+      if (hw) {
+        a1 = M::mma(bf[1], ca, a1);
+      } else {
+        b3 = M::mma(bf[3], cb, b3);
+      }
+    }
+    put_m<K>(a0, ia, 0, wa, d_h, fast, mh, sl, c);
+    put_m<K>(b0, ib, 0, wa, d_h, fast, mh, sl, c);
+    put_m<K>(b1, ib, 1, wa, d_h, fast, mh, sl, c);
+    put_m<K>(b2, ib, 2, wa, d_h, fast, mh, sl, c);
+    if (hw)
+      put_m<K>(a1, 1, 1, wa, d_h, fast, mh, sl, c);
+    else
+      put_m<K>(b3, 3, 3, wa, d_h, fast, mh, sl, c);
+  } else {
+    // blocks in row-major order over the lower triangle, block q to the head's wave q % WPH
+#pragma unroll
+    for (int kn = 0; kn < K::NKN; ++kn) dma(kn);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+#pragma unroll
+      for (int jt = 0; jt <= it; ++jt) {
+        if ((it * (it + 1) / 2 + jt) % K::WPH != hw) continue;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kn = 0; kn < K::NKN; ++kn)
+          acc = M::mma(bc_frag<K>(Bh, 16 * jt, kn, sl), bc_frag<K>(Ch, 16 * it, kn, sl), acc);
+        put_m<K>(acc, it, jt, wa, d_h, fast, mh, sl, c);
+      }
+  }
+}
+
 template <class K>
 __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     const u16* __restrict__ x, const u16* __restrict__ Bm, const u16* __restrict__ Cm,
@@ -629,6 +756,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     const float* __restrict__ h_run, u16* __restrict__ y, Dims d, int run_len, int nr) {
   using M = Mma<f16>;
   static_assert(K::SCAN_LDS <= 160 * 1024, "LDS budget");
+  // [stage 0][stage 1][M blocks per head][token arrays per head]
   __shared__ __align__(1024) char smem[K::SCAN_LDS];
   Coord c = coords<K>(d);
   DmaLanes<K> dl;
@@ -641,10 +769,14 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
   const int RS = run_len / T;  // sub-chunks per run (run_len is a multiple of every T)
   const int s_begin = c.r * RS, s_end = min(nsub, s_begin + RS);
   if (s_begin >= s_end) return;
-  float* cbs = reinterpret_cast<float*>(smem + K::NSCAN * K::SCAN_STAGE);
-  float* wa = reinterpret_cast<float*>(smem + K::NSCAN * K::SCAN_STAGE + K::CB_BYTES) +
-              c.wave * K::NWA * T;
-  const int xoff = 2 * K::BC_BYTES + (c.wave / K::WPH) * (T * K::ROW_P);
+  const int hb = c.wave / K::WPH;  // head within the block
+  char* mh = smem + K::NSCAN * K::SCAN_STAGE + hb * K::MT_HEAD;
+  // token arrays of the head: both of its waves compute and write identical values; they are
+  // read only between the two barriers of a sub-chunk
+  float* wa =
+      reinterpret_cast<float*>(smem + K::NSCAN * K::SCAN_STAGE + K::HPB * K::MT_HEAD) +
+      hb * K::NWA * T;
+  const int xoff = 2 * K::BC_BYTES + hb * (T * K::ROW_P);
   const float a_h = Av[c.h], d_h = Dv[c.h];
 
   // carried state S^T tiles (rows n, columns p): lane holds p = p0 + 16 pt + c16,
@@ -680,77 +812,67 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     if (ytok >= 0) store_y<K>(smem + (cur ^ 1) * K::SCAN_STAGE + xoff, y, d, c, ytok);
     const float dv = stage_dt<K>(st + K::SCAN_DT, d, c, s * T);
     convert_stage<K, true>(st, c);
-    // this wave's decay bookkeeping needs only its dt: done while other waves finish converting
+    // the head's decay bookkeeping needs only its dt: done while other waves finish converting
     bool fast;
     const float acs_end = decay_terms<K>(dv, a_h, wa, c, &fast);
-    __syncthreads();  // stage visible; every wave is done with sub-chunk s - 1 (CB, stage cur^1)
-    if (s + 1 < s_end)
-      issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, dt, d, c, dl, (s + 1) * T);
-    // C B^T lower-triangle tiles of the sub-chunk, shared by the block's heads: tile q (row-major
-    // over the lower triangle) goes to wave q % NW
-    constexpr int NTILE = NIT * (NIT + 1) / 2;
+    __syncthreads();  // A: stage and token arrays visible; every wave is done with sub-chunk s - 1
+    // the next stage's DMA (into the stage every wave is done with), spread over the M blocks
+    const bool more = s + 1 < s_end;
+    constexpr int NRND = (K::SCAN_NI + K::NW - 1) / K::NW, RPK = (NRND + K::NKN - 1) / K::NKN;
+    auto dma = [&](int kn) {
+      if (more)
+        issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, dt, d, c, dl,
+                             (s + 1) * T, kn * RPK, (kn + 1) * RPK, kn == K::NKN - 1);
+    };
+
+    f32x4 Y[NPT][NIT];
+    f16x8 w16[K::NJS];  // state weights of the lane's 8 tokens per K step
+    if (!c.active) {
 #pragma unroll
-    for (int q0 = 0; q0 < NTILE; q0 += K::NW) {
-      const int q = q0 + c.wave;
-      if (q < NTILE) {
-        int it = 0;
-        while ((it + 1) * (it + 2) / 2 <= q) ++it;
-        const int jt = q - it * (it + 1) / 2;
-        f32x4 acc = zero4();
-        const int j = 16 * jt + c.c16;
-        const char* crow = Ch + 16 * it * K::ROW_N;
-        const char* brow = Bh + 16 * jt * K::ROW_N;
+      for (int kn = 0; kn < K::NKN; ++kn) dma(kn);
+    } else {
+      build_m<K>(Bh, Ch, wa, d_h, fast, mh, sl, c, dma);
+
+      // readout of the carried state: Y^T = S C^T (K index n in accumulator order)
 #pragma unroll
-        for (int kn = 0; kn < K::NKN; ++kn) {
-          const int o = (kn / SL::KP) * (16 * SL::KP * 4);  // piece bits above the pattern
-          const f16x8 a = *reinterpret_cast<const f16x8*>(crow + sl.cbr[kn % SL::KP] + o);
-          const f16x8 bb = *reinterpret_cast<const f16x8*>(brow + sl.cbr[kn % SL::KP] + o);
-          acc = M::mma(a, bb, acc);
+      for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) Y[pt][it] = zero4();
+#pragma unroll
+      for (int kn = 0; kn < K::NKN; ++kn) {
+        f16x8 sa[NPT];
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) {
+          const float v[8] = {S[2 * kn][pt][0],     S[2 * kn][pt][1],     S[2 * kn][pt][2],
+                              S[2 * kn][pt][3],     S[2 * kn + 1][pt][0], S[2 * kn + 1][pt][1],
+                              S[2 * kn + 1][pt][2], S[2 * kn + 1][pt][3]};
+          sa[pt] = cvt_f16x8(v);
         }
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) cbs[(16 * it + 4 * c.g + rr) * K::LDCB + j] = acc[rr];
-      }
-    }
-    // readout of the carried state first: it needs no C B^T, so it absorbs the uneven C B^T
-    // shares before the barrier that publishes the tiles
-    f32x4 Y[NPT][NIT];
-    float acs2_i[NIT];
-    if (c.active) {
-
-    // readout of the carried state: Y^T = S C^T (K index n in accumulator order)
+        for (int it = 0; it < NIT; ++it) {
+          const char* crow = Ch + 16 * it * K::ROW_N + (kn / SL::KP) * (16 * SL::KP * 4);
+          const uint2 lo = *reinterpret_cast<const uint2*>(crow + sl.cro[kn % SL::KP][0]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(crow + sl.cro[kn % SL::KP][1]);
+          const f16x8 cf = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-    for (int pt = 0; pt < NPT; ++pt)
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) Y[pt][it] = zero4();
-#pragma unroll
-    for (int kn = 0; kn < K::NKN; ++kn) {
-      f16x8 sa[NPT];
-#pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) {
-        const float v[8] = {S[2 * kn][pt][0],     S[2 * kn][pt][1],     S[2 * kn][pt][2],
-                            S[2 * kn][pt][3],     S[2 * kn + 1][pt][0], S[2 * kn + 1][pt][1],
-                            S[2 * kn + 1][pt][2], S[2 * kn + 1][pt][3]};
-        sa[pt] = cvt_f16x8(v);
+          for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(sa[pt], cf, Y[pt][it]);
+        }
       }
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
-        const char* crow = Ch + 16 * it * K::ROW_N + (kn / SL::KP) * (16 * SL::KP * 4);
-        const uint2 lo = *reinterpret_cast<const uint2*>(crow + sl.cro[kn % SL::KP][0]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(crow + sl.cro[kn % SL::KP][1]);
-        const f16x8 cf = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const float e = __builtin_amdgcn_exp2f(wa[16 * it + c.c16]);
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(sa[pt], cf, Y[pt][it]);
+        for (int pt = 0; pt < NPT; ++pt) Y[pt][it] *= e;
+      }
+#pragma unroll
+      for (int js = 0; js < K::NJS; ++js) {
+        const float4 w0 = *reinterpret_cast<const float4*>(wa + 2 * T + 32 * js + 8 * c.g);
+        const float4 w1 = *reinterpret_cast<const float4*>(wa + 2 * T + 32 * js + 8 * c.g + 4);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        w16[js] = cvt_f16x8(wv);
       }
     }
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      acs2_i[it] = wa[16 * it + c.c16];
-      const float e = __builtin_amdgcn_exp2f(acs2_i[it]);
-#pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) Y[pt][it] *= e;
-    }
-    }
-    __syncthreads();  // C B^T tiles visible
+    __syncthreads();  // B: M blocks visible; the token arrays are free again
     if (!c.active) continue;
     SSD_SB();
 
@@ -763,73 +885,22 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
 
 #pragma unroll
     for (int js = 0; js < K::NJS; ++js) {
-      const int j0 = 32 * js + 8 * c.g;  // this lane's 8 tokens of the K step
       f16x8 xh[NPT], xs[NPT];
-      {
-        const float4 w0 = *reinterpret_cast<const float4*>(wa + 2 * T + j0);
-        const float4 w1 = *reinterpret_cast<const float4*>(wa + 2 * T + j0 + 4);
-        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        const f16x8 w16 = cvt_f16x8(wv);
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) {
-          const s16x8 r = tr8(xt + 32 * js * K::ROW_P, sl.xtr[pt][0], sl.xtr[pt][1]);
-          float v[8];
+      for (int pt = 0; pt < NPT; ++pt) {
+        const s16x8 r = tr8(xt + 32 * js * K::ROW_P, sl.xtr[pt][0], sl.xtr[pt][1]);
+        float v[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = __uint_as_float((uint32_t)(uint16_t)r[e] << 16);
-          xh[pt] = cvt_f16x8(v);
-          xs[pt] = xh[pt] * w16;  // packed fp16 multiply
-        }
+        for (int e = 0; e < 8; ++e) v[e] = __uint_as_float((uint32_t)(uint16_t)r[e] << 16);
+        xh[pt] = cvt_f16x8(v);
+        xs[pt] = xh[pt] * w16[js];  // packed fp16 multiply
       }
-      // intra-sub-chunk product: Y^T += x^T M^T, M_ij = CB_ij exp(acs_i - acs_j) dt_j (j <= i),
-      // plus D on the diagonal (the skip term D x_i rides along with the diagonal block)
+      // intra-sub-chunk product: Y^T += x^T M^T over the K step's 32 tokens; in the block row
+      // on the diagonal, lanes g >= 2 hold tokens after the row block (zero)
 #pragma unroll
       for (int it = 2 * js; it < NIT; ++it) {
-        const int i = 16 * it + c.c16;
-        const float4 c0 = *reinterpret_cast<const float4*>(cbs + i * K::LDCB + j0);
-        const float4 c1 = *reinterpret_cast<const float4*>(cbs + i * K::LDCB + j0 + 4);
-        const float cb[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        float m[8];
-        if (2 * js + 1 < it) {
-          // both 16-token blocks of the K step lie before token tile it: factor the decay
-          // through the end of the lane's block, exp(acs_i - acs_e) * [exp(acs_e - acs_j) dt_j]
-          const int e = 32 * js + 16 * (c.g >> 1) + 15;
-          const float r = __builtin_amdgcn_exp2f(acs2_i[it] - wa[e]);
-          const float4 f0 = *reinterpret_cast<const float4*>(wa + 3 * T + j0);
-          const float4 f1 = *reinterpret_cast<const float4*>(wa + 3 * T + j0 + 4);
-          const float cf[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-#pragma unroll
-          for (int q = 0; q < 8; ++q) m[q] = cb[q] * cf[q] * r;
-        } else if (fast) {
-          // tiles of the diagonal's block row: the lane's 8 tokens lie in row block it (decay
-          // factored through the block's last token, masked), in the block before it (factored
-          // through that block's last token) or after it (masked out)
-          const float4 f0 = *reinterpret_cast<const float4*>(wa + 3 * T + j0);
-          const float4 f1 = *reinterpret_cast<const float4*>(wa + 3 * T + j0 + 4);
-          const float cf[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-          float r = wa[4 * T + i];
-          if (2 * js + 1 == it) {  // lanes g < 2 hold tokens of block 2 js
-            const float rb = __builtin_amdgcn_exp2f(acs2_i[it] - wa[32 * js + 15]);
-            r = c.g < 2 ? rb : r;
-          }
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const float v = cb[q] * cf[q] * r;
-            m[q] = (j0 + q < i) ? v : ((j0 + q == i) ? v + d_h : 0.f);
-          }
-        } else {
-          const float4 a0 = *reinterpret_cast<const float4*>(wa + j0);
-          const float4 a1 = *reinterpret_cast<const float4*>(wa + j0 + 4);
-          const float4 d0 = *reinterpret_cast<const float4*>(wa + T + j0);
-          const float4 d1 = *reinterpret_cast<const float4*>(wa + T + j0 + 4);
-          const float acj[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-          const float dtj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const float v = cb[q] * __builtin_amdgcn_exp2f(fminf(acs2_i[it] - acj[q], 0.f)) * dtj[q];
-            m[q] = (j0 + q < i) ? v : ((j0 + q == i) ? v + d_h : 0.f);
-          }
-        }
-        const f16x8 mf = cvt_f16x8(m);
+        f16x8 mf = *reinterpret_cast<const f16x8*>(mh + mblk(it, 2 * js) + sl.mrd);
+        if (it == 2 * js) mf = c.g >= 2 ? f16x8{} : mf;
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(xh[pt], mf, Y[pt][it]);
       }
