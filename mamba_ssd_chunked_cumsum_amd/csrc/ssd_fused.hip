@@ -481,9 +481,9 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
     const float dv = stage_dt<K>(st + K::RUN_DT, d, c, s * T);
     convert_stage<K, false>(st, c);
     __syncthreads();  // stage visible to all waves; every wave is done with sub-chunk s - 1
-    if (s + 2 < s_end)
-      issue_stage<K, false>(smem + ((cur + 2) % K::NRUN) * K::RUN_STAGE, x, Bm, nullptr, dt, d, c,
-                            dl, (s + 2) * T);
+    // the DMA of sub-chunk s + 2 (into the stage of s - 1), spread over the K steps below
+    const bool more = s + 2 < s_end;
+    constexpr int NRND = (K::RUN_NI + K::NW - 1) / K::NW, RPJ = (NRND + K::NJS - 1) / K::NJS;
     const float acs_end = decay_terms<K>(dv, a_h, wa, c);
     logsum += acs_end;
     const float dec = __expf(acs_end);
@@ -493,6 +493,9 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
       for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] *= dec;
 #pragma unroll
     for (int js = 0; js < K::NJS; ++js) {
+      if (more)
+        issue_stage<K, false>(smem + ((cur + 2) % K::NRUN) * K::RUN_STAGE, x, Bm, nullptr, dt, d,
+                              c, dl, (s + 2) * T, js * RPJ, (js + 1) * RPJ, js == K::NJS - 1);
       const float4 w0 = *reinterpret_cast<const float4*>(wa + 2 * T + 32 * js + 8 * c.g);
       const float4 w1 = *reinterpret_cast<const float4*>(wa + 2 * T + 32 * js + 8 * c.g + 4);
       const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
