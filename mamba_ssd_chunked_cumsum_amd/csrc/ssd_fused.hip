@@ -819,20 +819,22 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     bool fast;
     const float acs_end = decay_terms<K>(dv, a_h, wa, c, &fast);
     __syncthreads();  // A: stage and token arrays visible; every wave is done with sub-chunk s - 1
-    // the next stage's DMA (into the stage every wave is done with), spread over the M blocks
+    // the next stage's DMA (into the stage every wave is done with), spread over the K steps of
+    // the M blocks (slots 0 .. NKN - 1) and of the readout (slots NKN .. 2 NKN - 1)
     const bool more = s + 1 < s_end;
-    constexpr int NRND = (K::SCAN_NI + K::NW - 1) / K::NW, RPK = (NRND + K::NKN - 1) / K::NKN;
-    auto dma = [&](int kn) {
+    constexpr int NSLOT = 2 * K::NKN;
+    constexpr int NRND = (K::SCAN_NI + K::NW - 1) / K::NW, RPS = (NRND + NSLOT - 1) / NSLOT;
+    auto dma = [&](int slot) {
       if (more)
         issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, dt, d, c, dl,
-                             (s + 1) * T, kn * RPK, (kn + 1) * RPK, kn == K::NKN - 1);
+                             (s + 1) * T, slot * RPS, (slot + 1) * RPS, slot == NSLOT - 1);
     };
 
     f32x4 Y[NPT][NIT];
     f16x8 w16[K::NJS];  // state weights of the lane's 8 tokens per K step
     if (!c.active) {
 #pragma unroll
-      for (int kn = 0; kn < K::NKN; ++kn) dma(kn);
+      for (int slot = 0; slot < NSLOT; ++slot) dma(slot);
     } else {
       build_m<K>(Bh, Ch, wa, d_h, fast, mh, sl, c, dma);
 
@@ -843,6 +845,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
         for (int it = 0; it < NIT; ++it) Y[pt][it] = zero4();
 #pragma unroll
       for (int kn = 0; kn < K::NKN; ++kn) {
+        dma(K::NKN + kn);
         f16x8 sa[NPT];
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
