@@ -162,6 +162,26 @@ ssd_status ssd_chunk_scan(const ssd_problem* prob, const void* x, const void* C,
 /* Bytes of each unfused workspace tensor, in the order Acs, dtc, CB, states, h_in. */
 ssd_status ssd_workspace_sizes(const ssd_problem* prob, int64_t chunk_size, int64_t sizes[5]);
 
+/* ---- Single-token recurrent step (decode): continue a sequence from its state. --------------
+ * One step of the selective state-space recurrence ("Why SSM and linear-RNN FLOPs do not convert
+ * into GPU FLOPs: the sequential scan bypasses the tensor cores", first paragraph) with SSD's
+ * scalar decay per head; per token it costs one pass over the fixed-size state ("nitter.gq/
+ * da_be19" thread, post 5/6). For every batch entry b and head h, with g = h / (nheads / ngroups):
+ *     a = exp(dt[b,h] A[h]);  state[b,h,p,n] <- a state[b,h,p,n] + dt[b,h] x[b,h,p] B[b,g,n];
+ *     y[b,h,p] = sum_n state[b,h,p,n] C[b,g,n] + D[h] x[b,h,p]          (the updated state)
+ * This is the recurrence ssd_forward evaluates by chunks: after ssd_forward over tokens 0..L-1
+ * with final_state S, ssd_step from S with token L gives token L's output.
+ * prob->seqlen must be 1. Layouts (row-major): x, y [batch, nheads, headdim] io dtype;
+ * dt [batch, nheads] f32; A, D [nheads] f32; B, C [batch, ngroups, dstate] io dtype;
+ * state_in, state_out [batch, nheads, headdim, dstate] f32. state_out may be state_in (updated
+ * in place); otherwise the two must not overlap. y must not overlap any other argument, nor
+ * state_out any input. headdim and dstate: multiples of 16 up to 256, as for the forward.
+ * Arithmetic is fp32; y is rounded once to the io dtype (nearest even for bf16). Every pointer
+ * 16-byte aligned. Errors as for ssd_forward: all checks on the host before any HIP call. */
+ssd_status ssd_step(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                    const void* B, const void* C, const float* D, const float* state_in,
+                    float* state_out, void* y, void* stream);
+
 /* Static text for a status code. */
 const char* ssd_status_string(ssd_status status);
 

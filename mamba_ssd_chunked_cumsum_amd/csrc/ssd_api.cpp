@@ -347,6 +347,33 @@ ssd_status ssd_chunk_state(const ssd_problem* prob, const void* x, const void* B
                                           static_cast<hipStream_t>(stream)));
 }
 
+ssd_status ssd_step(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                    const void* B, const void* C, const float* D, const float* state_in,
+                    float* state_out, void* y, void* stream) {
+  ssd_status st = check_problem(prob, 16);  // the chunk length plays no part in a step
+  if (st != SSD_OK) return st;
+  if (prob->seqlen != 1) return SSD_ERR_INVALID_ARGUMENT;
+  if (!x || !dt || !A || !B || !C || !D || !state_in || !state_out || !y)
+    return SSD_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x, dt, A, B, C, D, state_in, state_out, y};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return SSD_ERR_INVALID_ARGUMENT;
+  const Sizes s = sizes_of(prob);  // seqlen 1: x and y [batch, nheads, headdim], B/C per group
+  const Range ry = range_of(y, s.x), rso = range_of(state_out, s.state),
+              rsi = range_of(state_in, s.state);
+  const Range inputs[] = {range_of(x, s.x),  range_of(dt, s.dt), range_of(A, s.hd),
+                          range_of(B, s.bc), range_of(C, s.bc),  range_of(D, s.hd)};
+  for (const Range& r : inputs)
+    if (overlap(ry, r) || overlap(rso, r)) return SSD_ERR_INVALID_ARGUMENT;
+  if (overlap(ry, rsi) || overlap(ry, rso)) return SSD_ERR_INVALID_ARGUMENT;
+  if (state_out != state_in && overlap(rso, rsi)) return SSD_ERR_INVALID_ARGUMENT;
+  st = device_ready();
+  if (st != SSD_OK) return st;
+  const Dims d = make_dims(prob, 16);
+  return from_hip(ssd::launch_step(d, prob->io_dtype, x, dt, A, B, C, D, state_in, state_out, y,
+                                   static_cast<hipStream_t>(stream)));
+}
+
 ssd_status ssd_state_passing(const ssd_problem* prob, const float* states, const float* Acs,
                              int64_t chunk_size, const float* initial_state, float* h_in,
                              float* final_state, void* stream) {

@@ -48,4 +48,10 @@ hipError_t launch_fused_scan(const Dims& d, const FusedPlan& fp, const void* x, 
                              const void* C, const float* dt, const float* A, const float* D,
                              const float* h_run, void* y, hipStream_t s);
 
+// single-token step: state [Bt, H, P, N] fp32 (s_out may equal s_in); x, y [Bt, H, P];
+// dt [Bt, H]; B, C [Bt, G, N]
+hipError_t launch_step(const Dims& d, int io, const void* x, const float* dt, const float* A,
+                       const void* B, const void* C, const float* D, const float* s_in,
+                       float* s_out, void* y, hipStream_t s);
+
 }  // namespace ssd

@@ -24,7 +24,7 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 # Symbols include/ssd.h declares.
 EXPORTS = ("ssd_forward", "ssd_forward_ex", "ssd_chunk_cumsum", "ssd_bmm_chunk",
            "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_workspace_sizes",
-           "ssd_status_string", "ssd_version")
+           "ssd_step", "ssd_status_string", "ssd_version")
 
 
 class SSDProblem(ctypes.Structure):
@@ -76,6 +76,7 @@ def load():
         "ssd_state_passing": [P, vp, vp, i64, vp, vp, vp, vp],
         "ssd_chunk_scan": [P, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, O],
         "ssd_workspace_sizes": [P, i64, ctypes.POINTER(ctypes.c_int64)],
+        "ssd_step": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -192,6 +193,38 @@ def forward(x, dt, A, B, C, D, chunk_size, initial_state=None, *, variant="auto"
                                _stream(x), ctypes.byref(opts))
     _check(st, "ssd_forward_ex")
     return y, fin
+
+
+def step(state, x, dt, A, B, C, D, *, out_state=None, out=None):
+    """Single-token recurrent step (decode). state [Bt, H, P, N] f32; x [Bt, H, P]; dt [Bt, H];
+    B, C [Bt, G, N] (x's dtype); A, D [H]. Returns (y [Bt, H, P], new_state); out_state may be
+    `state` itself (updated in place)."""
+    dev = x.device
+    _require(x, "x", device=dev)
+    for n, t in (("B", B), ("C", C)):
+        _require(t, n, x.dtype, dev)
+    for n, t in (("state", state), ("dt", dt), ("A", A), ("D", D)):
+        _require(t, n, torch.float32, dev)
+    if x.dim() != 3 or B.dim() != 3 or x.dtype not in DTYPES:
+        raise ValueError("x must be [batch, nheads, headdim] and B/C [batch, ngroups, dstate], "
+                         "float32 or bfloat16")
+    Bt, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    for n, t, shp in (("B", B, (Bt, G, N)), ("C", C, (Bt, G, N)), ("dt", dt, (Bt, H)),
+                      ("A", A, (H,)), ("D", D, (H,)), ("state", state, (Bt, H, P, N))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {shp}")
+    prob = problem(Bt, 1, H, P, N, G, DTYPES[x.dtype])
+    y = out if out is not None else torch.empty_like(x)
+    _require(y, "out", x.dtype, dev)
+    so = out_state if out_state is not None else torch.empty_like(state)
+    _require(so, "out_state", torch.float32, dev)
+    if tuple(y.shape) != (Bt, H, P) or tuple(so.shape) != (Bt, H, P, N):
+        raise ValueError("out / out_state have the wrong shape")
+    st = load().ssd_step(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                         _ptr(D), _ptr(state), _ptr(so), _ptr(y), _stream(x))
+    _check(st, "ssd_step")
+    return y, so
 
 
 # ---- stages of the unfused path ------------------------------------------------------------------

@@ -217,3 +217,61 @@ def test_workspace_sizes():
                  2 * nc * 4 * 16 * 32 * 4, 2 * nc * 4 * 16 * 32 * 4]
     with pytest.raises(libssd.SSDError):
         libssd.workspace_sizes(p, 24)
+
+
+# ---- ssd_step (single-token decode step) ----------------------------------------------------------
+
+def call_step(prob, ptrs=None):
+    a = [addr(i) for i in range(10)] if ptrs is None else ptrs
+    x, dt, A, B, C, D, s_in, s_out, y = a[:9]
+    lib = libssd.load()
+    return lib.ssd_step(ctypes.byref(prob) if prob is not None else None, x, dt, A, B, C, D,
+                        s_in, s_out, y, None)
+
+
+@no_gpu
+def test_step_valid_request_reports_no_device():
+    assert call_step(good_problem(seqlen=1)) == libssd.SSD_ERR_NO_DEVICE
+
+
+@no_gpu
+def test_step_in_place_state_is_valid():
+    ptrs = [addr(i) for i in range(10)]
+    ptrs[7] = ptrs[6]
+    assert call_step(good_problem(seqlen=1), ptrs=ptrs) == libssd.SSD_ERR_NO_DEVICE
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [(dict(seqlen=2), 1), (dict(seqlen=0), 1),
+                                       (dict(nheads=3), 1), (dict(headdim=24), 2),
+                                       (dict(dstate=512), 2)])
+def test_step_invalid_problem(kw, status):
+    kw.setdefault("seqlen", 1)
+    assert call_step(good_problem(**kw)) == status
+
+
+@no_gpu
+@pytest.mark.parametrize("which", range(9))
+def test_step_null_or_misaligned_pointer(which):
+    ptrs = [addr(i) for i in range(10)]
+    ptrs[which] = None
+    assert call_step(good_problem(seqlen=1), ptrs=ptrs) == libssd.SSD_ERR_INVALID_ARGUMENT
+    ptrs = [addr(i) for i in range(10)]
+    ptrs[which] = addr(which, 4)
+    assert call_step(good_problem(seqlen=1), ptrs=ptrs) == libssd.SSD_ERR_INVALID_ARGUMENT
+
+
+@no_gpu
+@pytest.mark.parametrize("out,alias_of", [(8, i) for i in range(8)] + [(7, i) for i in range(6)])
+def test_step_output_aliasing_rejected(out, alias_of):
+    """y (8) may overlap nothing; state_out (7) no input (x, dt, A, B, C, D)."""
+    ptrs = [addr(i) for i in range(10)]
+    ptrs[out] = addr(alias_of)  # starts where the other buffer starts
+    assert call_step(good_problem(seqlen=1), ptrs=ptrs) == libssd.SSD_ERR_INVALID_ARGUMENT
+
+
+@no_gpu
+def test_step_partial_state_overlap_rejected():
+    ptrs = [addr(i) for i in range(10)]
+    ptrs[7] = addr(6, 16)
+    assert call_step(good_problem(seqlen=1), ptrs=ptrs) == libssd.SSD_ERR_INVALID_ARGUMENT

@@ -85,6 +85,40 @@ def test_step_matches_recurrence():
     assert np.allclose(fs, f, rtol=1e-13, atol=1e-13)
 
 
+def test_step_hand_worked_scalar():
+    """P = N = H = 1: a = exp(0.5 * -2 ln 2) = 1/2; s' = a * 2 + 0.5 * 3 * 4 = 7;
+    y = -1 * 7 + 0.25 * 3 = -6.25."""
+    st = np.array([[[[2.0]]]])
+    y, s = ssd_step(st, np.array([[[3.0]]]), np.array([[0.5]]), np.array([-2.0 * np.log(2.0)]),
+                    np.array([[[4.0]]]), np.array([[[-1.0]]]), np.array([0.25]))
+    assert abs(s[0, 0, 0, 0] - 7.0) < 1e-14 and abs(y[0, 0, 0] + 6.25) < 1e-14
+
+
+def test_step_closed_forms():
+    """dt = 0: the state is unchanged and y = S C + D x. A = 0: S + dt x B^T (no decay). A
+    group's B and C reach exactly its heads."""
+    rng = np.random.default_rng(21)
+    Bt, H, P, N, G = 2, 4, 3, 5, 2
+    S = rng.standard_normal((Bt, H, P, N))
+    x = rng.standard_normal((Bt, H, P))
+    B, C = rng.standard_normal((Bt, G, N)), rng.standard_normal((Bt, G, N))
+    A, D = -rng.uniform(0.5, 2, H), rng.uniform(0.5, 1.5, H)
+    grp = np.arange(H) // (H // G)
+    y, s = ssd_step(S, x, np.zeros((Bt, H)), A, B, C, D)
+    assert np.array_equal(s, S)
+    want = np.einsum("bhpn,bhn->bhp", S, C[:, grp]) + D[None, :, None] * x
+    assert np.allclose(y, want, rtol=1e-14, atol=1e-14)
+    dt = rng.uniform(0.1, 1, (Bt, H))
+    _, s = ssd_step(S, x, dt, np.zeros(H), B, C, D)
+    want = S + dt[:, :, None, None] * x[:, :, :, None] * B[:, grp][:, :, None, :]
+    assert np.allclose(s, want, rtol=1e-14, atol=1e-14)
+    B2 = B.copy()
+    B2[:, 1] = 0.0  # group 1 (heads 2, 3) gets no input term: pure decay
+    _, s = ssd_step(S, x, dt, A, B2, C, D)
+    assert np.allclose(s[:, 2:], np.exp(dt[:, 2:] * A[2:])[:, :, None, None] * S[:, 2:],
+                       rtol=1e-14, atol=1e-14)
+
+
 def test_linearity_and_causality():
     """With h0 = 0, y - D x is linear in x; perturbing x at t0 leaves y[:t0] unchanged."""
     rng = np.random.default_rng(9)
