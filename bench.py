@@ -62,10 +62,15 @@ def algorithmic(shape, with_initial_state: bool):
     }
 
 
+# Sources that define, plan or launch the fused forward's kernels (the traffic counters describe
+# these; the unfused kernels and the decode step do not change them).
+FUSED_SOURCES = ("ssd_api.cpp", "ssd_device.h", "ssd_fused.hip", "ssd_launch.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mamba_ssd_chunked_cumsum_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in FUSED_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -222,6 +227,60 @@ def summarize_profiles(d: str) -> None:
     with open(os.path.join(ROOT, "profiles", f"traffic_{dom}_{workload}.json"), "w") as f:
         json.dump(rec, f, indent=1)
     print("\n".join(lines))
+
+
+def decode_bench(shape, dev, layers: int = 64, rounds: int = 5) -> dict:
+    """ssd_step at the workload's layer shape (one token per sequence) over `layers` distinct
+    states, one in-place step per state per round, as a decode pass through a stack of layers
+    does: 64 states of the 2.7B-shaped layer are 335 MB, more than the 256 MB Infinity Cache, so
+    each step reads and writes its state in HBM. Returns per-step time and bandwidth."""
+    import torch
+
+    from mamba_ssd_chunked_cumsum_amd import libssd
+
+    Bt, H, P, N, G = shape.batch, shape.nheads, shape.headdim, shape.dstate, shape.ngroups
+    io = torch.bfloat16 if shape.io == "bf16" else torch.float32
+    g = torch.Generator(device=dev).manual_seed(7)
+    states = torch.randn((layers, Bt, H, P, N), device=dev, generator=g)
+    x = torch.randn((Bt, H, P), device=dev, generator=g).to(io)
+    Bm = torch.randn((Bt, G, N), device=dev, generator=g).to(io)
+    Cm = torch.randn((Bt, G, N), device=dev, generator=g).to(io)
+    dt = torch.rand((Bt, H), device=dev, generator=g) * 0.1
+    A = -1.0 - 15.0 * torch.rand((H,), device=dev, generator=g)
+    D = torch.ones((H,), device=dev)
+    y = torch.empty_like(x)
+
+    def one_round():
+        for k in range(layers):
+            libssd.step(states[k], x, dt, A, Bm, Cm, D, out_state=states[k], out=y)
+
+    # one round captured as a HIP graph and replayed: the launches then cost no host time (the
+    # step launches nothing but its kernel, so it captures as is)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_round()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_round()
+    graph.replay()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(rounds):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / (rounds * layers)
+    e = 2 if shape.io == "bf16" else 4
+    nbytes = (2 * Bt * H * P * N * 4 + 2 * Bt * H * P * e + 2 * Bt * G * N * e + Bt * H * 4
+              + 2 * H * 4)
+    return {"layers": layers, "us_per_step": us, "bytes_per_step": nbytes,
+            "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
+            "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "note": "ssd_step, one token per sequence, in-place state, rounds of steps replayed "
+                    "from a HIP graph"}
 
 
 def main():
@@ -381,6 +440,7 @@ def main():
         "wall_s_timed_loop": wall,
         "cpu_baseline": cpu,
         "parity": parity,
+        "decode_step": decode_bench(shape, dev),
     }
     print(json.dumps(out), flush=True)
 

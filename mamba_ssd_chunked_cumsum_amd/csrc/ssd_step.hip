@@ -11,8 +11,10 @@
 //
 // Layout: lanes run along n, four consecutive n per lane (16-byte loads and stores), LPR lanes per
 // state row (N / 4 rounded up to a power of two, so that the row sum C . S is a butterfly over
-// xor-shuffles); a wave covers 64 / LPR rows per pass and a block of four waves covers RB rows of
-// one head in two passes. B and C of the head's group are loaded once per lane.
+// xor-shuffles); a wave covers 64 / LPR rows and a block of four waves RB rows of one head. Every
+// load of a thread is issued before its first store, and the state is read and written with
+// nontemporal accesses (it is touched once per step): at the 2.7B-shaped layer (10.5 MB moved per
+// step) the step runs at ~88% of a device copy of the same bytes.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -23,26 +25,42 @@ namespace {
 __device__ __forceinline__ float ld_io(const float* p) { return *p; }
 __device__ __forceinline__ float ld_io(const u16* p) { return bf16_to_f32(*p); }
 
-// four consecutive io values -> floats
-__device__ __forceinline__ void ld4_io(const float* p, float (&v)[4]) {
-  const float4 q = *reinterpret_cast<const float4*>(p);
-  v[0] = q.x;
-  v[1] = q.y;
-  v[2] = q.z;
-  v[3] = q.w;
-}
-__device__ __forceinline__ void ld4_io(const u16* p, float (&v)[4]) {
-  const uint2 q = *reinterpret_cast<const uint2*>(p);
-  v[0] = __uint_as_float(q.x << 16);
-  v[1] = __uint_as_float(q.x & 0xffff0000u);
-  v[2] = __uint_as_float(q.y << 16);
-  v[3] = __uint_as_float(q.y & 0xffff0000u);
-}
+// Four consecutive io values, kept as loaded (16 or 8 bytes) until converted.
+template <typename IO>
+struct Raw4;
+template <>
+struct Raw4<float> {
+  float4 v;
+  static __device__ __forceinline__ Raw4 load(const float* p) {
+    return Raw4{*reinterpret_cast<const float4*>(p)};
+  }
+  __device__ __forceinline__ void get(float (&o)[4]) const {
+    o[0] = v.x;
+    o[1] = v.y;
+    o[2] = v.z;
+    o[3] = v.w;
+  }
+};
+template <>
+struct Raw4<u16> {
+  uint2 v;
+  static __device__ __forceinline__ Raw4 load(const u16* p) {
+    return Raw4{*reinterpret_cast<const uint2*>(p)};
+  }
+  __device__ __forceinline__ void get(float (&o)[4]) const {
+    o[0] = __uint_as_float(v.x << 16);
+    o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16);
+    o[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+};
 
 __device__ __forceinline__ void st_io(float* p, float v) { *p = v; }
 __device__ __forceinline__ void st_io(u16* p, float v) { *p = f32_to_bf16(v); }
 
-constexpr int kStepWaves = 4, kStepPasses = 2;
+// one pass (16 rows per block at N = 128): more, smaller blocks measured faster than two or more
+// rows per thread
+constexpr int kStepWaves = 4, kStepPasses = 1;
 
 template <typename IO, int LPR>
 __global__ __launch_bounds__(64 * kStepWaves) void k_step(
@@ -57,27 +75,45 @@ __global__ __launch_bounds__(64 * kStepWaves) void k_step(
   const int q = lane % LPR, n0 = 4 * q;
   const bool nv = n0 < d.N;  // lanes past the row end (N / 4 not a power of two) idle
   const float dtv = dt[bh], a = __expf(dtv * A[h]), dh = D[h];
-  float bv[4] = {0.f, 0.f, 0.f, 0.f}, cv[4] = {0.f, 0.f, 0.f, 0.f};
-  if (nv) {
-    ld4_io(B + ((int64_t)b * d.G + g) * d.N + n0, bv);
-    ld4_io(C + ((int64_t)b * d.G + g) * d.N + n0, cv);
-  }
+  // every load of the thread first (branch-free, on clamped addresses), then the stores:
+  // state_out may be state_in, and each element is read and written by the same lane, so reading
+  // all of them before any write keeps an in-place update correct, and all loads are in flight
+  // together
+  const int nc = nv ? n0 : d.N - 4;
+  const int64_t bg = ((int64_t)b * d.G + g) * d.N + nc;
+  const Raw4<IO> braw = Raw4<IO>::load(B + bg), craw = Raw4<IO>::load(C + bg);
+  float4 sv[kStepPasses];
+  IO xr[kStepPasses];
+  int pr[kStepPasses];
 #pragma unroll
   for (int pass = 0; pass < kStepPasses; ++pass) {
-    const int p = rb * RB + (pass * kStepWaves + wave) * RPW + lane / LPR;
+    pr[pass] = rb * RB + (pass * kStepWaves + wave) * RPW + lane / LPR;
+    const int pc = min(pr[pass], d.P - 1);
+    xr[pass] = x[(int64_t)bh * d.P + pc];
+    {  // streamed once per step: nontemporal (no cache allocation for the state)
+      const f32x4 v = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(s_in + ((int64_t)bh * d.P + pc) * d.N + nc));
+      sv[pass] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+  float bv[4], cv[4];
+  braw.get(bv);
+  craw.get(cv);
+#pragma unroll
+  for (int pass = 0; pass < kStepPasses; ++pass) {
+    const int p = pr[pass];
     const bool pv = p < d.P;
-    float part = 0.f, xp = 0.f;
-    if (pv) {
-      xp = ld_io(x + (int64_t)bh * d.P + p);
-      if (nv) {
-        const int64_t o = ((int64_t)bh * d.P + p) * d.N + n0;
-        const float4 s = *reinterpret_cast<const float4*>(s_in + o);
-        const float u = dtv * xp;
-        const float4 t = make_float4(a * s.x + u * bv[0], a * s.y + u * bv[1],
-                                     a * s.z + u * bv[2], a * s.w + u * bv[3]);
-        *reinterpret_cast<float4*>(s_out + o) = t;
-        part = t.x * cv[0] + t.y * cv[1] + t.z * cv[2] + t.w * cv[3];
-      }
+    const float xp = ld_io(&xr[pass]);
+    float part = 0.f;
+    if (pv && nv) {
+      const float4 s = sv[pass];
+      const float u = dtv * xp;
+      const float4 t = make_float4(a * s.x + u * bv[0], a * s.y + u * bv[1], a * s.z + u * bv[2],
+                                   a * s.w + u * bv[3]);
+      __builtin_nontemporal_store(f32x4{t.x, t.y, t.z, t.w},
+                                  reinterpret_cast<f32x4*>(s_out + ((int64_t)bh * d.P + p) * d.N +
+                                                           n0));
+      part = t.x * cv[0] + t.y * cv[1] + t.z * cv[2] + t.w * cv[3];
     }
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
