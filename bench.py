@@ -139,7 +139,7 @@ PROFILE_COMMANDS = [
 
 def _short_kernel(name: str):
     import re
-    m = re.search(r"ssd::k_(\w+)", name)
+    m = re.search(r"ssd::(?:\(anonymous namespace\)::)?k_(\w+)", name)
     if m:
         return m.group(1)
     if "copyBuffer" in name:
