@@ -290,6 +290,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload index (0..4)")
     ap.add_argument("--variant", default="auto", choices=["auto", "fused", "unfused"])
+    ap.add_argument("--precision", default="auto", choices=["auto", "fp16", "fp32"],
+                    help="operand precision (auto: fp16 operands, run states split hi + lo)")
     ap.add_argument("--run-chunks", type=int, default=0)
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the cache sweep before steps (inputs may then be served from the "
@@ -338,8 +340,8 @@ def main():
 
     def step(timer=None):
         ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], shape.chunk_size,
-                    d["initial_state"], variant=args.variant, run_chunks=args.run_chunks,
-                    out=y, final_out=fin, timer=timer)
+                    d["initial_state"], variant=args.variant, precision=args.precision,
+                    run_chunks=args.run_chunks, out=y, final_out=fin, timer=timer)
 
     # correctness run first, then the CPU oracle leg on the same inputs
     step()
@@ -422,7 +424,8 @@ def main():
             "workload": shape.name, "batch": shape.batch, "seqlen": shape.seqlen,
             "nheads": shape.nheads, "headdim": shape.headdim, "dstate": shape.dstate,
             "ngroups": shape.ngroups, "chunk_size": shape.chunk_size,
-            "variant": args.variant, "cache_flush": flush is not None,
+            "variant": args.variant, "precision": args.precision,
+            "cache_flush": flush is not None,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -264,14 +264,17 @@ ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* d
   const int prec = resolve_precision(prob->io_dtype, opts ? opts->precision : 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int variant = opts ? opts->variant : SSD_VARIANT_AUTO;
-  // The fused kernels cover bf16 io with fp16 operands (chained run states split hi + lo) for
-  // headdim 64 or 128 and dstate 64, 128 or 256.
+  // The fused kernels cover bf16 io with fp16 operands for headdim 64 or 128 and dstate 64,
+  // 128 or 256.
   ssd::FusedPlan fp{};
   const int64_t run_tokens = opts && opts->run_chunks > 0 ? (int64_t)opts->run_chunks * chunk_size : 0;
   const bool fusable = prob->io_dtype == SSD_DTYPE_BF16 && prec != ssd::kPrecFp32 &&
                        ssd::fused_plan(d, (int)(run_tokens < (1 << 30) ? run_tokens : (1 << 30)),
                                        compute_units(), &fp);
   if (variant == SSD_VARIANT_FUSED && !fusable) return SSD_ERR_UNSUPPORTED;
+  // auto: the run states chained over the sequence keep near-fp32 accuracy (hi + lo); fp16:
+  // every operand rounded once
+  fp.split = prec != ssd::kPrecFp16;
   Timer t;
   if (opts && opts->n_events > 0) {
     t.ev = opts->events;

@@ -429,7 +429,7 @@ __device__ __forceinline__ f16x8 b_frag(const char* Bh, int js, int col0, int la
 // state_r = sum_{t in run} exp(sum_{k in (t, end]} dt_k A) dt_t x_t B_t^T (zero entry state) and
 // logdecay_r = sum_{t in run} dt_t A. Walked forwards: per sub-chunk, S <- exp(acs_end) S +
 // B^T (w x), the weighted x split into fp16 high and low parts.
-template <class K>
+template <class K, bool SPLIT>
 __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ x,
                                                       const u16* __restrict__ Bm,
                                                       const float* __restrict__ dt,
@@ -507,9 +507,11 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= wj[e];
         xhi[pt] = cvt_f16x8(v);
+        if constexpr (SPLIT) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lo[e] = v[e] - (float)xhi[pt][e];
-        xlo[pt] = cvt_f16x8(lo);
+          for (int e = 0; e < 8; ++e) lo[e] = v[e] - (float)xhi[pt][e];
+          xlo[pt] = cvt_f16x8(lo);
+        }
       }
 #ifndef SSD_F1_NO_HOIST
       // all B^T fragments of the K step first (their LDS latency overlaps), then the high parts
@@ -521,10 +523,12 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
       for (int nt = 0; nt < K::NNT; ++nt)
 #pragma unroll
         for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] = M::mma(bts[nt], xhi[pt], S[nt][pt]);
+      if constexpr (SPLIT) {
 #pragma unroll
-      for (int nt = 0; nt < K::NNT; ++nt)
+        for (int nt = 0; nt < K::NNT; ++nt)
 #pragma unroll
-        for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] = M::mma(bts[nt], xlo[pt], S[nt][pt]);
+          for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] = M::mma(bts[nt], xlo[pt], S[nt][pt]);
+      }
 #else
 #pragma unroll
       for (int nt = 0; nt < K::NNT; ++nt) {
@@ -532,7 +536,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
 #pragma unroll
         for (int pt = 0; pt < K::NPT; ++pt) {
           S[nt][pt] = M::mma(bt, xhi[pt], S[nt][pt]);
-          S[nt][pt] = M::mma(bt, xlo[pt], S[nt][pt]);
+          if constexpr (SPLIT) S[nt][pt] = M::mma(bt, xlo[pt], S[nt][pt]);
         }
       }
 #endif
@@ -998,10 +1002,14 @@ static hipError_t launch_k(int phase, const Dims& d, const FusedPlan& fp, const 
                            const float* D, float* states, float* logdecay, const float* h_run,
                            void* y, hipStream_t s) {
   static_assert(64 % K1::T == 0 && 64 % K3::T == 0, "runs are whole sub-chunks of both kernels");
-  if (phase == 0)
-    hipLaunchKernelGGL(k_run_state<K1>, dim3(fp.nr, head_blocks<K1>(d), d.Bt), dim3(K1::NT), 0,
-                       s, (const u16*)x, (const u16*)B, dt, A, states, logdecay, d, fp.run_len,
-                       fp.nr);
+  if (phase == 0 && fp.split)
+    hipLaunchKernelGGL((k_run_state<K1, true>), dim3(fp.nr, head_blocks<K1>(d), d.Bt),
+                       dim3(K1::NT), 0, s, (const u16*)x, (const u16*)B, dt, A, states, logdecay,
+                       d, fp.run_len, fp.nr);
+  else if (phase == 0)
+    hipLaunchKernelGGL((k_run_state<K1, false>), dim3(fp.nr, head_blocks<K1>(d), d.Bt),
+                       dim3(K1::NT), 0, s, (const u16*)x, (const u16*)B, dt, A, states, logdecay,
+                       d, fp.run_len, fp.nr);
   else
     hipLaunchKernelGGL(k_fused_scan<K3>, dim3(fp.nr, head_blocks<K3>(d), d.Bt), dim3(K3::NT), 0,
                        s, (const u16*)x, (const u16*)B, (const u16*)C, dt, A, D, h_run, (u16*)y,

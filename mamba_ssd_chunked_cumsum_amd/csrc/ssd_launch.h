@@ -33,8 +33,10 @@ hipError_t launch_chunk_scan(const Dims& d, int io, int prec, const void* x, con
 // fused path (bf16 io)
 // Run plan of one fused forward: runs of run_len tokens (a multiple of 64), nr runs per sequence,
 // head_blocks fused-scan blocks per (batch, run).
+// split: F1 feeds the weighted x to the matrix cores as fp16 high + low parts (else high only).
 struct FusedPlan {
   int run_len, nr, head_blocks;
+  bool split = true;
 };
 // False when the fused kernels do not cover (P, N). run_tokens > 0 asks for runs of at least that
 // many tokens; 0 lets the plan aim at about one block per compute unit (n_cu of them).
