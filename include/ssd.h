@@ -106,6 +106,14 @@ typedef struct {
     int32_t* n_kernels; /* optional out: number of kernels the call launched (fused 3: run
                            states, state passing over runs, fused scan; unfused 5: cumsum,
                            C B^T, chunk states, state passing, chunk scan) */
+    /* dt pre-processing, applied by the kernels where they read dt (no separate pass), in this
+     * order: dt + dt_bias[h]; softplus, log(1 + exp(v)) (v itself above 20, where the two agree
+     * to fp32 precision); clamp to [dt_min, dt_max]. The recurrence then runs on that dt. With
+     * every field zero (or opts NULL) dt is used as given. */
+    const float* dt_bias; /* optional [nheads] f32, 16-byte aligned; NULL = no bias */
+    int32_t dt_softplus;  /* nonzero: apply softplus */
+    float dt_min, dt_max; /* dt_max > 0: clamp to [dt_min, dt_max] (needs dt_min <= dt_max);
+                             dt_max == 0: no clamp; dt_max < 0 is invalid */
 } ssd_options;
 
 /* Full forward. initial_state may be NULL (zeros); final_state may be NULL (not written).

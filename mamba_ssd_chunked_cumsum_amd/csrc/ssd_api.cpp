@@ -13,7 +13,7 @@ namespace {
 
 using ssd::Dims;
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
 
 struct Range {
@@ -97,6 +97,10 @@ ssd_status check_options(const ssd_options* o) {
   if (o->run_chunks < 0) return SSD_ERR_INVALID_ARGUMENT;
   if (o->n_events < 0 || (o->n_events > 0 && !o->events)) return SSD_ERR_INVALID_ARGUMENT;
   if (o->n_events > 0 && o->n_events < 6) return SSD_ERR_INVALID_ARGUMENT;
+  if (o->dt_bias && !aligned16(o->dt_bias)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!(o->dt_max >= 0.f) || !(o->dt_min == o->dt_min) ||
+      (o->dt_max > 0.f && !(o->dt_min <= o->dt_max)))  // also rejects NaN
+    return SSD_ERR_INVALID_ARGUMENT;
   return SSD_OK;
 }
 
@@ -258,9 +262,22 @@ ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* d
   if (st != SSD_OK) return st;
   st = check_options(opts);
   if (st != SSD_OK) return st;
+  if (opts && opts->dt_bias) {  // an input too: no output may overlap it
+    const Sizes sz = sizes_of(prob);
+    const Range rb = range_of(opts->dt_bias, sz.hd);
+    if (overlap(rb, range_of(y, sz.x)) ||
+        (final_state && overlap(rb, range_of(final_state, sz.state))))
+      return SSD_ERR_INVALID_ARGUMENT;
+  }
   st = device_ready();
   if (st != SSD_OK) return st;
-  const Dims d = make_dims(prob, chunk_size);
+  Dims d = make_dims(prob, chunk_size);
+  if (opts) {
+    d.dt_bias = opts->dt_bias;
+    d.dt_softplus = opts->dt_softplus;
+    d.dt_min = opts->dt_min;
+    d.dt_max = opts->dt_max;
+  }
   const int prec = resolve_precision(prob->io_dtype, opts ? opts->precision : 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int variant = opts ? opts->variant : SSD_VARIANT_AUTO;

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssd_launch.h"
+
 namespace ssd {
 
 typedef _Float16 f16;
@@ -22,6 +24,18 @@ __device__ __forceinline__ u16 f32_to_bf16(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (u16)(u >> 16);
+}
+
+// The effective dt of head h from the dt the caller passed (see Dims): + bias, softplus
+// (log(1 + exp(v)); v itself above 20, where the two agree to fp32 precision), clamp.
+__device__ __forceinline__ float dt_effective(float v, float bias, const Dims& d) {
+  v += bias;
+  if (d.dt_softplus) v = v <= 20.f ? log1pf(expf(v)) : v;
+  if (d.dt_max > 0.f) v = fminf(fmaxf(v, d.dt_min), d.dt_max);
+  return v;
+}
+__device__ __forceinline__ float dt_bias_of(const Dims& d, int h) {
+  return d.dt_bias ? d.dt_bias[h] : 0.f;
 }
 
 // IO element access: fp32 io stores float, bf16 io stores raw bf16 bits.

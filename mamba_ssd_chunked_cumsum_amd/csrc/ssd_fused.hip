@@ -353,12 +353,13 @@ __device__ __forceinline__ void convert_stage(char* st, const Coord& c) {
   }
 }
 
-// dt of this wave's head for the tokens of a staged sub-chunk (lane l: token tok0 + l), 0 past the
-// sequence end; dts is the stage's dt region (this wave's own DMA: readable after its own wait).
+// Effective dt of this wave's head for the tokens of a staged sub-chunk (lane l: token tok0 + l),
+// 0 past the sequence end; dts is the stage's dt region (this wave's own DMA: readable after its
+// own wait), dtb the head's dt bias.
 template <class K>
-__device__ __forceinline__ float stage_dt(const char* dts, const Dims& d, const Coord& c,
-                                          int tok0) {
-  const float v = reinterpret_cast<const float*>(dts + c.wave * 256)[c.lane];
+__device__ __forceinline__ float stage_dt(const char* dts, const Dims& d, const Coord& c, int tok0,
+                                          float dtb) {
+  const float v = dt_effective(reinterpret_cast<const float*>(dts + c.wave * 256)[c.lane], dtb, d);
   return (c.lane < K::T && tok0 + c.lane < d.L && c.active) ? v : 0.f;
 }
 
@@ -450,7 +451,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
   if (s_begin >= s_end) return;
   float* wa = reinterpret_cast<float*>(smem + K::NRUN * K::RUN_STAGE) + c.wave * K::NWA * T;
   const int xoff = K::BC_BYTES + (c.wave / K::WPH) * (T * K::ROW_P);
-  const float a_h = Av[c.h];
+  const float a_h = Av[c.h], dtb = dt_bias_of(d, c.h);
 
   f32x4 S[K::NNT][K::NPT];
 #pragma unroll
@@ -478,7 +479,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
       wait_vm_but<NLO + 1>();
     else
       wait_vm_but<NLO>();
-    const float dv = stage_dt<K>(st + K::RUN_DT, d, c, s * T);
+    const float dv = stage_dt<K>(st + K::RUN_DT, d, c, s * T, dtb);
     convert_stage<K, false>(st, c);
     __syncthreads();  // stage visible to all waves; every wave is done with sub-chunk s - 1
     // the DMA of sub-chunk s + 2 (into the stage of s - 1), spread over the K steps below
@@ -784,7 +785,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
       reinterpret_cast<float*>(smem + K::NSCAN * K::SCAN_STAGE + K::HPB * K::MT_HEAD) +
       hb * K::NWA * T;
   const int xoff = 2 * K::BC_BYTES + hb * (T * K::ROW_P);
-  const float a_h = Av[c.h], d_h = Dv[c.h];
+  const float a_h = Av[c.h], d_h = Dv[c.h], dtb = dt_bias_of(d, c.h);
 
   // carried state S^T tiles (rows n, columns p): lane holds p = p0 + 16 pt + c16,
   // n = 16 nt + 4 g + 0..3
@@ -817,7 +818,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     const char* xt = st + xoff;
     wait_vm_all();  // this stage's DMA and the y stores of the previous round
     if (ytok >= 0) store_y<K>(smem + (cur ^ 1) * K::SCAN_STAGE + xoff, y, d, c, ytok);
-    const float dv = stage_dt<K>(st + K::SCAN_DT, d, c, s * T);
+    const float dv = stage_dt<K>(st + K::SCAN_DT, d, c, s * T, dtb);
     convert_stage<K, true>(st, c);
     // the head's decay bookkeeping needs only its dt: done while other waves finish converting
     bool fast;

@@ -9,6 +9,11 @@ namespace ssd {
 
 struct Dims {
   int Bt, L, H, P, N, G, Q, nc;
+  // dt pre-processing where the kernels read dt: dt + dt_bias[h] (no bias when null), then
+  // softplus when dt_softplus != 0, then clamped to [dt_min, dt_max] when dt_max > 0
+  const float* dt_bias = nullptr;
+  int dt_softplus = 0;
+  float dt_min = 0.f, dt_max = 0.f;
 };
 
 constexpr int kIoF32 = 0, kIoBf16 = 1;

@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const float* __restrict__ 
   for (int e = threadIdx.x; e < d.Q * 16; e += 256) {
     const int i = e >> 4, hh = e & 15, h = h0 + hh;
     float v = 0.f;
-    if (i < q && h < d.H) v = dt[((int64_t)b * d.L + t0 + i) * d.H + h];
+    if (i < q && h < d.H)
+      v = dt_effective(dt[((int64_t)b * d.L + t0 + i) * d.H + h], dt_bias_of(d, h), d);
     tile[i][hh] = v;
   }
   __syncthreads();

@@ -38,7 +38,9 @@ class SSDOptions(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("precision", ctypes.c_int32),
                 ("run_chunks", ctypes.c_int32), ("n_events", ctypes.c_int32),
                 ("events", ctypes.POINTER(ctypes.c_void_p)),
-                ("n_kernels", ctypes.POINTER(ctypes.c_int32))]
+                ("n_kernels", ctypes.POINTER(ctypes.c_int32)),
+                ("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
 
 
 # kernel names, in launch order, for each number of kernels a call reports
@@ -137,8 +139,10 @@ def _require(t, name, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _options(variant, precision, run_chunks=0):
-    return SSDOptions(VARIANTS[variant], PRECISIONS[precision], int(run_chunks), 0, None, None)
+def _options(variant, precision, run_chunks=0, dt_bias=None, dt_softplus=False, dt_limit=None):
+    lo, hi = (0.0, 0.0) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
+    return SSDOptions(VARIANTS[variant], PRECISIONS[precision], int(run_chunks), 0, None, None,
+                      _ptr(dt_bias), 1 if dt_softplus else 0, lo, hi)
 
 
 class KernelTimer:
@@ -169,14 +173,20 @@ class KernelTimer:
 
 def forward(x, dt, A, B, C, D, chunk_size, initial_state=None, *, variant="auto",
             precision="auto", run_chunks=0, want_final=True, out=None, final_out=None,
-            timer: KernelTimer | None = None):
-    """SSD chunked forward. Returns (y, final_state) (final_state None if not wanted)."""
+            timer: KernelTimer | None = None, dt_bias=None, dt_softplus=False, dt_limit=None):
+    """SSD chunked forward. Returns (y, final_state) (final_state None if not wanted).
+
+    dt_bias [H], dt_softplus and dt_limit=(lo, hi) pre-process dt inside the kernels:
+    dt + dt_bias, softplus, clamp to [lo, hi] (hi > 0), in that order."""
     dev = x.device
     _require(x, "x", device=dev)
     for n, t in (("B", B), ("C", C)):
         _require(t, n, x.dtype, dev)
-    for n, t in (("dt", dt), ("A", A), ("D", D), ("initial_state", initial_state)):
+    for n, t in (("dt", dt), ("A", A), ("D", D), ("initial_state", initial_state),
+                 ("dt_bias", dt_bias)):
         _require(t, n, torch.float32, dev)
+    if dt_bias is not None and tuple(dt_bias.shape) != (x.shape[2],):
+        raise ValueError(f"dt_bias must have shape ({x.shape[2]},)")
     prob = _problem_from(x, B)
     y = out if out is not None else torch.empty_like(x)
     _require(y, "out", x.dtype, dev)
@@ -185,7 +195,7 @@ def forward(x, dt, A, B, C, D, chunk_size, initial_state=None, *, variant="auto"
         fin = final_out if final_out is not None else torch.empty(
             (x.shape[0], x.shape[2], x.shape[3], B.shape[3]), dtype=torch.float32, device=dev)
         _require(fin, "final_out", torch.float32, dev)
-    opts = _options(variant, precision, run_chunks)
+    opts = _options(variant, precision, run_chunks, dt_bias, dt_softplus, dt_limit)
     if timer is not None:
         timer.attach(opts)
     st = load().ssd_forward_ex(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),

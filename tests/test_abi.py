@@ -37,7 +37,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert libssd.version() == 10000
+    assert libssd.version() == 10100
     assert libssd.status_string(0) == "ok"
     assert libssd.status_string(3) == "no HIP device"
     assert libssd.status_string(99) == "unknown status"
@@ -45,7 +45,7 @@ def test_version_and_status_strings():
 
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(libssd.SSDProblem) == 6 * 8 + 2 * 4
-    assert ctypes.sizeof(libssd.SSDOptions) == 32
+    assert ctypes.sizeof(libssd.SSDOptions) == 56
 
 
 # placeholder device addresses: 16-byte aligned, far apart, never dereferenced
@@ -275,3 +275,30 @@ def test_step_partial_state_overlap_rejected():
     ptrs = [addr(i) for i in range(10)]
     ptrs[7] = addr(6, 16)
     assert call_step(good_problem(seqlen=1), ptrs=ptrs) == libssd.SSD_ERR_INVALID_ARGUMENT
+
+
+# ---- dt pre-processing options -------------------------------------------------------------------
+
+def dt_opts(**kw):
+    o = libssd._options("auto", "auto")
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt_softplus=1), 3), (dict(dt_min=0.1, dt_max=2.0), 3), (dict(dt_max=0.0, dt_min=5.0), 3),
+    (dict(dt_bias=BASE + 20 * SPAN), 3),
+    (dict(dt_max=-1.0), 1), (dict(dt_min=3.0, dt_max=2.0), 1), (dict(dt_max=float("nan")), 1),
+    (dict(dt_min=float("nan"), dt_max=1.0), 1), (dict(dt_bias=BASE + 20 * SPAN + 4), 1),
+])
+def test_dt_options_checked(kw, status):
+    assert call_forward(good_problem(), opts=dt_opts(**kw)) == status
+
+
+@no_gpu
+def test_dt_bias_may_not_overlap_outputs():
+    ptrs = [addr(i) for i in range(9)]
+    assert call_forward(good_problem(), ptrs=ptrs, opts=dt_opts(dt_bias=ptrs[7].value)) == 1
+    assert call_forward(good_problem(), ptrs=ptrs, opts=dt_opts(dt_bias=ptrs[8].value)) == 1

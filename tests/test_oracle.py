@@ -7,7 +7,7 @@ decomposition at several chunk sizes, the C/OpenMP recurrence) must pass every p
 import numpy as np
 import pytest
 
-from oracle import native, ssd_chunked, ssd_quadratic, ssd_recurrence, ssd_step
+from oracle import dt_effective, native, ssd_chunked, ssd_quadratic, ssd_recurrence, ssd_step
 from mamba_ssd_chunked_cumsum_amd import synth
 
 from pins import all_pins, rand_inputs
@@ -182,3 +182,22 @@ def test_native_unit_subset():
     assert np.isnan(ys[0, :, 0]).all()
     with pytest.raises(ValueError):
         native.forward(**inp, units=[6])
+
+
+def test_dt_effective_closed_forms():
+    """softplus(0) = ln 2; softplus(v) -> v for large v and -> exp(v) for very negative v; the bias
+    is added per head before softplus; the clamp bounds the result; nothing set = identity."""
+    dt = np.array([[[0.0, -30.0, 50.0, 0.5]]])
+    assert np.array_equal(dt_effective(dt), dt)
+    v = dt_effective(dt, softplus=True)
+    assert abs(v[0, 0, 0] - np.log(2.0)) < 1e-15
+    assert abs(v[0, 0, 1] / np.exp(-30.0) - 1.0) < 1e-12
+    assert abs(v[0, 0, 2] - 50.0) < 1e-15
+    assert abs(v[0, 0, 3] - np.log1p(np.exp(0.5))) < 1e-15
+    bias = np.array([1.0, 2.0, -3.0, 0.0])
+    assert np.allclose(dt_effective(dt, bias), dt + bias, rtol=0, atol=0)
+    w = dt_effective(dt, bias, softplus=True)
+    assert abs(w[0, 0, 0] - np.log1p(np.e)) < 1e-15   # softplus(0 + 1)
+    c = dt_effective(dt, bias, softplus=True, dt_min=0.1, dt_max=1.0)
+    assert c.min() >= 0.1 and c.max() <= 1.0
+    assert c[0, 0, 2] == 1.0 and abs(c[0, 0, 3] - np.log1p(np.exp(0.5))) < 1e-15

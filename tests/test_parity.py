@@ -10,10 +10,11 @@ import numpy as np
 import pytest
 import torch
 
+import mamba_ssd_chunked_cumsum_amd as ssd
 from mamba_ssd_chunked_cumsum_amd import synth
 from oracle import metrics, native
 
-from gpu_util import as64, check_shape, note, run_gpu, score, to_device
+from gpu_util import DEV, as64, check_shape, note, run_gpu, score, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -218,3 +219,35 @@ def test_group_replication(variant):
     d["C"] = d["C"].repeat(1, 1, 4, 1).contiguous()
     y2, f2 = run_gpu(d, 64, variant)
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+DT_SHAPES = [
+    synth.SSDShape("dt_p64n128_ragged", 2, 700, 4, 64, 128, 1, 64, init_state=True),
+    synth.SSDShape("dt_f32", 1, 300, 3, 32, 32, 1, 64, io="f32"),
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("clamp", [False, True])
+@pytest.mark.parametrize("shape", DT_SHAPES, ids=[s.name for s in DT_SHAPES])
+def test_dt_preprocessing(shape, clamp, variant):
+    """dt passed raw, with a per-head bias, softplus and (optionally) a clamp applied inside the
+    kernels, against the oracle run on the effective dt."""
+    from oracle import dt_effective
+    skip_unfusable(shape, variant)
+    inp = synth.make_inputs(shape, seed=41)
+    rng = np.random.default_rng(42)
+    raw = rng.normal(-2.5, 1.0, inp["dt"].shape).astype(np.float32)
+    bias = rng.uniform(-1.0, 1.0, shape.nheads).astype(np.float32)
+    lim = (0.02, 0.2) if clamp else None
+    eff = dt_effective(raw, bias, True, *(lim or (0.0, 0.0)))
+    note(f"{shape} dt pre-processing clamp={clamp} variant={variant}")
+    dinp = to_device(inp, shape.io)
+    y, f = ssd.forward(dinp["x"], torch.from_numpy(raw).to(DEV), dinp["A"], dinp["B"], dinp["C"],
+                       dinp["D"], shape.chunk_size, dinp["initial_state"], variant=variant,
+                       dt_bias=torch.from_numpy(bias).to(DEV), dt_softplus=True, dt_limit=lim)
+    torch.cuda.synchronize()
+    ref = dict(inp, dt=eff.astype(np.float32))
+    y_ref, f_ref = native.forward(**ref)
+    rep = score(as64(y), as64(f), y_ref, f_ref, shape.io)
+    assert rep["pass"], rep
