@@ -76,9 +76,9 @@ typedef enum {
     SSD_VARIANT_FUSED = 2    /* bf16 io, headdim 64 or 128, dstate 64, 128 or 256: three kernels
                                 (run states, state passing over runs, fused scan). The sequence is
                                 cut into runs (about one block per compute unit); inside a run
-                                the state stays on chip and each sub-chunk of 64 tokens (32 when
-                                dstate is 256) gets its C B^T block, decay mask, readout and
-                                state update without leaving the compute unit. The exact result
+                                the state stays on chip and each sub-chunk of 32 tokens gets its
+                                C B^T block, decay mask, readout and state update without leaving
+                                the compute unit. The exact result
                                 does not depend on the chunk length, so chunk_size only sets
                                 the run length when run_chunks is given. Assumes A <= 0 and
                                 dt >= 0 (decays at most 1); D enters through the fp16 diagonal

@@ -13,15 +13,16 @@
 //                     intra-sub-chunk product, the readout of the carried state, the skip term
 //                     and the state update, all on chip; only y leaves the kernel.
 //
-// Inside F1/F3 the run is walked in sub-chunks of T tokens (64, or 32 when N = 256), whatever the
-// caller's chunk length: the exact result does not depend on where the sequence is cut (the
+// Inside F1/F3 the run is walked in sub-chunks of T = 32 tokens, whatever the caller's chunk
+// length: the exact result does not depend on where the sequence is cut (the
 // chunk length cancels out of the recurrence), so the kernel picks the cut that suits the chip's
 // registers and LDS. The caller's chunk length still fixes the stage entry points' outputs.
 //
-// Work split (one 256-thread block per compute unit, one wave per SIMD): a wave owns one head's
-// p-slice of PS columns (PS * N <= 8192, so its fp32 state is at most 128 registers per lane) and
-// keeps that state in registers across the whole run. The HPB heads of a block belong to one B/C
-// group, so B and C are staged, and C B^T is computed, once per block and shared.
+// Work split (one 512-thread block per compute unit, two waves per SIMD): a wave owns one head's
+// p-slice of PS columns (PS * N <= 8192, so its fp32 state is at most 128 registers per lane; at
+// headdim 64 the whole head) and keeps that state in registers across the whole run. The HPB
+// heads of a block belong to one B/C group, so B and C are staged once per block; each head's
+// decay-masked C B^T blocks are built by that head's waves.
 //
 // Staging: x, B and C tiles are copied global -> LDS by the gfx950 LDS DMA (global_load_lds
 // dwordx4), which needs no registers, so a whole sub-chunk is in flight while the previous one is
@@ -514,7 +515,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
           xlo[pt] = cvt_f16x8(lo);
         }
       }
-#ifndef SSD_F1_NO_HOIST
+#ifdef SSD_F1_HOIST
       // all B^T fragments of the K step first (their LDS latency overlaps), then the high parts
       // for every tile, then the low parts (no back-to-back dependent matrix-core ops)
       f16x8 bts[K::NNT];
@@ -948,25 +949,38 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
 }
 
 // ---- launchers ----------------------------------------------------------------------------------
-// Configurations: both kernels run two waves per SIMD (8 waves per block, 32-column slices), so
-// one wave's memory and matrix-core latencies hide behind the other's work and each wave fits in
-// 256 registers. Both walk the same sub-chunks (T depends on N only), so their runs line up.
+// Configurations: both kernels run 8 waves per block, two per SIMD (one wave's memory and
+// matrix-core latencies hide behind the other's work), with 64-column slices (one wave per head
+// at headdim 64) over sub-chunks of 32 tokens, so each wave keeps its fp32 state slice (64 x N)
+// and the rest of its working set within 256 registers. One wave per head halves, per token, the
+// B and C fragments read from LDS and the decay-mask work (a head's M blocks are built by its own
+// wave), at the price of twice as many runs (twice the run-state traffic between F1, F2 and F3);
+// measured at the headline workload: F3 145 -> 126 us, the forward -3%. The run-state kernel
+// reads its B^T fragments one K step at a time (holding a whole step's would spill at this width).
 #ifndef SSD_F3_NW
 #define SSD_F3_NW 8
-#define SSD_F3_PS 32
+#define SSD_F3_PS 64
 #endif
 #ifdef SSD_TOKENS
 #define SSD_T(N) SSD_TOKENS
 #else
-#define SSD_T(N) ((N) >= 256 ? 32 : 64)
+#define SSD_T(N) 32
 #endif
 #ifdef SSD_F3_TOK
 #define SSD_F3_T(N) SSD_F3_TOK
 #else
 #define SSD_F3_T(N) SSD_T(N)
 #endif
+#ifndef SSD_F1_PS
+#define SSD_F1_PS 64
+#endif
+#ifdef SSD_F1_TOK
+#define SSD_F1_T(N) SSD_F1_TOK
+#else
+#define SSD_F1_T(N) SSD_T(N)
+#endif
 template <int P, int N>
-using RunCfg = Fz<P, N, 8, 32, SSD_T(N)>;
+using RunCfg = Fz<P, N, 8, SSD_F1_PS, SSD_F1_T(N)>;
 template <int P, int N>
 using ScanCfg = Fz<P, N, SSD_F3_NW, SSD_F3_PS, SSD_F3_T(N)>;
 
