@@ -583,8 +583,11 @@ __device__ __forceinline__ void store_y(const char* xt, u16* y, const Dims& d, c
     const int row0 = k * RPR;
     const uint4 v = *reinterpret_cast<const uint4*>(xt + xl[k % NPAT] + (row0 / (NPAT * RPR)) *
                                                                           (NPAT * RPR) * K::ROW_P);
-    if (nrow >= K::T || row0 + r < nrow)
-      *reinterpret_cast<uint4*>(yb + (int64_t)row0 * ld) = v;
+    if (nrow >= K::T || row0 + r < nrow) {  // y is not read again: nontemporal
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                  reinterpret_cast<u32x4*>(yb + (int64_t)row0 * ld));
+    }
   }
 }
 
