@@ -238,7 +238,7 @@ struct DmaGeo {
   }
 };
 
-template <class K>
+template <class K, bool WITH_C>
 struct DmaLanes {
   using GN = DmaGeo<K::N / 8>;
   using GP = DmaGeo<K::P / 8>;
@@ -246,11 +246,36 @@ struct DmaLanes {
   static_assert(K::NW % GP::NPAT == 0 && (K::T / GP::RPI) % GP::NPAT == 0 &&
                     K::BC_NI % GP::NPAT == 0,
                 "x pattern per wave");
-  uint32_t bc, x, dt;
+  static constexpr int NBC = (WITH_C ? 2 : 1) * K::BC_NI;  // B (and C) instructions per stage
+  static constexpr int NI = NBC + K::X_NI;                  // tile instructions per stage
+  static constexpr int XI = K::T / GP::RPI;                 // x instructions per head
+  // Direct form: every round of NW instructions (one per wave) lies inside one region (B, C or
+  // x) and a round of x instructions covers whole heads. A wave's instructions of a stage then
+  // read rows at one lane offset per region (wbc, wx: the wave's rows and, for x, its head within
+  // the round, folded in), from bases that differ by compile-time multiples of the row strides.
+  static constexpr bool DIRECT =
+      K::BC_NI % K::NW == 0 && NI % K::NW == 0 && K::NW % XI == 0;
+  static constexpr int NPW_DIRECT = NI / K::NW;  // instructions per wave and stage
+  uint32_t bc, x, dt;  // generic form: lane offsets of rows 0.. of an instruction
+  uint32_t wbc, wx;    // direct form
   __device__ __forceinline__ void init(const Dims& d, const Coord& c) {
-    bc = GN::lane_off(c.wave, c.lane, (uint32_t)d.G * K::N * 2);
-    x = GP::lane_off(c.wave, c.lane, (uint32_t)d.H * K::P * 2);
+    const uint32_t ldbc = (uint32_t)d.G * K::N * 2, ldx = (uint32_t)d.H * K::P * 2;
+    bc = GN::lane_off(c.wave, c.lane, ldbc);
+    x = GP::lane_off(c.wave, c.lane, ldx);
     dt = (uint32_t)min(c.lane, K::T - 1) * (uint32_t)d.H * 4;
+    if constexpr (DIRECT) {
+      constexpr int PPR_N = K::N / 8, PPR_P = K::P / 8;
+      const int tb = c.wave * GN::RPI + c.lane / PPR_N;
+      wbc = (uint32_t)tb * ldbc + (uint32_t)(((c.lane % PPR_N) ^ swz_key<PPR_N>(tb)) << 4);
+      const int tx = (c.wave % XI) * GP::RPI + c.lane / PPR_P;
+      wx = (uint32_t)((c.wave / XI) * (K::P * 2)) + (uint32_t)tx * ldx +
+           (uint32_t)(((c.lane % PPR_P) ^ swz_key<PPR_P>(tx)) << 4);
+    }
+  }
+  // Opaque copies at the top of every sub-chunk: the offsets stay in registers instead of being
+  // recomputed from the lane index where they are used.
+  __device__ __forceinline__ void pin() {
+    if constexpr (DIRECT) asm volatile("" : "+v"(wbc), "+v"(wx));
   }
 };
 
@@ -274,7 +299,7 @@ __device__ __forceinline__ void refresh_lane(Coord& c) {
 template <class K, bool WITH_C>
 __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* Bm, const u16* Cm,
                                             const float* dt, const Dims& d, const Coord& c,
-                                            const DmaLanes<K>& dl, int tok0, int r0 = 0,
+                                            const DmaLanes<K, WITH_C>& dl, int tok0, int r0 = 0,
                                             int r1 = 1 << 20, bool with_dt = true) {
   constexpr int NBC = (WITH_C ? 2 : 1) * K::BC_NI;
   constexpr int NI = NBC + K::X_NI;
@@ -289,7 +314,33 @@ __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* B
   const char* dbase = reinterpret_cast<const char*>(dt) + (row0 * d.H + c.h) * 4;
   const uint32_t l0 = lds_addr(st);
   const uint32_t ldt = l0 + NI * 1024 + c.wave * 256;
-  if (tok0 + K::T <= d.L) {
+  using DL = DmaLanes<K, WITH_C>;
+  if constexpr (DL::DIRECT) {
+    if (tok0 + K::T <= d.L) {
+      // full stage: round m is this wave's instruction m; x rows of heads past the group re-read
+      // its last head (their results are never used)
+      const uint32_t lw = l0 + c.wave * 1024;
+      const int hw = c.wave / DL::XI, hmax = c.hlast - c.hbase;
+      constexpr int BSTEP = K::NW * RPI_N;  // rows between a wave's B (C) instructions
+      constexpr int XSTEP = K::NW / DL::XI;  // heads between a wave's x instructions
+#pragma unroll
+      for (int m = 0; m < DL::NPW_DIRECT; ++m) {
+        if (m < r0 || m >= r1) continue;
+        const int k0 = K::NW * m;
+        if (k0 < NBC) {
+          const bool isC = WITH_C && k0 >= K::BC_NI;
+          const int j = (isC ? k0 - K::BC_NI : k0) / K::NW;
+          dma_x4((isC ? cbase : bbase) + (int64_t)(j * BSTEP) * ldbc, dl.wbc, lw + k0 * 1024);
+        } else {
+          const int hh = (k0 - NBC) / K::NW * XSTEP + hw;
+          dma_x4(xbase + (min(hh, hmax) - hw) * (K::P * 2), dl.wx, lw + k0 * 1024);
+        }
+      }
+      if (with_dt) dma_x1(dbase, dl.dt, ldt);
+      return;
+    }
+  }
+  if (!DL::DIRECT && tok0 + K::T <= d.L) {
     // row strides as opaque scalars: their per-instruction multiples are recomputed (scalar ALU)
     // each call rather than held in scalar registers across the loop
     uint32_t lb = (uint32_t)ldbc, lx = (uint32_t)ldx;
@@ -443,7 +494,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
   static_assert(K::RUN_LDS <= 160 * 1024, "LDS budget");
   __shared__ __align__(1024) char smem[K::RUN_LDS];
   Coord c = coords<K>(d);
-  DmaLanes<K> dl;
+  DmaLanes<K, false> dl;
   dl.init(d, c);
   constexpr int T = K::T;
   const int nsub = (d.L + T - 1) / T;
@@ -470,6 +521,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
   const bool hi = c.wave < K::RUN_NI % K::NW;
 
   for (int s = s_begin; s < s_end; ++s) {
+    dl.pin();
     const int cur = (s - s_begin) % K::NRUN;
     char* st = smem + cur * K::RUN_STAGE;
     // this stage's DMA done; the next stage's (this wave's instructions for it were issued after
@@ -744,19 +796,37 @@ __device__ __forceinline__ void build_m(const char* Bh, const char* Ch, const fl
     else
       put_m<K>(b3, 3, 3, wa, d_h, fast, mh, sl, c);
   } else {
-    // blocks in row-major order over the lower triangle, block q to the head's wave q % WPH
+    // blocks in row-major order over the lower triangle, block q to the head's wave q % WPH;
+    // K steps outermost: one B and one C fragment per 16-token block and K step feed every block
+    // (fewer LDS reads, and each K step's reads are in flight together)
+    f32x4 acc[K::NMB];
 #pragma unroll
-    for (int kn = 0; kn < K::NKN; ++kn) dma(kn);
+    for (int q = 0; q < K::NMB; ++q) acc[q] = zero4();
+#pragma unroll
+    for (int kn = 0; kn < K::NKN; ++kn) {
+      dma(kn);
+      f16x8 bf[NIT], cf[NIT];
+#pragma unroll
+      for (int t = 0; t < NIT; ++t) {
+        bf[t] = bc_frag<K>(Bh, 16 * t, kn, sl);
+        cf[t] = bc_frag<K>(Ch, 16 * t, kn, sl);
+      }
+#pragma unroll
+      for (int it = 0; it < NIT; ++it)
+#pragma unroll
+        for (int jt = 0; jt <= it; ++jt) {
+          const int q = it * (it + 1) / 2 + jt;
+          if (q % K::WPH != hw) continue;
+          acc[q] = M::mma(bf[jt], cf[it], acc[q]);
+        }
+    }
 #pragma unroll
     for (int it = 0; it < NIT; ++it)
 #pragma unroll
       for (int jt = 0; jt <= it; ++jt) {
-        if ((it * (it + 1) / 2 + jt) % K::WPH != hw) continue;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kn = 0; kn < K::NKN; ++kn)
-          acc = M::mma(bc_frag<K>(Bh, 16 * jt, kn, sl), bc_frag<K>(Ch, 16 * it, kn, sl), acc);
-        put_m<K>(acc, it, jt, wa, d_h, fast, mh, sl, c);
+        const int q = it * (it + 1) / 2 + jt;
+        if (q % K::WPH != hw) continue;
+        put_m<K>(acc[q], it, jt, wa, d_h, fast, mh, sl, c);
       }
   }
 }
@@ -771,7 +841,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
   // [stage 0][stage 1][M blocks per head][token arrays per head]
   __shared__ __align__(1024) char smem[K::SCAN_LDS];
   Coord c = coords<K>(d);
-  DmaLanes<K> dl;
+  DmaLanes<K, true> dl;
   dl.init(d, c);
   ScanLane<K> sl;
   sl.init(c);
@@ -815,6 +885,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
 
   for (int s = s_begin; s < s_end; ++s) {
     refresh_lane(c);
+    dl.pin();
     const int cur = (s - s_begin) & 1;
     char* st = smem + cur * K::SCAN_STAGE;
     const char* Bh = st;
@@ -887,7 +958,13 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
         w16[js] = cvt_f16x8(wv);
       }
     }
-    __syncthreads();  // B: M blocks visible; the token arrays are free again
+    if constexpr (K::WPH > 1) {
+      __syncthreads();  // B: every M block of the head visible to both of its waves
+    } else {
+      // one wave per head: it alone writes and reads its M blocks and token arrays, and a wave's
+      // LDS accesses complete in order, so only the compiler must keep them in program order
+      asm volatile("" ::: "memory");
+    }
     if (!c.active) continue;
     SSD_SB();
 
