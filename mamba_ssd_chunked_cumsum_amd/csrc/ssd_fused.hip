@@ -438,27 +438,30 @@ __device__ __forceinline__ float row_last(float v) { return dpp_mov<0x15f, 0xf>(
 
 // Per-sub-chunk decay bookkeeping of one wave (lane l = token l, acs = inclusive cumulative
 // log-decay from the sub-chunk start, e(l) the last token of l's 16-token block). Into the wave's
-// LDS arrays:
-//   acs2 = acs log2(e);  dt;  w = exp(acs_end - acs) dt (state weights);
+// LDS arrays (only w when WEIGHTS_ONLY):
+//   acs2 = acs log2(e);  dt;  w = exp(shift + acs_end - acs) dt (state weights, anchored shift
+//   (<= 0) past the sub-chunk end);
 //   cf = exp(acs_e - acs) dt (column factor of the decay mask through the end of the token's
 //   block; both of its factors are <= 1);  rdiag = exp(acs - acs_e) >= 1 (its row factor inside
 //   the token's own block).
 // Returns acs_end; *fast tells whether every block's decay span acs - acs_e stays below 2^100 in
 // base 2, so that rdiag and cf stay inside fp32's normal range and the factored diagonal is exact
 // up to rounding.
-template <class K>
+template <class K, bool WEIGHTS_ONLY = false>
 __device__ __forceinline__ float decay_terms(float dv, float a_h, float* wa, const Coord& c,
-                                             bool* fast = nullptr) {
+                                             bool* fast = nullptr, float shift = 0.f) {
   const float acs = wave_scan(a_h * dv);
   const float acs_end = __builtin_bit_cast(
       float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acs), K::T - 1));
   const float span = acs - row_last(acs);  // >= 0
   if (c.lane < K::T) {
-    wa[c.lane] = acs * kLog2e;
-    wa[K::T + c.lane] = dv;
-    wa[2 * K::T + c.lane] = __expf(acs_end - acs) * dv;
-    wa[3 * K::T + c.lane] = __expf(-span) * dv;
-    if (fast) wa[4 * K::T + c.lane] = __expf(span);
+    wa[2 * K::T + c.lane] = __expf(shift + (acs_end - acs)) * dv;
+    if constexpr (!WEIGHTS_ONLY) {
+      wa[c.lane] = acs * kLog2e;
+      wa[K::T + c.lane] = dv;
+      wa[3 * K::T + c.lane] = __expf(-span) * dv;
+      if (fast) wa[4 * K::T + c.lane] = __expf(span);
+    }
   }
   if (fast) *fast = __ballot(span * kLog2e >= 100.f) == 0;
   return acs_end;
@@ -480,8 +483,8 @@ __device__ __forceinline__ f16x8 b_frag(const char* Bh, int js, int col0, int la
 
 // ---- F1: run states -------------------------------------------------------------------------
 // state_r = sum_{t in run} exp(sum_{k in (t, end]} dt_k A) dt_t x_t B_t^T (zero entry state) and
-// logdecay_r = sum_{t in run} dt_t A. Walked forwards: per sub-chunk, S <- exp(acs_end) S +
-// B^T (w x), the weighted x split into fp16 high and low parts.
+// logdecay_r = sum_{t in run} dt_t A. Walked backwards: per sub-chunk, S += B^T (w x) with the
+// weights anchored at the run end, the weighted x split into fp16 high and low parts.
 template <class K, bool SPLIT>
 __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ x,
                                                       const u16* __restrict__ Bm,
@@ -510,23 +513,25 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
   for (int nt = 0; nt < K::NNT; ++nt)
 #pragma unroll
     for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] = zero4();
-  float logsum = 0.f;
+  // The run is walked backwards, last sub-chunk first, with token weights anchored at the run
+  // end: w_t = exp(sum of a over (t, run end]) dt_t. The state then never needs decaying.
+  float rem = 0.f;  // log-decay from the end of the current sub-chunk to the run end
 
-  // prologue: stages of the first two sub-chunks
-  issue_stage<K, false>(smem, x, Bm, nullptr, dt, d, c, dl, s_begin * T);
-  if (s_begin + 1 < s_end)
-    issue_stage<K, false>(smem + K::RUN_STAGE, x, Bm, nullptr, dt, d, c, dl, (s_begin + 1) * T);
+  // prologue: stages of the last two sub-chunks
+  issue_stage<K, false>(smem, x, Bm, nullptr, dt, d, c, dl, (s_end - 1) * T);
+  if (s_end - 2 >= s_begin)
+    issue_stage<K, false>(smem + K::RUN_STAGE, x, Bm, nullptr, dt, d, c, dl, (s_end - 2) * T);
   // DMA instructions this wave issues per stage: NLO or NLO + 1 tile pieces, and its dt
   constexpr int NLO = K::RUN_NI / K::NW + 1;
   const bool hi = c.wave < K::RUN_NI % K::NW;
 
-  for (int s = s_begin; s < s_end; ++s) {
+  for (int s = s_end - 1; s >= s_begin; --s) {
     dl.pin();
-    const int cur = (s - s_begin) % K::NRUN;
+    const int cur = (s_end - 1 - s) % K::NRUN;
     char* st = smem + cur * K::RUN_STAGE;
     // this stage's DMA done; the next stage's (this wave's instructions for it were issued after
     // this stage's) may still be in flight
-    if (s + 1 >= s_end)
+    if (s - 1 < s_begin)
       wait_vm_all();
     else if (hi)
       wait_vm_but<NLO + 1>();
@@ -534,22 +539,16 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
       wait_vm_but<NLO>();
     const float dv = stage_dt<K>(st + K::RUN_DT, d, c, s * T, dtb);
     convert_stage<K, false>(st, c);
-    __syncthreads();  // stage visible to all waves; every wave is done with sub-chunk s - 1
-    // the DMA of sub-chunk s + 2 (into the stage of s - 1), spread over the K steps below
-    const bool more = s + 2 < s_end;
+    __syncthreads();  // stage visible to all waves; every wave is done with sub-chunk s + 1
+    // the DMA of sub-chunk s - 2 (into the stage of s + 1), spread over the K steps below
+    const bool more = s - 2 >= s_begin;
     constexpr int NRND = (K::RUN_NI + K::NW - 1) / K::NW, RPJ = (NRND + K::NJS - 1) / K::NJS;
-    const float acs_end = decay_terms<K>(dv, a_h, wa, c);
-    logsum += acs_end;
-    const float dec = __expf(acs_end);
-#pragma unroll
-    for (int nt = 0; nt < K::NNT; ++nt)
-#pragma unroll
-      for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] *= dec;
+    rem += decay_terms<K, true>(dv, a_h, wa, c, nullptr, rem);
 #pragma unroll
     for (int js = 0; js < K::NJS; ++js) {
       if (more)
         issue_stage<K, false>(smem + ((cur + 2) % K::NRUN) * K::RUN_STAGE, x, Bm, nullptr, dt, d,
-                              c, dl, (s + 2) * T, js * RPJ, (js + 1) * RPJ, js == K::NJS - 1);
+                              c, dl, (s - 2) * T, js * RPJ, (js + 1) * RPJ, js == K::NJS - 1);
       const float4 w0 = *reinterpret_cast<const float4*>(wa + 2 * T + 32 * js + 8 * c.g);
       const float4 w1 = *reinterpret_cast<const float4*>(wa + 2 * T + 32 * js + 8 * c.g + 4);
       const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -607,7 +606,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
       *reinterpret_cast<float4*>(so + (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g) =
           make_float4(v[0], v[1], v[2], v[3]);
     }
-  if (c.lane == 0 && c.p0 == 0) logdecay[((int64_t)c.b * d.H + c.h) * nr + c.r] = logsum;
+  if (c.lane == 0 && c.p0 == 0) logdecay[((int64_t)c.b * d.H + c.h) * nr + c.r] = rem;
 }
 
 // Store the bf16 y tile that F3 left in the x tile of a stage: this wave's p-slice of its head,
