@@ -250,11 +250,12 @@ struct DmaLanes {
   static constexpr int NI = NBC + K::X_NI;                  // tile instructions per stage
   static constexpr int XI = K::T / GP::RPI;                 // x instructions per head
   // Direct form: every round of NW instructions (one per wave) lies inside one region (B, C or
-  // x) and a round of x instructions covers whole heads. A wave's instructions of a stage then
+  // x) and a round of x instructions covers whole heads (used by the fused scan only at one wave
+  // per head: with several waves per head it costs that kernel more registers than it has). A wave's instructions of a stage then
   // read rows at one lane offset per region (wbc, wx: the wave's rows and, for x, its head within
   // the round, folded in), from bases that differ by compile-time multiples of the row strides.
   static constexpr bool DIRECT =
-      K::BC_NI % K::NW == 0 && NI % K::NW == 0 && K::NW % XI == 0;
+      K::BC_NI % K::NW == 0 && NI % K::NW == 0 && K::NW % XI == 0 && (!WITH_C || K::WPH == 1);
   static constexpr int NPW_DIRECT = NI / K::NW;  // instructions per wave and stage
   uint32_t bc, x, dt;  // generic form: lane offsets of rows 0.. of an instruction
   uint32_t wbc, wx;    // direct form
@@ -794,10 +795,25 @@ __device__ __forceinline__ void build_m(const char* Bh, const char* Ch, const fl
       put_m<K>(a1, 1, 1, wa, d_h, fast, mh, sl, c);
     else
       put_m<K>(b3, 3, 3, wa, d_h, fast, mh, sl, c);
+  } else if constexpr (K::WPH > 1) {
+    // blocks in row-major order over the lower triangle, block q to the head's wave q % WPH
+#pragma unroll
+    for (int kn = 0; kn < K::NKN; ++kn) dma(kn);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+#pragma unroll
+      for (int jt = 0; jt <= it; ++jt) {
+        if ((it * (it + 1) / 2 + jt) % K::WPH != hw) continue;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kn = 0; kn < K::NKN; ++kn)
+          acc = M::mma(bc_frag<K>(Bh, 16 * jt, kn, sl), bc_frag<K>(Ch, 16 * it, kn, sl), acc);
+        put_m<K>(acc, it, jt, wa, d_h, fast, mh, sl, c);
+      }
   } else {
-    // blocks in row-major order over the lower triangle, block q to the head's wave q % WPH;
-    // K steps outermost: one B and one C fragment per 16-token block and K step feed every block
-    // (fewer LDS reads, and each K step's reads are in flight together)
+    // one wave builds every block of its head, K steps outermost: one B and one C fragment per
+    // 16-token block and K step feed every block (fewer LDS reads, and each K step's reads are
+    // in flight together)
     f32x4 acc[K::NMB];
 #pragma unroll
     for (int q = 0; q < K::NMB; ++q) acc[q] = zero4();
@@ -815,18 +831,13 @@ __device__ __forceinline__ void build_m(const char* Bh, const char* Ch, const fl
 #pragma unroll
         for (int jt = 0; jt <= it; ++jt) {
           const int q = it * (it + 1) / 2 + jt;
-          if (q % K::WPH != hw) continue;
           acc[q] = M::mma(bf[jt], cf[it], acc[q]);
         }
     }
 #pragma unroll
     for (int it = 0; it < NIT; ++it)
 #pragma unroll
-      for (int jt = 0; jt <= it; ++jt) {
-        const int q = it * (it + 1) / 2 + jt;
-        if (q % K::WPH != hw) continue;
-        put_m<K>(acc[q], it, jt, wa, d_h, fast, mh, sl, c);
-      }
+      for (int jt = 0; jt <= it; ++jt) put_m<K>(acc[it * (it + 1) / 2 + jt], it, jt, wa, d_h, fast, mh, sl, c);
   }
 }
 
