@@ -51,6 +51,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+
 // Scheduling fence: keeps the compiler from hoisting one step's LDS reads (and the registers they
 // hold) above the previous step.
 #ifdef SSD_SB_ON
@@ -187,7 +188,11 @@ struct Fz {
   static constexpr int WA_BYTES = NW * NWA * T * 4;   // acs2, dt, w, cf, rdiag (F1: per wave)
   static constexpr int WA_SCAN = HPB * NWA * T * 4;   // F3: per head
   static constexpr int NSCAN = 2, NRUN = 3;           // stages
-  static constexpr int SCAN_LDS = NSCAN * SCAN_STAGE + HPB * MT_HEAD + WA_SCAN;
+  // F3 at one wave per head: the sub-chunk's C B^T blocks, fp32, computed once for the block's
+  // heads (they share one B/C group)
+  static constexpr bool SHARED_CB = WPH == 1 && NMB <= NW;
+  static constexpr int CB_SHARED = SHARED_CB ? NMB * 1024 : 0;
+  static constexpr int SCAN_LDS = NSCAN * SCAN_STAGE + HPB * MT_HEAD + WA_SCAN + CB_SHARED;
   static constexpr int RUN_LDS = NRUN * RUN_STAGE + WA_BYTES;
   static_assert(P % PS == 0 && NW % WPH == 0, "whole waves per head");
   static_assert(N / 8 >= 8 && P / 8 >= 8, "swizzle needs 8 pieces per row");
@@ -257,13 +262,12 @@ struct DmaLanes {
   static constexpr bool DIRECT =
       K::BC_NI % K::NW == 0 && NI % K::NW == 0 && K::NW % XI == 0 && (!WITH_C || K::WPH == 1);
   static constexpr int NPW_DIRECT = NI / K::NW;  // instructions per wave and stage
-  uint32_t bc, x, dt;  // generic form: lane offsets of rows 0.. of an instruction
+  uint32_t bc, x;      // generic form: lane offsets of rows 0.. of an instruction
   uint32_t wbc, wx;    // direct form
   __device__ __forceinline__ void init(const Dims& d, const Coord& c) {
     const uint32_t ldbc = (uint32_t)d.G * K::N * 2, ldx = (uint32_t)d.H * K::P * 2;
     bc = GN::lane_off(c.wave, c.lane, ldbc);
     x = GP::lane_off(c.wave, c.lane, ldx);
-    dt = (uint32_t)min(c.lane, K::T - 1) * (uint32_t)d.H * 4;
     if constexpr (DIRECT) {
       constexpr int PPR_N = K::N / 8, PPR_P = K::P / 8;
       const int tb = c.wave * GN::RPI + c.lane / PPR_N;
@@ -337,7 +341,7 @@ __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* B
           dma_x4(xbase + (min(hh, hmax) - hw) * (K::P * 2), dl.wx, lw + k0 * 1024);
         }
       }
-      if (with_dt) dma_x1(dbase, dl.dt, ldt);
+      if (with_dt) dma_x1(dbase, (uint32_t)min(c.lane, K::T - 1) * (uint32_t)d.H * 4, ldt);
       return;
     }
   }
@@ -365,7 +369,7 @@ __device__ __forceinline__ void issue_stage(char* st, const u16* x, const u16* B
         dma_x4(xbase + hoff + (uint32_t)(kr * RPI_P) * lx, dl.x, l0 + k * 1024);
       }
     }
-    if (with_dt) dma_x1(dbase, dl.dt, ldt);
+    if (with_dt) dma_x1(dbase, (uint32_t)min(c.lane, K::T - 1) * (uint32_t)d.H * 4, ldt);
   } else {
     const int last = d.L - 1 - tok0;  // last valid row of the sub-chunk
 #pragma unroll
@@ -697,8 +701,10 @@ __device__ __forceinline__ s16x8 tr8(const char* base, uint32_t lo, uint32_t hi)
 //   y_i = sum_{j <= i} M_ij x_j + exp(acs_i) C_i . S,
 //   M_ij = (C_i . B_j) exp(acs_i - acs_j) dt_j (j <= i), plus D on the diagonal (skip term)
 //   S  <- exp(acs_end) S + sum_j exp(acs_end - acs_j) dt_j x_j B_j^T
-// A head's waves split the lower-triangle 16x16 blocks of its M, build them straight from the
-// C B^T accumulators and leave them in LDS in fp16. Each wave then computes y^T for its p-slice
+// The lower-triangle 16x16 blocks of a head's M are built from C B^T accumulators and left in LDS
+// in fp16: at one wave per head the C B^T blocks are computed once for the block's heads (which
+// share one B/C group) and each wave applies its head's decay; with several waves per head those
+// waves split the head's blocks. Each wave then computes y^T for its p-slice
 // (rows p, columns i), so every accumulator lane holds four consecutive p of one token: the
 // readout's A operand comes straight from the state accumulators (K index n in accumulator
 // order), and y leaves in 8-byte row pieces.
@@ -756,7 +762,8 @@ __device__ __forceinline__ f16x8 bc_frag(const char* tile, int r0, int kn, const
                                          (kn / SL::KP) * (16 * SL::KP * 4));
 }
 
-// This wave's share of its head's M blocks for the staged sub-chunk.
+// This wave's share of its head's M blocks for the staged sub-chunk (several waves per head; at
+// one wave per head the C B^T blocks are shared by the block's heads, see shared_cb).
 // dma(kn) issues the next stage's share for K step kn (0 .. NKN - 1), spread over the work.
 template <class K, class Dma>
 __device__ __forceinline__ void build_m(const char* Bh, const char* Ch, const float* wa, float d_h,
@@ -795,7 +802,7 @@ __device__ __forceinline__ void build_m(const char* Bh, const char* Ch, const fl
       put_m<K>(a1, 1, 1, wa, d_h, fast, mh, sl, c);
     else
       put_m<K>(b3, 3, 3, wa, d_h, fast, mh, sl, c);
-  } else if constexpr (K::WPH > 1) {
+  } else {
     // blocks in row-major order over the lower triangle, block q to the head's wave q % WPH
 #pragma unroll
     for (int kn = 0; kn < K::NKN; ++kn) dma(kn);
@@ -810,35 +817,41 @@ __device__ __forceinline__ void build_m(const char* Bh, const char* Ch, const fl
           acc = M::mma(bc_frag<K>(Bh, 16 * jt, kn, sl), bc_frag<K>(Ch, 16 * it, kn, sl), acc);
         put_m<K>(acc, it, jt, wa, d_h, fast, mh, sl, c);
       }
-  } else {
-    // one wave builds every block of its head, K steps outermost: one B and one C fragment per
-    // 16-token block and K step feed every block (fewer LDS reads, and each K step's reads are
-    // in flight together)
-    f32x4 acc[K::NMB];
-#pragma unroll
-    for (int q = 0; q < K::NMB; ++q) acc[q] = zero4();
-#pragma unroll
-    for (int kn = 0; kn < K::NKN; ++kn) {
-      dma(kn);
-      f16x8 bf[NIT], cf[NIT];
-#pragma unroll
-      for (int t = 0; t < NIT; ++t) {
-        bf[t] = bc_frag<K>(Bh, 16 * t, kn, sl);
-        cf[t] = bc_frag<K>(Ch, 16 * t, kn, sl);
-      }
-#pragma unroll
-      for (int it = 0; it < NIT; ++it)
-#pragma unroll
-        for (int jt = 0; jt <= it; ++jt) {
-          const int q = it * (it + 1) / 2 + jt;
-          acc[q] = M::mma(bf[jt], cf[it], acc[q]);
-        }
-    }
-#pragma unroll
-    for (int it = 0; it < NIT; ++it)
-#pragma unroll
-      for (int jt = 0; jt <= it; ++jt) put_m<K>(acc[it * (it + 1) / 2 + jt], it, jt, wa, d_h, fast, mh, sl, c);
   }
+}
+
+// Shared C B^T blocks (one wave per head): block q of the lower triangle (row-major) is computed
+// by wave q for the whole block and left in LDS in fp32, in the lane layout put_m takes; every
+// wave issues the next stage's DMA share for K steps 0 .. NKN - 1 meanwhile.
+template <class K, class Dma>
+__device__ __forceinline__ void shared_cb(const char* Bh, const char* Ch, char* cbs,
+                                          const ScanLane<K>& sl, const Coord& c, Dma&& dma) {
+  using M = Mma<f16>;
+  const bool mine = c.wave < K::NMB;  // wave-uniform
+  const int q = mine ? c.wave : 0;
+  const int it = (q >= 1) + (q >= 3) + (q >= 6), jt = q - it * (it + 1) / 2;
+  static_assert(K::NMB <= 10, "blocks of at most four row blocks");
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int kn = 0; kn < K::NKN; ++kn) {
+    dma(kn);
+    if (mine) acc = M::mma(bc_frag<K>(Bh, 16 * jt, kn, sl), bc_frag<K>(Ch, 16 * it, kn, sl), acc);
+  }
+  if (mine) *reinterpret_cast<f32x4*>(cbs + q * 1024 + c.lane * 16) = acc;
+}
+
+// This wave's head's M blocks from the shared C B^T blocks.
+template <class K>
+__device__ __forceinline__ void m_from_shared(const char* cbs, const float* wa, float d_h, bool fast,
+                                              char* mh, const ScanLane<K>& sl, const Coord& c) {
+#pragma unroll
+  for (int it = 0; it < K::NIT; ++it)
+#pragma unroll
+    for (int jt = 0; jt <= it; ++jt) {
+      const int q = it * (it + 1) / 2 + jt;
+      const f32x4 acc = *reinterpret_cast<const f32x4*>(cbs + q * 1024 + c.lane * 16);
+      put_m<K>(acc, it, jt, wa, d_h, fast, mh, sl, c);
+    }
 }
 
 template <class K>
@@ -870,6 +883,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
       hb * K::NWA * T;
   const int xoff = 2 * K::BC_BYTES + hb * (T * K::ROW_P);
   const float a_h = Av[c.h], d_h = Dv[c.h], dtb = dt_bias_of(d, c.h);
+  char* cbs = smem + K::NSCAN * K::SCAN_STAGE + K::HPB * K::MT_HEAD + K::WA_SCAN;
 
   // carried state S^T tiles (rows n, columns p): lane holds p = p0 + 16 pt + c16,
   // n = 16 nt + 4 g + 0..3
@@ -922,11 +936,16 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
 
     f32x4 Y[NPT][NIT];
     f16x8 w16[K::NJS];  // state weights of the lane's 8 tokens per K step
+    if constexpr (K::SHARED_CB) {
+      shared_cb<K>(Bh, Ch, cbs, sl, c, dma);
+      __syncthreads();  // the shared C B^T blocks visible to every wave
+      if (c.active) m_from_shared<K>(cbs, wa, d_h, fast, mh, sl, c);
+    }
     if (!c.active) {
 #pragma unroll
-      for (int slot = 0; slot < NSLOT; ++slot) dma(slot);
+      for (int slot = K::SHARED_CB ? K::NKN : 0; slot < NSLOT; ++slot) dma(slot);
     } else {
-      build_m<K>(Bh, Ch, wa, d_h, fast, mh, sl, c, dma);
+      if constexpr (!K::SHARED_CB) build_m<K>(Bh, Ch, wa, d_h, fast, mh, sl, c, dma);
 
       // readout of the carried state: Y^T = S C^T (K index n in accumulator order)
 #pragma unroll
@@ -971,8 +990,9 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     if constexpr (K::WPH > 1) {
       __syncthreads();  // B: every M block of the head visible to both of its waves
     } else {
-      // one wave per head: it alone writes and reads its M blocks and token arrays, and a wave's
-      // LDS accesses complete in order, so only the compiler must keep them in program order
+      // one wave per head: it alone writes and reads its M blocks and token arrays (the shared
+      // C B^T blocks were published by the barrier before them), and a wave's LDS accesses
+      // complete in order, so only the compiler must keep them in program order
       asm volatile("" ::: "memory");
     }
     if (!c.active) continue;
