@@ -885,6 +885,9 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
   const float a_h = Av[c.h], d_h = Dv[c.h], dtb = dt_bias_of(d, c.h);
   char* cbs = smem + K::NSCAN * K::SCAN_STAGE + K::HPB * K::MT_HEAD + K::WA_SCAN;
 
+  // the first stage's DMA first: it and the entry state below are then in flight together
+  issue_stage<K, true>(smem, x, Bm, Cm, dt, d, c, dl, s_begin * T);
+
   // carried state S^T tiles (rows n, columns p): lane holds p = p0 + 16 pt + c16,
   // n = 16 nt + 4 g + 0..3
   f32x4 S[K::NNT][NPT];
@@ -900,11 +903,11 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
         S[nt][pt] = f32x4{v.x, v.y, v.z, v.w};
       }
     // the compiler's own wait for these loads (it does not see the DMA waits, which are inline
-    // assembly), here rather than at the state's first use inside the loop
+    // assembly), here rather than at the state's first use inside the loop; it also covers the
+    // first stage's DMA, which the loop waits for anyway
     __builtin_amdgcn_s_waitcnt(0x0f70);
   }
 
-  issue_stage<K, true>(smem, x, Bm, Cm, dt, d, c, dl, s_begin * T);
   int ytok = -1;  // first token of the sub-chunk whose y waits in the previous stage's x tile
 
   for (int s = s_begin; s < s_end; ++s) {
