@@ -21,6 +21,8 @@ What it computes (float64 throughout, from exactly widened inputs):
   each chunk, then the outputs. It also returns every intermediate for per-stage checks.
 * ``native`` -- the token-by-token recurrence again, in plain C with OpenMP over (batch, head), for
   full-size workloads and the timed CPU baseline.
+* ``backward.ssd_backward`` -- the gradients of the recurrence with respect to every input, by
+  reverse-mode differentiation of its steps (the backward pass training needs).
 * ``dt.dt_effective`` -- the dt pre-processing (bias, softplus, clamp) written out from its
   definition; the recurrence then runs on its output.
 * ``metrics`` -- the error measures the parity tests apply.
@@ -34,5 +36,7 @@ from .recurrence import ssd_recurrence, ssd_step
 from .quadratic import ssd_quadratic
 from .chunked import ssd_chunked
 from .dt import dt_effective
+from .backward import ssd_backward
 
-__all__ = ["ssd_recurrence", "ssd_step", "ssd_quadratic", "ssd_chunked", "dt_effective"]
+__all__ = ["ssd_recurrence", "ssd_step", "ssd_quadratic", "ssd_chunked", "dt_effective",
+           "ssd_backward"]
