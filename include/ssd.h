@@ -190,6 +190,34 @@ ssd_status ssd_step(const ssd_problem* prob, const void* x, const float* dt, con
                     const void* B, const void* C, const float* D, const float* state_in,
                     float* state_out, void* y, void* stream);
 
+/* ---- Backward: gradients of the forward with respect to every input. ----------------------
+ * Training depends on the backward pass as well as the forward ("Mamba-2 in NVIDIA cuTile: Faster
+ * Forward Kernels and What the Benchmark Means", section "What the speedup does and does not
+ * establish"). Given dy = dL/dy and dfinal = dL/dfinal_state (NULL: zero), for the recurrence of
+ * ssd_forward (dt as given: no dt pre-processing options) this computes, with G_t = dL/dS_t:
+ *     G_t = dy_t C_t^T + exp(dt_{t+1} A) G_{t+1},  G_{L-1} = dy_{L-1} C_{L-1}^T + dfinal
+ *     dx_t = D dy_t + dt_t G_t B_t;   dB_t = sum over the group's heads of dt_t G_t^T x_t;
+ *     dC_t = sum over the group's heads of S_t^T dy_t;
+ *     ddt_t = A dlog_t + x_t . (G_t B_t) with dlog_t = <G_t, exp(dt_t A) S_{t-1}>;
+ *     dA = sum over batch and time of dt_t dlog_t;  dD = sum over batch and time of dy_t . x_t;
+ *     dinitial_state = exp(dt_0 A) G_0.
+ * It runs the chunked forward machinery four times in fp32 (the state part of y and the final
+ * state; the adjoint G in reversed time; the transposed state for dC; the transposed adjoint for
+ * dB) plus elementwise and reduction kernels. Inputs as for ssd_forward (io dtype for x, B, C and
+ * dy; initial_state and dfinal [batch, nheads, headdim, dstate] f32, both nullable). Outputs, all
+ * f32 and overwritten (not accumulated into): dx [batch, seqlen, nheads, headdim], ddt [batch,
+ * seqlen, nheads], dA and dD [nheads], dB and dC [batch, seqlen, ngroups, dstate],
+ * dinitial_state [batch, nheads, headdim, dstate] (nullable: not computed). No output may overlap
+ * an input or another output; every pointer 16-byte aligned. Shapes as for the forward, and the
+ * transposed problem (headdim and dstate swapped, one group per head) must pass the same checks.
+ * Workspace: about 6 fp32 copies of x-sized tensors and 4 of [batch, seqlen, nheads, dstate],
+ * allocated and released stream-ordered on `stream`. Errors as for ssd_forward. */
+ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                        const void* B, const void* C, const float* D, int64_t chunk_size,
+                        const float* initial_state, const void* dy, const float* dfinal,
+                        float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD,
+                        float* dinitial_state, void* stream);
+
 /* Static text for a status code. */
 const char* ssd_status_string(ssd_status status);
 

@@ -367,6 +367,125 @@ ssd_status ssd_chunk_state(const ssd_problem* prob, const void* x, const void* B
                                           static_cast<hipStream_t>(stream)));
 }
 
+ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                        const void* B, const void* C, const float* D, int64_t chunk_size,
+                        const float* initial_state, const void* dy, const float* dfinal,
+                        float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD,
+                        float* dinitial_state, void* stream) {
+  ssd_status st = check_problem(prob, chunk_size);
+  if (st != SSD_OK) return st;
+  // the transposed problems (head dim and state dim swapped, one group per head) must fit too
+  ssd_problem tp = *prob;
+  tp.headdim = prob->dstate;
+  tp.dstate = prob->headdim;
+  tp.ngroups = prob->nheads;
+  tp.io_dtype = SSD_DTYPE_F32;
+  st = check_problem(&tp, chunk_size);
+  if (st != SSD_OK) return st;
+  if (!x || !dt || !A || !B || !C || !D || !dy || !dx || !ddt || !dA || !dB || !dC || !dD)
+    return SSD_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x,  dt, A,  B,  C,  D,  initial_state, dy, dfinal,
+                        dx, ddt, dA, dB, dC, dD, dinitial_state};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return SSD_ERR_INVALID_ARGUMENT;
+  const Sizes s = sizes_of(prob);
+  const int64_t Bt = prob->batch, L = prob->seqlen, H = prob->nheads, P = prob->headdim,
+                N = prob->dstate, G = prob->ngroups;
+  const int64_t nx = Bt * L * H * P, nb = Bt * L * G * N, nt = Bt * L * H * N, nd = Bt * L * H,
+                ns = Bt * H * P * N;
+  const Range ins[] = {range_of(x, s.x),        range_of(dt, s.dt),  range_of(A, s.hd),
+                       range_of(B, s.bc),       range_of(C, s.bc),   range_of(D, s.hd),
+                       range_of(dy, s.x),       initial_state ? range_of(initial_state, s.state)
+                                                              : Range{0, 0},
+                       dfinal ? range_of(dfinal, s.state) : Range{0, 0}};
+  const Range outs[] = {range_of(dx, nx * 4),  range_of(ddt, nd * 4), range_of(dA, H * 4),
+                        range_of(dB, nb * 4),  range_of(dC, nb * 4),  range_of(dD, H * 4),
+                        dinitial_state ? range_of(dinitial_state, ns * 4) : Range{0, 0}};
+  for (int i = 0; i < 7; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return SSD_ERR_INVALID_ARGUMENT;
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i], outs[j])) return SSD_ERR_INVALID_ARGUMENT;
+  }
+  st = device_ready();
+  if (st != SSD_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  // workspace (fp32): see the steps below for what each holds
+  enum { X32, DY32, B32, C32, Y0, FIN0, XR, BR, CR, DTR, UR, G0, XT, YT, H0T, XTR, CTR, YTR, DFT,
+         Q, XU, DYX, FT, PA, PD, ZD, NBUF };
+  const int64_t el[NBUF] = {nx, nx, nb, nb, nx, ns, nx, nb, nb, nd, nx, ns, nt, nt, ns,
+                            nt, nx, nt, ns, nd, nd, nd, Bt * H, Bt * H, Bt * H, H};
+  int64_t off[NBUF], total = 0;
+  for (int i = 0; i < NBUF; ++i) {
+    off[i] = total;
+    total += (el[i] * 4 + 255) & ~int64_t(255);
+  }
+  void* base = nullptr;
+  if (hipMallocAsync(&base, (size_t)total, hs) != hipSuccess) return SSD_ERR_OUT_OF_MEMORY;
+  float* w[NBUF];
+  for (int i = 0; i < NBUF; ++i) w[i] = reinterpret_cast<float*>(static_cast<char*>(base) + off[i]);
+
+  const int io = prob->io_dtype;
+  const int iBt = (int)Bt, iL = (int)L, iH = (int)H, iP = (int)P, iN = (int)N, iG = (int)G;
+  ssd_problem p32 = *prob;
+  p32.io_dtype = SSD_DTYPE_F32;
+  const Dims d = make_dims(&p32, chunk_size);
+  Dims du = d;
+  du.unit_input = 1;
+  const Dims dT = make_dims(&tp, chunk_size);
+  Dims dTu = dT;
+  dTu.unit_input = 1;
+  Timer none;
+  ssd_status r = SSD_OK;
+  auto hip = [&](hipError_t e) {
+    if (r == SSD_OK && e != hipSuccess) r = from_hip(e);
+  };
+  auto fwd = [&](const ssd_problem* pp, const Dims& dd, const float* xx, const float* dtt,
+                 const float* bb, const float* cc, const float* h0, float* yy, float* fin) {
+    if (r == SSD_OK)
+      r = run_unfused(pp, dd, ssd::kPrecFp32, xx, dtt, A, bb, cc, w[ZD], h0, yy, fin, hs, none);
+  };
+  // fp32 copies of the inputs and a zero skip term (the forwards below compute state terms only)
+  hip(ssd::launch_gather(io, x, w[X32], iBt, iL, iH, 1, iP, false, hs));
+  hip(ssd::launch_gather(io, dy, w[DY32], iBt, iL, iH, 1, iP, false, hs));
+  hip(ssd::launch_gather(io, B, w[B32], iBt, iL, iG, 1, iN, false, hs));
+  hip(ssd::launch_gather(io, C, w[C32], iBt, iL, iG, 1, iN, false, hs));
+  if (r == SSD_OK) hip(hipMemsetAsync(w[ZD], 0, (size_t)H * 4, hs));
+  // 1. forward: the state part of y (ys = y - D x) and the final state
+  fwd(&p32, d, w[X32], dt, w[B32], w[C32], initial_state, w[Y0], dfinal ? w[FIN0] : nullptr);
+  // 2. adjoint G_t = dy_t C_t^T + exp(dt_{t+1} A) G_{t+1} as a forward recurrence in reversed
+  //    time (decay of the next token, unit input weight) from dfinal; its readout with B gives
+  //    u_t = G_t B_t, its final state G_0
+  hip(ssd::launch_gather(ssd::kIoF32, w[DY32], w[XR], iBt, iL, iH, 1, iP, true, hs));
+  hip(ssd::launch_gather(ssd::kIoF32, w[C32], w[BR], iBt, iL, iG, 1, iN, true, hs));
+  hip(ssd::launch_gather(ssd::kIoF32, w[B32], w[CR], iBt, iL, iG, 1, iN, true, hs));
+  hip(ssd::launch_dt_shift_rev(dt, w[DTR], iBt, iL, iH, hs));
+  fwd(&p32, du, w[XR], w[DTR], w[BR], w[CR], dfinal, w[UR], dinitial_state ? w[G0] : nullptr);
+  // 3. dC: the transposed state S_t^T (state dim N, head dim P) read out with dy
+  hip(ssd::launch_gather(ssd::kIoF32, w[B32], w[XT], iBt, iL, iH, iH / iG, iN, false, hs));
+  if (initial_state) hip(ssd::launch_transpose_state(initial_state, w[H0T], iBt, iH, iP, iN, hs));
+  fwd(&tp, dT, w[XT], dt, w[X32], w[DY32], initial_state ? w[H0T] : nullptr, w[YT], nullptr);
+  // 4. dB: the transposed adjoint G_t^T in reversed time, read out with x
+  hip(ssd::launch_gather(ssd::kIoF32, w[C32], w[XTR], iBt, iL, iH, iH / iG, iN, true, hs));
+  hip(ssd::launch_gather(ssd::kIoF32, w[X32], w[CTR], iBt, iL, iH, 1, iP, true, hs));
+  if (dfinal) hip(ssd::launch_transpose_state(dfinal, w[DFT], iBt, iH, iP, iN, hs));
+  fwd(&tp, dTu, w[XTR], w[DTR], w[XR], w[CTR], dfinal ? w[DFT] : nullptr, w[YTR], nullptr);
+  // 5. the gradients
+  hip(ssd::launch_bwd_pointwise(io, x, dy, w[UR], w[Y0], dt, D, dx, w[Q], w[XU], w[DYX], iBt, iL,
+                                iH, iP, hs));
+  if (dfinal) hip(ssd::launch_state_dot(dfinal, w[FIN0], w[FT], iBt, iH, iP * iN, hs));
+  hip(ssd::launch_bwd_scan(w[Q], w[XU], w[DYX], dt, A, dfinal ? w[FT] : nullptr, ddt, w[PA],
+                           w[PD], iBt, iL, iH, hs));
+  hip(ssd::launch_sum_batch(w[PA], w[PD], dA, dD, iBt, iH, hs));
+  hip(ssd::launch_group_sums(w[YTR], w[YT], dt, dB, dC, iBt, iL, iH, iG, iN, hs));
+  if (dinitial_state)
+    hip(ssd::launch_scale_state(w[G0], dt, A, dinitial_state, iBt, iL, iH, iP * iN, hs));
+  const hipError_t ef = hipFreeAsync(base, hs);
+  if (r != SSD_OK) return r;
+  return from_hip(ef);
+}
+
 ssd_status ssd_step(const ssd_problem* prob, const void* x, const float* dt, const float* A,
                     const void* B, const void* C, const float* D, const float* state_in,
                     float* state_out, void* y, void* stream) {

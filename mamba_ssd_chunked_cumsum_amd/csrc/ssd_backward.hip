@@ -1,0 +1,305 @@
+// Helper kernels of the SSD backward (ssd_backward in ssd_api.cpp). Library-internal.
+//
+// The backward reuses the forward's chunked kernels on rearranged inputs (see ssd_api.cpp); what
+// is here moves data between those calls (reversal in time, group -> head broadcast, state
+// transposes, fp32 conversion) and combines their outputs into the gradients: elementwise terms,
+// the reverse cumulative sum that gives the decay gradients, and sums over heads and batch. Every
+// kernel is memory-bound and bounds-checked per element.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+namespace {
+
+template <typename IO>
+__global__ __launch_bounds__(256) void k_gather(const IO* __restrict__ in, float* __restrict__ out,
+                                                int Bt, int L, int K, int rep, int E, int rev) {
+  const int64_t total = (int64_t)Bt * L * K * E;
+  const int Kin = K / rep;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int e = (int)(i % E);
+    int64_t r = i / E;
+    const int k = (int)(r % K);
+    r /= K;
+    const int t = (int)(r % L);
+    const int b = (int)(r / L);
+    const int ts = rev ? L - 1 - t : t;
+    out[i] = Io<IO>::load(in, (((int64_t)b * L + ts) * Kin + k / rep) * E + e);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dt_shift_rev(const float* __restrict__ dt,
+                                                      float* __restrict__ dtr, int Bt, int L,
+                                                      int H) {
+  const int64_t total = (int64_t)Bt * L * H;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int h = (int)(i % H);
+    const int t = (int)((i / H) % L);
+    const int b = (int)(i / ((int64_t)H * L));
+    dtr[i] = t == 0 ? 0.f : dt[((int64_t)b * L + (L - t)) * H + h];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_transpose_state(const float* __restrict__ in,
+                                                         float* __restrict__ out, int BH, int P,
+                                                         int N) {
+  const int64_t total = (int64_t)BH * P * N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int p = (int)(i % P);  // output index [bh, n, p]
+    const int n = (int)((i / P) % N);
+    const int64_t bh = i / ((int64_t)P * N);
+    out[i] = in[(bh * P + p) * N + n];
+  }
+}
+
+// Sum over the 64 lanes of a wave (every lane gets the total).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// One wave per (b, t, h); lanes over p (strided when P > 64).
+template <typename IO>
+__global__ __launch_bounds__(256) void k_bwd_pointwise(
+    const IO* __restrict__ x, const IO* __restrict__ dy, const float* __restrict__ ur,
+    const float* __restrict__ ys, const float* __restrict__ dt, const float* __restrict__ D,
+    float* __restrict__ dx, float* __restrict__ q, float* __restrict__ xu,
+    float* __restrict__ dyx, int Bt, int L, int H, int P) {
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (unit >= (int64_t)Bt * L * H) return;  // wave-uniform
+  const int h = (int)(unit % H);
+  const int t = (int)((unit / H) % L);
+  const int b = (int)(unit / ((int64_t)H * L));
+  const float dtv = dt[unit], dh = D[h];
+  const int64_t row = unit * P;                                          // [b, t, h, :]
+  const int64_t rrow = (((int64_t)b * L + (L - 1 - t)) * H + h) * P;    // reversed time
+  float s_dyys = 0.f, s_xu = 0.f, s_dyx = 0.f;
+  for (int p = lane; p < P; p += 64) {
+    const float xv = Io<IO>::load(x, row + p), dyv = Io<IO>::load(dy, row + p);
+    const float u = ur[rrow + p];
+    dx[row + p] = dh * dyv + dtv * u;
+    s_dyys += dyv * ys[row + p];
+    s_xu += xv * u;
+    s_dyx += dyv * xv;
+  }
+  s_dyys = wave_sum(s_dyys);
+  s_xu = wave_sum(s_xu);
+  s_dyx = wave_sum(s_dyx);
+  if (lane == 0) {
+    q[unit] = s_dyys - dtv * s_xu;
+    xu[unit] = s_xu;
+    dyx[unit] = s_dyx;
+  }
+}
+
+// One 256-thread block per (b, h).
+__global__ __launch_bounds__(256) void k_state_dot(const float* __restrict__ a,
+                                                   const float* __restrict__ c,
+                                                   float* __restrict__ out, int PN) {
+  __shared__ float part[4];
+  const int64_t base = (int64_t)blockIdx.x * PN;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < PN; i += 256) s += a[base + i] * c[base + i];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// One 256-thread block per (b, h): the sequence walked backwards in tiles of 256 tokens, each
+// tile's suffix sums by a block scan, plus the running total of the tiles after it.
+__global__ __launch_bounds__(256) void k_bwd_scan(const float* __restrict__ q,
+                                                  const float* __restrict__ xu,
+                                                  const float* __restrict__ dyx,
+                                                  const float* __restrict__ dt,
+                                                  const float* __restrict__ A,
+                                                  const float* __restrict__ fterm,
+                                                  float* __restrict__ ddt, float* __restrict__ pa,
+                                                  float* __restrict__ pd, int L, int H) {
+  __shared__ float wtot[4];
+  __shared__ float red[2][4];
+  const int bh = blockIdx.x, h = bh % H, b = bh / H;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float a = A[h];
+  float carry = fterm ? fterm[bh] : 0.f;  // sum of q over the tokens after the current tile
+  float sa = 0.f, sd = 0.f;
+  const int ntile = (L + 255) / 256;
+  for (int k = ntile - 1; k >= 0; --k) {
+    // thread j of the tile holds token t = 256 k + 255 - j (reversed, so a prefix scan over j
+    // is the suffix sum over t)
+    const int t = 256 * k + 255 - threadIdx.x;
+    const int64_t i = ((int64_t)b * L + t) * H + h;
+    const bool ok = t < L;
+    const float v = ok ? q[i] : 0.f;
+    const float incl = wave_inclusive_scan(v);
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    float before = 0.f;
+    for (int w = 0; w < wave; ++w) before += wtot[w];
+    const float tile_total = (wtot[0] + wtot[1]) + (wtot[2] + wtot[3]);
+    const float da = carry + before + incl;
+    if (ok) {
+      ddt[i] = a * da + xu[i];
+      sa += dt[i] * da;
+      sd += dyx[i];
+    }
+    carry += tile_total;
+    __syncthreads();  // wtot is rewritten by the next tile
+  }
+  sa = wave_sum(sa);
+  sd = wave_sum(sd);
+  if (lane == 0) {
+    red[0][wave] = sa;
+    red[1][wave] = sd;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    pa[bh] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    pd[bh] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_sum_batch(const float* __restrict__ pa,
+                                                   const float* __restrict__ pd,
+                                                   float* __restrict__ dA, float* __restrict__ dD,
+                                                   int Bt, int H) {
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  if (h >= H) return;
+  float sa = 0.f, sd = 0.f;
+  for (int b = 0; b < Bt; ++b) {
+    sa += pa[b * H + h];
+    sd += pd[b * H + h];
+  }
+  dA[h] = sa;
+  dD[h] = sd;
+}
+
+__global__ __launch_bounds__(256) void k_group_sums(const float* __restrict__ vb,
+                                                    const float* __restrict__ vc,
+                                                    const float* __restrict__ dt,
+                                                    float* __restrict__ dB, float* __restrict__ dC,
+                                                    int Bt, int L, int H, int G, int N) {
+  const int64_t total = (int64_t)Bt * L * G * N;
+  const int hpg = H / G;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int n = (int)(i % N);
+    const int g = (int)((i / N) % G);
+    const int t = (int)((i / ((int64_t)N * G)) % L);
+    const int b = (int)(i / ((int64_t)N * G * L));
+    float sb = 0.f, sc = 0.f;
+    for (int k = 0; k < hpg; ++k) {
+      const int h = g * hpg + k;
+      const int64_t f = ((int64_t)b * L + t) * H + h;
+      const int64_t r = ((int64_t)b * L + (L - 1 - t)) * H + h;
+      sb += dt[f] * vb[r * N + n];
+      sc += vc[f * N + n];
+    }
+    dB[i] = sb;
+    dC[i] = sc;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_scale_state(const float* __restrict__ g0,
+                                                     const float* __restrict__ dt,
+                                                     const float* __restrict__ A,
+                                                     float* __restrict__ out, int Bt, int L,
+                                                     int H, int PN) {
+  const int64_t total = (int64_t)Bt * H * PN;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t bh = i / PN;
+    const int h = (int)(bh % H);
+    const int b = (int)(bh / H);
+    out[i] = __expf(dt[(int64_t)b * L * H + h] * A[h]) * g0[i];
+  }
+}
+
+int grid_for(int64_t total) {
+  const int64_t blocks = (total + 255) / 256;
+  return (int)(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536);
+}
+
+}  // namespace
+
+hipError_t launch_gather(int io, const void* in, float* out, int Bt, int L, int K, int rep, int E,
+                         bool rev, hipStream_t s) {
+  const int g = grid_for((int64_t)Bt * L * K * E);
+  if (io == kIoBf16)
+    hipLaunchKernelGGL(k_gather<u16>, dim3(g), dim3(256), 0, s, (const u16*)in, out, Bt, L, K,
+                       rep, E, (int)rev);
+  else
+    hipLaunchKernelGGL(k_gather<float>, dim3(g), dim3(256), 0, s, (const float*)in, out, Bt, L,
+                       K, rep, E, (int)rev);
+  return hipGetLastError();
+}
+
+hipError_t launch_dt_shift_rev(const float* dt, float* dtr, int Bt, int L, int H, hipStream_t s) {
+  hipLaunchKernelGGL(k_dt_shift_rev, dim3(grid_for((int64_t)Bt * L * H)), dim3(256), 0, s, dt,
+                     dtr, Bt, L, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_state(const float* in, float* out, int Bt, int H, int P, int N,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(k_transpose_state, dim3(grid_for((int64_t)Bt * H * P * N)), dim3(256), 0, s,
+                     in, out, Bt * H, P, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pointwise(int io, const void* x, const void* dy, const float* ur,
+                                const float* ys, const float* dt, const float* D, float* dx,
+                                float* q, float* xu, float* dyx, int Bt, int L, int H, int P,
+                                hipStream_t s) {
+  const int64_t units = (int64_t)Bt * L * H;
+  const dim3 grid((unsigned)((units + 3) / 4));
+  if (io == kIoBf16)
+    hipLaunchKernelGGL(k_bwd_pointwise<u16>, grid, dim3(256), 0, s, (const u16*)x,
+                       (const u16*)dy, ur, ys, dt, D, dx, q, xu, dyx, Bt, L, H, P);
+  else
+    hipLaunchKernelGGL(k_bwd_pointwise<float>, grid, dim3(256), 0, s, (const float*)x,
+                       (const float*)dy, ur, ys, dt, D, dx, q, xu, dyx, Bt, L, H, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_dot(const float* dfinal, const float* fin, float* fterm, int Bt, int H,
+                            int PN, hipStream_t s) {
+  hipLaunchKernelGGL(k_state_dot, dim3(Bt * H), dim3(256), 0, s, dfinal, fin, fterm, PN);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_scan(const float* q, const float* xu, const float* dyx, const float* dt,
+                           const float* A, const float* fterm, float* ddt, float* pa, float* pd,
+                           int Bt, int L, int H, hipStream_t s) {
+  hipLaunchKernelGGL(k_bwd_scan, dim3(Bt * H), dim3(256), 0, s, q, xu, dyx, dt, A, fterm, ddt, pa,
+                     pd, L, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_batch(const float* pa, const float* pd, float* dA, float* dD, int Bt, int H,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(k_sum_batch, dim3((H + 255) / 256), dim3(256), 0, s, pa, pd, dA, dD, Bt, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_sums(const float* vb, const float* vc, const float* dt, float* dB,
+                             float* dC, int Bt, int L, int H, int G, int N, hipStream_t s) {
+  hipLaunchKernelGGL(k_group_sums, dim3(grid_for((int64_t)Bt * L * G * N)), dim3(256), 0, s, vb,
+                     vc, dt, dB, dC, Bt, L, H, G, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_state(const float* g0, const float* dt, const float* A, float* dh0,
+                              int Bt, int L, int H, int PN, hipStream_t s) {
+  hipLaunchKernelGGL(k_scale_state, dim3(grid_for((int64_t)Bt * H * PN)), dim3(256), 0, s, g0, dt,
+                     A, dh0, Bt, L, H, PN);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

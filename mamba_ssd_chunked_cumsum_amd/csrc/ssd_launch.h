@@ -14,6 +14,9 @@ struct Dims {
   const float* dt_bias = nullptr;
   int dt_softplus = 0;
   float dt_min = 0.f, dt_max = 0.f;
+  // unfused path only (the backward's adjoint recurrences): the input term is x B^T instead of
+  // dt x B^T, while dt still sets the decay exp(dt A)
+  int unit_input = 0;
 };
 
 constexpr int kIoF32 = 0, kIoBf16 = 1;
@@ -54,6 +57,40 @@ hipError_t launch_run_state(const Dims& d, const FusedPlan& fp, const void* x, c
 hipError_t launch_fused_scan(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
                              const void* C, const float* dt, const float* A, const float* D,
                              const float* h_run, void* y, hipStream_t s);
+
+// backward helpers (ssd_backward.hip); all outputs fp32, layouts row-major.
+// out[b, t, k, e] = in[b, rev ? L - 1 - t : t, k / rep, e]   (in: [Bt, L, K / rep, E], io dtype)
+hipError_t launch_gather(int io, const void* in, float* out, int Bt, int L, int K, int rep, int E,
+                         bool rev, hipStream_t s);
+// dtr[b, t, h] = t == 0 ? 0 : dt[b, L - t, h]
+hipError_t launch_dt_shift_rev(const float* dt, float* dtr, int Bt, int L, int H, hipStream_t s);
+// out[b, h, n, p] = in[b, h, p, n]
+hipError_t launch_transpose_state(const float* in, float* out, int Bt, int H, int P, int N,
+                                  hipStream_t s);
+// per (b, t, h): dx = D dy + dt u; q = dy . ys - dt x . u; xu = x . u; dyx = dy . x, where
+// u = ur[b, L - 1 - t, h, :] (the adjoint readout, stored in reversed time)
+hipError_t launch_bwd_pointwise(int io, const void* x, const void* dy, const float* ur,
+                                const float* ys, const float* dt, const float* D, float* dx,
+                                float* q, float* xu, float* dyx, int Bt, int L, int H, int P,
+                                hipStream_t s);
+// fterm[b, h] = <dfinal[b, h], fin[b, h]> (0 when dfinal is null)
+hipError_t launch_state_dot(const float* dfinal, const float* fin, float* fterm, int Bt, int H,
+                            int PN, hipStream_t s);
+// per (b, h): da_t = sum_{s >= t} q_s + fterm; ddt = A da + xu; per-(b, h) partial sums of
+// dt da (for dA) and of dyx (for dD)
+hipError_t launch_bwd_scan(const float* q, const float* xu, const float* dyx, const float* dt,
+                           const float* A, const float* fterm, float* ddt, float* pa, float* pd,
+                           int Bt, int L, int H, hipStream_t s);
+// dA[h] = sum_b pa[b, h]; dD[h] = sum_b pd[b, h]
+hipError_t launch_sum_batch(const float* pa, const float* pd, float* dA, float* dD, int Bt, int H,
+                            hipStream_t s);
+// dB[b, t, g, n] = sum_{h in g} dt[b, t, h] vb[b, L - 1 - t, h, n];
+// dC[b, t, g, n] = sum_{h in g} vc[b, t, h, n]
+hipError_t launch_group_sums(const float* vb, const float* vc, const float* dt, float* dB,
+                             float* dC, int Bt, int L, int H, int G, int N, hipStream_t s);
+// dh0[b, h] = exp(dt[b, 0, h] A[h]) g0[b, h]
+hipError_t launch_scale_state(const float* g0, const float* dt, const float* A, float* dh0,
+                              int Bt, int L, int H, int PN, hipStream_t s);
 
 // single-token step: state [Bt, H, P, N] fp32 (s_out may equal s_in); x, y [Bt, H, P];
 // dt [Bt, H]; B, C [Bt, G, N]

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const float* __restrict__ 
       const int i = lane * E + e;
       if (e < E && i < d.Q) {
         Acs[base + i] = (i < q) ? excl + loc[e] : vlast;
-        dtc[base + i] = tile[i][hh];
+        dtc[base + i] = (d.unit_input && i < q) ? 1.f : tile[i][hh];
       }
     }
   }

@@ -24,7 +24,7 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 # Symbols include/ssd.h declares.
 EXPORTS = ("ssd_forward", "ssd_forward_ex", "ssd_chunk_cumsum", "ssd_bmm_chunk",
            "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_workspace_sizes",
-           "ssd_step", "ssd_status_string", "ssd_version")
+           "ssd_step", "ssd_backward", "ssd_status_string", "ssd_version")
 
 
 class SSDProblem(ctypes.Structure):
@@ -79,6 +79,8 @@ def load():
         "ssd_chunk_scan": [P, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, O],
         "ssd_workspace_sizes": [P, i64, ctypes.POINTER(ctypes.c_int64)],
         "ssd_step": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "ssd_backward": [P, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                         vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -235,6 +237,37 @@ def step(state, x, dt, A, B, C, D, *, out_state=None, out=None):
                          _ptr(D), _ptr(state), _ptr(so), _ptr(y), _stream(x))
     _check(st, "ssd_step")
     return y, so
+
+
+def backward(x, dt, A, B, C, D, dy, chunk_size, initial_state=None, dfinal=None, *,
+             want_initial_grad=True):
+    """Gradients of the forward for output gradient dy (x's dtype and shape) and final-state
+    gradient dfinal ([Bt, H, P, N] f32, or None for zero). Returns a dict of float32 tensors:
+    dx, ddt, dA, dB, dC, dD and dinitial_state (None unless want_initial_grad)."""
+    dev = x.device
+    _require(x, "x", device=dev)
+    for n, t in (("B", B), ("C", C), ("dy", dy)):
+        _require(t, n, x.dtype, dev)
+    for n, t in (("dt", dt), ("A", A), ("D", D), ("initial_state", initial_state),
+                 ("dfinal", dfinal)):
+        _require(t, n, torch.float32, dev)
+    if tuple(dy.shape) != tuple(x.shape):
+        raise ValueError(f"dy has shape {tuple(dy.shape)}, expected {tuple(x.shape)}")
+    prob = _problem_from(x, B)
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dx=torch.empty((Bt, L, H, P), **f32), ddt=torch.empty((Bt, L, H), **f32),
+               dA=torch.empty((H,), **f32), dB=torch.empty((Bt, L, G, N), **f32),
+               dC=torch.empty((Bt, L, G, N), **f32), dD=torch.empty((H,), **f32),
+               dinitial_state=torch.empty((Bt, H, P, N), **f32) if want_initial_grad else None)
+    st = load().ssd_backward(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                             _ptr(D), int(chunk_size), _ptr(initial_state), _ptr(dy),
+                             _ptr(dfinal), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]),
+                             _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                             _ptr(out["dinitial_state"]), _stream(x))
+    _check(st, "ssd_backward")
+    return out
 
 
 # ---- stages of the unfused path ------------------------------------------------------------------

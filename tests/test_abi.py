@@ -302,3 +302,46 @@ def test_dt_bias_may_not_overlap_outputs():
     ptrs = [addr(i) for i in range(9)]
     assert call_forward(good_problem(), ptrs=ptrs, opts=dt_opts(dt_bias=ptrs[7].value)) == 1
     assert call_forward(good_problem(), ptrs=ptrs, opts=dt_opts(dt_bias=ptrs[8].value)) == 1
+
+
+# ---- ssd_backward -----------------------------------------------------------------------------
+
+def call_backward(prob, Q=64, ptrs=None):
+    # x, dt, A, B, C, D, h0, dy, dfinal, dx, ddt, dA, dB, dC, dD, dh0
+    a = [addr(i) for i in range(16)] if ptrs is None else ptrs
+    lib = libssd.load()
+    return lib.ssd_backward(ctypes.byref(prob), a[0], a[1], a[2], a[3], a[4], a[5], Q, a[6],
+                            a[7], a[8], a[9], a[10], a[11], a[12], a[13], a[14], a[15], None)
+
+
+@no_gpu
+def test_backward_valid_request_reports_no_device():
+    assert call_backward(good_problem()) == libssd.SSD_ERR_NO_DEVICE
+    ptrs = [addr(i) for i in range(16)]
+    ptrs[6] = ptrs[8] = ptrs[15] = None          # initial state, dfinal, its gradient: optional
+    assert call_backward(good_problem(), ptrs=ptrs) == libssd.SSD_ERR_NO_DEVICE
+
+
+@no_gpu
+@pytest.mark.parametrize("which", [0, 1, 2, 3, 4, 5, 7, 9, 10, 11, 12, 13, 14])
+def test_backward_null_required_pointer(which):
+    ptrs = [addr(i) for i in range(16)]
+    ptrs[which] = None
+    assert call_backward(good_problem(), ptrs=ptrs) == libssd.SSD_ERR_INVALID_ARGUMENT
+
+
+@no_gpu
+@pytest.mark.parametrize("out,alias_of", [(9, 0), (9, 7), (12, 3), (13, 4), (11, 2), (15, 6),
+                                          (10, 9), (13, 12)])
+def test_backward_output_aliasing_rejected(out, alias_of):
+    ptrs = [addr(i) for i in range(16)]
+    ptrs[out] = ptrs[alias_of]
+    assert call_backward(good_problem(), ptrs=ptrs) == libssd.SSD_ERR_INVALID_ARGUMENT
+
+
+@no_gpu
+def test_backward_misaligned_and_unsupported():
+    ptrs = [addr(i) for i in range(16)]
+    ptrs[7] = addr(7, 4)
+    assert call_backward(good_problem(), ptrs=ptrs) == libssd.SSD_ERR_INVALID_ARGUMENT
+    assert call_backward(good_problem(headdim=24)) == libssd.SSD_ERR_UNSUPPORTED

@@ -1,0 +1,112 @@
+"""ssd_backward on the GPU against the float64 backward oracle, element by element.
+
+The GPU backward computes in fp32 throughout (its four chunked recurrences run the fp32 matrix
+cores; the inputs are exact in fp32, also for bf16 io), so each gradient is held to
+max |g - r| <= TOL * max|r| over the tensor: fp32 rounding (2^-24 per operation) accumulated over
+a few hundred terms of mixed sign leaves a few 1e-6; TOL = 1e-4 keeps a margin for the decay
+gradients, which are long reverse sums of such terms.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mamba_ssd_chunked_cumsum_amd as ssd
+from oracle.backward import ssd_backward as oracle_backward
+
+from gpu_util import DEV, note
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+# Bt, L, H, P, N, G, chunk, io, h0, dfinal
+CASES = [
+    (1, 64, 2, 16, 16, 1, 16, "f32", False, False),
+    (2, 100, 4, 32, 16, 2, 32, "f32", True, True),     # ragged last chunk
+    (1, 48, 3, 16, 32, 3, 16, "f32", True, False),     # one group per head
+    (1, 96, 2, 64, 128, 1, 64, "bf16", True, True),    # the workloads' head shape
+    (2, 130, 8, 64, 64, 2, 64, "bf16", False, True),
+    (1, 1, 2, 16, 16, 1, 16, "f32", True, True),       # a single token
+]
+
+
+def _case_id(c):
+    return f"{c[0]}x{c[1]}x{c[2]}x{c[3]}x{c[4]}_g{c[5]}_q{c[6]}_{c[7]}" + (
+        "_h0" if c[8] else "") + ("_df" if c[9] else "")
+
+
+def _bf16_exact(a):
+    return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def _inputs(rng, Bt, L, H, P, N, G, io, h0, df):
+    f32 = lambda a: a.astype(np.float32)
+    inp = dict(
+        x=f32(rng.standard_normal((Bt, L, H, P))),
+        dt=f32(rng.uniform(1e-3, 0.3, (Bt, L, H))),
+        A=f32(-rng.uniform(0.5, 4.0, H)),
+        B=f32(rng.standard_normal((Bt, L, G, N))),
+        C=f32(rng.standard_normal((Bt, L, G, N))),
+        D=f32(rng.uniform(0.5, 1.5, H)),
+        initial_state=f32(rng.standard_normal((Bt, H, P, N))) if h0 else None,
+    )
+    dy = f32(rng.standard_normal((Bt, L, H, P)))
+    dfinal = f32(rng.standard_normal((Bt, H, P, N))) if df else None
+    if io == "bf16":
+        for k in ("x", "B", "C"):
+            inp[k] = _bf16_exact(inp[k])
+        dy = _bf16_exact(dy)
+    return inp, dy, dfinal
+
+
+def _dev(a, io, io_tensor):
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return t.to(torch.bfloat16) if (io_tensor and io == "bf16") else t
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_backward_matches_oracle(case):
+    Bt, L, H, P, N, G, Q, io, h0, df = case
+    rng = np.random.default_rng(100 + L + 7 * H + N)
+    inp, dy, dfinal = _inputs(rng, Bt, L, H, P, N, G, io, h0, df)
+    note(f"backward {_case_id(case)}")
+    d = {k: _dev(v, io, k in ("x", "B", "C")) for k, v in inp.items()}
+    g = ssd.backward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], _dev(dy, io, True), Q,
+                     d["initial_state"], _dev(dfinal, io, False))
+    torch.cuda.synchronize()
+    ref = oracle_backward(**inp, dy=dy, dfinal=dfinal)
+    for k, r in ref.items():
+        gk = g[k].cpu().numpy().astype(np.float64)
+        err = float(np.max(np.abs(gk - r)))
+        scale = float(np.max(np.abs(r)))
+        print(f"{k}: max|g - r| = {err:.3e}, max|r| = {scale:.3e}, ratio {err / max(scale, 1e-30):.2e}")
+        assert np.all(np.isfinite(gk)), k
+        assert err <= TOL * max(scale, 1e-30), f"{k}: {err:.3e} > {TOL} * {scale:.3e}"
+
+
+def test_backward_of_forward_loss_matches_directional_derivative():
+    """Consistency of the GPU backward with the GPU forward: for a random direction v in x,
+    <dL/dx, v> equals (L(x + e v) - L(x - e v)) / 2e with L = sum(dy * y), both from libssd
+    (fp32 io, so the finite difference is not swamped by output rounding)."""
+    rng = np.random.default_rng(5)
+    Bt, L, H, P, N, G, Q = 1, 80, 2, 32, 32, 1, 32
+    inp, dy, _ = _inputs(rng, Bt, L, H, P, N, G, "f32", True, False)
+    d = {k: _dev(v, "f32", False) for k, v in inp.items()}
+    dyt = _dev(dy, "f32", False)
+    note("backward directional derivative")
+    g = ssd.backward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], dyt, Q, d["initial_state"])
+    v = torch.from_numpy(rng.standard_normal(inp["x"].shape).astype(np.float32)).to(DEV)
+    eps = 1.0  # y is linear in x: the central difference is exact up to rounding
+
+    def loss(xx):
+        y, _ = ssd.forward(xx, d["dt"], d["A"], d["B"], d["C"], d["D"], Q, d["initial_state"],
+                           want_final=False)
+        return float(torch.sum(dyt.double() * y.double()))
+
+    fd = (loss(d["x"] + eps * v) - loss(d["x"] - eps * v)) / (2 * eps)
+    an = float(torch.sum(g["dx"].double() * v.double()))
+    torch.cuda.synchronize()
+    assert abs(fd - an) <= 1e-4 * max(1.0, abs(an)), (fd, an)
