@@ -129,11 +129,11 @@ def cpu_baseline(inp, shape, y_gpu, f_gpu, max_seconds: float):
 PROFILE_COMMANDS = [
     "python3 bench.py --steps 20 --warmup 3 > DIR/bench.json",
     "rocprofv3 --kernel-trace --stats -d DIR/prof_kt -o kt --output-format csv -- "
-    "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+    "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-backward",
     "rocprofv3 --pmc FETCH_SIZE -d DIR/prof_fetch -o fetch --output-format csv -- "
-    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --copy-calibration",
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-backward --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE -d DIR/prof_write -o write --output-format csv -- "
-    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --copy-calibration",
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-backward --copy-calibration",
     "python3 bench.py --summarize-profiles DIR",
 ]
 
@@ -284,6 +284,55 @@ def decode_bench(shape, dev, layers: int = 64, rounds: int = 5) -> dict:
                     "from a HIP graph"}
 
 
+def backward_bench(shape, d, flush, flush_out, steps: int = 3) -> dict:
+    """ssd_backward at the workload's shape: output gradient dy of x's dtype and a final-state
+    gradient, cold cache before every call. Reports ms per call and tokens/s; the bytes it must
+    move (x, dy, B, C, dt in; dx, ddt, dB, dC out in fp32) and the flops of its four fp32
+    chunked recurrences give its roofline (fp32 matrix cores: 157.3 TFLOP/s)."""
+    import numpy as np
+    import torch
+
+    from mamba_ssd_chunked_cumsum_amd import libssd
+
+    x = d["x"]
+    g = torch.Generator(device=x.device).manual_seed(11)
+    dy = torch.randn(x.shape, device=x.device, generator=g).to(x.dtype)
+    dfinal = torch.randn((shape.batch, shape.nheads, shape.headdim, shape.dstate),
+                         device=x.device, generator=g)
+
+    def call():
+        return libssd.backward(x, d["dt"], d["A"], d["B"], d["C"], d["D"], dy, shape.chunk_size,
+                               d["initial_state"], dfinal)
+
+    call()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        if flush is not None:
+            torch.sum(flush, dim=0, dtype=torch.int64, out=flush_out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out = call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+        del out
+    t = float(np.mean(ms)) if ms else float("nan")
+    s_io = 2 if shape.io == "bf16" else 4
+    tokens = shape.batch * shape.seqlen
+    H, P, N, G = shape.nheads, shape.headdim, shape.dstate, shape.ngroups
+    nbytes = tokens * (H * P * (2 * s_io + 4) + 2 * G * N * (s_io + 4) + 2 * H * 4)
+    alg = algorithmic(shape, d["initial_state"] is not None)
+    flops = 4 * alg["flops"]  # four chunked recurrences of the forward's size
+    t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (FP32_PEAK_TFLOPS * 1e12))
+    return {"ms_per_call": t, "tokens_per_s": tokens / (t / 1e3), "bytes": nbytes,
+            "flops": flops, "bound": "fp32 matrix cores", "t_roofline_us": t_roof * 1e6,
+            "frac": t_roof / (t / 1e3),
+            "note": "ssd_backward (dx, ddt, dA, dB, dC, dD, initial-state gradient) from dy and "
+                    "a final-state gradient; four fp32 chunked recurrences plus elementwise "
+                    "kernels"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,6 +347,8 @@ def main():
                     help="skip the cache sweep before steps (inputs may then be served from the "
                          "256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the timed ssd_backward calls reported under 'backward'")
     ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 output under DIR and exit")
@@ -460,6 +511,8 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "decode_step": decode_bench(shape, dev),
+        "backward": None if args.no_backward else backward_bench(
+            shape, d, flush, flush_out if flush is not None else None),
     }
     print(json.dumps(out), flush=True)
 

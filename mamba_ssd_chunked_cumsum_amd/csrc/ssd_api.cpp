@@ -415,7 +415,7 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   enum { X32, DY32, B32, C32, Y0, FIN0, XR, BR, CR, DTR, UR, G0, XT, YT, H0T, XTR, CTR, YTR, DFT,
          Q, XU, DYX, FT, PA, PD, ZD, NBUF };
   const int64_t el[NBUF] = {nx, nx, nb, nb, nx, ns, nx, nb, nb, nd, nx, ns, nt, nt, ns,
-                            nt, nx, nt, ns, nd, nd, nd, Bt * H, Bt * H, Bt * H, H};
+                            nt, nx, nt, ns, nd, nd, nd, Bt * H, 2 * Bt * H, 2 * Bt * H, H};
   int64_t off[NBUF], total = 0;
   for (int i = 0; i < NBUF; ++i) {
     off[i] = total;
@@ -475,9 +475,11 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   hip(ssd::launch_bwd_pointwise(io, x, dy, w[UR], w[Y0], dt, D, dx, w[Q], w[XU], w[DYX], iBt, iL,
                                 iH, iP, hs));
   if (dfinal) hip(ssd::launch_state_dot(dfinal, w[FIN0], w[FT], iBt, iH, iP * iN, hs));
-  hip(ssd::launch_bwd_scan(w[Q], w[XU], w[DYX], dt, A, dfinal ? w[FT] : nullptr, ddt, w[PA],
-                           w[PD], iBt, iL, iH, hs));
-  hip(ssd::launch_sum_batch(w[PA], w[PD], dA, dD, iBt, iH, hs));
+  double* pa = reinterpret_cast<double*>(w[PA]);
+  double* pd = reinterpret_cast<double*>(w[PD]);
+  hip(ssd::launch_bwd_scan(w[Q], w[XU], w[DYX], dt, A, dfinal ? w[FT] : nullptr, ddt, pa, pd, iBt,
+                           iL, iH, hs));
+  hip(ssd::launch_sum_batch(pa, pd, dA, dD, iBt, iH, hs));
   hip(ssd::launch_group_sums(w[YTR], w[YT], dt, dB, dC, iBt, iL, iH, iG, iN, hs));
   if (dinitial_state)
     hip(ssd::launch_scale_state(w[G0], dt, A, dinitial_state, iBt, iL, iH, iP * iN, hs));

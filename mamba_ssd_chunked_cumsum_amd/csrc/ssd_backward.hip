@@ -57,9 +57,21 @@ __global__ __launch_bounds__(256) void k_transpose_state(const float* __restrict
 }
 
 // Sum over the 64 lanes of a wave (every lane gets the total).
-__device__ __forceinline__ float wave_sum(float v) {
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Inclusive prefix sum over the wave's lanes, in double.
+__device__ __forceinline__ double wave_scan_f64(double v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double t = __shfl_up(v, off, kWave);
+    if (lane >= off) v += t;
+  }
   return v;
 }
 
@@ -113,22 +125,24 @@ __global__ __launch_bounds__(256) void k_state_dot(const float* __restrict__ a,
 }
 
 // One 256-thread block per (b, h): the sequence walked backwards in tiles of 256 tokens, each
-// tile's suffix sums by a block scan, plus the running total of the tiles after it.
+// tile's suffix sums by a block scan, plus the running total of the tiles after it. The sums run
+// in double: da_t sums up to L terms of mixed sign and dA sums dt_t da_t over batch and time, so
+// fp32 accumulation would lose digits that the gradients keep.
 __global__ __launch_bounds__(256) void k_bwd_scan(const float* __restrict__ q,
                                                   const float* __restrict__ xu,
                                                   const float* __restrict__ dyx,
                                                   const float* __restrict__ dt,
                                                   const float* __restrict__ A,
                                                   const float* __restrict__ fterm,
-                                                  float* __restrict__ ddt, float* __restrict__ pa,
-                                                  float* __restrict__ pd, int L, int H) {
-  __shared__ float wtot[4];
-  __shared__ float red[2][4];
+                                                  float* __restrict__ ddt, double* __restrict__ pa,
+                                                  double* __restrict__ pd, int L, int H) {
+  __shared__ double wtot[4];
+  __shared__ double red[2][4];
   const int bh = blockIdx.x, h = bh % H, b = bh / H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const float a = A[h];
-  float carry = fterm ? fterm[bh] : 0.f;  // sum of q over the tokens after the current tile
-  float sa = 0.f, sd = 0.f;
+  const double a = A[h];
+  double carry = fterm ? (double)fterm[bh] : 0.0;  // sum of q over the tokens after the tile
+  double sa = 0.0, sd = 0.0;
   const int ntile = (L + 255) / 256;
   for (int k = ntile - 1; k >= 0; --k) {
     // thread j of the tile holds token t = 256 k + 255 - j (reversed, so a prefix scan over j
@@ -136,18 +150,18 @@ __global__ __launch_bounds__(256) void k_bwd_scan(const float* __restrict__ q,
     const int t = 256 * k + 255 - threadIdx.x;
     const int64_t i = ((int64_t)b * L + t) * H + h;
     const bool ok = t < L;
-    const float v = ok ? q[i] : 0.f;
-    const float incl = wave_inclusive_scan(v);
+    const double v = ok ? (double)q[i] : 0.0;
+    const double incl = wave_scan_f64(v);
     if (lane == 63) wtot[wave] = incl;
     __syncthreads();
-    float before = 0.f;
+    double before = 0.0;
     for (int w = 0; w < wave; ++w) before += wtot[w];
-    const float tile_total = (wtot[0] + wtot[1]) + (wtot[2] + wtot[3]);
-    const float da = carry + before + incl;
+    const double tile_total = (wtot[0] + wtot[1]) + (wtot[2] + wtot[3]);
+    const double da = carry + before + incl;
     if (ok) {
-      ddt[i] = a * da + xu[i];
-      sa += dt[i] * da;
-      sd += dyx[i];
+      ddt[i] = (float)(a * da + (double)xu[i]);
+      sa += (double)dt[i] * da;
+      sd += (double)dyx[i];
     }
     carry += tile_total;
     __syncthreads();  // wtot is rewritten by the next tile
@@ -165,19 +179,19 @@ __global__ __launch_bounds__(256) void k_bwd_scan(const float* __restrict__ q,
   }
 }
 
-__global__ __launch_bounds__(256) void k_sum_batch(const float* __restrict__ pa,
-                                                   const float* __restrict__ pd,
+__global__ __launch_bounds__(256) void k_sum_batch(const double* __restrict__ pa,
+                                                   const double* __restrict__ pd,
                                                    float* __restrict__ dA, float* __restrict__ dD,
                                                    int Bt, int H) {
   const int h = blockIdx.x * 256 + threadIdx.x;
   if (h >= H) return;
-  float sa = 0.f, sd = 0.f;
+  double sa = 0.0, sd = 0.0;
   for (int b = 0; b < Bt; ++b) {
     sa += pa[b * H + h];
     sd += pd[b * H + h];
   }
-  dA[h] = sa;
-  dD[h] = sd;
+  dA[h] = (float)sa;
+  dD[h] = (float)sd;
 }
 
 __global__ __launch_bounds__(256) void k_group_sums(const float* __restrict__ vb,
@@ -275,15 +289,15 @@ hipError_t launch_state_dot(const float* dfinal, const float* fin, float* fterm,
 }
 
 hipError_t launch_bwd_scan(const float* q, const float* xu, const float* dyx, const float* dt,
-                           const float* A, const float* fterm, float* ddt, float* pa, float* pd,
+                           const float* A, const float* fterm, float* ddt, double* pa, double* pd,
                            int Bt, int L, int H, hipStream_t s) {
   hipLaunchKernelGGL(k_bwd_scan, dim3(Bt * H), dim3(256), 0, s, q, xu, dyx, dt, A, fterm, ddt, pa,
                      pd, L, H);
   return hipGetLastError();
 }
 
-hipError_t launch_sum_batch(const float* pa, const float* pd, float* dA, float* dD, int Bt, int H,
-                            hipStream_t s) {
+hipError_t launch_sum_batch(const double* pa, const double* pd, float* dA, float* dD, int Bt,
+                            int H, hipStream_t s) {
   hipLaunchKernelGGL(k_sum_batch, dim3((H + 255) / 256), dim3(256), 0, s, pa, pd, dA, dD, Bt, H);
   return hipGetLastError();
 }

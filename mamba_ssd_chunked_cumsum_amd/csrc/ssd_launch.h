@@ -78,12 +78,13 @@ hipError_t launch_state_dot(const float* dfinal, const float* fin, float* fterm,
                             int PN, hipStream_t s);
 // per (b, h): da_t = sum_{s >= t} q_s + fterm; ddt = A da + xu; per-(b, h) partial sums of
 // dt da (for dA) and of dyx (for dD)
+// (sums in double)
 hipError_t launch_bwd_scan(const float* q, const float* xu, const float* dyx, const float* dt,
-                           const float* A, const float* fterm, float* ddt, float* pa, float* pd,
+                           const float* A, const float* fterm, float* ddt, double* pa, double* pd,
                            int Bt, int L, int H, hipStream_t s);
 // dA[h] = sum_b pa[b, h]; dD[h] = sum_b pd[b, h]
-hipError_t launch_sum_batch(const float* pa, const float* pd, float* dA, float* dD, int Bt, int H,
-                            hipStream_t s);
+hipError_t launch_sum_batch(const double* pa, const double* pd, float* dA, float* dD, int Bt,
+                            int H, hipStream_t s);
 // dB[b, t, g, n] = sum_{h in g} dt[b, t, h] vb[b, L - 1 - t, h, n];
 // dC[b, t, g, n] = sum_{h in g} vc[b, t, h, n]
 hipError_t launch_group_sums(const float* vb, const float* vc, const float* dt, float* dB,

@@ -26,7 +26,8 @@ def ssd_backward(x, dt, A, B, C, D, dy, initial_state=None, dfinal=None):
     """Gradients of sum(dy * y) + sum(dfinal * final_state) with respect to every input.
 
     Shapes as in ``ssd_recurrence``; dy [Bt, L, H, P], dfinal [Bt, H, P, N] or None.
-    Returns a dict of float64 arrays: dx, ddt, dA, dB, dC, dD, dinitial_state.
+    Returns a dict of float64 arrays: dx, ddt, dA, dB, dC, dD, dinitial_state, and dlog_decay
+    [Bt, L, H] = dL/d(dt_t A), the per-token terms that dA and ddt are built from.
     """
     x, dt, A, B, C, D, dy = (_as64(v) for v in (x, dt, A, B, C, D, dy))
     Bt, L, H, P = x.shape
@@ -45,6 +46,7 @@ def ssd_backward(x, dt, A, B, C, D, dy, initial_state=None, dfinal=None):
 
     dx = np.empty_like(x)
     ddt = np.empty_like(dt)
+    dlog = np.empty_like(dt)
     dA = np.zeros(H)
     dBh = np.zeros((Bt, L, H, N))
     dCh = np.zeros((Bt, L, H, N))
@@ -59,6 +61,7 @@ def ssd_backward(x, dt, A, B, C, D, dy, initial_state=None, dfinal=None):
         dBh[:, t] = dt[:, t, :, None] * (np.swapaxes(Gs, 2, 3) @ x[:, t][..., None])[..., 0]
         dCh[:, t] = (np.swapaxes(states[t + 1], 2, 3) @ dy[:, t][..., None])[..., 0]
         dloga = np.einsum("bhpn,bhpn->bh", Gs, a[:, t, :, None, None] * states[t])
+        dlog[:, t] = dloga
         ddt[:, t] = A[None, :] * dloga + np.einsum("bhp,bhp->bh", x[:, t], GB)
         dA += np.sum(dt[:, t] * dloga, axis=0)
         Gs = a[:, t, :, None, None] * Gs                            # into dL/dS_{t-1}
@@ -68,4 +71,4 @@ def ssd_backward(x, dt, A, B, C, D, dy, initial_state=None, dfinal=None):
         dB[:, :, grp[h]] += dBh[:, :, h]
         dC[:, :, grp[h]] += dCh[:, :, h]
     dD = np.einsum("blhp,blhp->h", dy, x)
-    return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD, dinitial_state=Gs)
+    return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD, dinitial_state=Gs, dlog_decay=dlog)
