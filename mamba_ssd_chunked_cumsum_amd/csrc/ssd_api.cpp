@@ -367,6 +367,14 @@ ssd_status ssd_chunk_state(const ssd_problem* prob, const void* x, const void* B
                                           static_cast<hipStream_t>(stream)));
 }
 
+// The backward's own chunk length: its fp32 recurrences cost least with short chunks (the
+// quadratic intra-chunk work shrinks with the chunk, the chunk states it adds are cheap), and the
+// result does not depend on where the chunks start.
+#ifndef SSD_BWD_Q
+#define SSD_BWD_Q 64
+#endif
+constexpr int64_t kBackwardChunk = SSD_BWD_Q;
+
 ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt, const float* A,
                         const void* B, const void* C, const float* D, int64_t chunk_size,
                         const float* initial_state, const void* dy, const float* dfinal,
@@ -374,13 +382,15 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
                         float* dinitial_state, void* stream) {
   ssd_status st = check_problem(prob, chunk_size);
   if (st != SSD_OK) return st;
+  st = check_problem(prob, kBackwardChunk);  // the backward's own chunking must fit too
+  if (st != SSD_OK) return st;
   // the transposed problems (head dim and state dim swapped, one group per head) must fit too
   ssd_problem tp = *prob;
   tp.headdim = prob->dstate;
   tp.dstate = prob->headdim;
   tp.ngroups = prob->nheads;
   tp.io_dtype = SSD_DTYPE_F32;
-  st = check_problem(&tp, chunk_size);
+  st = check_problem(&tp, kBackwardChunk);
   if (st != SSD_OK) return st;
   if (!x || !dt || !A || !B || !C || !D || !dy || !dx || !ddt || !dA || !dB || !dC || !dD)
     return SSD_ERR_INVALID_ARGUMENT;
@@ -430,10 +440,10 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   const int iBt = (int)Bt, iL = (int)L, iH = (int)H, iP = (int)P, iN = (int)N, iG = (int)G;
   ssd_problem p32 = *prob;
   p32.io_dtype = SSD_DTYPE_F32;
-  const Dims d = make_dims(&p32, chunk_size);
+  const Dims d = make_dims(&p32, kBackwardChunk);
   Dims du = d;
   du.unit_input = 1;
-  const Dims dT = make_dims(&tp, chunk_size);
+  const Dims dT = make_dims(&tp, kBackwardChunk);
   Dims dTu = dT;
   dTu.unit_input = 1;
   Timer none;
