@@ -9,6 +9,8 @@
 // Matrix-core use: C B^T (contraction over the state size), the chunk states (over the tokens of
 // a chunk), the masked intra-chunk product (over the tokens) and the inter-chunk readout (over
 // the state size) run on 16x16 MFMA tiles; the cumulative sum, decays and masks run on VALU.
+#include <algorithm>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -309,6 +311,11 @@ __global__ __launch_bounds__(256) void k_state_passing(const float* __restrict__
   if (fin) *reinterpret_cast<float4*>(fin + sb) = s;
 }
 
+// Whether the chunk scan stages the entering state in LDS (P x (N + 4) floats within 96 KB).
+__host__ __device__ inline bool scan_state_in_lds(const Dims& d) {
+  return (int64_t)d.P * (d.N + 4) * 4 <= 96 * 1024;
+}
+
 // =============================================================================================
 // Stage 5: y = intra + exp(Acs_i) * (C_i . h_in) + D x.
 // Grid (nc * ceil(Q/64), H, batch), 256 threads; wave w computes 16 rows of a 64-row block.
@@ -402,9 +409,22 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     }
     __syncthreads();
   }
-  if (!active) return;
   // inter-chunk readout: C_i . h_in[p, :]
   const float* hb = h_in + (((int64_t)b * d.nc + c) * d.H + h) * d.P * d.N;
+  // The chunk's entering state, staged once for the block's waves over the X slabs (no longer
+  // read), rows p padded by 4 floats so the 16 rows of a fragment read fall in distinct banks.
+  // Too large a state (P (N + 4) floats past the budget) is read from global memory instead.
+  const bool hlds = scan_state_in_lds(d);
+  const int ldh = d.N + 4;
+  float* Hs = reinterpret_cast<float*>(Xs);
+  if (hlds) {
+    for (int e = threadIdx.x * 4; e < d.P * d.N; e += 1024) {
+      const float4 v = *reinterpret_cast<const float4*>(hb + e);
+      *reinterpret_cast<float4*>(Hs + (e / d.N) * ldh + e % d.N) = v;
+    }
+    __syncthreads();
+  }
+  if (!active) return;
   const int64_t crow = (((int64_t)b * d.L + t0 + ia) * d.G + g) * d.N;
   for (int k0 = 0; k0 < d.N; k0 += M::KSTEP) {
     const int n = k0 + M::KPL * kg;
@@ -414,7 +434,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     for (int pt = 0; pt < 16; ++pt) {
       if (pt < npt) {
         typename M::Frag bf;
-        const float* hp = hb + (int64_t)(pt * 16 + col) * d.N + n;
+        const float* hp = hlds ? Hs + (pt * 16 + col) * ldh + n
+                               : hb + (int64_t)(pt * 16 + col) * d.N + n;
         if constexpr (sizeof(T) == 2) {
           float hv[8];
           if (nvalid) {
@@ -518,7 +539,9 @@ static hipError_t scan_impl(const Dims& d, const void* x, const void* C, const f
                             const float* D, void* y, hipStream_t s) {
   constexpr int SX = (sizeof(T) == 2) ? 64 : 32;
   constexpr int LD = SX + Pad<T>::v;
-  const size_t shm = 512 * 4 + (size_t)d.P * LD * sizeof(T);
+  size_t slab = (size_t)d.P * LD * sizeof(T);
+  if (scan_state_in_lds(d)) slab = std::max(slab, (size_t)d.P * (d.N + 4) * 4);
+  const size_t shm = 512 * 4 + slab;
   auto kern = k_chunk_scan<IO, T>;
   if (shm > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
