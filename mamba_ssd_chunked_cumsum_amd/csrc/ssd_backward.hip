@@ -12,21 +12,27 @@ namespace ssd {
 
 namespace {
 
+// One block per output row (b, t): K * E values, four per thread step (E is a multiple of 16).
 template <typename IO>
 __global__ __launch_bounds__(256) void k_gather(const IO* __restrict__ in, float* __restrict__ out,
-                                                int Bt, int L, int K, int rep, int E, int rev) {
-  const int64_t total = (int64_t)Bt * L * K * E;
+                                                int L, int K, int rep, int E, int rev) {
+  const int row = blockIdx.x, t = row % L, b = row / L;
+  const int ts = rev ? L - 1 - t : t;
   const int Kin = K / rep;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * 256) {
-    const int e = (int)(i % E);
-    int64_t r = i / E;
-    const int k = (int)(r % K);
-    r /= K;
-    const int t = (int)(r % L);
-    const int b = (int)(r / L);
-    const int ts = rev ? L - 1 - t : t;
-    out[i] = Io<IO>::load(in, (((int64_t)b * L + ts) * Kin + k / rep) * E + e);
+  float* o = out + (int64_t)row * K * E;
+  const IO* src = in + ((int64_t)b * L + ts) * Kin * E;
+  for (int f = threadIdx.x * 4; f < K * E; f += 1024) {
+    const int k = f / E, e = f % E;
+    const int64_t si = (int64_t)(k / rep) * E + e;
+    float4 v;
+    if constexpr (sizeof(IO) == 4) {
+      v = *reinterpret_cast<const float4*>(src + si);
+    } else {
+      const uint2 r = *reinterpret_cast<const uint2*>(src + si);
+      v = make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                      __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+    }
+    *reinterpret_cast<float4*>(o + f) = v;
   }
 }
 
@@ -244,13 +250,13 @@ int grid_for(int64_t total) {
 
 hipError_t launch_gather(int io, const void* in, float* out, int Bt, int L, int K, int rep, int E,
                          bool rev, hipStream_t s) {
-  const int g = grid_for((int64_t)Bt * L * K * E);
+  const dim3 g((unsigned)Bt * (unsigned)L);
   if (io == kIoBf16)
-    hipLaunchKernelGGL(k_gather<u16>, dim3(g), dim3(256), 0, s, (const u16*)in, out, Bt, L, K,
-                       rep, E, (int)rev);
+    hipLaunchKernelGGL(k_gather<u16>, g, dim3(256), 0, s, (const u16*)in, out, L, K, rep, E,
+                       (int)rev);
   else
-    hipLaunchKernelGGL(k_gather<float>, dim3(g), dim3(256), 0, s, (const float*)in, out, Bt, L,
-                       K, rep, E, (int)rev);
+    hipLaunchKernelGGL(k_gather<float>, g, dim3(256), 0, s, (const float*)in, out, L, K, rep, E,
+                       (int)rev);
   return hipGetLastError();
 }
 
