@@ -13,7 +13,7 @@ namespace {
 
 using ssd::Dims;
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;  // 1.2: ssd_backward
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
 
 struct Range {
