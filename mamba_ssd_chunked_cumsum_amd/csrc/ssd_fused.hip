@@ -496,7 +496,8 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
                                                       const float* __restrict__ dt,
                                                       const float* __restrict__ Av,
                                                       float* __restrict__ states,
-                                                      float* __restrict__ logdecay, Dims d,
+                                                      float* __restrict__ logdecay,
+                                                      const float* __restrict__ h0, Dims d,
                                                       int run_len, int nr) {
   using M = Mma<f16>;
   static_assert(K::RUN_LDS <= 160 * 1024, "LDS budget");
@@ -601,17 +602,26 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
     }
   }
   if (!c.active) return;
-  float* so = states + (((int64_t)c.b * nr + c.r) * d.H + c.h) * (int64_t)(K::P * K::N) +
-              (int64_t)c.p0 * K::N;
+  // h0 not null (one run per sequence, logdecay null): the run state is completed into the final
+  // state, S + exp(log-decay of the run) h0, written to states as [Bt, H, P, N]
+  const int64_t off = (((int64_t)c.b * nr + c.r) * d.H + c.h) * (int64_t)(K::P * K::N) +
+                      (int64_t)c.p0 * K::N;
+  float* so = states + off;
+  const float e0 = __expf(rem);
 #pragma unroll
   for (int nt = 0; nt < K::NNT; ++nt)
 #pragma unroll
     for (int pt = 0; pt < K::NPT; ++pt) {
-      const f32x4 v = S[nt][pt];
-      *reinterpret_cast<float4*>(so + (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g) =
-          make_float4(v[0], v[1], v[2], v[3]);
+      const int o = (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g;
+      f32x4 v = S[nt][pt];
+      if (h0 != nullptr) {
+        const float4 h = *reinterpret_cast<const float4*>(h0 + off + o);
+        v += e0 * f32x4{h.x, h.y, h.z, h.w};
+      }
+      *reinterpret_cast<float4*>(so + o) = make_float4(v[0], v[1], v[2], v[3]);
     }
-  if (c.lane == 0 && c.p0 == 0) logdecay[((int64_t)c.b * d.H + c.h) * nr + c.r] = rem;
+  if (logdecay != nullptr && c.lane == 0 && c.p0 == 0)
+    logdecay[((int64_t)c.b * d.H + c.h) * nr + c.r] = rem;
 }
 
 // Store the bf16 y tile that F3 left in the x tile of a stage: this wave's p-slice of its head,
@@ -854,6 +864,7 @@ __device__ __forceinline__ void m_from_shared(const char* cbs, const float* wa, 
     }
 }
 
+// h_run null: zero entry states.
 template <class K>
 __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
     const u16* __restrict__ x, const u16* __restrict__ Bm, const u16* __restrict__ Cm,
@@ -891,7 +902,12 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
   // carried state S^T tiles (rows n, columns p): lane holds p = p0 + 16 pt + c16,
   // n = 16 nt + 4 g + 0..3
   f32x4 S[K::NNT][NPT];
-  {
+  if (h_run == nullptr) {
+#pragma unroll
+    for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) S[nt][pt] = zero4();
+  } else {
     const float* hr = h_run + (((int64_t)c.b * nr + c.r) * d.H + c.h) * (int64_t)(K::P * K::N) +
                       (int64_t)c.p0 * K::N;
 #pragma unroll
@@ -902,6 +918,8 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
             *reinterpret_cast<const float4*>(hr + (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g);
         S[nt][pt] = f32x4{v.x, v.y, v.z, v.w};
       }
+  }
+  {
     // the compiler's own wait for these loads (it does not see the DMA waits, which are inline
     // assembly), here rather than at the state's first use inside the loop; it also covers the
     // first stage's DMA, which the loop waits for anyway
@@ -1135,14 +1153,15 @@ static hipError_t launch_k(int phase, const Dims& d, const FusedPlan& fp, const 
                            const float* D, float* states, float* logdecay, const float* h_run,
                            void* y, hipStream_t s) {
   static_assert(64 % K1::T == 0 && 64 % K3::T == 0, "runs are whole sub-chunks of both kernels");
-  if (phase == 0 && fp.split)
+  // phase 0: run states (h_run unused); phase 2: final state from h_run = h0 (one run)
+  if (phase != 1 && fp.split)
     hipLaunchKernelGGL((k_run_state<K1, true>), dim3(fp.nr, head_blocks<K1>(d), d.Bt),
                        dim3(K1::NT), 0, s, (const u16*)x, (const u16*)B, dt, A, states, logdecay,
-                       d, fp.run_len, fp.nr);
-  else if (phase == 0)
+                       h_run, d, fp.run_len, fp.nr);
+  else if (phase != 1)
     hipLaunchKernelGGL((k_run_state<K1, false>), dim3(fp.nr, head_blocks<K1>(d), d.Bt),
                        dim3(K1::NT), 0, s, (const u16*)x, (const u16*)B, dt, A, states, logdecay,
-                       d, fp.run_len, fp.nr);
+                       h_run, d, fp.run_len, fp.nr);
   else
     hipLaunchKernelGGL(k_fused_scan<K3>, dim3(fp.nr, head_blocks<K3>(d), d.Bt), dim3(K3::NT), 0,
                        s, (const u16*)x, (const u16*)B, (const u16*)C, dt, A, D, h_run, (u16*)y,
@@ -1188,6 +1207,13 @@ hipError_t launch_fused_scan(const Dims& d, const FusedPlan& fp, const void* x, 
                              const void* C, const float* dt, const float* A, const float* D,
                              const float* h_run, void* y, hipStream_t s) {
   return dispatch(1, d, fp, x, B, C, dt, A, D, nullptr, nullptr, h_run, y, s);
+}
+
+hipError_t launch_final_state(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
+                              const float* dt, const float* A, const float* h0, float* fin,
+                              hipStream_t s) {
+  if (fp.nr != 1) return hipErrorInvalidValue;
+  return dispatch(2, d, fp, x, B, nullptr, dt, A, nullptr, fin, nullptr, h0, nullptr, s);
 }
 
 }  // namespace ssd

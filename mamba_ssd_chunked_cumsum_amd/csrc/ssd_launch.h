@@ -53,10 +53,16 @@ bool fused_plan(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp);
 hipError_t launch_run_state(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
                             const float* dt, const float* A, float* states, float* logdecay,
                             hipStream_t s);
-// h_run [Bt, nr, H, P, N]: the state entering each run
+// h_run [Bt, nr, H, P, N]: the state entering each run (null: zero)
 hipError_t launch_fused_scan(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
                              const void* C, const float* dt, const float* A, const float* D,
                              const float* h_run, void* y, hipStream_t s);
+// One run per sequence (fp.nr == 1): the run-state kernel writes the final state
+// fin [Bt, H, P, N] = (state of the sequence from a zero entry) + exp(sum of dt A) h0 (h0 null:
+// zero); the scan kernel then takes h0 itself as its entry state, and no chain is needed.
+hipError_t launch_final_state(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
+                              const float* dt, const float* A, const float* h0, float* fin,
+                              hipStream_t s);
 
 // backward helpers (ssd_backward.hip); all outputs fp32, layouts row-major.
 // out[b, t, k, e] = in[b, rev ? L - 1 - t : t, k / rep, e]   (in: [Bt, L, K / rep, E], io dtype)

@@ -92,6 +92,40 @@ def test_fused_run_lengths(shape, run_chunks):
     assert rep["pass"], rep
 
 
+# One run per sequence. The plan gives it when the (batch, head block) units alone fill at least
+# half the device (16 batch entries x 10 blocks of 8 heads = 160 blocks in the first shape), or
+# when asked for runs longer than the sequence; the forward is then the run-state kernel
+# completing the final state and the scan kernel starting from the initial state, with no chain
+# between runs.
+SINGLE_RUN = [
+    synth.SSDShape("batched_prefill", 16, 300, 80, 64, 128, 1, 256, init_state=True),
+    synth.SSDShape("batched_prefill_q64", 24, 130, 48, 64, 128, 1, 64),
+    synth.SSDShape("batched_p128n256", 20, 200, 32, 128, 256, 4, 128, init_state=True),
+    synth.SSDShape("batched_p64n64_len40", 40, 40, 64, 64, 64, 2, 32, init_state=True),
+]
+
+
+@pytest.mark.parametrize("precision", ["auto", "fp16"])
+@pytest.mark.parametrize("shape", SINGLE_RUN, ids=[s.name for s in SINGLE_RUN])
+def test_single_run_plan(shape, precision):
+    rep = check_shape(shape, seed=21, variant="fused", precision=precision, max_units=8)
+    assert rep["pass"], rep
+    if precision == "auto":   # the final state keeps the run-state kernel's hi + lo accuracy
+        assert rep["final_rms_literal"] <= 1e-3, rep
+
+
+def test_single_run_null_state_and_no_final():
+    shape = synth.CONFIGS[1].replace(seqlen=200, batch=2)
+    d = to_device(synth.make_inputs(shape, seed=13), "bf16")
+    note("single run: null initial state, no final state")
+    y0, f0 = run_gpu(d, 64, "fused", run_chunks=1000)
+    d["initial_state"] = torch.zeros_like(f0)
+    y1, f1 = run_gpu(d, 64, "fused", run_chunks=1000)
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+    y2, f2 = run_gpu(d, 64, "fused", run_chunks=1000, want_final=False)
+    assert f2 is None and torch.equal(y2, y1)
+
+
 def _strong_decay(inp):
     """Decay far beyond fp32's exponent range inside one 16-token block: head 0 everywhere,
     head 1 in bursts of 40 tokens, head 2 left as drawn (the fused kernel's factored decay
