@@ -73,7 +73,7 @@ typedef enum {
     SSD_VARIANT_AUTO = 0,
     SSD_VARIANT_UNFUSED = 1, /* cumsum, C B^T, chunk states, state passing, chunk scan: five
                                 kernels, intermediates in workspace */
-    SSD_VARIANT_FUSED = 2    /* bf16 io, headdim 64 or 128, dstate 64, 128 or 256: three kernels
+    SSD_VARIANT_FUSED = 2,   /* bf16 io, headdim 64 or 128, dstate 64, 128 or 256: three kernels
                                 (run states, state passing over runs, fused scan). The sequence is
                                 cut into runs (about one block per compute unit); inside a run
                                 the state stays on chip and each sub-chunk of 32 tokens gets its
@@ -83,6 +83,16 @@ typedef enum {
                                 the run length when run_chunks is given. Assumes A <= 0 and
                                 dt >= 0 (decays at most 1); D enters through the fp16 diagonal
                                 of the masked block (exact for D = 1) */
+    SSD_VARIANT_QUADRATIC = 3 /* seqlen <= 256, dstate <= 256, either io: one kernel, the whole
+                                sequence as a single block of the quadratic (masked,
+                                attention-like) form y = (L o C B^T)(dt x) + D x plus the
+                                initial state's readout, and the final state, in fp32 arithmetic
+                                whatever the precision option ("Transformers are SSMs", the
+                                quadratic mode of state space duality, cheaper for short
+                                sequences). chunk_size is checked but not used. Assumes A <= 0
+                                and dt >= 0. AUTO takes it for problems the fused kernels do not
+                                cover with seqlen * dstate <= 8192 and a launch of at most two
+                                blocks per compute unit; otherwise the unfused kernels */
 } ssd_variant;
 
 typedef enum {
@@ -105,7 +115,9 @@ typedef struct {
                            kernels + 1 (6 covers every variant), else SSD_ERR_INVALID_ARGUMENT. */
     int32_t* n_kernels; /* optional out: number of kernels the call launched (fused 3: run
                            states, state passing over runs, fused scan; unfused 5: cumsum,
-                           C B^T, chunk states, state passing, chunk scan) */
+                           C B^T, chunk states, state passing, chunk scan; quadratic 1). A fused
+                           call with one run per sequence leaves the state-passing interval
+                           empty (and the run-state one when no final state is wanted). */
     /* dt pre-processing, applied by the kernels where they read dt (no separate pass), in this
      * order: dt + dt_bias[h]; softplus, log(1 + exp(v)) (v itself above 20, where the two agree
      * to fp32 precision); clamp to [dt_min, dt_max]. The recurrence then runs on that dt. With

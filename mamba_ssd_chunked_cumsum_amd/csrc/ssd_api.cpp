@@ -13,7 +13,7 @@ namespace {
 
 using ssd::Dims;
 
-constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;  // 1.2: ssd_backward
+constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;  // 1.2: ssd_backward; 1.3: quadratic variant
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
 
 struct Range {
@@ -89,7 +89,7 @@ Sizes sizes_of(const ssd_problem* p) {
 
 ssd_status check_options(const ssd_options* o) {
   if (!o) return SSD_OK;
-  if (o->variant < SSD_VARIANT_AUTO || o->variant > SSD_VARIANT_FUSED)
+  if (o->variant < SSD_VARIANT_AUTO || o->variant > SSD_VARIANT_QUADRATIC)
     return SSD_ERR_INVALID_ARGUMENT;
   if (o->precision != SSD_PRECISION_AUTO && o->precision != SSD_PRECISION_FP16 &&
       o->precision != SSD_PRECISION_FP32)
@@ -308,6 +308,24 @@ ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* d
   if (opts && opts->n_events > 0) {
     t.ev = opts->events;
     t.n = opts->n_events;
+  }
+  const bool quad = ssd::quadratic_covers(d);
+  if (variant == SSD_VARIANT_QUADRATIC && !quad) return SSD_ERR_UNSUPPORTED;
+  // auto: problems the fused kernels do not cover, short and small enough that the one-kernel
+  // quadratic form stays latency-bound (at most 8192 token x dstate products per row of its
+  // masked block, at most two blocks per compute unit), take it instead of the five unfused
+  // kernels (measured: 256 tokens, dstate 16, 2 heads: 32 vs 51 us; it loses beyond these bounds)
+  const bool quad_auto = variant == SSD_VARIANT_AUTO && !fusable && quad &&
+                         (int64_t)d.L * d.N <= 8192 &&
+                         ssd::quadratic_blocks(d) <= 2 * (int64_t)compute_units();
+  if (variant == SSD_VARIANT_QUADRATIC || quad_auto) {
+    if (opts && opts->n_kernels) *opts->n_kernels = 1;
+    hipError_t e = t.mark(s);
+    if (e == hipSuccess)
+      e = ssd::launch_quadratic(d, prob->io_dtype, x, dt, A, B, C, D, initial_state, y,
+                                final_state, s);
+    if (e == hipSuccess) e = t.mark(s);
+    return from_hip(e);
   }
   const bool fused = variant != SSD_VARIANT_UNFUSED && fusable;
   if (opts && opts->n_kernels) *opts->n_kernels = fused ? 3 : 5;

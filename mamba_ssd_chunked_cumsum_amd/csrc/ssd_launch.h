@@ -57,6 +57,15 @@ hipError_t launch_run_state(const Dims& d, const FusedPlan& fp, const void* x, c
 hipError_t launch_fused_scan(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
                              const void* C, const float* dt, const float* A, const float* D,
                              const float* h_run, void* y, hipStream_t s);
+// Short sequences (L <= kQuadMaxLen, dstate <= 256): the whole forward in one kernel, the
+// sequence as a single block of the quadratic (masked) form, fp32 arithmetic; h0 and fin
+// nullable. quadratic_covers() tells whether a problem qualifies.
+constexpr int kQuadMaxLen = 256;
+bool quadratic_covers(const Dims& d);
+int64_t quadratic_blocks(const Dims& d);  // blocks of its launch
+hipError_t launch_quadratic(const Dims& d, int io, const void* x, const float* dt, const float* A,
+                            const void* B, const void* C, const float* D, const float* h0,
+                            void* y, float* fin, hipStream_t s);
 // One run per sequence (fp.nr == 1): the run-state kernel writes the final state
 // fin [Bt, H, P, N] = (state of the sequence from a zero entry) + exp(sum of dt A) h0 (h0 null:
 // zero); the scan kernel then takes h0 itself as its entry state, and no chain is needed.

@@ -17,7 +17,7 @@ from .build import LIB
 SSD_OK, SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED = 0, 1, 2
 SSD_ERR_NO_DEVICE, SSD_ERR_OUT_OF_MEMORY, SSD_ERR_HIP = 3, 4, 5
 
-VARIANTS = {"auto": 0, "unfused": 1, "fused": 2}
+VARIANTS = {"auto": 0, "unfused": 1, "fused": 2, "quadratic": 3}
 PRECISIONS = {"auto": 0, "fp16": 1, "fp32": 3}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
@@ -44,7 +44,8 @@ class SSDOptions(ctypes.Structure):
 
 
 # kernel names, in launch order, for each number of kernels a call reports
-KERNELS = {3: ("run_state", "state_passing", "fused_scan"),
+KERNELS = {1: ("quadratic",),
+           3: ("run_state", "state_passing", "fused_scan"),
            5: ("chunk_cumsum", "bmm_chunk", "chunk_state", "state_passing", "chunk_scan")}
 
 

@@ -37,7 +37,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert libssd.version() == 10200
+    assert libssd.version() == 10300
     assert libssd.status_string(0) == "ok"
     assert libssd.status_string(3) == "no HIP device"
     assert libssd.status_string(99) == "unknown status"
@@ -166,8 +166,8 @@ def test_adjacent_buffers_are_not_aliasing():
 
 
 @no_gpu
-@pytest.mark.parametrize("variant,precision,status", [(0, 0, 3), (1, 1, 3), (1, 3, 3), (3, 0, 1),
-                                                      (-1, 0, 1), (0, 2, 1), (0, 9, 1)])
+@pytest.mark.parametrize("variant,precision,status", [(0, 0, 3), (1, 1, 3), (1, 3, 3), (3, 0, 3),
+                                                      (4, 0, 1), (-1, 0, 1), (0, 2, 1), (0, 9, 1)])
 def test_options(variant, precision, status):
     assert call_forward(good_problem(),
                         opts=libssd.SSDOptions(variant, precision, 0, 0, None, None)) == status
