@@ -87,9 +87,9 @@ typedef enum {
                                 sequence as a single block of the quadratic (masked,
                                 attention-like) form y = (L o C B^T)(dt x) + D x plus the
                                 initial state's readout, and the final state, in fp32 arithmetic
-                                whatever the precision option ("Transformers are SSMs", the
-                                quadratic mode of state space duality, cheaper for short
-                                sequences). chunk_size is checked but not used. Assumes A <= 0
+                                whatever the precision option (the naive quadratic form that
+                                the "nitter.gq/da_be19" thread, post 5/6, finds cheaper for
+                                short sequences). chunk_size is checked but not used. Assumes A <= 0
                                 and dt >= 0. AUTO takes it for problems the fused kernels do not
                                 cover with seqlen * dstate <= 8192 and a launch of at most two
                                 blocks per compute unit; otherwise the unfused kernels */

@@ -1,12 +1,13 @@
 // Short-sequence forward in one kernel: the whole sequence as a single block of the quadratic
 // (masked, attention-like) form, with no chunking and no state passed between chunks.
 //
-// "Transformers are SSMs: Generalized Models and Efficient Algorithms Through Structured State
-// Space Duality" (the state space duality framework, section on the quadratic mode): for one head
-// with scalar decay the SSM output is y = (L o C B^T) (dt x) + D x with the 1-semiseparable mask
-// L[t, s] = exp(sum of dt A over (s, t]) for s <= t, else 0; the same pages note that this naive
-// quadratic form is the cheaper one for short sequences. With an initial state h0 the readout
-// adds exp(sum of dt A over [0, t]) C_t h0, and the final state is
+// The "nitter.gq/da_be19" thread (post 5/6) notes that for short sequences the chunked
+// algorithm's constant overheads can make the naive quadratic form the cheaper one; the chunked
+// algorithm's intra-chunk step is that form. Unrolling the recurrence S_t = exp(dt_t A) S_{t-1} +
+// dt_t x_t B_t^T, y_t = S_t C_t + D x_t over the whole sequence gives, per head,
+// y = (L o C B^T) (dt x) + D x with the decay mask L[t, s] = exp(sum of dt A over (s, t]) for
+// s <= t, else 0. With an initial state h0 the readout adds exp(sum of dt A over [0, t]) C_t h0,
+// and the final state is
 //     h_L = sum_s exp(sum of dt A over (s, L-1]) dt_s x_s B_s^T + exp(sum of dt A over [0, L-1]) h0.
 //
 // One block (4 waves) per (p tile, row tile, head, batch), plus one per (p tile, head, batch) for
