@@ -452,10 +452,10 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
   // workspace (fp32): see the steps below for what each holds
-  enum { X32, DY32, B32, C32, Y0, FIN0, XR, BR, CR, DTR, UR, G0, XT, YT, H0T, XTR, CTR, YTR, DFT,
+  enum { X32, DY32, B32, C32, Y0, FIN0, XR, BR, CR, DTR, UR, G0, YT, H0T, CTR, YTR, DFT,
          Q, XU, DYX, FT, PA, PD, ZD, NBUF };
-  const int64_t el[NBUF] = {nx, nx, nb, nb, nx, ns, nx, nb, nb, nd, nx, ns, nt, nt, ns,
-                            nt, nx, nt, ns, nd, nd, nd, Bt * H, 2 * Bt * H, 2 * Bt * H, H};
+  const int64_t el[NBUF] = {nx, nx, nb, nb, nx, ns, nx, nb, nb, nd, nx, ns, nt, ns,
+                            nx, nt, ns, nd, nd, nd, Bt * H, 2 * Bt * H, 2 * Bt * H, H};
   int64_t off[NBUF], total = 0;
   for (int i = 0; i < NBUF; ++i) {
     off[i] = total;
@@ -473,7 +473,9 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   const Dims d = make_dims(&p32, kBackwardChunk);
   Dims du = d;
   du.unit_input = 1;
-  const Dims dT = make_dims(&tp, kBackwardChunk);
+  // the transposed problems' input is B (or C) per head: read in place, shared by each group
+  Dims dT = make_dims(&tp, kBackwardChunk);
+  dT.x_groups = (int)G;
   Dims dTu = dT;
   dTu.unit_input = 1;
   Timer none;
@@ -502,15 +504,15 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   hip(ssd::launch_gather(ssd::kIoF32, w[B32], w[CR], iBt, iL, iG, 1, iN, true, hs));
   hip(ssd::launch_dt_shift_rev(dt, w[DTR], iBt, iL, iH, hs));
   fwd(&p32, du, w[XR], w[DTR], w[BR], w[CR], dfinal, w[UR], dinitial_state ? w[G0] : nullptr);
-  // 3. dC: the transposed state S_t^T (state dim N, head dim P) read out with dy
-  hip(ssd::launch_gather(ssd::kIoF32, w[B32], w[XT], iBt, iL, iH, iH / iG, iN, false, hs));
+  // 3. dC: the transposed state S_t^T (state dim N, head dim P) read out with dy; its input is
+  //    B of the head's group
   if (initial_state) hip(ssd::launch_transpose_state(initial_state, w[H0T], iBt, iH, iP, iN, hs));
-  fwd(&tp, dT, w[XT], dt, w[X32], w[DY32], initial_state ? w[H0T] : nullptr, w[YT], nullptr);
-  // 4. dB: the transposed adjoint G_t^T in reversed time, read out with x
-  hip(ssd::launch_gather(ssd::kIoF32, w[C32], w[XTR], iBt, iL, iH, iH / iG, iN, true, hs));
+  fwd(&tp, dT, w[B32], dt, w[X32], w[DY32], initial_state ? w[H0T] : nullptr, w[YT], nullptr);
+  // 4. dB: the transposed adjoint G_t^T in reversed time, read out with x; its input is C of the
+  //    head's group in reversed time (step 2's BR)
   hip(ssd::launch_gather(ssd::kIoF32, w[X32], w[CTR], iBt, iL, iH, 1, iP, true, hs));
   if (dfinal) hip(ssd::launch_transpose_state(dfinal, w[DFT], iBt, iH, iP, iN, hs));
-  fwd(&tp, dTu, w[XTR], w[DTR], w[XR], w[CTR], dfinal ? w[DFT] : nullptr, w[YTR], nullptr);
+  fwd(&tp, dTu, w[BR], w[DTR], w[XR], w[CTR], dfinal ? w[DFT] : nullptr, w[YTR], nullptr);
   // 5. the gradients
   hip(ssd::launch_bwd_pointwise(io, x, dy, w[UR], w[Y0], dt, D, dx, w[Q], w[XU], w[DYX], iBt, iL,
                                 iH, iP, hs));

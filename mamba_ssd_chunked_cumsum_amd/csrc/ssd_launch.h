@@ -17,6 +17,9 @@ struct Dims {
   // unfused path only (the backward's adjoint recurrences): the input term is x B^T instead of
   // dt x B^T, while dt still sets the decay exp(dt A)
   int unit_input = 0;
+  // unfused path only (the backward's transposed recurrences): 0 = x has one row per head; else x
+  // has x_groups rows per token and head h reads row h / (H / x_groups) (x shared like B and C)
+  int x_groups = 0;
 };
 
 constexpr int kIoF32 = 0, kIoBf16 = 1;

@@ -151,6 +151,13 @@ __global__ __launch_bounds__(256) void k_bmm_chunk(const IO* __restrict__ Bm,
 // =============================================================================================
 constexpr int SJ = 32;
 
+// The x row of head h: one per head, or shared by the heads of a group when d.x_groups > 0.
+struct XRow {
+  int n, row;  // x rows per token, this head's row
+  __device__ XRow(const Dims& d, int h)
+      : n(d.x_groups ? d.x_groups : d.H), row(d.x_groups ? h / (d.H / d.x_groups) : h) {}
+};
+
 template <typename T> struct Pad { static constexpr int v = 8; };
 template <> struct Pad<float> { static constexpr int v = 1; };
 
@@ -166,6 +173,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const IO* __restrict__ x,
   const int npb = (d.P + 63) / 64;
   const int c = blockIdx.x / npb, pb = blockIdx.x % npb, h = blockIdx.y, b = blockIdx.z;
   const int g = h / (d.H / d.G);
+  const XRow xh(d, h);
   const int p0 = pb * 64, np = min(64, d.P - p0);
   T* Wh = reinterpret_cast<T*>(smem);
   T* Wl = Wh + 64 * LD;
@@ -197,7 +205,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const IO* __restrict__ x,
       const int j = j0 + jj;
       float v[8];
       if (j < q) {
-        const int64_t off = ((((int64_t)b * d.L + t0 + j) * d.H + h) * d.P) + p0 + p8;
+        const int64_t off = ((((int64_t)b * d.L + t0 + j) * xh.n + xh.row) * d.P) + p0 + p8;
         if constexpr (sizeof(IO) == 2) load8(reinterpret_cast<const u16*>(x) + off, v);
         else load8(reinterpret_cast<const float*>(x) + off, v);
       } else {
@@ -339,6 +347,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   const int nib = (d.Q + 63) / 64;
   const int c = blockIdx.x / nib, ib = blockIdx.x % nib, h = blockIdx.y, b = blockIdx.z;
   const int g = h / (d.H / d.G);
+  const XRow xh(d, h);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, kg = lane >> 4;
   const int t0 = c * d.Q, q = min(d.Q, d.L - t0);
@@ -367,7 +376,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
       const int j = j0 + jj;
       float v[8];
       if (j < q) {
-        const int64_t off = (((int64_t)b * d.L + t0 + j) * d.H + h) * d.P + p8;
+        const int64_t off = (((int64_t)b * d.L + t0 + j) * xh.n + xh.row) * d.P + p8;
         if constexpr (sizeof(IO) == 2) load8(reinterpret_cast<const u16*>(x) + off, v);
         else load8(reinterpret_cast<const float*>(x) + off, v);
       } else {
@@ -460,11 +469,12 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     if (i >= q) continue;
     const float e = __expf(acs[i]);
     const int64_t row = (((int64_t)b * d.L + t0 + i) * d.H + h) * d.P;
+    const int64_t xrow = (((int64_t)b * d.L + t0 + i) * xh.n + xh.row) * d.P;
 #pragma unroll
     for (int pt = 0; pt < 16; ++pt) {
       if (pt < npt) {
         const int p = pt * 16 + col;
-        const float xv = Io<IO>::load(x, row + p);
+        const float xv = Io<IO>::load(x, xrow + p);
         Io<IO>::store(y, row + p, acc[pt][r] + e * inter[pt][r] + dh * xv);
       }
     }
