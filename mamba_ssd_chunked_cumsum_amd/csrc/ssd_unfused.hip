@@ -387,7 +387,32 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
       for (int k = 0; k < 8; ++k) Xs[(p8 + k) * LD + jj] = (T)v[k];
     }
     __syncthreads();
-    if (active) {
+    if constexpr (sizeof(T) == 4) {
+      // fp32: the slab's A fragments (one masked, decayed C B^T value per K step) are computed
+      // before its matrix-core steps, from clamped addresses, so their loads are in flight
+      // together instead of one per step
+      if (active) {
+        constexpr int NKS = SX / M::KSTEP;
+        float av[NKS];
+        const float acs_i = acs[ia];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          const int j = j0 + s * M::KSTEP + kg, jc = min(j, d.Q - 1);
+          const float cv = cb[(int64_t)ia * d.Q + jc];
+          av[s] = (j <= ia && j < d.Q) ? cv * __expf(acs_i - acs[jc]) * dts[jc] : 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          const int k0 = s * M::KSTEP;
+          if (k0 < sx && j0 + k0 <= i0 + 15) {
+#pragma unroll
+            for (int pt = 0; pt < 16; ++pt)
+              if (pt < npt)
+                acc[pt] = M::mma(av[s], M::lds(Xs + (pt * 16 + col) * LD + k0 + kg), acc[pt]);
+          }
+        }
+      }
+    } else if (active) {
       for (int k0 = 0; k0 < sx && j0 + k0 <= i0 + 15; k0 += M::KSTEP) {
         const int jb = j0 + k0 + M::KPL * kg;  // first j of this lane's K slice
         typename M::Frag a;
@@ -435,6 +460,37 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   }
   if (!active) return;
   const int64_t crow = (((int64_t)b * d.L + t0 + ia) * d.G + g) * d.N;
+  if constexpr (sizeof(T) == 4) {
+    // fp32: C fragments of 8 K steps loaded together (row clamped to the chunk, zero past it)
+    constexpr int GK = 8;
+    const int64_t crow_c = (((int64_t)b * d.L + t0 + min(ia, q - 1)) * d.G + g) * d.N;
+    // the state operand from LDS or (too large a state) global memory: one loop each, so that
+    // every access has a fixed address space
+    auto readout = [&](const float* hs, int ldr) {
+      for (int k00 = 0; k00 < d.N; k00 += GK * M::KSTEP) {
+        float av[GK];
+#pragma unroll
+        for (int s = 0; s < GK; ++s) {
+          const int n = k00 + s * M::KSTEP + kg;
+          const float v = Io<IO>::load(Cm, crow_c + min(n, d.N - 1));
+          av[s] = (ia < q && n < d.N) ? v : 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < GK; ++s) {
+          const int n = k00 + s * M::KSTEP + kg;
+          if (k00 + s * M::KSTEP < d.N) {
+#pragma unroll
+            for (int pt = 0; pt < 16; ++pt)
+              if (pt < npt) inter[pt] = M::mma(av[s], hs[(pt * 16 + col) * ldr + n], inter[pt]);
+          }
+        }
+      }
+    };
+    if (hlds)
+      readout(Hs, ldh);
+    else
+      readout(hb, d.N);
+  } else
   for (int k0 = 0; k0 < d.N; k0 += M::KSTEP) {
     const int n = k0 + M::KPL * kg;
     const bool nvalid = n < d.N;  // the fp16 K step is 32 wide, N only a multiple of 16
