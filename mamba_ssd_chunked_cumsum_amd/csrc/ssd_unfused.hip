@@ -128,12 +128,34 @@ __global__ __launch_bounds__(256) void k_bmm_chunk(const IO* __restrict__ Bm,
     const int ia = ti * 16 + col;  // row of C this lane feeds
     const int jb = tj * 16 + col;  // row of B this lane feeds
     f32x4 acc = zero4();
-    for (int k0 = 0; k0 < d.N; k0 += M::KSTEP) {
-      const int n = k0 + M::KPL * kg;
-      // n < N also guards the 32-wide fp16 K step when N is a multiple of 16 only
-      auto a = FragLoad<IO, T>::load(Cm, gbase + ia * rowstride + n, ia < q && n < d.N);
-      auto bb = FragLoad<IO, T>::load(Bm, gbase + jb * rowstride + n, jb < q && n < d.N);
-      acc = M::mma(a, bb, acc);
+    if constexpr (sizeof(T) == 4) {
+      // fp32: 8 K steps of operands loaded together from clamped rows, zeroed past the chunk
+      constexpr int GK = 8;
+      const int64_t arow = gbase + min(ia, q - 1) * rowstride;
+      const int64_t brow = gbase + min(jb, q - 1) * rowstride;
+      for (int k00 = 0; k00 < d.N; k00 += GK * M::KSTEP) {
+        float av[GK], bv[GK];
+#pragma unroll
+        for (int s = 0; s < GK; ++s) {
+          const int nc = min(k00 + s * M::KSTEP + kg, d.N - 1);
+          av[s] = Io<IO>::load(Cm, arow + nc);
+          bv[s] = Io<IO>::load(Bm, brow + nc);
+        }
+#pragma unroll
+        for (int s = 0; s < GK; ++s) {
+          const int n = k00 + s * M::KSTEP + kg;
+          if (k00 + s * M::KSTEP < d.N)
+            acc = M::mma(ia < q && n < d.N ? av[s] : 0.f, jb < q && n < d.N ? bv[s] : 0.f, acc);
+        }
+      }
+    } else {
+      for (int k0 = 0; k0 < d.N; k0 += M::KSTEP) {
+        const int n = k0 + M::KPL * kg;
+        // n < N also guards the 32-wide fp16 K step when N is a multiple of 16 only
+        auto a = FragLoad<IO, T>::load(Cm, gbase + ia * rowstride + n, ia < q && n < d.N);
+        auto bb = FragLoad<IO, T>::load(Bm, gbase + jb * rowstride + n, jb < q && n < d.N);
+        acc = M::mma(a, bb, acc);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -319,14 +341,17 @@ __global__ __launch_bounds__(256) void k_state_passing(const float* __restrict__
   if (fin) *reinterpret_cast<float4*>(fin + sb) = s;
 }
 
-// Whether the chunk scan stages the entering state in LDS (P x (N + 4) floats within 96 KB).
+// Whether the chunk scan stages the entering state in LDS (the block's rows, at most 64, of
+// N + 4 floats within 96 KB).
 __host__ __device__ inline bool scan_state_in_lds(const Dims& d) {
-  return (int64_t)d.P * (d.N + 4) * 4 <= 96 * 1024;
+  return (int64_t)min(d.P, 64) * (d.N + 4) * 4 <= 96 * 1024;
 }
 
 // =============================================================================================
 // Stage 5: y = intra + exp(Acs_i) * (C_i . h_in) + D x.
-// Grid (nc * ceil(Q/64), H, batch), 256 threads; wave w computes 16 rows of a 64-row block.
+// Grid (nc * ceil(Q/64) * ceil(P/64), H, batch), 256 threads; a block takes 64 rows and 64
+// columns of headdim (wave w 16 rows of them: four 16x16 accumulator tiles for each of the
+// intra and inter parts, few enough registers for three waves per SIMD in fp32).
 // intra: for each K step over j <= i, the A fragment M[i][j] = CB[i][j] exp(Acs_i - Acs_j) dt_j
 // (selected to 0 for j > i) is formed in registers straight from CB; X^T slabs [p][j] are staged
 // in LDS. inter: C rows and h_in rows are read from global memory (both contiguous along n).
@@ -344,10 +369,13 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   float* dts = acs + 256;
   T* Xs = reinterpret_cast<T*>(dts + 256);
 
-  const int nib = (d.Q + 63) / 64;
-  const int c = blockIdx.x / nib, ib = blockIdx.x % nib, h = blockIdx.y, b = blockIdx.z;
+  constexpr int NPT = 4;  // 16-column tiles of the block's 64 columns
+  const int nib = (d.Q + 63) / 64, npb = (d.P + 63) / 64;
+  const int c = blockIdx.x / (nib * npb), ib = (blockIdx.x / npb) % nib, pb = blockIdx.x % npb;
+  const int h = blockIdx.y, b = blockIdx.z;
   const int g = h / (d.H / d.G);
   const XRow xh(d, h);
+  const int p0 = pb * 64, np = min(64, d.P - p0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, kg = lane >> 4;
   const int t0 = c * d.Q, q = min(d.Q, d.L - t0);
@@ -359,10 +387,10 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     acs[i] = Acs[abase + i];
     dts[i] = dtc[abase + i];
   }
-  const int npt = d.P / 16;
-  f32x4 acc[16], inter[16];
+  const int npt = np / 16;
+  f32x4 acc[NPT], inter[NPT];
 #pragma unroll
-  for (int pt = 0; pt < 16; ++pt) { acc[pt] = zero4(); inter[pt] = zero4(); }
+  for (int pt = 0; pt < NPT; ++pt) { acc[pt] = zero4(); inter[pt] = zero4(); }
   const float* cb = CB + (((int64_t)b * d.nc + c) * d.G + g) * d.Q * d.Q;
   const int ia = i0 + col;  // row this lane feeds into A fragments
   __syncthreads();
@@ -371,12 +399,12 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     const int sx = min(SX, d.Q - j0);
     // Stage all SX columns: those past the chunk (or past Q when Q < one K step) are zeros, so
     // every fragment read below sees finite values.
-    for (int e = threadIdx.x; e < SX * (d.P / 8); e += 256) {
-      const int jj = e / (d.P / 8), p8 = (e % (d.P / 8)) * 8;
+    for (int e = threadIdx.x; e < SX * (np / 8); e += 256) {
+      const int jj = e / (np / 8), p8 = (e % (np / 8)) * 8;
       const int j = j0 + jj;
       float v[8];
       if (j < q) {
-        const int64_t off = (((int64_t)b * d.L + t0 + j) * xh.n + xh.row) * d.P + p8;
+        const int64_t off = (((int64_t)b * d.L + t0 + j) * xh.n + xh.row) * d.P + p0 + p8;
         if constexpr (sizeof(IO) == 2) load8(reinterpret_cast<const u16*>(x) + off, v);
         else load8(reinterpret_cast<const float*>(x) + off, v);
       } else {
@@ -406,7 +434,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
           const int k0 = s * M::KSTEP;
           if (k0 < sx && j0 + k0 <= i0 + 15) {
 #pragma unroll
-            for (int pt = 0; pt < 16; ++pt)
+            for (int pt = 0; pt < NPT; ++pt)
               if (pt < npt)
                 acc[pt] = M::mma(av[s], M::lds(Xs + (pt * 16 + col) * LD + k0 + kg), acc[pt]);
           }
@@ -436,7 +464,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
           a = (j <= ia) ? m : 0.f;
         }
 #pragma unroll
-        for (int pt = 0; pt < 16; ++pt)
+        for (int pt = 0; pt < NPT; ++pt)
           if (pt < npt) acc[pt] = M::mma(a, M::lds(Xs + (pt * 16 + col) * LD + k0 + M::KPL * kg),
                                          acc[pt]);
       }
@@ -444,7 +472,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     __syncthreads();
   }
   // inter-chunk readout: C_i . h_in[p, :]
-  const float* hb = h_in + (((int64_t)b * d.nc + c) * d.H + h) * d.P * d.N;
+  const float* hb = h_in + ((((int64_t)b * d.nc + c) * d.H + h) * d.P + p0) * d.N;  // row p0
   // The chunk's entering state, staged once for the block's waves over the X slabs (no longer
   // read), rows p padded by 4 floats so the 16 rows of a fragment read fall in distinct banks.
   // Too large a state (P (N + 4) floats past the budget) is read from global memory instead.
@@ -452,9 +480,18 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   const int ldh = d.N + 4;
   float* Hs = reinterpret_cast<float*>(Xs);
   if (hlds) {
-    for (int e = threadIdx.x * 4; e < d.P * d.N; e += 1024) {
-      const float4 v = *reinterpret_cast<const float4*>(hb + e);
-      *reinterpret_cast<float4*>(Hs + (e / d.N) * ldh + e % d.N) = v;
+    // 8 float4 loads per thread in flight at a time (clamped; the extra ones are not stored)
+    const int nv = np * d.N / 4;
+    for (int e0 = threadIdx.x; e0 < nv; e0 += 256 * 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = *reinterpret_cast<const float4*>(hb + 4 * min(e0 + 256 * u, nv - 1));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = 4 * (e0 + 256 * u);
+        if (e0 + 256 * u < nv) *reinterpret_cast<float4*>(Hs + (e / d.N) * ldh + e % d.N) = v[u];
+      }
     }
     __syncthreads();
   }
@@ -480,7 +517,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
           const int n = k00 + s * M::KSTEP + kg;
           if (k00 + s * M::KSTEP < d.N) {
 #pragma unroll
-            for (int pt = 0; pt < 16; ++pt)
+            for (int pt = 0; pt < NPT; ++pt)
               if (pt < npt) inter[pt] = M::mma(av[s], hs[(pt * 16 + col) * ldr + n], inter[pt]);
           }
         }
@@ -496,7 +533,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     const bool nvalid = n < d.N;  // the fp16 K step is 32 wide, N only a multiple of 16
     const auto a = FragLoad<IO, T>::load(Cm, crow + n, ia < q && nvalid);
 #pragma unroll
-    for (int pt = 0; pt < 16; ++pt) {
+    for (int pt = 0; pt < NPT; ++pt) {
       if (pt < npt) {
         typename M::Frag bf;
         const float* hp = hlds ? Hs + (pt * 16 + col) * ldh + n
@@ -527,9 +564,9 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     const int64_t row = (((int64_t)b * d.L + t0 + i) * d.H + h) * d.P;
     const int64_t xrow = (((int64_t)b * d.L + t0 + i) * xh.n + xh.row) * d.P;
 #pragma unroll
-    for (int pt = 0; pt < 16; ++pt) {
+    for (int pt = 0; pt < NPT; ++pt) {
       if (pt < npt) {
-        const int p = pt * 16 + col;
+        const int p = p0 + pt * 16 + col;
         const float xv = Io<IO>::load(x, xrow + p);
         Io<IO>::store(y, row + p, acc[pt][r] + e * inter[pt][r] + dh * xv);
       }
@@ -605,8 +642,9 @@ static hipError_t scan_impl(const Dims& d, const void* x, const void* C, const f
                             const float* D, void* y, hipStream_t s) {
   constexpr int SX = (sizeof(T) == 2) ? 64 : 32;
   constexpr int LD = SX + Pad<T>::v;
-  size_t slab = (size_t)d.P * LD * sizeof(T);
-  if (scan_state_in_lds(d)) slab = std::max(slab, (size_t)d.P * (d.N + 4) * 4);
+  const int rows = std::min(d.P, 64);  // headdim columns per block
+  size_t slab = (size_t)rows * LD * sizeof(T);
+  if (scan_state_in_lds(d)) slab = std::max(slab, (size_t)rows * (d.N + 4) * 4);
   const size_t shm = 512 * 4 + slab;
   auto kern = k_chunk_scan<IO, T>;
   if (shm > 64 * 1024) {
@@ -614,7 +652,7 @@ static hipError_t scan_impl(const Dims& d, const void* x, const void* C, const f
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     if (e != hipSuccess) return e;
   }
-  dim3 grid(d.nc * ((d.Q + 63) / 64), d.H, d.Bt);
+  dim3 grid(d.nc * ((d.Q + 63) / 64) * ((d.P + 63) / 64), d.H, d.Bt);
   hipLaunchKernelGGL(kern, grid, dim3(256), shm, s, (const IO*)x, (const IO*)C, CB, Acs, dtc,
                      h_in, D, (IO*)y, d);
   return hipGetLastError();
