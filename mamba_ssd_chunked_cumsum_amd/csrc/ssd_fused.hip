@@ -607,19 +607,27 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
   const int64_t off = (((int64_t)c.b * nr + c.r) * d.H + c.h) * (int64_t)(K::P * K::N) +
                       (int64_t)c.p0 * K::N;
   float* so = states + off;
-  const float e0 = __expf(rem);
+  if (h0 == nullptr) {
 #pragma unroll
-  for (int nt = 0; nt < K::NNT; ++nt)
+    for (int nt = 0; nt < K::NNT; ++nt)
 #pragma unroll
-    for (int pt = 0; pt < K::NPT; ++pt) {
-      const int o = (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g;
-      f32x4 v = S[nt][pt];
-      if (h0 != nullptr) {
-        const float4 h = *reinterpret_cast<const float4*>(h0 + off + o);
-        v += e0 * f32x4{h.x, h.y, h.z, h.w};
+      for (int pt = 0; pt < K::NPT; ++pt) {
+        const f32x4 v = S[nt][pt];
+        *reinterpret_cast<float4*>(so + (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g) =
+            make_float4(v[0], v[1], v[2], v[3]);
       }
-      *reinterpret_cast<float4*>(so + o) = make_float4(v[0], v[1], v[2], v[3]);
-    }
+  } else {
+    const float e0 = __expf(rem);
+#pragma unroll
+    for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < K::NPT; ++pt) {
+        const int o = (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g;
+        const float4 h = *reinterpret_cast<const float4*>(h0 + off + o);
+        const f32x4 v = S[nt][pt] + e0 * f32x4{h.x, h.y, h.z, h.w};
+        *reinterpret_cast<float4*>(so + o) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+  }
   if (logdecay != nullptr && c.lane == 0 && c.p0 == 0)
     logdecay[((int64_t)c.b * d.H + c.h) * nr + c.r] = rem;
 }
