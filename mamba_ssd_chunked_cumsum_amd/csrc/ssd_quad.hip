@@ -133,34 +133,34 @@ __global__ __launch_bounds__(kQuadThreads) void k_quadratic(
     __syncthreads();
   }
 
-  // T rows (tokens s0 + j, zero past the sequence) of B or C into dst[n][j] (transposed) or,
-  // with ROWS, dst[j][n] (row length N + 4)
-  auto stage_bc = [&](float* dst, const IO* src, int s0, bool rows) {
-    float v[Q::NLD];
+  // A token tile is loaded into registers (load_bc, load_x: every load issued, none waited for)
+  // and stored to LDS later (store_bc, store_x), so that the next tile's loads are in flight
+  // while the current one is computed. B or C: T rows (tokens s0 + j, zero past the sequence)
+  // into dst[n][j] (transposed) or, with ROWS, dst[j][n] (row length N + 4).
+  auto load_bc = [&](float (&v)[Q::NLD], const IO* src, int s0) {
 #pragma unroll
     for (int c = 0; c < Q::NLD; ++c) {
       const int e = tid + kQuadThreads * c, j = e / Q::NMAX, n = e % Q::NMAX;
       v[c] = Io<IO>::load(src, (int64_t)min(s0 + j, L - 1) * brow + min(n, N - 1));
     }
-#pragma unroll
-    for (int c = 0; c < Q::NLD; ++c) {
-      const int e = tid + kQuadThreads * c, j = e / Q::NMAX;
-      if (s0 + j >= L) v[c] = 0.f;
-    }
+  };
+  auto store_bc = [&](const float (&v)[Q::NLD], float* dst, int s0, bool rows) {
 #pragma unroll
     for (int c = 0; c < Q::NLD; ++c) {
       const int e = tid + kQuadThreads * c, j = e / Q::NMAX, n = e % Q::NMAX;
-      if (n < N) dst[rows ? j * (N + 4) + n : n * LDT + j] = v[c];
+      if (n < N) dst[rows ? j * (N + 4) + n : n * LDT + j] = s0 + j < L ? v[c] : 0.f;
     }
   };
-  // w_s x_s[p0 + p] for tokens s0 + j into Xs[j][p] (zero past the sequence or headdim)
-  auto stage_x = [&](int s0, float acs_end, bool to_end) {
-    float v[Q::NLX];
+  // x of tokens s0 + j, columns p0 + p; stored weighted, w_s x_s, into Xs[j][p] (zero past the
+  // sequence or headdim)
+  auto load_x = [&](float (&v)[Q::NLX], int s0) {
 #pragma unroll
     for (int c = 0; c < Q::NLX; ++c) {
       const int e = tid + kQuadThreads * c, j = e / T, p = e % T, s = s0 + j;
       v[c] = Io<IO>::load(xb, (int64_t)min(s, L - 1) * xrow + min(p0 + p, P - 1));
     }
+  };
+  auto store_x = [&](const float (&v)[Q::NLX], int s0, float acs_end, bool to_end) {
 #pragma unroll
     for (int c = 0; c < Q::NLX; ++c) {
       const int e = tid + kQuadThreads * c, j = e / T, p = e % T, s = s0 + j;
@@ -168,13 +168,20 @@ __global__ __launch_bounds__(kQuadThreads) void k_quadratic(
       Xs[j * LDT + p] = (s < L && p0 + p < P) ? w * v[c] : 0.f;
     }
   };
+  float vb[Q::NLD], vx[Q::NLX];
 
   const int ty = tid >> 4, tx = tid & 15;  // micro-tile rows ty * M .., columns tx * M ..
 
   if (rt < ntile) {
     // 2. outputs of row tile rt
     const int t0 = rt * T;
-    stage_bc(Ct, Cb, t0, false);
+    {
+      float vc[Q::NLD];
+      load_bc(vc, Cb, t0);
+      load_bc(vb, Bb, 0);
+      load_x(vx, 0);
+      store_bc(vc, Ct, t0, false);
+    }
     float yacc[M][M];
 #pragma unroll
     for (int i = 0; i < M; ++i)
@@ -185,9 +192,13 @@ __global__ __launch_bounds__(kQuadThreads) void k_quadratic(
     for (int i = 0; i < M; ++i) acs_t[i] = acs[min(t0 + ty * M + i, L - 1)];
     for (int st = 0; st <= rt; ++st) {
       const int s0 = st * T;
-      stage_bc(Bt, Bb, s0, false);
-      stage_x(s0, 0.f, false);
+      store_bc(vb, Bt, s0, false);
+      store_x(vx, s0, 0.f, false);
       __syncthreads();  // C, B and x tiles staged
+      if (st < rt) {  // the next token tile's loads, in flight during this tile's products
+        load_bc(vb, Bb, s0 + T);
+        load_x(vx, s0 + T);
+      }
       float acc[M][M];
       micro_dots<Q>(Ct, Bt, N, ty * M, tx * M, acc);
       // mask and decay, stored transposed: Gt[j][i]
@@ -264,11 +275,17 @@ __global__ __launch_bounds__(kQuadThreads) void k_quadratic(
   for (int i = 0; i < M; ++i)
 #pragma unroll
     for (int c = 0; c < Q::NG; ++c) facc[i][c] = 0.f;
+  load_bc(vb, Bb, 0);
+  load_x(vx, 0);
   for (int st = 0; st < ntile; ++st) {
     const int s0 = st * T;
-    stage_bc(Bn, Bb, s0, true);
-    stage_x(s0, acs_end, true);
+    store_bc(vb, Bn, s0, true);
+    store_x(vx, s0, acs_end, true);
     __syncthreads();
+    if (st + 1 < ntile) {
+      load_bc(vb, Bb, s0 + T);
+      load_x(vx, s0 + T);
+    }
 #pragma unroll 2
     for (int j = 0; j < T; ++j) {
       float xv[M];
