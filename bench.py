@@ -284,6 +284,58 @@ def decode_bench(shape, dev, layers: int = 64, rounds: int = 5) -> dict:
                     "from a HIP graph"}
 
 
+def short_sequence_bench(dev, flush, flush_out, steps: int = 10) -> dict:
+    """The short-sequence dispatch: whole forwards (cold cache) of two short workloads under the
+    auto variant and the alternatives it chose between. The tiny fp32 workload (auto: the one-
+    kernel quadratic form) against the five unfused kernels; a batched bf16 prefill of 32
+    sequences of 128 tokens at the 2.7B layer's head shape (auto: one run per sequence, no chain
+    kernel) against the unfused kernels."""
+    import numpy as np
+    import torch
+
+    import mamba_ssd_chunked_cumsum_amd as ssd
+    from mamba_ssd_chunked_cumsum_amd import synth
+
+    cases = [
+        ("tiny_fp32 (1 x 256 tokens, 2 heads, headdim 16, dstate 16)", synth.CONFIGS[0],
+         ("auto", "unfused")),
+        ("batched_prefill_bf16 (32 x 128 tokens, 80 heads, headdim 64, dstate 128)",
+         synth.SSDShape("batched_prefill", 32, 128, 80, 64, 128, 1, 128, init_state=True),
+         ("auto", "unfused")),
+    ]
+    out = {}
+    for name, shape, variants in cases:
+        inp = synth.make_inputs(shape, seed=7)
+        io = torch.bfloat16 if shape.io == "bf16" else torch.float32
+        d = {k: (None if v is None else torch.from_numpy(v).to(dev)) for k, v in inp.items()}
+        for k in ("x", "B", "C"):
+            d[k] = d[k].to(io)
+        y = torch.empty_like(d["x"])
+        fin = torch.empty((shape.batch, shape.nheads, shape.headdim, shape.dstate),
+                          dtype=torch.float32, device=dev)
+        row = {}
+        for v in variants:
+            def call():
+                ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], shape.chunk_size,
+                            d["initial_state"], variant=v, out=y, final_out=fin)
+            call()
+            torch.cuda.synchronize()
+            ms = []
+            for _ in range(steps):
+                if flush is not None:
+                    torch.sum(flush, dim=0, dtype=torch.int64, out=flush_out)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call()
+                e1.record()
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            row[v] = float(np.mean(ms))
+        out[name] = {"ms_per_forward": row}
+        del d, y, fin
+    return out
+
+
 def backward_bench(shape, d, flush, flush_out, steps: int = 3) -> dict:
     """ssd_backward at the workload's shape: output gradient dy of x's dtype and a final-state
     gradient, cold cache before every call. Reports ms per call and tokens/s; the bytes it must
@@ -348,7 +400,8 @@ def main():
                          "256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the timed ssd_backward calls reported under 'backward'")
+                    help="skip the timed ssd_backward calls reported under 'backward' and the "
+                         "short-sequence forwards under 'short_sequence'")
     ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 output under DIR and exit")
@@ -513,6 +566,8 @@ def main():
         "decode_step": decode_bench(shape, dev),
         "backward": None if args.no_backward else backward_bench(
             shape, d, flush, flush_out if flush is not None else None),
+        "short_sequence": None if args.no_backward else short_sequence_bench(
+            dev, flush, flush_out if flush is not None else None),
     }
     print(json.dumps(out), flush=True)
 
