@@ -183,7 +183,8 @@ struct XRow {
 template <typename T> struct Pad { static constexpr int v = 8; };
 template <> struct Pad<float> { static constexpr int v = 1; };
 
-template <typename IO, typename T, bool HILO>
+// NU: n-tile slots per wave (wave w takes n-tiles w, w + 4, ...; dstate <= 64 NU)
+template <typename IO, typename T, bool HILO, int NU>
 __global__ __launch_bounds__(256) void k_chunk_state(const IO* __restrict__ x,
                                                      const IO* __restrict__ Bm,
                                                      const float* __restrict__ Acs,
@@ -209,11 +210,11 @@ __global__ __launch_bounds__(256) void k_chunk_state(const IO* __restrict__ x,
   const float alast = Acs[abase + d.Q - 1];
   const int npt = np / 16, nnt = d.N / 16;
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][NU];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+    for (int j = 0; j < NU; ++j) acc[i][j] = zero4();
 
   for (int j0 = 0; j0 < d.Q; j0 += SJ) {
     if (threadIdx.x < SJ) {
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const IO* __restrict__ x,
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < NU; ++u) {
         const int nt = wave + 4 * u;
         if (nt < nnt) {
           const typename M::Frag bf = M::lds(Bt + (nt * 16 + col) * LD + kk);
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const IO* __restrict__ x,
   }
   float* out = states + (((int64_t)b * d.nc + c) * d.H + h) * d.P * d.N;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < NU; ++u) {
     const int nt = wave + 4 * u;
     if (nt >= nnt) continue;
 #pragma unroll
@@ -601,7 +602,9 @@ static hipError_t state_impl(const Dims& d, const void* x, const void* B, const 
                              const float* dtc, float* states, hipStream_t s) {
   constexpr int LD = SJ + Pad<T>::v;
   const size_t shm = (size_t)(64 * LD * (HILO ? 2 : 1) + d.N * LD) * sizeof(T) + SJ * 4;
-  auto kern = k_chunk_state<IO, T, HILO>;
+  // n-tile slots per wave: 2 for dstate <= 128 (76 registers in fp32 instead of 140, so twice
+  // the waves per SIMD), else 4 (a 1-slot build is larger than the 2-slot one: more hoisting)
+  auto kern = d.N <= 128 ? k_chunk_state<IO, T, HILO, 2> : k_chunk_state<IO, T, HILO, 4>;
   if (shm > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
