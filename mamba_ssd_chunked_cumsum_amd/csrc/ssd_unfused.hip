@@ -165,6 +165,66 @@ __global__ __launch_bounds__(256) void k_bmm_chunk(const IO* __restrict__ Bm,
   }
 }
 
+// Stage 2 for fp32 io with chunks of at most 64 tokens and dstate at most 128: the chunk's C and
+// B rows are staged in LDS once per block ([Q][N + 4] floats each: 16-byte rows, and the 16 rows
+// of a fragment fall in distinct banks; rows past the sequence are zero), then every 16x16 block
+// is computed from LDS. Each row serves up to four blocks of the lower triangle, which the
+// global-memory version reads once per block.
+__global__ __launch_bounds__(256) void k_bmm_chunk_lds(const float* __restrict__ Bm,
+                                                       const float* __restrict__ Cm,
+                                                       float* __restrict__ CB, Dims d) {
+  using M = Mma<float>;
+  extern __shared__ __align__(16) float sm_bmm[];
+  const int ldn = d.N + 4;
+  float* Cs = sm_bmm;
+  float* Bs = sm_bmm + d.Q * ldn;
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, kg = lane >> 4;
+  const int t0 = c * d.Q, q = min(d.Q, d.L - t0);
+  const int64_t rowstride = (int64_t)d.G * d.N;
+  const int64_t gbase = ((int64_t)b * d.L + t0) * rowstride + (int64_t)g * d.N;
+  {
+    // up to 64 x 128 floats per operand: 8 float4 per thread, all loads issued first
+    constexpr int NV = 64 * 128 / 4 / 256;
+    const int nv4 = d.N / 4, nall = d.Q * nv4;
+    float4 vc[NV], vb[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = min((int)threadIdx.x + 256 * u, nall - 1), r = e / nv4, c4 = e - r * nv4;
+      const int64_t o = gbase + (int64_t)min(r, q - 1) * rowstride + 4 * c4;
+      vc[u] = *reinterpret_cast<const float4*>(Cm + o);
+      vb[u] = *reinterpret_cast<const float4*>(Bm + o);
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = threadIdx.x + 256 * u, r = e / nv4, c4 = e - r * nv4;
+      if (e < nall) {
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(Cs + r * ldn + 4 * c4) = r < q ? vc[u] : z;
+        *reinterpret_cast<float4*>(Bs + r * ldn + 4 * c4) = r < q ? vb[u] : z;
+      }
+    }
+  }
+  __syncthreads();
+  const int nt = d.Q / 16, ntiles = nt * (nt + 1) / 2;
+  float* out = CB + (((int64_t)b * d.nc + c) * d.G + g) * d.Q * d.Q;
+  for (int k = wave; k < ntiles; k += 4) {
+    int ti = (int)((sqrtf(8.f * k + 1.f) - 1.f) * 0.5f);
+    while ((ti + 1) * (ti + 2) / 2 <= k) ++ti;
+    while (ti * (ti + 1) / 2 > k) --ti;
+    const int tj = k - ti * (ti + 1) / 2;
+    const float* ca = Cs + (ti * 16 + col) * ldn + kg;
+    const float* bb = Bs + (tj * 16 + col) * ldn + kg;
+    f32x4 acc = zero4();
+#pragma unroll 8
+    for (int k0 = 0; k0 < d.N; k0 += M::KSTEP) acc = M::mma(ca[k0], bb[k0], acc);
+    const int jb = tj * 16 + col;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[(int64_t)(ti * 16 + 4 * kg + r) * d.Q + jb] = acc[r];
+  }
+}
+
 // =============================================================================================
 // Stage 3: states[b, c, h, p, n] = sum_j w_j x[j, p] B[j, n], w_j = exp(Acs_last - Acs_j) dt_j.
 // Grid (nc * ceil(P/64), H, batch), 256 threads. Tokens are taken in slabs of SJ = 32; each slab
@@ -588,10 +648,19 @@ hipError_t launch_chunk_cumsum(const Dims& d, const float* dt, const float* A, f
 hipError_t launch_bmm_chunk(const Dims& d, int io, const void* B, const void* C, float* CB,
                             hipStream_t s) {
   dim3 grid(d.nc, d.G, d.Bt);
-  if (io == kIoBf16)
+  if (io == kIoBf16) {
     hipLaunchKernelGGL((k_bmm_chunk<u16, f16>), grid, dim3(256), 0, s, (const u16*)B,
                        (const u16*)C, CB, d);
-  else
+  } else if (d.Q <= 64 && d.N <= 128) {
+    const size_t shm = (size_t)2 * d.Q * (d.N + 4) * 4;
+    if (shm > 64 * 1024) {
+      hipError_t e = hipFuncSetAttribute((const void*)k_bmm_chunk_lds,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_bmm_chunk_lds, grid, dim3(256), shm, s, (const float*)B, (const float*)C,
+                       CB, d);
+  } else
     hipLaunchKernelGGL((k_bmm_chunk<float, float>), grid, dim3(256), 0, s, (const float*)B,
                        (const float*)C, CB, d);
   return hipGetLastError();
