@@ -13,6 +13,10 @@
 //                     intra-sub-chunk product, the readout of the carried state, the skip term
 //                     and the state update, all on chip; only y leaves the kernel.
 //
+// With one run per sequence (a short sequence, or enough batch and heads to fill the device)
+// there is nothing to chain: F1 writes its run state completed with the decayed initial state,
+// which is the final state, and F3 reads the initial state itself; F2 is not launched.
+//
 // Inside F1/F3 the run is walked in sub-chunks of T = 32 tokens, whatever the caller's chunk
 // length: the exact result does not depend on where the sequence is cut (the
 // chunk length cancels out of the recurrence), so the kernel picks the cut that suits the chip's

@@ -389,15 +389,30 @@ __global__ __launch_bounds__(256) void k_state_passing(const float* __restrict__
   if (h0) s = *reinterpret_cast<const float4*>(h0 + sb);
   const float* ldp = ld + ((int64_t)b * d.H + h) * ld_bh;
   const int64_t cstride = (int64_t)d.H * PN;
-  int64_t off = ((int64_t)b * nsteps * d.H + h) * PN + e;
-  for (int c = 0; c < nsteps; ++c, off += cstride) {
-    if (h_in) *reinterpret_cast<float4*>(h_in + off) = s;
-    const float a = __expf(ldp[(int64_t)c * ld_step]);
-    const float4 st = *reinterpret_cast<const float4*>(states + off);
-    s.x = a * s.x + st.x;
-    s.y = a * s.y + st.y;
-    s.z = a * s.z + st.z;
-    s.w = a * s.w + st.w;
+  const int64_t off0 = ((int64_t)b * nsteps * d.H + h) * PN + e;
+  // 8 steps' states and decays loaded together (clamped to the last step), then the chain: only
+  // the multiply-adds depend on the step before
+  constexpr int GS = 8;
+  for (int c0 = 0; c0 < nsteps; c0 += GS) {
+    float4 st[GS];
+    float a[GS];
+#pragma unroll
+    for (int u = 0; u < GS; ++u) {
+      const int c = min(c0 + u, nsteps - 1);
+      st[u] = *reinterpret_cast<const float4*>(states + off0 + c * cstride);
+      a[u] = ldp[(int64_t)c * ld_step];
+    }
+#pragma unroll
+    for (int u = 0; u < GS; ++u) {
+      if (c0 + u < nsteps) {
+        if (h_in) *reinterpret_cast<float4*>(h_in + off0 + (c0 + u) * cstride) = s;
+        const float dec = __expf(a[u]);
+        s.x = dec * s.x + st[u].x;
+        s.y = dec * s.y + st[u].y;
+        s.z = dec * s.z + st[u].z;
+        s.w = dec * s.w + st[u].w;
+      }
+    }
   }
   if (fin) *reinterpret_cast<float4*>(fin + sb) = s;
 }
