@@ -185,24 +185,29 @@ __global__ __launch_bounds__(256) void k_bmm_chunk_lds(const float* __restrict__
   const int64_t rowstride = (int64_t)d.G * d.N;
   const int64_t gbase = ((int64_t)b * d.L + t0) * rowstride + (int64_t)g * d.N;
   {
-    // up to 64 x 128 floats per operand: 8 float4 per thread, all loads issued first
-    constexpr int NV = 64 * 128 / 4 / 256;
-    const int nv4 = d.N / 4, nall = d.Q * nv4;
-    float4 vc[NV], vb[NV];
+    // up to 64 rows x 128 floats per operand: thread = (float4 column tid % 32, rows tid / 32
+    // + 8 u), 8 float4 per operand, all loads issued first from clamped rows and columns
+    const int nv4 = d.N / 4, c4 = threadIdx.x & 31, r0 = threadIdx.x >> 5;
+    const int c4c = min(c4, nv4 - 1);
+    float4 vc[8], vb[8];
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int e = min((int)threadIdx.x + 256 * u, nall - 1), r = e / nv4, c4 = e - r * nv4;
-      const int64_t o = gbase + (int64_t)min(r, q - 1) * rowstride + 4 * c4;
+    for (int u = 0; u < 8; ++u) {
+      const int64_t o = gbase + (int64_t)min(r0 + 8 * u, q - 1) * rowstride + 4 * c4c;
       vc[u] = *reinterpret_cast<const float4*>(Cm + o);
       vb[u] = *reinterpret_cast<const float4*>(Bm + o);
     }
+    // rows past the sequence are zeroed component by component (a select between two float4
+    // values would become a load through a selected pointer, which puts the arrays in scratch)
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int e = threadIdx.x + 256 * u, r = e / nv4, c4 = e - r * nv4;
-      if (e < nall) {
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(Cs + r * ldn + 4 * c4) = r < q ? vc[u] : z;
-        *reinterpret_cast<float4*>(Bs + r * ldn + 4 * c4) = r < q ? vb[u] : z;
+    for (int u = 0; u < 8; ++u) {
+      const int r = r0 + 8 * u;
+      if (c4 < nv4 && r < d.Q) {
+        const bool in = r < q;
+        const float4 c = vc[u], bv = vb[u];
+        *reinterpret_cast<float4*>(Cs + r * ldn + 4 * c4) =
+            make_float4(in ? c.x : 0.f, in ? c.y : 0.f, in ? c.z : 0.f, in ? c.w : 0.f);
+        *reinterpret_cast<float4*>(Bs + r * ldn + 4 * c4) =
+            make_float4(in ? bv.x : 0.f, in ? bv.y : 0.f, in ? bv.z : 0.f, in ? bv.w : 0.f);
       }
     }
   }
