@@ -13,13 +13,21 @@ pytestmark = pytest.mark.gpu
 
 
 def _launch(shape, want_final=True, variant="auto"):
+    """Per-kernel event intervals of one call, after an untimed call of the same problem (the
+    first calls of a process show event gaps of several microseconds)."""
     d = to_device(synth.make_inputs(shape, seed=3), shape.io)
-    timer = libssd.KernelTimer()
     note(f"dispatch {shape} want_final={want_final}")
-    ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], shape.chunk_size,
-                d["initial_state"], variant=variant, want_final=want_final, timer=timer)
-    torch.cuda.synchronize()
+    for timer in (None, libssd.KernelTimer()):
+        ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], shape.chunk_size,
+                    d["initial_state"], variant=variant, want_final=want_final, timer=timer)
+        torch.cuda.synchronize()
     return timer.times_ms()
+
+
+# An empty interval (two events recorded back to back) against the scan kernel's time, and the
+# share a kernel that ran takes at least at these shapes (run states and the chain take 30% or
+# more of the scan's time there; an empty interval has measured below 11%).
+EMPTY, RAN = 0.25, 0.3
 
 
 def test_tiny_fp32_takes_the_quadratic_kernel():
@@ -41,15 +49,13 @@ def test_batched_prefill_runs_without_the_chain():
     shape = synth.SSDShape("prefill", 16, 300, 80, 64, 128, 1, 256, init_state=True)
     t = _launch(shape)
     assert list(t) == ["run_state", "state_passing", "fused_scan"], t
-    # an empty interval (two events back to back) against the scan kernel's time
-    empty = 0.1 * t["fused_scan"]
-    assert t["state_passing"] < empty < t["run_state"], t
+    assert t["state_passing"] < EMPTY * t["fused_scan"], t
+    assert t["run_state"] > RAN * t["fused_scan"], t
     t = _launch(shape, want_final=False)
-    empty = 0.1 * t["fused_scan"]
-    assert t["run_state"] < empty and t["state_passing"] < empty, t
+    assert max(t["run_state"], t["state_passing"]) < EMPTY * t["fused_scan"], t
 
 
 def test_long_bf16_sequence_chains_runs():
     t = _launch(synth.CONFIGS[1])
     assert list(t) == ["run_state", "state_passing", "fused_scan"], t
-    assert t["state_passing"] > 0.1 * t["fused_scan"], t       # the chain kernel ran
+    assert t["state_passing"] > RAN * t["fused_scan"], t       # the chain kernel ran
