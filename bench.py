@@ -297,7 +297,7 @@ def short_sequence_bench(dev, flush, flush_out, steps: int = 10) -> dict:
     from mamba_ssd_chunked_cumsum_amd import synth
 
     cases = [
-        ("tiny_fp32 (1 x 256 tokens, 2 heads, headdim 16, dstate 16)", synth.CONFIGS[0],
+        ("tiny_fp32 (1 x 256 tokens, 2 heads, headdim 16, dstate 16)", synth.config("tiny_fp32"),
          ("auto", "unfused")),
         ("batched_prefill_bf16 (32 x 128 tokens, 80 heads, headdim 64, dstate 128)",
          synth.SSDShape("batched_prefill", 32, 128, 80, 64, 128, 1, 128, init_state=True),

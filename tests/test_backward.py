@@ -128,7 +128,7 @@ def test_backward_full_size_sampled_heads():
     a head depend on that head only; dB and dC sum over all 80 heads and are checked above at
     sizes the oracle covers whole)."""
     from mamba_ssd_chunked_cumsum_amd import synth
-    shape = synth.CONFIGS[2]
+    shape = synth.config("mamba2_2p7b_layer")
     inp = synth.make_inputs(shape, cfg_index=2)
     rng = np.random.default_rng(77)
     dy = _bf16_exact(rng.standard_normal(inp["x"].shape).astype(np.float32))

@@ -31,7 +31,7 @@ EMPTY, RAN = 0.25, 0.3
 
 
 def test_tiny_fp32_takes_the_quadratic_kernel():
-    t = _launch(synth.CONFIGS[0])
+    t = _launch(synth.config("tiny_fp32"))
     assert list(t) == ["quadratic"], t
 
 
@@ -56,6 +56,6 @@ def test_batched_prefill_runs_without_the_chain():
 
 
 def test_long_bf16_sequence_chains_runs():
-    t = _launch(synth.CONFIGS[1])
+    t = _launch(synth.config("mamba2_130m_layer"))
     assert list(t) == ["run_state", "state_passing", "fused_scan"], t
     assert t["state_passing"] > RAN * t["fused_scan"], t       # the chain kernel ran

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _inputs():
-    shape = synth.CONFIGS[1].replace(seqlen=128, batch=1, nheads=2)
+    shape = synth.config("mamba2_130m_layer").replace(seqlen=128, batch=1, nheads=2)
     return to_device(synth.make_inputs(shape, seed=1), "bf16")
 
 

@@ -164,7 +164,7 @@ def test_native_matches_numpy_on_workload(cfg):
 
 def test_native_matches_numpy_mamba_shaped():
     """A shortened Mamba-2-130M-shaped layer (L = 256), bf16 inputs, nonzero initial state."""
-    shape = synth.CONFIGS[1].replace(seqlen=256, batch=2, init_state=True)
+    shape = synth.config("mamba2_130m_layer").replace(seqlen=256, batch=2, init_state=True)
     inp = synth.make_inputs(shape, seed=21)
     y, f = ssd_recurrence(**inp)
     yc, fc = native.forward(**inp)

@@ -115,7 +115,7 @@ def test_single_run_plan(shape, precision):
 
 
 def test_single_run_null_state_and_no_final():
-    shape = synth.CONFIGS[1].replace(seqlen=200, batch=2)
+    shape = synth.config("mamba2_130m_layer").replace(seqlen=200, batch=2)
     d = to_device(synth.make_inputs(shape, seed=13), "bf16")
     note("single run: null initial state, no final state")
     y0, f0 = run_gpu(d, 64, "fused", run_chunks=1000)
@@ -153,7 +153,7 @@ def test_strong_decay(shape, variant):
 @pytest.mark.parametrize("precision", ["fp16", "fp32"])
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_precision_options(precision, variant):
-    shape = synth.CONFIGS[1].replace(seqlen=512)
+    shape = synth.config("mamba2_130m_layer").replace(seqlen=512)
     skip_unfusable(shape, variant, precision)
     rep = check_shape(shape, seed=5, variant=variant, precision=precision)
     assert rep["pass"], rep
@@ -163,7 +163,7 @@ def test_precision_options(precision, variant):
 
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_null_initial_state_equals_zeros_and_no_final(variant):
-    shape = synth.CONFIGS[1].replace(seqlen=300, batch=1)
+    shape = synth.config("mamba2_130m_layer").replace(seqlen=300, batch=1)
     inp = synth.make_inputs(shape, seed=3)
     d = to_device(inp, "bf16")
     note(f"null-vs-zero {variant}")
@@ -178,7 +178,7 @@ def test_null_initial_state_equals_zeros_and_no_final(variant):
 
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_deterministic(variant):
-    shape = synth.CONFIGS[1].replace(seqlen=1024)
+    shape = synth.config("mamba2_130m_layer").replace(seqlen=1024)
     d = to_device(synth.make_inputs(shape, seed=8), "bf16")
     note(f"determinism {variant}")
     ya, fa = run_gpu(d, 64, variant)
@@ -188,7 +188,7 @@ def test_deterministic(variant):
 
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_zero_readout_gives_skip_exactly(variant):
-    shape = synth.CONFIGS[1].replace(seqlen=256, batch=1)
+    shape = synth.config("mamba2_130m_layer").replace(seqlen=256, batch=1)
     inp = synth.make_inputs(shape, seed=4)
     inp["C"] = np.zeros_like(inp["C"])
     d = to_device(inp, "bf16")
@@ -207,7 +207,7 @@ def test_zero_readout_gives_skip_exactly(variant):
 
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_causality(variant):
-    shape = synth.CONFIGS[1].replace(seqlen=256, batch=1)
+    shape = synth.config("mamba2_130m_layer").replace(seqlen=256, batch=1)
     inp = synth.make_inputs(shape, seed=6)
     d = to_device(inp, "bf16")
     note(f"causality {variant}")
@@ -221,7 +221,7 @@ def test_causality(variant):
 
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_chunk_size_invariance_and_state_composition(variant):
-    shape = synth.CONFIGS[1].replace(seqlen=700, batch=2, nheads=6, init_state=True)
+    shape = synth.config("mamba2_130m_layer").replace(seqlen=700, batch=2, nheads=6, init_state=True)
     inp = synth.make_inputs(shape, seed=9)
     y_ref, f_ref = native.forward(**inp)
     d = to_device(inp, "bf16")

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 FP32_BAR = 1e-4
 
 QUAD_SHAPES = [
-    synth.CONFIGS[0],                                                        # tiny fp32 workload
+    synth.config("tiny_fp32"),                                                        # tiny fp32 workload
     synth.SSDShape("len1", 1, 1, 2, 16, 16, 1, 64, init_state=True),
     synth.SSDShape("len256_p64n128", 2, 256, 4, 64, 128, 1, 64, init_state=True),
     synth.SSDShape("ragged_p48n48_g2", 2, 130, 4, 48, 48, 2, 32, io="f32", init_state=True),

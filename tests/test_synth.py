@@ -36,7 +36,7 @@ def test_reproducible_and_shapes(idx):
 
 
 def test_bf16_rounding_is_rne_and_exact():
-    s = synth.CONFIGS[1].replace(seqlen=64)
+    s = synth.config("mamba2_130m_layer").replace(seqlen=64)
     inp = synth.make_inputs(s)
     for k in ("x", "B", "C"):
         bits = synth.bf16_bits(inp[k])                       # raises if not bf16-exact
@@ -48,7 +48,7 @@ def test_bf16_rounding_is_rne_and_exact():
 
 
 def test_dt_distribution():
-    s = synth.CONFIGS[1].replace(seqlen=512)
+    s = synth.config("mamba2_130m_layer").replace(seqlen=512)
     dt = synth.make_inputs(s)["dt"]
     assert 1e-5 < dt.min() and dt.max() < 2.0
     med = np.median(dt, axis=(0, 1))            # per-head median tracks the log-uniform bias
@@ -56,10 +56,10 @@ def test_dt_distribution():
 
 
 def test_initial_state_and_d():
-    s3 = synth.CONFIGS[3].replace(seqlen=64)
+    s3 = synth.config("long_seq_layer").replace(seqlen=64)
     inp = synth.make_inputs(s3, cfg_index=3)
     assert inp["initial_state"].shape == (1, 32, 64, 128)
-    s4 = synth.CONFIGS[4].replace(seqlen=32)
+    s4 = synth.config("wide_grouped_layer").replace(seqlen=32)
     d = synth.make_inputs(s4, cfg_index=4)["D"]
     assert d.shape == (64,) and 0.5 < d.mean() < 1.5 and d.std() > 0.01
-    assert np.all(synth.make_inputs(synth.CONFIGS[0])["D"] == 1.0)
+    assert np.all(synth.make_inputs(synth.config("tiny_fp32"))["D"] == 1.0)
