@@ -81,16 +81,21 @@ __device__ __forceinline__ double wave_scan_f64(double v) {
   return v;
 }
 
-// One wave per (b, t, h); lanes over p (strided when P > 64).
+// dx = D dy + dt u, and the per-(b, t, h) sums the decay gradients are built from.
 template <typename IO>
 __global__ __launch_bounds__(256) void k_bwd_pointwise(
     const IO* __restrict__ x, const IO* __restrict__ dy, const float* __restrict__ ur,
     const float* __restrict__ ys, const float* __restrict__ dt, const float* __restrict__ D,
     float* __restrict__ dx, float* __restrict__ q, float* __restrict__ xu,
     float* __restrict__ dyx, int Bt, int L, int H, int P) {
-  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (unit >= (int64_t)Bt * L * H) return;  // wave-uniform
+  // 16 lanes per (b, t, h) unit, four units per wave: lane k of a unit takes p = 4 k + 64 m
+  // (16-byte accesses); headdim is a multiple of 16. Lanes of a unit past the last one compute on
+  // a clamped unit and store nothing (all lanes take part in the reductions).
+  const int64_t nunit = (int64_t)Bt * L * H;
+  const int64_t unit_raw = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const bool valid = unit_raw < nunit;
+  const int64_t unit = valid ? unit_raw : nunit - 1;
+  const int sl = threadIdx.x & 15;
   const int h = (int)(unit % H);
   const int t = (int)((unit / H) % L);
   const int b = (int)(unit / ((int64_t)H * L));
@@ -98,18 +103,33 @@ __global__ __launch_bounds__(256) void k_bwd_pointwise(
   const int64_t row = unit * P;                                          // [b, t, h, :]
   const int64_t rrow = (((int64_t)b * L + (L - 1 - t)) * H + h) * P;    // reversed time
   float s_dyys = 0.f, s_xu = 0.f, s_dyx = 0.f;
-  for (int p = lane; p < P; p += 64) {
-    const float xv = Io<IO>::load(x, row + p), dyv = Io<IO>::load(dy, row + p);
-    const float u = ur[rrow + p];
-    dx[row + p] = dh * dyv + dtv * u;
-    s_dyys += dyv * ys[row + p];
-    s_xu += xv * u;
-    s_dyx += dyv * xv;
+  for (int p = 4 * sl; p < P; p += 64) {
+    float xv[4], dyv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      xv[k] = Io<IO>::load(x, row + p + k);
+      dyv[k] = Io<IO>::load(dy, row + p + k);
+    }
+    const float4 u = *reinterpret_cast<const float4*>(ur + rrow + p);
+    const float4 yv = *reinterpret_cast<const float4*>(ys + row + p);
+    const float uu[4] = {u.x, u.y, u.z, u.w}, yy[4] = {yv.x, yv.y, yv.z, yv.w};
+    float o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[k] = dh * dyv[k] + dtv * uu[k];
+      s_dyys += dyv[k] * yy[k];
+      s_xu += xv[k] * uu[k];
+      s_dyx += dyv[k] * xv[k];
+    }
+    if (valid) *reinterpret_cast<float4*>(dx + row + p) = make_float4(o[0], o[1], o[2], o[3]);
   }
-  s_dyys = wave_sum(s_dyys);
-  s_xu = wave_sum(s_xu);
-  s_dyx = wave_sum(s_dyx);
-  if (lane == 0) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) {
+    s_dyys += __shfl_xor(s_dyys, off, 16);
+    s_xu += __shfl_xor(s_xu, off, 16);
+    s_dyx += __shfl_xor(s_dyx, off, 16);
+  }
+  if (valid && sl == 0) {
     q[unit] = s_dyys - dtv * s_xu;
     xu[unit] = s_xu;
     dyx[unit] = s_dyx;
@@ -278,7 +298,7 @@ hipError_t launch_bwd_pointwise(int io, const void* x, const void* dy, const flo
                                 float* q, float* xu, float* dyx, int Bt, int L, int H, int P,
                                 hipStream_t s) {
   const int64_t units = (int64_t)Bt * L * H;
-  const dim3 grid((unsigned)((units + 3) / 4));
+  const dim3 grid((unsigned)((units + 15) / 16));  // 16 units per block
   if (io == kIoBf16)
     hipLaunchKernelGGL(k_bwd_pointwise<u16>, grid, dim3(256), 0, s, (const u16*)x,
                        (const u16*)dy, ur, ys, dt, D, dx, q, xu, dyx, Bt, L, H, P);
