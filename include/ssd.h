@@ -26,8 +26,8 @@
  * Ownership: the caller owns every buffer; the library keeps no pointer after a call returns.
  * Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null stream):
  * device faults surface at the caller's next synchronisation. Workspace (unfused path, and the
- * segment states of the fused path) is allocated stream-ordered on `stream` and released the same
- * way.
+ * run states and chain counters of the fused path) is allocated stream-ordered on `stream` and
+ * released the same way.
  *
  * Errors: every argument check runs on the host before any HIP call; on failure nothing is
  * launched and nothing is written. Status codes are never thrown across the ABI.
@@ -73,15 +73,17 @@ typedef enum {
     SSD_VARIANT_AUTO = 0,
     SSD_VARIANT_UNFUSED = 1, /* cumsum, C B^T, chunk states, state passing, chunk scan: five
                                 kernels, intermediates in workspace */
-    SSD_VARIANT_FUSED = 2,   /* bf16 io, headdim 64 or 128, dstate 64, 128 or 256: three kernels
-                                (run states, state passing over runs, fused scan). The sequence is
-                                cut into runs (about one block per compute unit); inside a run
-                                the state stays on chip and each sub-chunk of 32 tokens gets its
-                                C B^T block, decay mask, readout and state update without leaving
-                                the compute unit. The exact result
-                                does not depend on the chunk length, so chunk_size only sets
-                                the run length when run_chunks is given. Assumes A <= 0 and
-                                dt >= 0 (decays at most 1); D enters through the fp16 diagonal
+    SSD_VARIANT_FUSED = 2,   /* bf16 io, headdim 64 or 128, dstate 64, 128 or 256: one forward
+                                kernel (after a reset of its chain counters when a sequence is cut
+                                into several runs). The sequence is cut into runs (about one block
+                                per compute unit); a block computes its run's own end state, the
+                                blocks of a sequence then chain those states into the state
+                                entering each run and the final state, and each block walks its
+                                run in sub-chunks of 32 tokens with the state on chip: C B^T block,
+                                decay mask, readout and state update never leave the compute unit.
+                                The exact result does not depend on the chunk length, so chunk_size
+                                only sets the run length when run_chunks is given. Assumes A <= 0
+                                and dt >= 0 (decays at most 1); D enters through the fp16 diagonal
                                 of the masked block (exact for D = 1) */
     SSD_VARIANT_QUADRATIC = 3 /* seqlen <= 256, dstate <= 256, either io: one kernel, the whole
                                 sequence as a single block of the quadratic (masked,
@@ -106,18 +108,15 @@ typedef struct {
     int32_t variant;    /* ssd_variant */
     int32_t precision;  /* ssd_precision */
     int32_t run_chunks; /* fused variant: runs of run_chunks * chunk_size tokens (rounded up to
-                           the kernels' sub-chunk); 0 = chosen from the problem size and the
+                           64 tokens, and lengthened where needed so that a sequence has at most
+                           one run per compute unit); 0 = chosen from the problem size and the
                            device's compute units; must be >= 0 */
     int32_t n_events;   /* capacity of `events`; 0 = no timing events */
     void** events;      /* optional hipEvent_t[n_events], created by the caller: events[0] is
                            recorded on `stream` before the first kernel and events[k] after the
                            k-th kernel, so the caller can time each kernel. Needs n_events >=
                            kernels + 1 (6 covers every variant), else SSD_ERR_INVALID_ARGUMENT. */
-    int32_t* n_kernels; /* optional out: number of kernels the call launched (fused 3: run
-                           states, state passing over runs, fused scan; unfused 5: cumsum,
-                           C B^T, chunk states, state passing, chunk scan; quadratic 1). A fused
-                           call with one run per sequence leaves the state-passing interval
-                           empty (and the run-state one when no final state is wanted). */
+    int32_t* n_kernels; /* optional out: number of kernels the call launched */
     /* dt pre-processing, applied by the kernels where they read dt (no separate pass), in this
      * order: dt + dt_bias[h]; softplus, log(1 + exp(v)) (v itself above 20, where the two agree
      * to fp32 precision); clamp to [dt_min, dt_max]. The recurrence then runs on that dt. With
@@ -126,7 +125,21 @@ typedef struct {
     int32_t dt_softplus;  /* nonzero: apply softplus */
     float dt_min, dt_max; /* dt_max > 0: clamp to [dt_min, dt_max] (needs dt_min <= dt_max);
                              dt_max == 0: no clamp; dt_max < 0 is invalid */
+    int32_t* kernel_mask; /* optional out: the ssd_kernel bits of the kernels the call launched;
+                             they were launched in increasing bit order */
 } ssd_options;
+
+/* Kernels of a forward, as reported in ssd_options.kernel_mask. */
+typedef enum {
+    SSD_KERNEL_QUADRATIC = 1,       /* quadratic variant: the whole forward */
+    SSD_KERNEL_CHUNK_CUMSUM = 2,    /* unfused: stage 1 */
+    SSD_KERNEL_BMM_CHUNK = 4,       /* unfused: stage 2 */
+    SSD_KERNEL_CHUNK_STATE = 8,     /* unfused: stage 3 */
+    SSD_KERNEL_STATE_PASSING = 16,  /* unfused: stage 4 */
+    SSD_KERNEL_CHUNK_SCAN = 32,     /* unfused: stage 5 */
+    SSD_KERNEL_SYNC_RESET = 64,     /* fused, several runs per sequence: zeroes the chain counters */
+    SSD_KERNEL_FUSED_FORWARD = 128  /* fused: the whole forward */
+} ssd_kernel;
 
 /* Full forward. initial_state may be NULL (zeros); final_state may be NULL (not written).
  * Alignment: every pointer 16-byte aligned. y must not overlap any input; final_state must not

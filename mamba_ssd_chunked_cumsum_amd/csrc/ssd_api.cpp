@@ -13,7 +13,8 @@ namespace {
 
 using ssd::Dims;
 
-constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;  // 1.2: ssd_backward; 1.3: quadratic variant
+constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;  // 1.2: ssd_backward; 1.3: quadratic variant;
+                                                   // 1.4: one-kernel fused forward, kernel_mask
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
 
 struct Range {
@@ -143,14 +144,7 @@ ssd_status check_forward_args(const ssd_problem* prob, const void* x, const floa
 }
 
 // Optional timing events around each kernel (caller-owned hipEvent_t's).
-struct Timer {
-  void** ev = nullptr;
-  int n = 0, k = 0;
-  hipError_t mark(hipStream_t s) {
-    if (!ev || k >= n) return hipSuccess;
-    return hipEventRecord(static_cast<hipEvent_t>(ev[k++]), s);
-  }
-};
+using Timer = ssd::KernelMarks;
 
 struct Workspace {
   float *Acs, *dtc, *CB, *states, *h_in;
@@ -219,46 +213,28 @@ int compute_units() {
   return n;
 }
 
-// Fused forward: F1 run states, F2 chain over runs (state entering each run, final state),
-// F3 fused scan. Runs are run_chunks chunks long when run_chunks > 0, else planned to give about
-// one block per compute unit (each run boundary costs one fp32 state write and read). With one
-// run per sequence (short sequences, or enough batch and heads to fill the device) there is
-// nothing to chain: F1 completes its run state into the final state (skipped when that is not
-// wanted) and F3 starts from the initial state itself.
+// Fused forward: one kernel (after a reset of its chain counters when a sequence has several
+// runs). Runs are run_chunks chunks long when run_chunks > 0, else planned to give about one block
+// per compute unit (each run boundary costs one fp32 state write and read). The workspace (run
+// states, decays, counters; none with one run per sequence) is allocated stream-ordered.
 ssd_status run_fused(const Dims& d, const ssd::FusedPlan& fp, const void* x, const float* dt,
                      const float* A, const void* B, const void* C, const float* D,
                      const float* h0, void* y, float* fin, hipStream_t s, Timer& t) {
-  const int nr = fp.nr;
-  if (nr == 1) {  // the F2 interval of the timer stays empty
-    hipError_t e = t.mark(s);
-    if (e == hipSuccess && fin) e = ssd::launch_final_state(d, fp, x, B, dt, A, h0, fin, s);
-    if (e == hipSuccess) e = t.mark(s);
-    if (e == hipSuccess) e = t.mark(s);
-    if (e == hipSuccess) e = ssd::launch_fused_scan(d, fp, x, B, C, dt, A, D, h0, y, s);
-    if (e == hipSuccess) e = t.mark(s);
-    return from_hip(e);
-  }
-  const int64_t st_bytes = (int64_t)d.Bt * nr * d.H * d.P * d.N * 4;
-  const int64_t ld_bytes = (int64_t)d.Bt * d.H * nr * 4;
-  const int64_t a = (st_bytes + 255) & ~int64_t(255);
-  const int64_t total = 2 * a + ((ld_bytes + 255) & ~int64_t(255));
-  void* base = nullptr;
-  if (hipMallocAsync(&base, (size_t)total, s) != hipSuccess) return SSD_ERR_OUT_OF_MEMORY;
-  char* b = static_cast<char*>(base);
-  float* states = reinterpret_cast<float*>(b);
-  float* h_run = reinterpret_cast<float*>(b + a);
-  float* logdecay = reinterpret_cast<float*>(b + 2 * a);
-  hipError_t e = t.mark(s);
-  if (e == hipSuccess) e = ssd::launch_run_state(d, fp, x, B, dt, A, states, logdecay, s);
-  if (e == hipSuccess) e = t.mark(s);
-  if (e == hipSuccess)
-    e = ssd::launch_chain_passing(d, nr, states, logdecay, nr, 1, h0, h_run, fin, s);
-  if (e == hipSuccess) e = t.mark(s);
-  if (e == hipSuccess) e = ssd::launch_fused_scan(d, fp, x, B, C, dt, A, D, h_run, y, s);
-  if (e == hipSuccess) e = t.mark(s);
-  hipError_t ef = hipFreeAsync(base, s);
+  const int64_t bytes = ssd::fused_workspace_bytes(d, fp);
+  void* ws = nullptr;
+  if (bytes > 0 && hipMallocAsync(&ws, (size_t)bytes, s) != hipSuccess)
+    return SSD_ERR_OUT_OF_MEMORY;
+  hipError_t e = ssd::launch_fused(d, fp, x, B, C, dt, A, D, h0, y, fin, ws, &t, s);
+  hipError_t ef = ws ? hipFreeAsync(ws, s) : hipSuccess;
   if (e != hipSuccess) return from_hip(e);
   return from_hip(ef);
+}
+
+// The kernels a forward launches, for the caller's optional out fields.
+void report_kernels(const ssd_options* o, int mask) {
+  if (!o) return;
+  if (o->n_kernels) *o->n_kernels = __builtin_popcount((unsigned)mask);
+  if (o->kernel_mask) *o->kernel_mask = mask;
 }
 
 }  // namespace
@@ -319,7 +295,7 @@ ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* d
                          (int64_t)d.L * d.N <= 8192 &&
                          ssd::quadratic_blocks(d) <= 2 * (int64_t)compute_units();
   if (variant == SSD_VARIANT_QUADRATIC || quad_auto) {
-    if (opts && opts->n_kernels) *opts->n_kernels = 1;
+    report_kernels(opts, SSD_KERNEL_QUADRATIC);
     hipError_t e = t.mark(s);
     if (e == hipSuccess)
       e = ssd::launch_quadratic(d, prob->io_dtype, x, dt, A, B, C, D, initial_state, y,
@@ -328,7 +304,12 @@ ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* d
     return from_hip(e);
   }
   const bool fused = variant != SSD_VARIANT_UNFUSED && fusable;
-  if (opts && opts->n_kernels) *opts->n_kernels = fused ? 3 : 5;
+  if (fused)
+    report_kernels(opts, (fp.nr > 1 ? SSD_KERNEL_SYNC_RESET : 0) | SSD_KERNEL_FUSED_FORWARD);
+  else
+    report_kernels(opts, SSD_KERNEL_CHUNK_CUMSUM | SSD_KERNEL_BMM_CHUNK |
+                             SSD_KERNEL_CHUNK_STATE | SSD_KERNEL_STATE_PASSING |
+                             SSD_KERNEL_CHUNK_SCAN);
   if (fused)
     return run_fused(d, fp, x, dt, A, B, C, D, initial_state, y, final_state, s, t);
   return run_unfused(prob, d, prec, x, dt, A, B, C, D, initial_state, y, final_state, s, t);
@@ -400,10 +381,7 @@ ssd_status ssd_chunk_state(const ssd_problem* prob, const void* x, const void* B
 // The backward's own chunk length: its fp32 recurrences cost least with short chunks (the
 // quadratic intra-chunk work shrinks with the chunk, the chunk states it adds are cheap), and the
 // result does not depend on where the chunks start.
-#ifndef SSD_BWD_Q
-#define SSD_BWD_Q 64
-#endif
-constexpr int64_t kBackwardChunk = SSD_BWD_Q;
+constexpr int64_t kBackwardChunk = 64;
 
 ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt, const float* A,
                         const void* B, const void* C, const float* D, int64_t chunk_size,

@@ -1,26 +1,34 @@
-// Fused SSD chunked forward (bf16 io).
+// Fused SSD chunked forward (bf16 io): one kernel for the whole forward.
 //
 // The chunked algorithm ("nitter.gq/da_be19" thread, post 5/6; stage order as in "Mamba-2 in
 // NVIDIA cuTile: Faster Forward Kernels and What the Benchmark Means", section "Why Mamba-2 is a
 // useful kernel example") needs the state entering every chunk. A (batch, head)'s fp32 state
 // (P x N) is as large as its bf16 x tile of 256 tokens, so materialising one per chunk would
 // double the HBM traffic. Here each sequence is cut into a few runs of consecutive tokens (about
-// one block per compute unit in total):
+// one block per compute unit in total), and one block per (batch, head block, run) does, in one
+// launch:
 //
-//   F1 k_run_state    each run's own end state (zero entry state) and total log-decay
-//   F2 k_state_pass   (shared with the unfused path) the state entering each run; final state
-//   F3 k_fused_scan   per run, sub-chunk by sub-chunk: cumulative decay, C B^T, the masked
-//                     intra-sub-chunk product, the readout of the carried state, the skip term
-//                     and the state update, all on chip; only y leaves the kernel.
+//   phase A   its run's own end state (zero entry state) and total log-decay, kept in registers
+//             and published to a workspace slot;
+//   chain     once every run of its chain (batch, head block) has published, the block walks the
+//             runs for 1 / nr of the chain's state entries, h_in(r+1) = exp(logdecay_r) h_in(r)
+//             + state_r, overwriting each run's slot with the state entering the next run, and
+//             writes the final state;
+//   phase B   once every part of the chain is written, its run sub-chunk by sub-chunk:
+//             cumulative decay, C B^T, the masked intra-sub-chunk product, the readout of the
+//             carried state, the skip term and the state update, all on chip; only y leaves.
 //
-// With one run per sequence (a short sequence, or enough batch and heads to fill the device)
-// there is nothing to chain: F1 writes its run state completed with the decayed initial state,
-// which is the final state, and F3 reads the initial state itself; F2 is not launched.
+// Blocks take their (chain, run) from a ticket counter in start order, chains one after another,
+// so a block only ever waits for blocks of its own chain, and every such block has started or
+// will start as soon as a compute unit is free: with at most one run per compute unit in a
+// sequence, the waits always end. With one run per sequence there is no chain: phase A completes
+// its state into the final state (S + exp(sum of dt A) h0; skipped when no final state is
+// wanted) and phase B starts from the initial state itself.
 //
-// Inside F1/F3 the run is walked in sub-chunks of T = 32 tokens, whatever the caller's chunk
-// length: the exact result does not depend on where the sequence is cut (the
-// chunk length cancels out of the recurrence), so the kernel picks the cut that suits the chip's
-// registers and LDS. The caller's chunk length still fixes the stage entry points' outputs.
+// Inside the phases the run is walked in sub-chunks of T = 32 tokens, whatever the caller's chunk
+// length: the exact result does not depend on where the sequence is cut (the chunk length cancels
+// out of the recurrence), so the kernel picks the cut that suits the chip's registers and LDS.
+// The caller's chunk length still fixes the stage entry points' outputs.
 //
 // Work split (one 512-thread block per compute unit, two waves per SIMD): a wave owns one head's
 // p-slice of PS columns (PS * N <= 8192, so its fp32 state is at most 128 registers per lane; at
@@ -30,18 +38,18 @@
 //
 // Staging: x, B and C tiles are copied global -> LDS by the gfx950 LDS DMA (global_load_lds
 // dwordx4), which needs no registers, so a whole sub-chunk is in flight while the previous one is
-// computed (F3: two stages, F1: three). The DMA writes each wave instruction's 64 pieces of 16
-// bytes contiguously; the swizzle (16-byte piece c of row t stored at position c ^ key(t)) is
-// applied by choosing which global piece each lane fetches. B and C are converted to fp16 in
+// computed (phase B: two stages, phase A: three). The DMA writes each wave instruction's 64 pieces
+// of 16 bytes contiguously; the swizzle (16-byte piece c of row t stored at position c ^ key(t))
+// is applied by choosing which global piece each lane fetches. B and C are converted to fp16 in
 // place after arrival; x stays raw bf16 (the skip term D x uses it exactly) and is converted while
 // its fragments are built. Fragments whose K index is the token are read with the gfx950
 // transposing LDS load (ds_read_b64_tr_b16).
 //
 // Matrix-core operand precision: x, B, C enter as exact fp16 copies of the bf16 inputs (inputs
 // are assumed to lie in fp16's range); the decay-masked C B^T block, the carried state (for the
-// readout) and the decay-weighted x (for the state update) are rounded to fp16; F1 splits the
-// weighted x into fp16 high and low parts (two passes), so the run states that are chained over
-// the sequence carry near-fp32 accuracy. All accumulation is fp32.
+// readout) and the decay-weighted x (for the state update) are rounded to fp16; phase A splits
+// the weighted x into fp16 high and low parts (two passes), so the run states that are chained
+// over the sequence, and the final state, carry near-fp32 accuracy. All accumulation is fp32.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -54,15 +62,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-
-
-// Scheduling fence: keeps the compiler from hoisting one step's LDS reads (and the registers they
-// hold) above the previous step.
-#ifdef SSD_SB_ON
-#define SSD_SB() __builtin_amdgcn_sched_barrier(0)
-#else
-#define SSD_SB()
-#endif
 
 // ---- small helpers ------------------------------------------------------------------------------
 __device__ __forceinline__ f16x2 cvt_f16x2(float a, float b) {  // v_cvt_pk_f16_f32, RNE
@@ -189,10 +188,10 @@ struct Fz {
   static constexpr int NMB = NIT * (NIT + 1) / 2;    // lower-triangle 16x16 blocks of M
   static constexpr int MT_HEAD = NMB * 512;           // a head's fp16 M blocks
   static constexpr int NWA = 5;                       // per-wave token arrays
-  static constexpr int WA_BYTES = NW * NWA * T * 4;   // acs2, dt, w, cf, rdiag (F1: per wave)
-  static constexpr int WA_SCAN = HPB * NWA * T * 4;   // F3: per head
+  static constexpr int WA_BYTES = NW * NWA * T * 4;   // acs2, dt, w, cf, rdiag (phase A: per wave)
+  static constexpr int WA_SCAN = HPB * NWA * T * 4;   // phase B: per head
   static constexpr int NSCAN = 2, NRUN = 3;           // stages
-  // F3 at one wave per head: the sub-chunk's C B^T blocks, fp32, computed once for the block's
+  // phase B at one wave per head: the sub-chunk's C B^T blocks, fp32, computed once for the block's
   // heads (they share one B/C group)
   static constexpr bool SHARED_CB = WPH == 1 && NMB <= NW;
   static constexpr int CB_SHARED = SHARED_CB ? NMB * 1024 : 0;
@@ -204,7 +203,8 @@ struct Fz {
   static_assert(BC_BYTES >= 1024, "whole DMA instructions");
 };
 
-// Block / wave coordinates shared by F1 and F3. Grid (nr, G * head-blocks per group, batch).
+// Block / wave coordinates shared by both phases: run r, head block hbi (over every group's head
+// blocks) and batch entry b.
 struct Coord {
   int b, r, grp, hbase, hlast;  // block: batch, run, group, first head, last head of the group
   int wave, lane, g, c16;       // wave, lane, lane group, lane % 16
@@ -213,13 +213,13 @@ struct Coord {
 };
 
 template <class K>
-__device__ __forceinline__ Coord coords(const Dims& d) {
+__device__ __forceinline__ Coord coords(const Dims& d, int r, int hbi, int b) {
   Coord c;
   const int hpg = d.H / d.G, hbg = (hpg + K::HPB - 1) / K::HPB;
-  c.r = blockIdx.x;
-  c.b = blockIdx.z;
-  c.grp = blockIdx.y / hbg;
-  const int first = (blockIdx.y % hbg) * K::HPB;
+  c.r = r;
+  c.b = b;
+  c.grp = hbi / hbg;
+  const int first = (hbi % hbg) * K::HPB;
   c.hbase = c.grp * hpg + first;
   c.hlast = c.grp * hpg + hpg - 1;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar registers
@@ -490,35 +490,24 @@ __device__ __forceinline__ f16x8 b_frag(const char* Bh, int js, int col0, int la
   return __builtin_bit_cast(f16x8, frag_tr<K::ROW_N>(Bh, 32 * js, col0, lane));
 }
 
-// ---- F1: run states -------------------------------------------------------------------------
+// ---- phase A: run states ------------------------------------------------------------------------
 // state_r = sum_{t in run} exp(sum_{k in (t, end]} dt_k A) dt_t x_t B_t^T (zero entry state) and
 // logdecay_r = sum_{t in run} dt_t A. Walked backwards: per sub-chunk, S += B^T (w x) with the
-// weights anchored at the run end, the weighted x split into fp16 high and low parts.
+// weights anchored at the run end, the weighted x split into fp16 high and low parts. Leaves the
+// state in S (lane: p = p0 + 16 pt + c16, n = 16 nt + 4 g + 0..3) and returns the log-decay.
 template <class K, bool SPLIT>
-__global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ x,
-                                                      const u16* __restrict__ Bm,
-                                                      const float* __restrict__ dt,
-                                                      const float* __restrict__ Av,
-                                                      float* __restrict__ states,
-                                                      float* __restrict__ logdecay,
-                                                      const float* __restrict__ h0, Dims d,
-                                                      int run_len, int nr) {
+__device__ __forceinline__ float run_state(char* smem, const Coord& c, const u16* __restrict__ x,
+                                           const u16* __restrict__ Bm,
+                                           const float* __restrict__ dt, float a_h, float dtb,
+                                           const Dims& d, int s_begin, int s_end,
+                                           f32x4 (&S)[K::NNT][K::NPT]) {
   using M = Mma<f16>;
-  static_assert(K::RUN_LDS <= 160 * 1024, "LDS budget");
-  __shared__ __align__(1024) char smem[K::RUN_LDS];
-  Coord c = coords<K>(d);
   DmaLanes<K, false> dl;
   dl.init(d, c);
   constexpr int T = K::T;
-  const int nsub = (d.L + T - 1) / T;
-  const int RS = run_len / T;  // sub-chunks per run (run_len is a multiple of every T)
-  const int s_begin = c.r * RS, s_end = min(nsub, s_begin + RS);
-  if (s_begin >= s_end) return;
   float* wa = reinterpret_cast<float*>(smem + K::NRUN * K::RUN_STAGE) + c.wave * K::NWA * T;
   const int xoff = K::BC_BYTES + (c.wave / K::WPH) * (T * K::ROW_P);
-  const float a_h = Av[c.h], dtb = dt_bias_of(d, c.h);
 
-  f32x4 S[K::NNT][K::NPT];
 #pragma unroll
   for (int nt = 0; nt < K::NNT; ++nt)
 #pragma unroll
@@ -576,23 +565,6 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
           xlo[pt] = cvt_f16x8(lo);
         }
       }
-#ifdef SSD_F1_HOIST
-      // all B^T fragments of the K step first (their LDS latency overlaps), then the high parts
-      // for every tile, then the low parts (no back-to-back dependent matrix-core ops)
-      f16x8 bts[K::NNT];
-#pragma unroll
-      for (int nt = 0; nt < K::NNT; ++nt) bts[nt] = b_frag<K>(st, js, 16 * nt, c.lane);
-#pragma unroll
-      for (int nt = 0; nt < K::NNT; ++nt)
-#pragma unroll
-        for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] = M::mma(bts[nt], xhi[pt], S[nt][pt]);
-      if constexpr (SPLIT) {
-#pragma unroll
-        for (int nt = 0; nt < K::NNT; ++nt)
-#pragma unroll
-          for (int pt = 0; pt < K::NPT; ++pt) S[nt][pt] = M::mma(bts[nt], xlo[pt], S[nt][pt]);
-      }
-#else
 #pragma unroll
       for (int nt = 0; nt < K::NNT; ++nt) {
         const f16x8 bt = b_frag<K>(st, js, 16 * nt, c.lane);
@@ -602,41 +574,33 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_state(const u16* __restrict__ 
           if constexpr (SPLIT) S[nt][pt] = M::mma(bt, xlo[pt], S[nt][pt]);
         }
       }
-#endif
     }
   }
-  if (!c.active) return;
-  // h0 not null (one run per sequence, logdecay null): the run state is completed into the final
-  // state, S + exp(log-decay of the run) h0, written to states as [Bt, H, P, N]
-  const int64_t off = (((int64_t)c.b * nr + c.r) * d.H + c.h) * (int64_t)(K::P * K::N) +
-                      (int64_t)c.p0 * K::N;
-  float* so = states + off;
-  if (h0 == nullptr) {
-#pragma unroll
-    for (int nt = 0; nt < K::NNT; ++nt)
-#pragma unroll
-      for (int pt = 0; pt < K::NPT; ++pt) {
-        const f32x4 v = S[nt][pt];
-        *reinterpret_cast<float4*>(so + (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g) =
-            make_float4(v[0], v[1], v[2], v[3]);
-      }
-  } else {
-    const float e0 = __expf(rem);
-#pragma unroll
-    for (int nt = 0; nt < K::NNT; ++nt)
-#pragma unroll
-      for (int pt = 0; pt < K::NPT; ++pt) {
-        const int o = (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g;
-        const float4 h = *reinterpret_cast<const float4*>(h0 + off + o);
-        const f32x4 v = S[nt][pt] + e0 * f32x4{h.x, h.y, h.z, h.w};
-        *reinterpret_cast<float4*>(so + o) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-  }
-  if (logdecay != nullptr && c.lane == 0 && c.p0 == 0)
-    logdecay[((int64_t)c.b * d.H + c.h) * nr + c.r] = rem;
+  return rem;
 }
 
-// Store the bf16 y tile that F3 left in the x tile of a stage: this wave's p-slice of its head,
+// Store this wave's state slice S (layout of run_state) to the [P, N] state at `so` (the head's
+// state, row-major), plus e0 times the matching slice of h (when not null).
+template <class K>
+__device__ __forceinline__ void store_state(const f32x4 (&S)[K::NNT][K::NPT], const Coord& c,
+                                            float* __restrict__ so, const float* __restrict__ h,
+                                            float e0) {
+#pragma unroll
+  for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+    for (int pt = 0; pt < K::NPT; ++pt) {
+      const int o = (c.p0 + 16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g;
+      f32x4 v = S[nt][pt];
+      if (h) {
+        const float4 q = *reinterpret_cast<const float4*>(h + o);
+        v += e0 * f32x4{q.x, q.y, q.z, q.w};
+      }
+      *reinterpret_cast<float4*>(so + o) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+
+// Store the bf16 y tile that phase B left in the x tile of a stage: this wave's p-slice of its head,
 // rows tok0 .. tok0 + T - 1 (rows past the sequence end skipped), 16 bytes per lane. Round k
 // covers rows k * RPR .. + RPR - 1; the swizzle key repeats every 16 rows, so the LDS lane offset
 // takes 16 / RPR values (at least one).
@@ -669,7 +633,7 @@ __device__ __forceinline__ void store_y(const char* xt, u16* y, const Dims& d, c
   }
 }
 
-// Lane-constant byte offsets of F3's LDS fragment accesses, relative to the tile they read,
+// Lane-constant byte offsets of phase B's LDS fragment accesses, relative to the tile they read,
 // computed once per kernel. The swizzle key sees only a row's low 4 bits and a piece's low bits,
 // so the unrolled loop indices it does not see (token-tile rows, high piece bits) enter as
 // immediates on top of these.
@@ -679,7 +643,10 @@ struct ScanLane {
   static constexpr int KP = PPR_N >= 16 ? 4 : 2;   // K steps over n with distinct patterns
   static constexpr int NP = PPR_N >= 16 ? 8 : 4;   // n tiles with distinct patterns
   uint32_t cro[KP][2];      // readout C^T fragment: row c16, piece 4 kn + 2 h + g/2, half g&1
-  uint32_t btr[NP][2];      // B^T fragment (transposing read): rows 8 g + j/4 (+4), piece 2 nt + ..
+  // B^T fragment (transposing read) of n tile 0: rows 8 g + j/4 (+4), pieces 0..1; n tile b < NP
+  // reads at btr0 ^ (b << 5) (its pieces 2 b, 2 b + 1: the swizzle key flips bits of the piece
+  // index, and the row's own offset has no bits in 5..7 below the NP tiles)
+  uint32_t btr0[2];
   uint32_t xtr[K::NPT][2];  // x fragment (transposing read)
   uint32_t cbr[KP];         // C B^T inputs: row c16, piece 4 kn + g
   uint32_t epi[K::NPT];     // y write into the x tile: row c16, piece (p0 + 16 pt) / 8 + g/2
@@ -700,8 +667,7 @@ struct ScanLane {
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) {
       const int t = 8 * g + (j >> 2) + 4 * hi;
-#pragma unroll
-      for (int b = 0; b < NP; ++b) btr[b][hi] = swz<K::ROW_N>(t, 2 * b + ((j & 3) >> 1)) + ((j & 1) << 3);
+      btr0[hi] = swz<K::ROW_N>(t, (j & 3) >> 1) + ((j & 1) << 3);
 #pragma unroll
       for (int pt = 0; pt < K::NPT; ++pt)
         xtr[pt][hi] = swz<K::ROW_P>(t, ((c.p0 + 16 * pt) >> 3) + ((j & 3) >> 1)) + ((j & 1) << 3);
@@ -718,7 +684,7 @@ __device__ __forceinline__ s16x8 tr8(const char* base, uint32_t lo, uint32_t hi)
   return s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// ---- F3: fused scan -----------------------------------------------------------------------------
+// ---- phase B helpers: the fused scan -------------------------------------------------------------
 // Per sub-chunk (tokens i, j), with acs the inclusive cumulative log-decay from its start:
 //   y_i = sum_{j <= i} M_ij x_j + exp(acs_i) C_i . S,
 //   M_ij = (C_i . B_j) exp(acs_i - acs_j) dt_j (j <= i), plus D on the diagonal (skip term)
@@ -876,27 +842,23 @@ __device__ __forceinline__ void m_from_shared(const char* cbs, const float* wa, 
     }
 }
 
-// h_run null: zero entry states.
+// ---- phase B: fused scan ------------------------------------------------------------------------
+// hr_head: the state entering the run for this wave's head ([P, N], row-major); null: zero.
 template <class K>
-__global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
-    const u16* __restrict__ x, const u16* __restrict__ Bm, const u16* __restrict__ Cm,
-    const float* __restrict__ dt, const float* __restrict__ Av, const float* __restrict__ Dv,
-    const float* __restrict__ h_run, u16* __restrict__ y, Dims d, int run_len, int nr) {
+__device__ __forceinline__ void fused_scan(char* smem, Coord c, const u16* __restrict__ x,
+                                           const u16* __restrict__ Bm, const u16* __restrict__ Cm,
+                                           const float* __restrict__ dt,
+                                           const float* __restrict__ Av,
+                                           const float* __restrict__ Dv,
+                                           const float* __restrict__ hr_head, u16* __restrict__ y,
+                                           const Dims& d, int s_begin, int s_end) {
   using M = Mma<f16>;
-  static_assert(K::SCAN_LDS <= 160 * 1024, "LDS budget");
-  // [stage 0][stage 1][M blocks per head][token arrays per head]
-  __shared__ __align__(1024) char smem[K::SCAN_LDS];
-  Coord c = coords<K>(d);
   DmaLanes<K, true> dl;
   dl.init(d, c);
   ScanLane<K> sl;
   sl.init(c);
   using SL = ScanLane<K>;
   constexpr int T = K::T, NPT = K::NPT, NIT = K::NIT;
-  const int nsub = (d.L + T - 1) / T;
-  const int RS = run_len / T;  // sub-chunks per run (run_len is a multiple of every T)
-  const int s_begin = c.r * RS, s_end = min(nsub, s_begin + RS);
-  if (s_begin >= s_end) return;
   const int hb = c.wave / K::WPH;  // head within the block
   char* mh = smem + K::NSCAN * K::SCAN_STAGE + hb * K::MT_HEAD;
   // token arrays of the head: both of its waves compute and write identical values; they are
@@ -914,14 +876,13 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
   // carried state S^T tiles (rows n, columns p): lane holds p = p0 + 16 pt + c16,
   // n = 16 nt + 4 g + 0..3
   f32x4 S[K::NNT][NPT];
-  if (h_run == nullptr) {
+  if (hr_head == nullptr) {
 #pragma unroll
     for (int nt = 0; nt < K::NNT; ++nt)
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) S[nt][pt] = zero4();
   } else {
-    const float* hr = h_run + (((int64_t)c.b * nr + c.r) * d.H + c.h) * (int64_t)(K::P * K::N) +
-                      (int64_t)c.p0 * K::N;
+    const float* hr = hr_head + (int64_t)c.p0 * K::N;
 #pragma unroll
     for (int nt = 0; nt < K::NNT; ++nt)
 #pragma unroll
@@ -1029,7 +990,6 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
       asm volatile("" ::: "memory");
     }
     if (!c.active) continue;
-    SSD_SB();
 
     // Raised wave priority from here to the y tile: the SIMD's other wave is then usually in
     // its readout or bookkeeping, and the state update's matrix-core chain is the longer one
@@ -1063,17 +1023,15 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(xh[pt], mf, Y[pt][it]);
       }
-      SSD_SB();
       // state update: S^T += B^T (w x)
 #pragma unroll
       for (int nt = 0; nt < K::NNT; ++nt) {
         const char* bb = Bh + 32 * js * K::ROW_N + (nt / SL::NP) * (16 * 2 * SL::NP);
         const f16x8 bt = __builtin_bit_cast(
-            f16x8, tr8(bb, sl.btr[nt % SL::NP][0], sl.btr[nt % SL::NP][1]));
+            f16x8, tr8(bb, sl.btr0[0] ^ ((nt % SL::NP) << 5), sl.btr0[1] ^ ((nt % SL::NP) << 5)));
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) S[nt][pt] = M::mma(bt, xs[pt], S[nt][pt]);
       }
-      SSD_SB();
     }
 
     __builtin_amdgcn_s_setprio(0);
@@ -1096,41 +1054,190 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(
   }
 }
 
-// ---- launchers ----------------------------------------------------------------------------------
-// Configurations: both kernels run 8 waves per block, two per SIMD (one wave's memory and
-// matrix-core latencies hide behind the other's work), with 64-column slices (one wave per head
-// at headdim 64) over sub-chunks of 32 tokens, so each wave keeps its fp32 state slice (64 x N)
-// and the rest of its working set within 256 registers. One wave per head halves, per token, the
-// B and C fragments read from LDS and the decay-mask work (a head's M blocks are built by its own
-// wave), at the price of twice as many runs (twice the run-state traffic between F1, F2 and F3);
-// measured at the headline workload: F3 145 -> 126 us, the forward -3%. The run-state kernel
-// reads its B^T fragments one K step at a time (holding a whole step's would spill at this width).
-#ifndef SSD_F3_NW
-#define SSD_F3_NW 8
-#define SSD_F3_PS 64
-#endif
-#ifdef SSD_TOKENS
-#define SSD_T(N) SSD_TOKENS
-#else
-#define SSD_T(N) 32
-#endif
-#ifdef SSD_F3_TOK
-#define SSD_F3_T(N) SSD_F3_TOK
-#else
-#define SSD_F3_T(N) SSD_T(N)
-#endif
-#ifndef SSD_F1_PS
-#define SSD_F1_PS 64
-#endif
-#ifdef SSD_F1_TOK
-#define SSD_F1_T(N) SSD_F1_TOK
-#else
-#define SSD_F1_T(N) SSD_T(N)
-#endif
+
+// ---- chain between runs -------------------------------------------------------------------------
+// Arrive at a chain counter and wait until `target` blocks have. Release: every wave waits for
+// its own stores (they have then reached this XCD's L2), then one thread's release atomic writes
+// the L2's dirty lines back to memory before the increment. Acquire: one thread polls with plain
+// device-scope loads (an acquire per poll would invalidate the XCD's L2 under every other block
+// on it), then invalidates this CU's L1 and the XCD's L2 once; the barrier orders every wave's
+// later reads after it. The wait is bounded (seconds of polling), so a block can never hang the
+// device; on a time-out it counts it in *timeouts and goes on.
+__device__ __forceinline__ void chain_arrive_wait(int* cnt, int target, int* timeouts) {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are done
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    int polls = 0;
+    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(4);
+      if (++polls == (1 << 22)) {
+        __hip_atomic_fetch_add(timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+// This block's share (1 / nr of the entries) of its chain: for each entry, walk the runs,
+// h <- exp(logdecay_q) h + state_q starting from h0 (or 0), writing the state entering run q + 1
+// over slot q; after the last run (when a final state is wanted) h is the final state. A thread
+// takes EPT entries (NT apart) at once and loads GS runs' states and decays of all of them
+// together: only the multiply-adds depend on the run before, so a share costs about
+// nr / GS memory round trips.
+template <class K>
+__device__ __forceinline__ void chain_scan(float* __restrict__ states,
+                                           const float* __restrict__ logdecay,
+                                           const float* __restrict__ h0, float* __restrict__ fin,
+                                           const Dims& d, int nr, int b, int hbase, int nh, int r) {
+  constexpr int PN = K::P * K::N, PN4 = PN / 4;
+  constexpr int EPT = 3, GS = 6;
+  const int E4 = nh * PN4;
+  const int per = (E4 + nr - 1) / nr;
+  const int lo = r * per, hi = min(E4, lo + per);
+  const int nsteps = fin ? nr : nr - 1;
+  const int64_t cstride = (int64_t)d.H * PN;  // floats between runs' slots
+  for (int i0 = lo + (int)threadIdx.x; i0 < hi; i0 += EPT * K::NT) {
+    float4 s[EPT];
+    float* sp[EPT];
+    const float* ldp[EPT];
+    int64_t sb[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int i = min(i0 + k * K::NT, hi - 1);  // past the share: a copy of its last entry
+      const int h = hbase + i / PN4, e = (i % PN4) * 4;
+      sb[k] = ((int64_t)b * d.H + h) * PN + e;
+      s[k] = h0 ? *reinterpret_cast<const float4*>(h0 + sb[k]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      ldp[k] = logdecay + ((int64_t)b * d.H + h) * nr;
+      sp[k] = states + ((int64_t)b * nr * d.H + h) * PN + e;
+    }
+    for (int c0 = 0; c0 < nsteps; c0 += GS) {
+      float4 st[EPT][GS];
+      float a[EPT][GS];
+#pragma unroll
+      for (int k = 0; k < EPT; ++k)
+#pragma unroll
+        for (int u = 0; u < GS; ++u) {
+          const int q = min(c0 + u, nsteps - 1);
+          st[k][u] = *reinterpret_cast<const float4*>(sp[k] + q * cstride);
+          a[k][u] = ldp[k][q];
+        }
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) {
+        const bool own = i0 + k * K::NT < hi;
+#pragma unroll
+        for (int u = 0; u < GS; ++u) {
+          if (c0 + u < nsteps) {
+            const float dec = __expf(a[k][u]);
+            s[k].x = dec * s[k].x + st[k][u].x;
+            s[k].y = dec * s[k].y + st[k][u].y;
+            s[k].z = dec * s[k].z + st[k][u].z;
+            s[k].w = dec * s[k].w + st[k][u].w;
+            if (own && c0 + u < nr - 1)
+              *reinterpret_cast<float4*>(sp[k] + (c0 + u) * cstride) = s[k];
+          }
+        }
+      }
+    }
+    if (fin) {
+#pragma unroll
+      for (int k = 0; k < EPT; ++k)
+        if (i0 + k * K::NT < hi) *reinterpret_cast<float4*>(fin + sb[k]) = s[k];
+    }
+  }
+}
+
+// ---- the forward kernel -------------------------------------------------------------------------
+struct FwdArgs {
+  const u16 *x, *B, *C;
+  const float *dt, *A, *D, *h0;
+  u16* y;
+  float* fin;       // final state [Bt, H, P, N]; null: not written
+  float* states;    // [Bt, nr, H, P, N]: run states, then the state entering the next run
+  float* logdecay;  // [Bt, H, nr]
+  int* sync;        // zero at launch: [0] ticket, [1 + 2 k], [2 + 2 k] chain k's two counters,
+                    // [1 + 2 chains] wait time-outs
+  Dims d;
+  int run_len, nr, hb;  // run length (tokens), runs per sequence, head blocks per batch entry
+};
+
+template <class K>
+constexpr int fwd_lds() {
+  return K::RUN_LDS > K::SCAN_LDS ? K::RUN_LDS : K::SCAN_LDS;
+}
+
+template <class K, bool SPLIT>
+__global__ __launch_bounds__(K::NT, 1) void k_forward(FwdArgs a) {
+  static_assert(fwd_lds<K>() <= 160 * 1024, "LDS budget");
+  __shared__ __align__(1024) char smem[fwd_lds<K>()];
+  __shared__ int s_item;
+  const Dims& d = a.d;
+  const int chains = d.Bt * a.hb;
+  int item = blockIdx.x;
+  if (a.nr > 1) {  // ticket in start order (see the top of this file)
+    if (threadIdx.x == 0)
+      s_item = __hip_atomic_fetch_add(a.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(s_item);
+  }
+  const int chain = item / a.nr, r = item % a.nr;
+  const int b = chain / a.hb;
+  const Coord c = coords<K>(d, r, chain % a.hb, b);
+  constexpr int T = K::T;
+  const int nsub = (d.L + T - 1) / T;
+  const int RS = a.run_len / T;  // sub-chunks per run (run_len is a multiple of T)
+  const int s_begin = r * RS, s_end = min(nsub, s_begin + RS);  // never empty (the plan)
+  const int64_t PN = (int64_t)K::P * K::N;
+
+  // phase A: this run's state, needed by the runs after it and for the final state
+  if ((a.nr > 1 && r < a.nr - 1) || a.fin) {
+    f32x4 S[K::NNT][K::NPT];
+    const float ld = run_state<K, SPLIT>(smem, c, a.x, a.B, a.dt, a.A[c.h],
+                                         dt_bias_of(d, c.h), d, s_begin, s_end, S);
+    if (c.active) {
+      if (a.nr == 1) {  // the final state: S + exp(sum of dt A) h0
+        const int64_t o = ((int64_t)b * d.H + c.h) * PN;
+        store_state<K>(S, c, a.fin + o, a.h0 ? a.h0 + o : nullptr, __expf(ld));
+      } else {
+        store_state<K>(S, c, a.states + (((int64_t)b * a.nr + r) * d.H + c.h) * PN, nullptr,
+                       0.f);
+        if (c.lane == 0 && c.p0 == 0) a.logdecay[((int64_t)b * d.H + c.h) * a.nr + r] = ld;
+      }
+    }
+  }
+  if (a.nr > 1) {
+    int* cnt = a.sync + 1 + 2 * chain;
+    int* timeouts = a.sync + 1 + 2 * chains;
+    chain_arrive_wait(cnt, a.nr, timeouts);  // every run's state published
+    const int nh = min(K::HPB, c.hlast - c.hbase + 1);
+    chain_scan<K>(a.states, a.logdecay, a.h0, a.fin, d, a.nr, b, c.hbase, nh, r);
+    chain_arrive_wait(cnt + 1, a.nr, timeouts);  // every entry state written
+  } else {
+    __syncthreads();  // phase A is done with the LDS
+  }
+  // phase B from the state entering the run
+  const float* hr = r == 0 ? (a.h0 ? a.h0 + ((int64_t)b * d.H + c.h) * PN : nullptr)
+                           : a.states + (((int64_t)b * a.nr + (r - 1)) * d.H + c.h) * PN;
+  fused_scan<K>(smem, c, a.x, a.B, a.C, a.dt, a.A, a.D, hr, a.y, d, s_begin, s_end);
+}
+
+__global__ __launch_bounds__(256) void k_sync_zero(int* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) p[i] = 0;
+}
+
+// ---- plan and launch ----------------------------------------------------------------------------
+// Both phases run 8 waves per block, two per SIMD (one wave's memory and matrix-core latencies
+// hide behind the other's work), with 64-column slices (one wave per head at headdim 64) over
+// sub-chunks of 32 tokens, so each wave keeps its fp32 state slice (64 x N) and the rest of its
+// working set within 256 registers. One wave per head halves, per token, the B and C fragments
+// read from LDS and the decay-mask work (a head's M blocks are built by its own wave), at the
+// price of twice as many runs (twice the run-state traffic); measured with separate kernels at the
+// headline workload: fused scan 145 -> 126 us, the forward -3%. The run-state phase reads its B^T
+// fragments one K step at a time (holding a whole step's would spill at this width).
 template <int P, int N>
-using RunCfg = Fz<P, N, 8, SSD_F1_PS, SSD_F1_T(N)>;
-template <int P, int N>
-using ScanCfg = Fz<P, N, SSD_F3_NW, SSD_F3_PS, SSD_F3_T(N)>;
+using Cfg = Fz<P, N, 8, 64, 32>;
 
 template <class K>
 static int head_blocks(const Dims& d) {
@@ -1138,94 +1245,110 @@ static int head_blocks(const Dims& d) {
   return d.G * ((hpg + K::HPB - 1) / K::HPB);
 }
 
-// Runs are planned in tokens, as whole multiples of 64 (so of every kernel's sub-chunk).
-template <class K3>
+// Runs are planned in tokens, as whole multiples of 64 (so of the sub-chunk). The waits between
+// the runs of a chain need every run of a sequence resident at once: at most n_cu runs (one block
+// per compute unit), which lengthens runs asked shorter.
+template <class K>
 static void plan_for(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
   constexpr int U = 64;
   const int nunit = (d.L + U - 1) / U;
-  fp->head_blocks = head_blocks<K3>(d);
+  fp->head_blocks = head_blocks<K>(d);
   const int units = d.Bt * fp->head_blocks;
   int RU;
   if (run_tokens > 0) {
     RU = (run_tokens + U - 1) / U;
   } else {
-    int want = n_cu / units;  // runs per sequence: about one scan block per compute unit
+    int want = n_cu / units;  // runs per sequence: about one block per compute unit
     if (want < 1) want = 1;
     RU = (nunit + want - 1) / want;
   }
   if (RU < 1) RU = 1;
   if (RU > nunit) RU = nunit;
+  const int cap = n_cu < 1 ? 1 : n_cu;
+  if ((nunit + RU - 1) / RU > cap) RU = (nunit + cap - 1) / cap;
   fp->run_len = RU * U;
   fp->nr = (nunit + RU - 1) / RU;
 }
 
-template <class K1, class K3>
-static hipError_t launch_k(int phase, const Dims& d, const FusedPlan& fp, const void* x,
-                           const void* B, const void* C, const float* dt, const float* A,
-                           const float* D, float* states, float* logdecay, const float* h_run,
-                           void* y, hipStream_t s) {
-  static_assert(64 % K1::T == 0 && 64 % K3::T == 0, "runs are whole sub-chunks of both kernels");
-  // phase 0: run states (h_run unused); phase 2: final state from h_run = h0 (one run)
-  if (phase != 1 && fp.split)
-    hipLaunchKernelGGL((k_run_state<K1, true>), dim3(fp.nr, head_blocks<K1>(d), d.Bt),
-                       dim3(K1::NT), 0, s, (const u16*)x, (const u16*)B, dt, A, states, logdecay,
-                       h_run, d, fp.run_len, fp.nr);
-  else if (phase != 1)
-    hipLaunchKernelGGL((k_run_state<K1, false>), dim3(fp.nr, head_blocks<K1>(d), d.Bt),
-                       dim3(K1::NT), 0, s, (const u16*)x, (const u16*)B, dt, A, states, logdecay,
-                       h_run, d, fp.run_len, fp.nr);
-  else
-    hipLaunchKernelGGL(k_fused_scan<K3>, dim3(fp.nr, head_blocks<K3>(d), d.Bt), dim3(K3::NT), 0,
-                       s, (const u16*)x, (const u16*)B, (const u16*)C, dt, A, D, h_run, (u16*)y,
-                       d, fp.run_len, fp.nr);
-  return hipGetLastError();
-}
-
-#ifndef SSD_FUSED_SHAPES
 #define SSD_FUSED_SHAPES(X) X(64, 64) X(64, 128) X(64, 256) X(128, 64) X(128, 128) X(128, 256)
-#endif
 
 bool fused_plan(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
-#define SSD_PLAN(P_, N_)                                   \
-  if (d.P == P_ && d.N == N_) {                            \
-    plan_for<ScanCfg<P_, N_>>(d, run_tokens, n_cu, fp);    \
-    return true;                                           \
+#define SSD_PLAN(P_, N_)                                 \
+  if (d.P == P_ && d.N == N_) {                          \
+    plan_for<Cfg<P_, N_>>(d, run_tokens, n_cu, fp);      \
+    return true;                                         \
   }
   SSD_FUSED_SHAPES(SSD_PLAN)
 #undef SSD_PLAN
   return false;
 }
 
-static hipError_t dispatch(int phase, const Dims& d, const FusedPlan& fp, const void* x,
-                           const void* B, const void* C, const float* dt, const float* A,
-                           const float* D, float* states, float* logdecay, const float* h_run,
-                           void* y, hipStream_t s) {
-#define SSD_LAUNCH(P_, N_)                                                                  \
-  if (d.P == P_ && d.N == N_)                                                               \
-    return launch_k<RunCfg<P_, N_>, ScanCfg<P_, N_>>(phase, d, fp, x, B, C, dt, A, D, states, \
-                                                     logdecay, h_run, y, s);
+int64_t fused_workspace_bytes(const Dims& d, const FusedPlan& fp) {
+  if (fp.nr <= 1) return 0;
+  const int64_t st = (int64_t)d.Bt * fp.nr * d.H * d.P * d.N * 4;
+  const int64_t ld = (int64_t)d.Bt * d.H * fp.nr * 4;
+  const int64_t sy = (int64_t)(2 + 2 * d.Bt * fp.head_blocks) * 4;
+  auto up = [](int64_t v) { return (v + 255) & ~int64_t(255); };
+  return up(st) + up(ld) + up(sy);
+}
+
+template <class K>
+static hipError_t launch_k(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
+                           const void* C, const float* dt, const float* A, const float* D,
+                           const float* h0, void* y, float* fin, void* ws, FusedTimer* tm,
+                           hipStream_t s) {
+  FwdArgs a{};
+  a.x = (const u16*)x;
+  a.B = (const u16*)B;
+  a.C = (const u16*)C;
+  a.dt = dt;
+  a.A = A;
+  a.D = D;
+  a.h0 = h0;
+  a.y = (u16*)y;
+  a.fin = fin;
+  a.d = d;
+  a.run_len = fp.run_len;
+  a.nr = fp.nr;
+  a.hb = fp.head_blocks;
+  const int chains = d.Bt * fp.head_blocks;
+  hipError_t e = hipSuccess;
+  if (fp.nr > 1) {
+    const int64_t st = (int64_t)d.Bt * fp.nr * d.H * d.P * d.N * 4;
+    const int64_t ld = (int64_t)d.Bt * d.H * fp.nr * 4;
+    auto up = [](int64_t v) { return (v + 255) & ~int64_t(255); };
+    char* w = static_cast<char*>(ws);
+    a.states = reinterpret_cast<float*>(w);
+    a.logdecay = reinterpret_cast<float*>(w + up(st));
+    a.sync = reinterpret_cast<int*>(w + up(st) + up(ld));
+    if (tm) e = tm->mark(s);
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(k_sync_zero, dim3(1), dim3(256), 0, s, a.sync, 2 + 2 * chains);
+      e = hipGetLastError();
+    }
+  }
+  if (e == hipSuccess && tm) e = tm->mark(s);
+  if (e != hipSuccess) return e;
+  const dim3 grid(chains * fp.nr);
+  if (fp.split)
+    hipLaunchKernelGGL((k_forward<K, true>), grid, dim3(K::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_forward<K, false>), grid, dim3(K::NT), 0, s, a);
+  e = hipGetLastError();
+  if (e == hipSuccess && tm) e = tm->mark(s);
+  return e;
+}
+
+hipError_t launch_fused(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
+                        const void* C, const float* dt, const float* A, const float* D,
+                        const float* h0, void* y, float* fin, void* ws, FusedTimer* tm,
+                        hipStream_t s) {
+#define SSD_LAUNCH(P_, N_)                                                                    \
+  if (d.P == P_ && d.N == N_)                                                                 \
+    return launch_k<Cfg<P_, N_>>(d, fp, x, B, C, dt, A, D, h0, y, fin, ws, tm, s);
   SSD_FUSED_SHAPES(SSD_LAUNCH)
 #undef SSD_LAUNCH
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_run_state(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
-                            const float* dt, const float* A, float* states, float* logdecay,
-                            hipStream_t s) {
-  return dispatch(0, d, fp, x, B, nullptr, dt, A, nullptr, states, logdecay, nullptr, nullptr, s);
-}
-
-hipError_t launch_fused_scan(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
-                             const void* C, const float* dt, const float* A, const float* D,
-                             const float* h_run, void* y, hipStream_t s) {
-  return dispatch(1, d, fp, x, B, C, dt, A, D, nullptr, nullptr, h_run, y, s);
-}
-
-hipError_t launch_final_state(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
-                              const float* dt, const float* A, const float* h0, float* fin,
-                              hipStream_t s) {
-  if (fp.nr != 1) return hipErrorInvalidValue;
-  return dispatch(2, d, fp, x, B, nullptr, dt, A, nullptr, fin, nullptr, h0, nullptr, s);
 }
 
 }  // namespace ssd

@@ -43,23 +43,36 @@ hipError_t launch_chunk_scan(const Dims& d, int io, int prec, const void* x, con
 
 // fused path (bf16 io)
 // Run plan of one fused forward: runs of run_len tokens (a multiple of 64), nr runs per sequence,
-// head_blocks fused-scan blocks per (batch, run).
-// split: F1 feeds the weighted x to the matrix cores as fp16 high + low parts (else high only).
+// head_blocks blocks per (batch, run).
+// split: phase A feeds the weighted x to the matrix cores as fp16 high + low parts (else high
+// only).
 struct FusedPlan {
   int run_len, nr, head_blocks;
   bool split = true;
 };
+// Optional timing events: ev[k++] recorded on the stream before the first launch and after each.
+struct KernelMarks {
+  void** ev = nullptr;
+  int n = 0, k = 0;
+  hipError_t mark(hipStream_t s) {
+    if (!ev || k >= n) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(ev[k++]), s);
+  }
+};
+using FusedTimer = KernelMarks;
 // False when the fused kernels do not cover (P, N). run_tokens > 0 asks for runs of at least that
-// many tokens; 0 lets the plan aim at about one block per compute unit (n_cu of them).
+// many tokens; 0 lets the plan aim at about one block per compute unit (n_cu of them). Runs are
+// lengthened so that a sequence has at most n_cu of them.
 bool fused_plan(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp);
-// states [Bt, nr, H, P, N] (each run's end state from a zero entry state), logdecay [Bt, H, nr]
-hipError_t launch_run_state(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
-                            const float* dt, const float* A, float* states, float* logdecay,
-                            hipStream_t s);
-// h_run [Bt, nr, H, P, N]: the state entering each run (null: zero)
-hipError_t launch_fused_scan(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
-                             const void* C, const float* dt, const float* A, const float* D,
-                             const float* h_run, void* y, hipStream_t s);
+// Workspace bytes of a plan (0 for one run per sequence): run states [Bt, nr, H, P, N] f32,
+// run log-decays [Bt, H, nr] f32 and the chain counters, each 256-byte aligned.
+int64_t fused_workspace_bytes(const Dims& d, const FusedPlan& fp);
+// The whole fused forward: a counter reset (nr > 1) and one forward kernel. h0 and fin nullable;
+// ws: fused_workspace_bytes(d, fp) bytes of device memory (unused when nr == 1).
+hipError_t launch_fused(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
+                        const void* C, const float* dt, const float* A, const float* D,
+                        const float* h0, void* y, float* fin, void* ws, FusedTimer* tm,
+                        hipStream_t s);
 // Short sequences (L <= kQuadMaxLen, dstate <= 256): the whole forward in one kernel, the
 // sequence as a single block of the quadratic (masked) form, fp32 arithmetic; h0 and fin
 // nullable. quadratic_covers() tells whether a problem qualifies.
@@ -69,12 +82,6 @@ int64_t quadratic_blocks(const Dims& d);  // blocks of its launch
 hipError_t launch_quadratic(const Dims& d, int io, const void* x, const float* dt, const float* A,
                             const void* B, const void* C, const float* D, const float* h0,
                             void* y, float* fin, hipStream_t s);
-// One run per sequence (fp.nr == 1): the run-state kernel writes the final state
-// fin [Bt, H, P, N] = (state of the sequence from a zero entry) + exp(sum of dt A) h0 (h0 null:
-// zero); the scan kernel then takes h0 itself as its entry state, and no chain is needed.
-hipError_t launch_final_state(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
-                              const float* dt, const float* A, const float* h0, float* fin,
-                              hipStream_t s);
 
 // backward helpers (ssd_backward.hip); all outputs fp32, layouts row-major.
 // out[b, t, k, e] = in[b, rev ? L - 1 - t : t, k / rep, e]   (in: [Bt, L, K / rep, E], io dtype)

@@ -40,13 +40,20 @@ class SSDOptions(ctypes.Structure):
                 ("events", ctypes.POINTER(ctypes.c_void_p)),
                 ("n_kernels", ctypes.POINTER(ctypes.c_int32)),
                 ("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
-                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
+                ("kernel_mask", ctypes.POINTER(ctypes.c_int32))]
 
 
-# kernel names, in launch order, for each number of kernels a call reports
-KERNELS = {1: ("quadratic",),
-           3: ("run_state", "state_passing", "fused_scan"),
-           5: ("chunk_cumsum", "bmm_chunk", "chunk_state", "state_passing", "chunk_scan")}
+# ssd_kernel bits (include/ssd.h) and the names the timer reports; a call launches its kernels in
+# increasing bit order
+KERNEL_BITS = ((1, "quadratic"), (2, "chunk_cumsum"), (4, "bmm_chunk"), (8, "chunk_state"),
+               (16, "state_passing"), (32, "chunk_scan"), (64, "sync_reset"),
+               (128, "forward"))
+
+
+def kernel_names(mask: int) -> tuple:
+    """Names of the kernels a forward launched, in launch order, from its kernel mask."""
+    return tuple(name for bit, name in KERNEL_BITS if mask & bit)
 
 
 class SSDError(RuntimeError):
@@ -145,7 +152,7 @@ def _require(t, name, dtype=None, device=None):
 def _options(variant, precision, run_chunks=0, dt_bias=None, dt_softplus=False, dt_limit=None):
     lo, hi = (0.0, 0.0) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
     return SSDOptions(VARIANTS[variant], PRECISIONS[precision], int(run_chunks), 0, None, None,
-                      _ptr(dt_bias), 1 if dt_softplus else 0, lo, hi)
+                      _ptr(dt_bias), 1 if dt_softplus else 0, lo, hi, None)
 
 
 class KernelTimer:
@@ -162,16 +169,22 @@ class KernelTimer:
             raise RuntimeError("could not create timing events")
         self._arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(h) for h in handles])
         self.n_kernels = ctypes.c_int32(0)
+        self.kernel_mask = ctypes.c_int32(0)
 
     def attach(self, opts: SSDOptions):
         opts.n_events = 6
         opts.events = ctypes.cast(self._arr, ctypes.POINTER(ctypes.c_void_p))
         opts.n_kernels = ctypes.pointer(self.n_kernels)
+        opts.kernel_mask = ctypes.pointer(self.kernel_mask)
+
+    def kernels(self) -> tuple:
+        """Names of the kernels the last call launched, in launch order."""
+        return kernel_names(self.kernel_mask.value)
 
     def times_ms(self) -> dict:
-        n = self.n_kernels.value
-        names = KERNELS[n]
-        return {names[k]: self.events[k].elapsed_time(self.events[k + 1]) for k in range(n)}
+        names = self.kernels()
+        return {names[k]: self.events[k].elapsed_time(self.events[k + 1])
+                for k in range(len(names))}
 
 
 def forward(x, dt, A, B, C, D, chunk_size, initial_state=None, *, variant="auto",

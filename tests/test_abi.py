@@ -37,7 +37,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert libssd.version() == 10300
+    assert libssd.version() == 10400
     assert libssd.status_string(0) == "ok"
     assert libssd.status_string(3) == "no HIP device"
     assert libssd.status_string(99) == "unknown status"
@@ -45,7 +45,7 @@ def test_version_and_status_strings():
 
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(libssd.SSDProblem) == 6 * 8 + 2 * 4
-    assert ctypes.sizeof(libssd.SSDOptions) == 56
+    assert ctypes.sizeof(libssd.SSDOptions) == 64
 
 
 # placeholder device addresses: 16-byte aligned, far apart, never dereferenced

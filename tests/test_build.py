@@ -57,8 +57,8 @@ def _kernel_descriptors(obj=OBJ):
 
 def test_fused_kernels_use_no_scratch():
     kernels = _kernel_descriptors()
-    fused = {k: v for k, v in kernels.items() if "k_run_state" in k or "k_fused_scan" in k}
-    assert len(fused) == 18, sorted(kernels)  # 6 (headdim, dstate) shapes x (F1 split/plain, F3)
+    fused = {k: v for k, v in kernels.items() if "k_forward" in k}
+    assert len(fused) == 12, sorted(kernels)  # 6 (headdim, dstate) shapes x (split or not)
     bad = {k: v for k, v in fused.items()
            if v.get("private_segment_fixed_size", 0) or v.get("vgpr_spill_count", 0)}
     assert not bad, f"fused kernels spilling to scratch: {bad}"

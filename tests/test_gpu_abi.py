@@ -53,7 +53,7 @@ def test_kernel_timer_events():
     """Per-kernel timing events recorded by the library around each kernel."""
     d = _inputs()
     note("kernel timer")
-    for variant, n in (("fused", 3), ("unfused", 5)):
+    for variant, n in (("fused", 2), ("unfused", 5)):
         tm = libssd.KernelTimer()
         ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 64, variant=variant,
                     timer=tm)
