@@ -58,7 +58,9 @@ typedef enum {
                                      multiple of 16 or above 256, sizes beyond 32-bit indexing */
     SSD_ERR_NO_DEVICE = 3,        /* no HIP device visible */
     SSD_ERR_OUT_OF_MEMORY = 4,    /* workspace allocation failed */
-    SSD_ERR_HIP = 5               /* a HIP call or kernel launch failed */
+    SSD_ERR_HIP = 5,              /* a HIP call or kernel launch failed */
+    SSD_ERR_WORKSPACE_LIMIT = 6   /* ssd_forward_noalloc: the request's workspace does not fit the
+                                     library's static scratch (SSD_SCRATCH_BYTES) */
 } ssd_status;
 
 typedef enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype; /* dtype of x, B, C, y */
@@ -154,6 +156,25 @@ ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* d
                           const void* B, const void* C, const float* D, int64_t chunk_size,
                           const float* initial_state, void* y, float* final_state, void* stream,
                           const ssd_options* opts);
+
+/* ---- Forward without device allocation. ---------------------------------------------------
+ * For callers that cannot allocate device memory during the call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, checks and results as
+ * ssd_forward_ex, but the call allocates nothing: its workspace is a static array of
+ * SSD_SCRATCH_BYTES in device memory, one per device, held from the library's load until the
+ * process ends (the first call on a device looks up that device's copy). The fused variant plans
+ * its runs so that their states fit (longer runs, down to one run per sequence, which needs no
+ * workspace); the quadratic variant needs none; the unfused variant's intermediates must fit as
+ * they are, else SSD_ERR_WORKSPACE_LIMIT and nothing is launched. Every call on a device shares its
+ * scratch, which keeps the last call's contents: the kernels clear the counters they need, and
+ * calls that overlap on one device (other streams, other host threads) race and must not be
+ * issued. Results may differ from ssd_forward_ex within the stated tolerance where the fitted
+ * plan's run boundaries differ; with the same plan they are bitwise equal. */
+#define SSD_SCRATCH_BYTES (64ll << 20)
+ssd_status ssd_forward_noalloc(const ssd_problem* prob, const void* x, const float* dt,
+                               const float* A, const void* B, const void* C, const float* D,
+                               int64_t chunk_size, const float* initial_state, void* y,
+                               float* final_state, void* stream, const ssd_options* opts);
 
 /* ---- Stages of the unfused path, exposed so each can be checked on its own. -----------------
  * nc = ceil(seqlen / chunk_size), Q = chunk_size. Workspace layouts (fp32, row-major):

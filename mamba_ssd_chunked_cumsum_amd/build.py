@@ -21,7 +21,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libssd.so")
 
 SOURCES = ["ssd_api.cpp", "ssd_unfused.hip", "ssd_fused.hip", "ssd_step.hip", "ssd_backward.hip",
-           "ssd_quad.hip"]
+           "ssd_quad.hip", "ssd_scratch.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms stay disabled in device code (the compiler would otherwise fuse pairs of

@@ -164,26 +164,32 @@ int resolve_precision(int io, int prec) {
   return prec;  // auto, fp16 or fp32 for bf16 io
 }
 
-ssd_status run_unfused(const ssd_problem* prob, const Dims& d, int prec, const void* x,
-                       const float* dt, const float* A, const void* B, const void* C,
-                       const float* D, const float* h0, void* y, float* fin, hipStream_t s,
-                       Timer& t) {
+int64_t unfused_workspace_bytes(const Dims& d, int64_t off[5]) {
   int64_t sz[5];
   workspace_sizes(d, sz);
-  int64_t total = 0, off[5];
+  int64_t total = 0;
   for (int i = 0; i < 5; ++i) {
     off[i] = total;
     total += (sz[i] + 255) & ~int64_t(255);
   }
-  void* base = nullptr;
-  hipError_t e = hipMallocAsync(&base, (size_t)total, s);
-  if (e != hipSuccess) return SSD_ERR_OUT_OF_MEMORY;
+  return total;
+}
+
+// ws: unfused_workspace_bytes(d) bytes of device memory, or null to allocate them stream-ordered.
+ssd_status run_unfused(const ssd_problem* prob, const Dims& d, int prec, const void* x,
+                       const float* dt, const float* A, const void* B, const void* C,
+                       const float* D, const float* h0, void* y, float* fin, hipStream_t s,
+                       Timer& t, void* ws) {
+  int64_t off[5];
+  const int64_t total = unfused_workspace_bytes(d, off);
+  void* base = ws;
+  if (!base && hipMallocAsync(&base, (size_t)total, s) != hipSuccess) return SSD_ERR_OUT_OF_MEMORY;
   char* b = static_cast<char*>(base);
   Workspace w{reinterpret_cast<float*>(b + off[0]), reinterpret_cast<float*>(b + off[1]),
               reinterpret_cast<float*>(b + off[2]), reinterpret_cast<float*>(b + off[3]),
               reinterpret_cast<float*>(b + off[4])};
   const int io = prob->io_dtype;
-  e = t.mark(s);
+  hipError_t e = t.mark(s);
   if (e == hipSuccess) e = ssd::launch_chunk_cumsum(d, dt, A, w.Acs, w.dtc, s);
   if (e == hipSuccess) e = t.mark(s);
   if (e == hipSuccess) e = ssd::launch_bmm_chunk(d, io, B, C, w.CB, s);
@@ -195,7 +201,7 @@ ssd_status run_unfused(const ssd_problem* prob, const Dims& d, int prec, const v
   if (e == hipSuccess)
     e = ssd::launch_chunk_scan(d, io, prec, x, C, w.CB, w.Acs, w.dtc, w.h_in, D, y, s);
   if (e == hipSuccess) e = t.mark(s);
-  hipError_t ef = hipFreeAsync(base, s);
+  hipError_t ef = ws ? hipSuccess : hipFreeAsync(base, s);
   if (e != hipSuccess) return from_hip(e);
   return from_hip(ef);
 }
@@ -215,17 +221,18 @@ int compute_units() {
 
 // Fused forward: one kernel (after a reset of its chain counters when a sequence has several
 // runs). Runs are run_chunks chunks long when run_chunks > 0, else planned to give about one block
-// per compute unit (each run boundary costs one fp32 state write and read). The workspace (run
-// states, decays, counters; none with one run per sequence) is allocated stream-ordered.
+// per compute unit (each run boundary costs one fp32 state write and read). ws: the workspace
+// (run states, decays, counters; none with one run per sequence), or null to allocate it
+// stream-ordered.
 ssd_status run_fused(const Dims& d, const ssd::FusedPlan& fp, const void* x, const float* dt,
                      const float* A, const void* B, const void* C, const float* D,
-                     const float* h0, void* y, float* fin, hipStream_t s, Timer& t) {
+                     const float* h0, void* y, float* fin, hipStream_t s, Timer& t, void* ws) {
   const int64_t bytes = ssd::fused_workspace_bytes(d, fp);
-  void* ws = nullptr;
-  if (bytes > 0 && hipMallocAsync(&ws, (size_t)bytes, s) != hipSuccess)
-    return SSD_ERR_OUT_OF_MEMORY;
-  hipError_t e = ssd::launch_fused(d, fp, x, B, C, dt, A, D, h0, y, fin, ws, &t, s);
-  hipError_t ef = ws ? hipFreeAsync(ws, s) : hipSuccess;
+  void* w = ws;
+  const bool own = bytes > 0 && !ws;
+  if (own && hipMallocAsync(&w, (size_t)bytes, s) != hipSuccess) return SSD_ERR_OUT_OF_MEMORY;
+  hipError_t e = ssd::launch_fused(d, fp, x, B, C, dt, A, D, h0, y, fin, w, &t, s);
+  hipError_t ef = own ? hipFreeAsync(w, s) : hipSuccess;
   if (e != hipSuccess) return from_hip(e);
   return from_hip(ef);
 }
@@ -237,14 +244,12 @@ void report_kernels(const ssd_options* o, int mask) {
   if (o->kernel_mask) *o->kernel_mask = mask;
 }
 
-}  // namespace
-
-extern "C" {
-
-ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* dt, const float* A,
-                          const void* B, const void* C, const float* D, int64_t chunk_size,
-                          const float* initial_state, void* y, float* final_state, void* stream,
-                          const ssd_options* opts) {
+// The forward behind ssd_forward_ex (noalloc false: workspace allocated stream-ordered) and
+// ssd_forward_noalloc (noalloc true: workspace from the device's static scratch, plans fitted to it).
+ssd_status forward_impl(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                        const void* B, const void* C, const float* D, int64_t chunk_size,
+                        const float* initial_state, void* y, float* final_state, void* stream,
+                        const ssd_options* opts, bool noalloc) {
   ssd_status st = check_forward_args(prob, x, dt, A, B, C, D, chunk_size, initial_state, y,
                                      final_state);
   if (st != SSD_OK) return st;
@@ -304,6 +309,23 @@ ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* d
     return from_hip(e);
   }
   const bool fused = variant != SSD_VARIANT_UNFUSED && fusable;
+  void* ws = nullptr;
+  if (noalloc) {
+    // the fused plan's runs are lengthened until its workspace fits the scratch (one run per
+    // sequence needs none); the unfused workspace must fit as it is
+    if (fused) {
+      while (ssd::fused_workspace_bytes(d, fp) > ssd::kScratchBytes && fp.nr > 1) {
+        const bool split = fp.split;
+        ssd::fused_plan(d, fp.run_len * 2, compute_units(), &fp);
+        fp.split = split;
+      }
+    } else {
+      int64_t off[5];
+      if (unfused_workspace_bytes(d, off) > ssd::kScratchBytes) return SSD_ERR_WORKSPACE_LIMIT;
+    }
+    const hipError_t e = ssd::scratch_address(&ws);
+    if (e != hipSuccess) return from_hip(e);
+  }
   if (fused)
     report_kernels(opts, (fp.nr > 1 ? SSD_KERNEL_SYNC_RESET : 0) | SSD_KERNEL_FUSED_FORWARD);
   else
@@ -311,8 +333,28 @@ ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* d
                              SSD_KERNEL_CHUNK_STATE | SSD_KERNEL_STATE_PASSING |
                              SSD_KERNEL_CHUNK_SCAN);
   if (fused)
-    return run_fused(d, fp, x, dt, A, B, C, D, initial_state, y, final_state, s, t);
-  return run_unfused(prob, d, prec, x, dt, A, B, C, D, initial_state, y, final_state, s, t);
+    return run_fused(d, fp, x, dt, A, B, C, D, initial_state, y, final_state, s, t, ws);
+  return run_unfused(prob, d, prec, x, dt, A, B, C, D, initial_state, y, final_state, s, t, ws);
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* dt, const float* A,
+                          const void* B, const void* C, const float* D, int64_t chunk_size,
+                          const float* initial_state, void* y, float* final_state, void* stream,
+                          const ssd_options* opts) {
+  return forward_impl(prob, x, dt, A, B, C, D, chunk_size, initial_state, y, final_state, stream,
+                      opts, false);
+}
+
+ssd_status ssd_forward_noalloc(const ssd_problem* prob, const void* x, const float* dt,
+                               const float* A, const void* B, const void* C, const float* D,
+                               int64_t chunk_size, const float* initial_state, void* y,
+                               float* final_state, void* stream, const ssd_options* opts) {
+  return forward_impl(prob, x, dt, A, B, C, D, chunk_size, initial_state, y, final_state, stream,
+                      opts, true);
 }
 
 ssd_status ssd_forward(const ssd_problem* prob, const void* x, const float* dt, const float* A,
@@ -464,7 +506,8 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   auto fwd = [&](const ssd_problem* pp, const Dims& dd, const float* xx, const float* dtt,
                  const float* bb, const float* cc, const float* h0, float* yy, float* fin) {
     if (r == SSD_OK)
-      r = run_unfused(pp, dd, ssd::kPrecFp32, xx, dtt, A, bb, cc, w[ZD], h0, yy, fin, hs, none);
+      r = run_unfused(pp, dd, ssd::kPrecFp32, xx, dtt, A, bb, cc, w[ZD], h0, yy, fin, hs, none,
+                      nullptr);
   };
   // fp32 copies of the inputs and a zero skip term (the forwards below compute state terms only)
   hip(ssd::launch_gather(io, x, w[X32], iBt, iL, iH, 1, iP, false, hs));
@@ -584,6 +627,7 @@ const char* ssd_status_string(ssd_status status) {
     case SSD_ERR_NO_DEVICE: return "no HIP device";
     case SSD_ERR_OUT_OF_MEMORY: return "out of device memory";
     case SSD_ERR_HIP: return "HIP error";
+    case SSD_ERR_WORKSPACE_LIMIT: return "workspace beyond the no-allocation scratch";
   }
   return "unknown status";
 }

@@ -83,6 +83,11 @@ hipError_t launch_quadratic(const Dims& d, int io, const void* x, const float* d
                             const void* B, const void* C, const float* D, const float* h0,
                             void* y, float* fin, hipStream_t s);
 
+// No-allocation forward: the per-device static scratch (ssd_scratch.hip), kScratchBytes long,
+// shared by every call on a device. *out = this device's copy (looked up once per device).
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+hipError_t scratch_address(void** out);
+
 // backward helpers (ssd_backward.hip); all outputs fp32, layouts row-major.
 // out[b, t, k, e] = in[b, rev ? L - 1 - t : t, k / rep, e]   (in: [Bt, L, K / rep, E], io dtype)
 hipError_t launch_gather(int io, const void* in, float* out, int Bt, int L, int K, int rep, int E,

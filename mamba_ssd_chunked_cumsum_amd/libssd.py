@@ -15,14 +15,15 @@ import torch
 from .build import LIB
 
 SSD_OK, SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED = 0, 1, 2
-SSD_ERR_NO_DEVICE, SSD_ERR_OUT_OF_MEMORY, SSD_ERR_HIP = 3, 4, 5
+SSD_ERR_NO_DEVICE, SSD_ERR_OUT_OF_MEMORY, SSD_ERR_HIP, SSD_ERR_WORKSPACE_LIMIT = 3, 4, 5, 6
 
 VARIANTS = {"auto": 0, "unfused": 1, "fused": 2, "quadratic": 3}
 PRECISIONS = {"auto": 0, "fp16": 1, "fp32": 3}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 # Symbols include/ssd.h declares.
-EXPORTS = ("ssd_forward", "ssd_forward_ex", "ssd_chunk_cumsum", "ssd_bmm_chunk",
+EXPORTS = ("ssd_forward", "ssd_forward_ex", "ssd_forward_noalloc", "ssd_chunk_cumsum",
+           "ssd_bmm_chunk",
            "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_workspace_sizes",
            "ssd_step", "ssd_backward", "ssd_status_string", "ssd_version")
 
@@ -80,6 +81,7 @@ def load():
     sig = {
         "ssd_forward": [P, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp],
         "ssd_forward_ex": [P, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, O],
+        "ssd_forward_noalloc": [P, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, O],
         "ssd_chunk_cumsum": [P, vp, vp, i64, vp, vp, vp],
         "ssd_bmm_chunk": [P, vp, vp, i64, vp, vp],
         "ssd_chunk_state": [P, vp, vp, vp, vp, i64, vp, vp, O],
@@ -189,11 +191,14 @@ class KernelTimer:
 
 def forward(x, dt, A, B, C, D, chunk_size, initial_state=None, *, variant="auto",
             precision="auto", run_chunks=0, want_final=True, out=None, final_out=None,
-            timer: KernelTimer | None = None, dt_bias=None, dt_softplus=False, dt_limit=None):
+            timer: KernelTimer | None = None, dt_bias=None, dt_softplus=False, dt_limit=None,
+            noalloc=False):
     """SSD chunked forward. Returns (y, final_state) (final_state None if not wanted).
 
     dt_bias [H], dt_softplus and dt_limit=(lo, hi) pre-process dt inside the kernels:
-    dt + dt_bias, softplus, clamp to [lo, hi] (hi > 0), in that order."""
+    dt + dt_bias, softplus, clamp to [lo, hi] (hi > 0), in that order. noalloc: call
+    ssd_forward_noalloc (workspace from the library's static scratch; give out and final_out to
+    keep torch from allocating too)."""
     dev = x.device
     _require(x, "x", device=dev)
     for n, t in (("B", B), ("C", C)):
@@ -214,10 +219,11 @@ def forward(x, dt, A, B, C, D, chunk_size, initial_state=None, *, variant="auto"
     opts = _options(variant, precision, run_chunks, dt_bias, dt_softplus, dt_limit)
     if timer is not None:
         timer.attach(opts)
-    st = load().ssd_forward_ex(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
-                               _ptr(D), int(chunk_size), _ptr(initial_state), _ptr(y), _ptr(fin),
-                               _stream(x), ctypes.byref(opts))
-    _check(st, "ssd_forward_ex")
+    entry = "ssd_forward_noalloc" if noalloc else "ssd_forward_ex"
+    st = getattr(load(), entry)(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                _ptr(D), int(chunk_size), _ptr(initial_state), _ptr(y),
+                                _ptr(fin), _stream(x), ctypes.byref(opts))
+    _check(st, entry)
     return y, fin
 
 
