@@ -75,18 +75,18 @@ typedef enum {
     SSD_VARIANT_AUTO = 0,
     SSD_VARIANT_UNFUSED = 1, /* cumsum, C B^T, chunk states, state passing, chunk scan: five
                                 kernels, intermediates in workspace */
-    SSD_VARIANT_FUSED = 2,   /* bf16 io, headdim 64 or 128, dstate 64, 128 or 256: one forward
-                                kernel (after a reset of its chain counters when a sequence is cut
-                                into several runs). The sequence is cut into runs (about one block
-                                per compute unit); a block computes its run's own end state, the
-                                blocks of a sequence then chain those states into the state
-                                entering each run and the final state, and each block walks its
-                                run in sub-chunks of 32 tokens with the state on chip: C B^T block,
-                                decay mask, readout and state update never leave the compute unit.
-                                The exact result does not depend on the chunk length, so chunk_size
-                                only sets the run length when run_chunks is given. Assumes A <= 0
-                                and dt >= 0 (decays at most 1); D enters through the fp16 diagonal
-                                of the masked block (exact for D = 1) */
+    SSD_VARIANT_FUSED = 2,   /* bf16 io, headdim 64 or 128, dstate 64, 128 or 256: up to three
+                                kernels. The sequence is cut into runs (about one block per compute
+                                unit); one kernel computes each run's own end state (skipped with
+                                one run per sequence and no final state), one chains those states
+                                into the state entering each run and the final state (skipped with
+                                one run per sequence), and one walks every run in sub-chunks of 32
+                                tokens with the state on chip: C B^T block, decay mask, readout and
+                                state update never leave the compute unit. The exact result does
+                                not depend on the chunk length, so chunk_size only sets the run
+                                length when run_chunks is given. Assumes A <= 0 and dt >= 0
+                                (decays at most 1); D enters through the fp16 diagonal of the
+                                masked block (exact for D = 1) */
     SSD_VARIANT_QUADRATIC = 3 /* seqlen <= 256, dstate <= 256, either io: one kernel, the whole
                                 sequence as a single block of the quadratic (masked,
                                 attention-like) form y = (L o C B^T)(dt x) + D x plus the
@@ -110,9 +110,8 @@ typedef struct {
     int32_t variant;    /* ssd_variant */
     int32_t precision;  /* ssd_precision */
     int32_t run_chunks; /* fused variant: runs of run_chunks * chunk_size tokens (rounded up to
-                           64 tokens, and lengthened where needed so that a sequence has at most
-                           one run per compute unit); 0 = chosen from the problem size and the
-                           device's compute units; must be >= 0 */
+                           64 tokens); 0 = chosen from the problem size and the device's compute
+                           units; must be >= 0 */
     int32_t n_events;   /* capacity of `events`; 0 = no timing events */
     void** events;      /* optional hipEvent_t[n_events], created by the caller: events[0] is
                            recorded on `stream` before the first kernel and events[k] after the
@@ -139,8 +138,10 @@ typedef enum {
     SSD_KERNEL_CHUNK_STATE = 8,     /* unfused: stage 3 */
     SSD_KERNEL_STATE_PASSING = 16,  /* unfused: stage 4 */
     SSD_KERNEL_CHUNK_SCAN = 32,     /* unfused: stage 5 */
-    SSD_KERNEL_SYNC_RESET = 64,     /* fused, several runs per sequence: zeroes the chain counters */
-    SSD_KERNEL_FUSED_FORWARD = 128  /* fused: the whole forward */
+    SSD_KERNEL_FUSED_RUN_STATES = 64, /* fused: each run's own end state (several runs per
+                                         sequence, or a final state wanted) */
+    SSD_KERNEL_FUSED_CHAIN = 128,     /* fused, several runs per sequence: the chain over runs */
+    SSD_KERNEL_FUSED_SCAN = 256       /* fused: the outputs, run by run */
 } ssd_kernel;
 
 /* Full forward. initial_state may be NULL (zeros); final_state may be NULL (not written).
@@ -166,9 +167,9 @@ ssd_status ssd_forward_ex(const ssd_problem* prob, const void* x, const float* d
  * its runs so that their states fit (longer runs, down to one run per sequence, which needs no
  * workspace); the quadratic variant needs none; the unfused variant's intermediates must fit as
  * they are, else SSD_ERR_WORKSPACE_LIMIT and nothing is launched. Every call on a device shares its
- * scratch, which keeps the last call's contents: the kernels clear the counters they need, and
- * calls that overlap on one device (other streams, other host threads) race and must not be
- * issued. Results may differ from ssd_forward_ex within the stated tolerance where the fitted
+ * scratch, which keeps the last call's contents (no kernel reads what it did not write in the same
+ * call), and calls that overlap on one device (other streams, other host threads) race and must
+ * not be issued. Results may differ from ssd_forward_ex within the stated tolerance where the fitted
  * plan's run boundaries differ; with the same plan they are bitwise equal. */
 #define SSD_SCRATCH_BYTES (64ll << 20)
 ssd_status ssd_forward_noalloc(const ssd_problem* prob, const void* x, const float* dt,

@@ -13,8 +13,9 @@ namespace {
 
 using ssd::Dims;
 
-constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;  // 1.2: ssd_backward; 1.3: quadratic variant;
-                                                   // 1.4: one-kernel fused forward, kernel_mask
+constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;  // 1.2: ssd_backward; 1.3: quadratic variant;
+                                                   // 1.4: kernel_mask; 1.5: fused forward as run
+                                                   // states, chain and fused scan
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
 
 struct Range {
@@ -327,7 +328,8 @@ ssd_status forward_impl(const ssd_problem* prob, const void* x, const float* dt,
     if (e != hipSuccess) return from_hip(e);
   }
   if (fused)
-    report_kernels(opts, (fp.nr > 1 ? SSD_KERNEL_SYNC_RESET : 0) | SSD_KERNEL_FUSED_FORWARD);
+    report_kernels(opts, ((fp.nr > 1 || final_state) ? SSD_KERNEL_FUSED_RUN_STATES : 0) |
+                             (fp.nr > 1 ? SSD_KERNEL_FUSED_CHAIN : 0) | SSD_KERNEL_FUSED_SCAN);
   else
     report_kernels(opts, SSD_KERNEL_CHUNK_CUMSUM | SSD_KERNEL_BMM_CHUNK |
                              SSD_KERNEL_CHUNK_STATE | SSD_KERNEL_STATE_PASSING |

@@ -1056,31 +1056,6 @@ __device__ __forceinline__ void fused_scan(char* smem, Coord c, const u16* __res
 
 
 // ---- chain between runs -------------------------------------------------------------------------
-// Arrive at a chain counter and wait until `target` blocks have. Release: every wave waits for
-// its own stores (they have then reached this XCD's L2), then one thread's release atomic writes
-// the L2's dirty lines back to memory before the increment. Acquire: one thread polls with plain
-// device-scope loads (an acquire per poll would invalidate the XCD's L2 under every other block
-// on it), then invalidates this CU's L1 and the XCD's L2 once; the barrier orders every wave's
-// later reads after it. The wait is bounded (seconds of polling), so a block can never hang the
-// device; on a time-out it counts it in *timeouts and goes on.
-__device__ __forceinline__ void chain_arrive_wait(int* cnt, int target, int* timeouts) {
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are done
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    int polls = 0;
-    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(4);
-      if (++polls == (1 << 22)) {
-        __hip_atomic_fetch_add(timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
-}
-
 // This block's share (1 / nr of the entries) of its chain: for each entry, walk the runs,
 // h <- exp(logdecay_q) h + state_q starting from h0 (or 0), writing the state entering run q + 1
 // over slot q; after the last run (when a final state is wanted) h is the final state. A thread
@@ -1149,7 +1124,7 @@ __device__ __forceinline__ void chain_scan(float* __restrict__ states,
   }
 }
 
-// ---- the forward kernel -------------------------------------------------------------------------
+// ---- the three kernels ---------------------------------------------------------------------------
 struct FwdArgs {
   const u16 *x, *B, *C;
   const float *dt, *A, *D, *h0;
@@ -1157,74 +1132,78 @@ struct FwdArgs {
   float* fin;       // final state [Bt, H, P, N]; null: not written
   float* states;    // [Bt, nr, H, P, N]: run states, then the state entering the next run
   float* logdecay;  // [Bt, H, nr]
-  int* sync;        // zero at launch: [0] ticket, [1 + 2 k], [2 + 2 k] chain k's two counters,
-                    // [1 + 2 chains] wait time-outs
   Dims d;
   int run_len, nr, hb;  // run length (tokens), runs per sequence, head blocks per batch entry
+  int na;               // runs per sequence whose state phase A computes
 };
 
+// A block's (batch, head block, run) and sub-chunk range from its item index: chains (batch,
+// head block) one after another, nper runs per chain.
+struct Item {
+  int chain, r, b, s_begin, s_end;
+};
 template <class K>
-constexpr int fwd_lds() {
-  return K::RUN_LDS > K::SCAN_LDS ? K::RUN_LDS : K::SCAN_LDS;
+__device__ __forceinline__ Item item_of(const FwdArgs& a, int item, int nper) {
+  Item it;
+  it.chain = item / nper;
+  it.r = item % nper;
+  it.b = it.chain / a.hb;
+  const int nsub = (a.d.L + K::T - 1) / K::T;
+  const int RS = a.run_len / K::T;  // sub-chunks per run (run_len is a multiple of T)
+  it.s_begin = it.r * RS;
+  it.s_end = min(nsub, it.s_begin + RS);  // never empty (the plan)
+  return it;
 }
 
+// Phase A, one block per (chain, run) whose state is needed: the runs before the last (for the
+// chain) and, when a final state is wanted, the last one too. With one run per sequence the state
+// is completed into the final state here: S + exp(sum of dt A) h0.
 template <class K, bool SPLIT>
-__global__ __launch_bounds__(K::NT, 1) void k_forward(FwdArgs a) {
-  static_assert(fwd_lds<K>() <= 160 * 1024, "LDS budget");
-  __shared__ __align__(1024) char smem[fwd_lds<K>()];
-  __shared__ int s_item;
+__global__ __launch_bounds__(K::NT, 1) void k_run_states(FwdArgs a) {
+  static_assert(K::RUN_LDS <= 160 * 1024, "LDS budget");
+  __shared__ __align__(1024) char smem[K::RUN_LDS];
   const Dims& d = a.d;
-  const int chains = d.Bt * a.hb;
-  int item = blockIdx.x;
-  if (a.nr > 1) {  // ticket in start order (see the top of this file)
-    if (threadIdx.x == 0)
-      s_item = __hip_atomic_fetch_add(a.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    item = __builtin_amdgcn_readfirstlane(s_item);
-  }
-  const int chain = item / a.nr, r = item % a.nr;
-  const int b = chain / a.hb;
-  const Coord c = coords<K>(d, r, chain % a.hb, b);
-  constexpr int T = K::T;
-  const int nsub = (d.L + T - 1) / T;
-  const int RS = a.run_len / T;  // sub-chunks per run (run_len is a multiple of T)
-  const int s_begin = r * RS, s_end = min(nsub, s_begin + RS);  // never empty (the plan)
+  const Item it = item_of<K>(a, blockIdx.x, a.na);
+  const Coord c = coords<K>(d, it.r, it.chain % a.hb, it.b);
   const int64_t PN = (int64_t)K::P * K::N;
-
-  // phase A: this run's state, needed by the runs after it and for the final state
-  if ((a.nr > 1 && r < a.nr - 1) || a.fin) {
-    f32x4 S[K::NNT][K::NPT];
-    const float ld = run_state<K, SPLIT>(smem, c, a.x, a.B, a.dt, a.A[c.h],
-                                         dt_bias_of(d, c.h), d, s_begin, s_end, S);
-    if (c.active) {
-      if (a.nr == 1) {  // the final state: S + exp(sum of dt A) h0
-        const int64_t o = ((int64_t)b * d.H + c.h) * PN;
-        store_state<K>(S, c, a.fin + o, a.h0 ? a.h0 + o : nullptr, __expf(ld));
-      } else {
-        store_state<K>(S, c, a.states + (((int64_t)b * a.nr + r) * d.H + c.h) * PN, nullptr,
-                       0.f);
-        if (c.lane == 0 && c.p0 == 0) a.logdecay[((int64_t)b * d.H + c.h) * a.nr + r] = ld;
-      }
-    }
-  }
-  if (a.nr > 1) {
-    int* cnt = a.sync + 1 + 2 * chain;
-    int* timeouts = a.sync + 1 + 2 * chains;
-    chain_arrive_wait(cnt, a.nr, timeouts);  // every run's state published
-    const int nh = min(K::HPB, c.hlast - c.hbase + 1);
-    chain_scan<K>(a.states, a.logdecay, a.h0, a.fin, d, a.nr, b, c.hbase, nh, r);
-    chain_arrive_wait(cnt + 1, a.nr, timeouts);  // every entry state written
+  f32x4 S[K::NNT][K::NPT];
+  const float ld = run_state<K, SPLIT>(smem, c, a.x, a.B, a.dt, a.A[c.h], dt_bias_of(d, c.h), d,
+                                       it.s_begin, it.s_end, S);
+  if (!c.active) return;
+  if (a.nr == 1) {
+    const int64_t o = ((int64_t)it.b * d.H + c.h) * PN;
+    store_state<K>(S, c, a.fin + o, a.h0 ? a.h0 + o : nullptr, __expf(ld));
   } else {
-    __syncthreads();  // phase A is done with the LDS
+    store_state<K>(S, c, a.states + (((int64_t)it.b * a.nr + it.r) * d.H + c.h) * PN, nullptr,
+                   0.f);
+    if (c.lane == 0 && c.p0 == 0) a.logdecay[((int64_t)it.b * d.H + c.h) * a.nr + it.r] = ld;
   }
-  // phase B from the state entering the run
-  const float* hr = r == 0 ? (a.h0 ? a.h0 + ((int64_t)b * d.H + c.h) * PN : nullptr)
-                           : a.states + (((int64_t)b * a.nr + (r - 1)) * d.H + c.h) * PN;
-  fused_scan<K>(smem, c, a.x, a.B, a.C, a.dt, a.A, a.D, hr, a.y, d, s_begin, s_end);
 }
 
-__global__ __launch_bounds__(256) void k_sync_zero(int* __restrict__ p, int n) {
-  for (int i = threadIdx.x; i < n; i += 256) p[i] = 0;
+// The chain (nr > 1): nr blocks per chain, each walking the runs for its 1 / nr of the chain's
+// state entries.
+template <class K>
+__global__ __launch_bounds__(K::NT) void k_state_chain(FwdArgs a) {
+  const Dims& d = a.d;
+  const Item it = item_of<K>(a, blockIdx.x, a.nr);
+  const Coord c = coords<K>(d, it.r, it.chain % a.hb, it.b);
+  const int nh = min(K::HPB, c.hlast - c.hbase + 1);
+  chain_scan<K>(a.states, a.logdecay, a.h0, a.fin, d, a.nr, it.b, c.hbase, nh, it.r);
+}
+
+// Phase B, one block per (chain, run), from the state entering the run.
+template <class K>
+__global__ __launch_bounds__(K::NT, 1) void k_fused_scan(FwdArgs a) {
+  static_assert(K::SCAN_LDS <= 160 * 1024, "LDS budget");
+  __shared__ __align__(1024) char smem[K::SCAN_LDS];
+  const Dims& d = a.d;
+  const Item it = item_of<K>(a, blockIdx.x, a.nr);
+  const Coord c = coords<K>(d, it.r, it.chain % a.hb, it.b);
+  const int64_t PN = (int64_t)K::P * K::N;
+  const float* hr = it.r == 0
+                        ? (a.h0 ? a.h0 + ((int64_t)it.b * d.H + c.h) * PN : nullptr)
+                        : a.states + (((int64_t)it.b * a.nr + (it.r - 1)) * d.H + c.h) * PN;
+  fused_scan<K>(smem, c, a.x, a.B, a.C, a.dt, a.A, a.D, hr, a.y, d, it.s_begin, it.s_end);
 }
 
 // ---- plan and launch ----------------------------------------------------------------------------
@@ -1245,9 +1224,8 @@ static int head_blocks(const Dims& d) {
   return d.G * ((hpg + K::HPB - 1) / K::HPB);
 }
 
-// Runs are planned in tokens, as whole multiples of 64 (so of the sub-chunk). The waits between
-// the runs of a chain need every run of a sequence resident at once: at most n_cu runs (one block
-// per compute unit), which lengthens runs asked shorter.
+// Runs are planned in tokens, as whole multiples of 64 (so of the sub-chunk): by default about one
+// block per compute unit in each of the two phases.
 template <class K>
 static void plan_for(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
   constexpr int U = 64;
@@ -1264,8 +1242,6 @@ static void plan_for(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
   }
   if (RU < 1) RU = 1;
   if (RU > nunit) RU = nunit;
-  const int cap = n_cu < 1 ? 1 : n_cu;
-  if ((nunit + RU - 1) / RU > cap) RU = (nunit + cap - 1) / cap;
   fp->run_len = RU * U;
   fp->nr = (nunit + RU - 1) / RU;
 }
@@ -1287,9 +1263,7 @@ int64_t fused_workspace_bytes(const Dims& d, const FusedPlan& fp) {
   if (fp.nr <= 1) return 0;
   const int64_t st = (int64_t)d.Bt * fp.nr * d.H * d.P * d.N * 4;
   const int64_t ld = (int64_t)d.Bt * d.H * fp.nr * 4;
-  const int64_t sy = (int64_t)(2 + 2 * d.Bt * fp.head_blocks) * 4;
-  auto up = [](int64_t v) { return (v + 255) & ~int64_t(255); };
-  return up(st) + up(ld) + up(sy);
+  return ((st + 255) & ~int64_t(255)) + ld;
 }
 
 template <class K>
@@ -1311,31 +1285,33 @@ static hipError_t launch_k(const Dims& d, const FusedPlan& fp, const void* x, co
   a.run_len = fp.run_len;
   a.nr = fp.nr;
   a.hb = fp.head_blocks;
-  const int chains = d.Bt * fp.head_blocks;
-  hipError_t e = hipSuccess;
+  a.na = fin ? fp.nr : fp.nr - 1;  // phase A: every run but the last, unless a final state
   if (fp.nr > 1) {
     const int64_t st = (int64_t)d.Bt * fp.nr * d.H * d.P * d.N * 4;
-    const int64_t ld = (int64_t)d.Bt * d.H * fp.nr * 4;
-    auto up = [](int64_t v) { return (v + 255) & ~int64_t(255); };
-    char* w = static_cast<char*>(ws);
-    a.states = reinterpret_cast<float*>(w);
-    a.logdecay = reinterpret_cast<float*>(w + up(st));
-    a.sync = reinterpret_cast<int*>(w + up(st) + up(ld));
-    if (tm) e = tm->mark(s);
-    if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_sync_zero, dim3(1), dim3(256), 0, s, a.sync, 2 + 2 * chains);
-      e = hipGetLastError();
-    }
+    a.states = static_cast<float*>(ws);
+    a.logdecay = reinterpret_cast<float*>(static_cast<char*>(ws) + ((st + 255) & ~int64_t(255)));
   }
-  if (e == hipSuccess && tm) e = tm->mark(s);
-  if (e != hipSuccess) return e;
-  const dim3 grid(chains * fp.nr);
-  if (fp.split)
-    hipLaunchKernelGGL((k_forward<K, true>), grid, dim3(K::NT), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_forward<K, false>), grid, dim3(K::NT), 0, s, a);
-  e = hipGetLastError();
-  if (e == hipSuccess && tm) e = tm->mark(s);
+  const int chains = d.Bt * fp.head_blocks;
+  hipError_t e = tm ? tm->mark(s) : hipSuccess;
+  if (e == hipSuccess && a.na > 0) {
+    const dim3 grid(chains * a.na);
+    if (fp.split)
+      hipLaunchKernelGGL((k_run_states<K, true>), grid, dim3(K::NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_run_states<K, false>), grid, dim3(K::NT), 0, s, a);
+    e = hipGetLastError();
+    if (e == hipSuccess && tm) e = tm->mark(s);
+  }
+  if (e == hipSuccess && fp.nr > 1) {
+    hipLaunchKernelGGL((k_state_chain<K>), dim3(chains * fp.nr), dim3(K::NT), 0, s, a);
+    e = hipGetLastError();
+    if (e == hipSuccess && tm) e = tm->mark(s);
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL((k_fused_scan<K>), dim3(chains * fp.nr), dim3(K::NT), 0, s, a);
+    e = hipGetLastError();
+    if (e == hipSuccess && tm) e = tm->mark(s);
+  }
   return e;
 }
 

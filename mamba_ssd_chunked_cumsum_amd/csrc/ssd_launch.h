@@ -61,13 +61,14 @@ struct KernelMarks {
 };
 using FusedTimer = KernelMarks;
 // False when the fused kernels do not cover (P, N). run_tokens > 0 asks for runs of at least that
-// many tokens; 0 lets the plan aim at about one block per compute unit (n_cu of them). Runs are
-// lengthened so that a sequence has at most n_cu of them.
+// many tokens (rounded up to 64); 0 lets the plan aim at about one block per compute unit (n_cu of
+// them).
 bool fused_plan(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp);
-// Workspace bytes of a plan (0 for one run per sequence): run states [Bt, nr, H, P, N] f32,
-// run log-decays [Bt, H, nr] f32 and the chain counters, each 256-byte aligned.
+// Workspace bytes of a plan (0 for one run per sequence): run states [Bt, nr, H, P, N] f32 (256-byte
+// aligned), then run log-decays [Bt, H, nr] f32.
 int64_t fused_workspace_bytes(const Dims& d, const FusedPlan& fp);
-// The whole fused forward: a counter reset (nr > 1) and one forward kernel. h0 and fin nullable;
+// The whole fused forward, up to three kernels: run states (skipped with one run per sequence and
+// no final state), the chain over runs (nr > 1) and the fused scan. h0 and fin nullable;
 // ws: fused_workspace_bytes(d, fp) bytes of device memory (unused when nr == 1).
 hipError_t launch_fused(const Dims& d, const FusedPlan& fp, const void* x, const void* B,
                         const void* C, const float* dt, const float* A, const float* D,

@@ -48,8 +48,8 @@ class SSDOptions(ctypes.Structure):
 # ssd_kernel bits (include/ssd.h) and the names the timer reports; a call launches its kernels in
 # increasing bit order
 KERNEL_BITS = ((1, "quadratic"), (2, "chunk_cumsum"), (4, "bmm_chunk"), (8, "chunk_state"),
-               (16, "state_passing"), (32, "chunk_scan"), (64, "sync_reset"),
-               (128, "forward"))
+               (16, "state_passing"), (32, "chunk_scan"), (64, "run_states"),
+               (128, "chain"), (256, "fused_scan"))
 
 
 def kernel_names(mask: int) -> tuple:

@@ -37,7 +37,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert libssd.version() == 10400
+    assert libssd.version() == 10500
     assert libssd.status_string(0) == "ok"
     assert libssd.status_string(3) == "no HIP device"
     assert libssd.status_string(99) == "unknown status"

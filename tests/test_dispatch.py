@@ -40,15 +40,17 @@ def test_fp32_beyond_the_quadratic_bounds_takes_the_unfused_kernels():
 
 
 def test_batched_prefill_runs_without_the_chain():
-    # 16 x 10 head blocks fill more than half the device: one run per sequence, so no chain and
-    # no counters to reset; the forward kernel alone, with or without a final state
+    # 16 x 10 head blocks fill more than half the device: one run per sequence, so no chain; the
+    # run-state kernel only for the final state
     shape = synth.SSDShape("prefill", 16, 300, 80, 64, 128, 1, 256, init_state=True)
-    assert _launch(shape) == ("forward",)
-    assert _launch(shape, want_final=False) == ("forward",)
+    assert _launch(shape) == ("run_states", "fused_scan")
+    assert _launch(shape, want_final=False) == ("fused_scan",)
 
 
 def test_long_bf16_sequence_chains_runs():
-    assert _launch(synth.config("mamba2_130m_layer")) == ("sync_reset", "forward")
+    shape = synth.config("mamba2_130m_layer")
+    assert _launch(shape) == ("run_states", "chain", "fused_scan")
+    assert _launch(shape, want_final=False) == ("run_states", "chain", "fused_scan")
 
 
 def test_unfused_request_on_a_fusable_shape():

@@ -53,10 +53,13 @@ def test_kernel_timer_events():
     """Per-kernel timing events recorded by the library around each kernel."""
     d = _inputs()
     note("kernel timer")
-    for variant, n in (("fused", 2), ("unfused", 5)):
+    for variant, names in (("fused", ("run_states", "chain", "fused_scan")),
+                           ("unfused", ("chunk_cumsum", "bmm_chunk", "chunk_state",
+                                        "state_passing", "chunk_scan"))):
         tm = libssd.KernelTimer()
         ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 64, variant=variant,
                     timer=tm)
         torch.cuda.synchronize()
         times = tm.times_ms()
-        assert len(times) == n and all(t >= 0 for t in times.values())
+        assert tm.kernels() == names, (variant, tm.kernels())
+        assert len(times) == len(names) and all(t >= 0 for t in times.values())
