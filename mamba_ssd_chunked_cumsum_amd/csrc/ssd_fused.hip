@@ -600,6 +600,22 @@ __device__ __forceinline__ void store_state(const f32x4 (&S)[K::NNT][K::NPT], co
 }
 
 
+// The same slice rounded to fp16 (a run's state handed to the chain).
+template <class K>
+__device__ __forceinline__ void store_state_h(const f32x4 (&S)[K::NNT][K::NPT], const Coord& c,
+                                              u16* __restrict__ so) {
+#pragma unroll
+  for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+    for (int pt = 0; pt < K::NPT; ++pt) {
+      const int o = (c.p0 + 16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g;
+      const f32x4 v = S[nt][pt];
+      *reinterpret_cast<uint2*>(so + o) =
+          make_uint2(__builtin_bit_cast(uint32_t, cvt_f16x2(v[0], v[1])),
+                     __builtin_bit_cast(uint32_t, cvt_f16x2(v[2], v[3])));
+    }
+}
+
 // Store the bf16 y tile that phase B left in the x tile of a stage: this wave's p-slice of its head,
 // rows tok0 .. tok0 + T - 1 (rows past the sequence end skipped), 16 bytes per lane. Round k
 // covers rows k * RPR .. + RPR - 1; the swizzle key repeats every 16 rows, so the LDS lane offset
@@ -843,14 +859,16 @@ __device__ __forceinline__ void m_from_shared(const char* cbs, const float* wa, 
 }
 
 // ---- phase B: fused scan ------------------------------------------------------------------------
-// hr_head: the state entering the run for this wave's head ([P, N], row-major); null: zero.
+// The state entering the run for this wave's head ([P, N], row-major): h0_head (fp32) or
+// hin_head (fp16, from the chain), at most one of them not null; both null: zero.
 template <class K>
 __device__ __forceinline__ void fused_scan(char* smem, Coord c, const u16* __restrict__ x,
                                            const u16* __restrict__ Bm, const u16* __restrict__ Cm,
                                            const float* __restrict__ dt,
                                            const float* __restrict__ Av,
                                            const float* __restrict__ Dv,
-                                           const float* __restrict__ hr_head, u16* __restrict__ y,
+                                           const float* __restrict__ h0_head,
+                                           const u16* __restrict__ hin_head, u16* __restrict__ y,
                                            const Dims& d, int s_begin, int s_end) {
   using M = Mma<f16>;
   DmaLanes<K, true> dl;
@@ -876,13 +894,8 @@ __device__ __forceinline__ void fused_scan(char* smem, Coord c, const u16* __res
   // carried state S^T tiles (rows n, columns p): lane holds p = p0 + 16 pt + c16,
   // n = 16 nt + 4 g + 0..3
   f32x4 S[K::NNT][NPT];
-  if (hr_head == nullptr) {
-#pragma unroll
-    for (int nt = 0; nt < K::NNT; ++nt)
-#pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) S[nt][pt] = zero4();
-  } else {
-    const float* hr = hr_head + (int64_t)c.p0 * K::N;
+  if (h0_head != nullptr) {
+    const float* hr = h0_head + (int64_t)c.p0 * K::N;
 #pragma unroll
     for (int nt = 0; nt < K::NNT; ++nt)
 #pragma unroll
@@ -891,6 +904,22 @@ __device__ __forceinline__ void fused_scan(char* smem, Coord c, const u16* __res
             *reinterpret_cast<const float4*>(hr + (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g);
         S[nt][pt] = f32x4{v.x, v.y, v.z, v.w};
       }
+  } else if (hin_head != nullptr) {
+    const u16* hr = hin_head + (int64_t)c.p0 * K::N;
+#pragma unroll
+    for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) {
+        const uint2 v =
+            *reinterpret_cast<const uint2*>(hr + (16 * pt + c.c16) * K::N + 16 * nt + 4 * c.g);
+        const f16x2 lo = __builtin_bit_cast(f16x2, v.x), hi = __builtin_bit_cast(f16x2, v.y);
+        S[nt][pt] = f32x4{(float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]};
+      }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) S[nt][pt] = zero4();
   }
   {
     // the compiler's own wait for these loads (it does not see the DMA waits, which are inline
@@ -1056,71 +1085,82 @@ __device__ __forceinline__ void fused_scan(char* smem, Coord c, const u16* __res
 
 
 // ---- chain between runs -------------------------------------------------------------------------
-// This block's share (1 / nr of the entries) of its chain: for each entry, walk the runs,
-// h <- exp(logdecay_q) h + state_q starting from h0 (or 0), writing the state entering run q + 1
-// over slot q; after the last run (when a final state is wanted) h is the final state. A thread
-// takes EPT entries (NT apart) at once and loads GS runs' states and decays of all of them
-// together: only the multiply-adds depend on the run before, so a share costs about
-// nr / GS memory round trips.
-template <class K>
-__device__ __forceinline__ void chain_scan(float* __restrict__ states,
-                                           const float* __restrict__ logdecay,
-                                           const float* __restrict__ h0, float* __restrict__ fin,
-                                           const Dims& d, int nr, int b, int hbase, int nh, int r) {
-  constexpr int PN = K::P * K::N, PN4 = PN / 4;
-  constexpr int EPT = 3, GS = 6;
-  const int E4 = nh * PN4;
-  const int per = (E4 + nr - 1) / nr;
-  const int lo = r * per, hi = min(E4, lo + per);
-  const int nsteps = fin ? nr : nr - 1;
-  const int64_t cstride = (int64_t)d.H * PN;  // floats between runs' slots
-  for (int i0 = lo + (int)threadIdx.x; i0 < hi; i0 += EPT * K::NT) {
-    float4 s[EPT];
-    float* sp[EPT];
-    const float* ldp[EPT];
-    int64_t sb[EPT];
+// One thread per 8 consecutive entries of one (batch, head) state: walk the runs,
+// h <- exp(logdecay_q) h + state_q starting from h0 (or 0), in fp32, writing the state entering
+// run q + 1 over slot q (fp16); after the last run (when a final state is wanted) h is the final
+// state. Only the multiply-adds depend on the run before: the loads of GS runs are issued
+// together.
+struct ChainArgs {
+  u16* states;              // [Bt, nr, H, P, N] fp16
+  const float* logdecay;    // [Bt, H, nr]
+  const float* h0;          // [Bt, H, P, N] or null
+  float* fin;               // [Bt, H, P, N] or null
+  int64_t pieces;           // Bt * H * P * N / 8
+  int PN8, H, nr;
+};
+
+__device__ __forceinline__ void unpack8(uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      const int i = min(i0 + k * K::NT, hi - 1);  // past the share: a copy of its last entry
-      const int h = hbase + i / PN4, e = (i % PN4) * 4;
-      sb[k] = ((int64_t)b * d.H + h) * PN + e;
-      s[k] = h0 ? *reinterpret_cast<const float4*>(h0 + sb[k]) : make_float4(0.f, 0.f, 0.f, 0.f);
-      ldp[k] = logdecay + ((int64_t)b * d.H + h) * nr;
-      sp[k] = states + ((int64_t)b * nr * d.H + h) * PN + e;
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+    f[2 * i] = (float)h[0];
+    f[2 * i + 1] = (float)h[1];
+  }
+}
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = __builtin_bit_cast(uint32_t, cvt_f16x2(f[2 * i], f[2 * i + 1]));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ __launch_bounds__(256) void k_state_chain(ChainArgs a) {
+  constexpr int GS = 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.pieces) return;
+  const int64_t bh = i / a.PN8;        // batch * H + head
+  const int64_t e = (i % a.PN8) * 8;   // entry within the state
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const int64_t PN = (int64_t)a.PN8 * 8;
+  const int64_t slot = (int64_t)a.H * PN;  // elements between runs' slots
+  u16* sp = a.states + (b * a.nr * a.H + h) * PN + e;
+  const float* ld = a.logdecay + bh * a.nr;
+  float acc[8];
+  if (a.h0) {
+    const float4 u = *reinterpret_cast<const float4*>(a.h0 + bh * PN + e);
+    const float4 v = *reinterpret_cast<const float4*>(a.h0 + bh * PN + e + 4);
+    acc[0] = u.x; acc[1] = u.y; acc[2] = u.z; acc[3] = u.w;
+    acc[4] = v.x; acc[5] = v.y; acc[6] = v.z; acc[7] = v.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  }
+  const int nsteps = a.fin ? a.nr : a.nr - 1;
+  for (int q0 = 0; q0 < nsteps; q0 += GS) {
+    uint4 st[GS];
+    float dec[GS];
+#pragma unroll
+    for (int u = 0; u < GS; ++u) {
+      const int q = min(q0 + u, nsteps - 1);
+      st[u] = *reinterpret_cast<const uint4*>(sp + q * slot);
+      dec[u] = __expf(ld[q]);
     }
-    for (int c0 = 0; c0 < nsteps; c0 += GS) {
-      float4 st[EPT][GS];
-      float a[EPT][GS];
 #pragma unroll
-      for (int k = 0; k < EPT; ++k)
+    for (int u = 0; u < GS; ++u) {
+      if (q0 + u < nsteps) {
+        float f[8];
+        unpack8(st[u], f);
 #pragma unroll
-        for (int u = 0; u < GS; ++u) {
-          const int q = min(c0 + u, nsteps - 1);
-          st[k][u] = *reinterpret_cast<const float4*>(sp[k] + q * cstride);
-          a[k][u] = ldp[k][q];
-        }
-#pragma unroll
-      for (int k = 0; k < EPT; ++k) {
-        const bool own = i0 + k * K::NT < hi;
-#pragma unroll
-        for (int u = 0; u < GS; ++u) {
-          if (c0 + u < nsteps) {
-            const float dec = __expf(a[k][u]);
-            s[k].x = dec * s[k].x + st[k][u].x;
-            s[k].y = dec * s[k].y + st[k][u].y;
-            s[k].z = dec * s[k].z + st[k][u].z;
-            s[k].w = dec * s[k].w + st[k][u].w;
-            if (own && c0 + u < nr - 1)
-              *reinterpret_cast<float4*>(sp[k] + (c0 + u) * cstride) = s[k];
-          }
-        }
+        for (int k = 0; k < 8; ++k) acc[k] = dec[u] * acc[k] + f[k];
+        if (q0 + u < a.nr - 1) *reinterpret_cast<uint4*>(sp + (q0 + u) * slot) = pack8(acc);
       }
     }
-    if (fin) {
-#pragma unroll
-      for (int k = 0; k < EPT; ++k)
-        if (i0 + k * K::NT < hi) *reinterpret_cast<float4*>(fin + sb[k]) = s[k];
-    }
+  }
+  if (a.fin) {
+    *reinterpret_cast<float4*>(a.fin + bh * PN + e) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4*>(a.fin + bh * PN + e + 4) =
+        make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
 }
 
@@ -1130,7 +1170,7 @@ struct FwdArgs {
   const float *dt, *A, *D, *h0;
   u16* y;
   float* fin;       // final state [Bt, H, P, N]; null: not written
-  float* states;    // [Bt, nr, H, P, N]: run states, then the state entering the next run
+  u16* states;      // [Bt, nr, H, P, N] fp16: run states, then the state entering the next run
   float* logdecay;  // [Bt, H, nr]
   Dims d;
   int run_len, nr, hb;  // run length (tokens), runs per sequence, head blocks per batch entry
@@ -1174,21 +1214,9 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_states(FwdArgs a) {
     const int64_t o = ((int64_t)it.b * d.H + c.h) * PN;
     store_state<K>(S, c, a.fin + o, a.h0 ? a.h0 + o : nullptr, __expf(ld));
   } else {
-    store_state<K>(S, c, a.states + (((int64_t)it.b * a.nr + it.r) * d.H + c.h) * PN, nullptr,
-                   0.f);
+    store_state_h<K>(S, c, a.states + (((int64_t)it.b * a.nr + it.r) * d.H + c.h) * PN);
     if (c.lane == 0 && c.p0 == 0) a.logdecay[((int64_t)it.b * d.H + c.h) * a.nr + it.r] = ld;
   }
-}
-
-// The chain (nr > 1): nr blocks per chain, each walking the runs for its 1 / nr of the chain's
-// state entries.
-template <class K>
-__global__ __launch_bounds__(K::NT) void k_state_chain(FwdArgs a) {
-  const Dims& d = a.d;
-  const Item it = item_of<K>(a, blockIdx.x, a.nr);
-  const Coord c = coords<K>(d, it.r, it.chain % a.hb, it.b);
-  const int nh = min(K::HPB, c.hlast - c.hbase + 1);
-  chain_scan<K>(a.states, a.logdecay, a.h0, a.fin, d, a.nr, it.b, c.hbase, nh, it.r);
 }
 
 // Phase B, one block per (chain, run), from the state entering the run.
@@ -1200,10 +1228,10 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(FwdArgs a) {
   const Item it = item_of<K>(a, blockIdx.x, a.nr);
   const Coord c = coords<K>(d, it.r, it.chain % a.hb, it.b);
   const int64_t PN = (int64_t)K::P * K::N;
-  const float* hr = it.r == 0
-                        ? (a.h0 ? a.h0 + ((int64_t)it.b * d.H + c.h) * PN : nullptr)
-                        : a.states + (((int64_t)it.b * a.nr + (it.r - 1)) * d.H + c.h) * PN;
-  fused_scan<K>(smem, c, a.x, a.B, a.C, a.dt, a.A, a.D, hr, a.y, d, it.s_begin, it.s_end);
+  const float* h0 = it.r == 0 && a.h0 ? a.h0 + ((int64_t)it.b * d.H + c.h) * PN : nullptr;
+  const u16* hin =
+      it.r > 0 ? a.states + (((int64_t)it.b * a.nr + (it.r - 1)) * d.H + c.h) * PN : nullptr;
+  fused_scan<K>(smem, c, a.x, a.B, a.C, a.dt, a.A, a.D, h0, hin, a.y, d, it.s_begin, it.s_end);
 }
 
 // ---- plan and launch ----------------------------------------------------------------------------
@@ -1261,7 +1289,7 @@ bool fused_plan(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
 
 int64_t fused_workspace_bytes(const Dims& d, const FusedPlan& fp) {
   if (fp.nr <= 1) return 0;
-  const int64_t st = (int64_t)d.Bt * fp.nr * d.H * d.P * d.N * 4;
+  const int64_t st = (int64_t)d.Bt * fp.nr * d.H * d.P * d.N * 2;
   const int64_t ld = (int64_t)d.Bt * d.H * fp.nr * 4;
   return ((st + 255) & ~int64_t(255)) + ld;
 }
@@ -1287,15 +1315,17 @@ static hipError_t launch_k(const Dims& d, const FusedPlan& fp, const void* x, co
   a.hb = fp.head_blocks;
   a.na = fin ? fp.nr : fp.nr - 1;  // phase A: every run but the last, unless a final state
   if (fp.nr > 1) {
-    const int64_t st = (int64_t)d.Bt * fp.nr * d.H * d.P * d.N * 4;
-    a.states = static_cast<float*>(ws);
+    const int64_t st = (int64_t)d.Bt * fp.nr * d.H * d.P * d.N * 2;
+    a.states = static_cast<u16*>(ws);
     a.logdecay = reinterpret_cast<float*>(static_cast<char*>(ws) + ((st + 255) & ~int64_t(255)));
   }
   const int chains = d.Bt * fp.head_blocks;
   hipError_t e = tm ? tm->mark(s) : hipSuccess;
   if (e == hipSuccess && a.na > 0) {
     const dim3 grid(chains * a.na);
-    if (fp.split)
+    // the split pays only where the run state is the final state itself (one run per sequence):
+    // a state handed to the chain is rounded to fp16 anyway
+    if (fp.split && fp.nr == 1)
       hipLaunchKernelGGL((k_run_states<K, true>), grid, dim3(K::NT), 0, s, a);
     else
       hipLaunchKernelGGL((k_run_states<K, false>), grid, dim3(K::NT), 0, s, a);
@@ -1303,7 +1333,10 @@ static hipError_t launch_k(const Dims& d, const FusedPlan& fp, const void* x, co
     if (e == hipSuccess && tm) e = tm->mark(s);
   }
   if (e == hipSuccess && fp.nr > 1) {
-    hipLaunchKernelGGL((k_state_chain<K>), dim3(chains * fp.nr), dim3(K::NT), 0, s, a);
+    ChainArgs ca{a.states, a.logdecay, h0, fin, (int64_t)d.Bt * d.H * d.P * d.N / 8,
+                 (int)(d.P * d.N / 8), (int)d.H, fp.nr};
+    hipLaunchKernelGGL(k_state_chain, dim3((unsigned)((ca.pieces + 255) / 256)), dim3(256), 0, s,
+                       ca);
     e = hipGetLastError();
     if (e == hipSuccess && tm) e = tm->mark(s);
   }

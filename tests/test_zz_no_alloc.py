@@ -1,7 +1,7 @@
 """ssd_forward_noalloc, the forward that allocates nothing (workspace from the library's static
 per-device scratch), against ssd_forward_ex through the C ABI: two calls in a row, the second on a
 smaller input, each compared with ssd_forward_ex's output on the same inputs; a plan fitted to the
-scratch (runs lengthened) held to the parity bar against both ssd_forward_ex and the oracle; the
+scratch (runs lengthened) held to the parity bar against the oracle, as ssd_forward_ex is; the
 unfused path within the scratch; and an unfused request beyond it rejected with nothing written."""
 
 import numpy as np
@@ -17,7 +17,7 @@ from gpu_util import as64, note, score, to_device
 pytestmark = pytest.mark.gpu
 
 
-def _run(shape, seed, noalloc, variant="auto"):
+def _run(shape, seed, noalloc, variant="auto", run_chunks=0):
     d = to_device(synth.make_inputs(shape, seed=seed), shape.io)
     y = torch.full_like(d["x"], 3.0)
     fin = torch.full((shape.batch, shape.nheads, shape.headdim, shape.dstate), 3.0,
@@ -25,7 +25,7 @@ def _run(shape, seed, noalloc, variant="auto"):
     tm = libssd.KernelTimer()
     ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], shape.chunk_size,
                 d["initial_state"], variant=variant, out=y, final_out=fin, noalloc=noalloc,
-                timer=tm)
+                timer=tm, run_chunks=run_chunks)
     torch.cuda.synchronize()
     return y, fin, tm.kernels()
 
@@ -47,21 +47,22 @@ def test_two_calls_in_a_row_match_the_allocating_forward():
 
 
 def test_plan_fitted_to_the_scratch():
-    # headdim 128, dstate 256: 16 runs of 256 tokens per sequence would need 64 MiB of run states
-    # plus the decays; the no-allocation plan doubles the run length, so the numbers differ from
-    # the allocating forward's only by rounding
+    # headdim 128, dstate 256, runs of one 128-token chunk: 32 runs per sequence would need 64 MiB
+    # of fp16 run states plus the decays; the no-allocation plan doubles the run length, so the
+    # numbers differ from the allocating forward's only by rounding
     shape = synth.SSDShape("noalloc_fitted", 1, 4096, 32, 128, 256, 1, 128, init_state=True)
     note(f"noalloc fitted {shape}")
-    y0, f0, _ = _run(shape, 9, noalloc=False)
-    y1, f1, _ = _run(shape, 9, noalloc=True)
+    y0, f0, _ = _run(shape, 9, noalloc=False, run_chunks=1)
+    y1, f1, _ = _run(shape, 9, noalloc=True, run_chunks=1)
     assert not torch.equal(y0, y1)  # a different cut of the sequence
-    rep = score(as64(y1), as64(f1), as64(y0), as64(f0), "bf16")
-    assert rep["pass"], rep
+    # both held to the parity bar against the oracle (two bf16 outputs of different plans may
+    # differ by a rounding of each, which the bar's half-ulp allowance covers only once)
     inp = synth.make_inputs(shape, seed=9)
     units = [0, 13, 31]
     y_ref, f_ref = native.forward(**inp, units=units)
-    rep = score(as64(y1), as64(f1), y_ref, f_ref, "bf16", units, shape.nheads)
-    assert rep["pass"], rep
+    for y, f in ((y0, f0), (y1, f1)):
+        rep = score(as64(y), as64(f), y_ref, f_ref, "bf16", units, shape.nheads)
+        assert rep["pass"], rep
 
 
 def test_unfused_within_and_beyond_the_scratch():
