@@ -10,16 +10,20 @@ timed passes of K steps each, bracketed by device synchronisations: the first ti
 forward with HIP events on its stream (the reported ms per step and tokens/s), the second also
 records events around every kernel inside the forward (per-kernel durations; the roofline).
 
-Prints ONE JSON line: tokens/s, ms per step, the roofline of the dominant kernel (algorithmic
-bytes per launch over its measured duration, against MI355X's 8 TB/s), the whole forward's
-roofline fraction, and the CPU oracle's throughput on the same workload (with the parity of the
-GPU result on the units the oracle computed).
+Prints ONE JSON line: tokens/s (mean and median step), ms per step, the whole forward's roofline
+(its algorithmic bytes over its measured time, against MI355X's 8 TB/s; `roofline`), the dominant
+kernel's (its algorithmic bytes per launch over its measured duration;
+`dominant_kernel_roofline`), per-kernel times, the other bf16 workloads' cold-cache times and
+roofline fractions (`workloads`), run metadata (`run`: ROCm, compiler, GPU, clocks, revision,
+CPU), and the CPU oracle's throughput on the same workload (with the parity of the GPU result on
+the units the oracle computed).
 
     python bench.py --summarize-profiles DIR
 
-turns rocprofv3 output under DIR (a kernel-trace run and one FETCH_SIZE and one WRITE_SIZE counter
-run, each with --copy-calibration, plus DIR/bench.json from a plain bench run) into the text
-summaries under profiles/ and the traffic record the bench line reports; see PROFILE_COMMANDS.
+turns rocprofv3 output under DIR (a kernel-trace run, one FETCH_SIZE and one WRITE_SIZE counter
+run with --copy-calibration, two SQ counter runs, plus DIR/bench.json from a plain bench run)
+into the text summaries under profiles/ and the traffic record the bench line reports; see
+PROFILE_COMMANDS.
 """
 
 from __future__ import annotations
@@ -77,16 +81,22 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str, launches_bytes: float):
-    """HBM bytes per launch from committed counter runs, if they were taken on these sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+def measured_traffic(workload: str, kernels) -> float | None:
+    """L2-to-memory bytes per launch, summed over `kernels`, from committed counter runs taken on
+    these sources (None if there are none, or a kernel is missing from them). FETCH_SIZE and
+    WRITE_SIZE count what the L2s exchange with the memory side, part of which the Infinity Cache
+    may serve: an upper bound on HBM bytes."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("source_hash") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    per = rec.get("kernels", {})
+    if any(k not in per for k in kernels):
+        return None
+    return float(sum(per[k]["fetch_bytes"] + per[k]["write_bytes"] for k in kernels))
 
 
 def cpu_baseline(inp, shape, y_gpu, f_gpu, max_seconds: float):
@@ -126,14 +136,24 @@ def cpu_baseline(inp, shape, y_gpu, f_gpu, max_seconds: float):
     }, rep
 
 
+SQ_PASSES = {
+    "sq1": "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VMEM "
+           "SQ_WAVE_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "sq2": "SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_WAIT_INST_ANY SQ_WAIT_ANY "
+           "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_LDS SQ_INSTS_VALU_MFMA_MOPS_F16 "
+           "GRBM_GUI_ACTIVE",
+}
+_PROF_RUN = "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-backward --no-workloads"
 PROFILE_COMMANDS = [
     "python3 bench.py --steps 20 --warmup 3 > DIR/bench.json",
     "rocprofv3 --kernel-trace --stats -d DIR/prof_kt -o kt --output-format csv -- "
-    "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-backward",
+    "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-backward --no-workloads",
     "rocprofv3 --pmc FETCH_SIZE -d DIR/prof_fetch -o fetch --output-format csv -- "
-    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-backward --copy-calibration",
+    f"{_PROF_RUN} --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE -d DIR/prof_write -o write --output-format csv -- "
-    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-backward --copy-calibration",
+    f"{_PROF_RUN} --copy-calibration",
+    *[f"rocprofv3 --pmc {c} -d DIR/prof_{n} -o {n} --output-format csv -- {_PROF_RUN}"
+      for n, c in SQ_PASSES.items()],
     "python3 bench.py --summarize-profiles DIR",
 ]
 
@@ -158,9 +178,17 @@ def _csv_rows(path):
     return rows
 
 
+# The forward's kernels as the library's timer names them, and their rocprofv3 names (k_<name>).
+_KERNEL_OBJ = {"run_states": "run_states", "chain": "state_chain", "fused_scan": "fused_scan",
+               "chunk_cumsum": "chunk_cumsum", "bmm_chunk": "bmm_chunk",
+               "chunk_state": "chunk_state", "state_passing": "state_passing",
+               "chunk_scan": "chunk_scan", "quadratic": "quadratic"}
+
+
 def summarize_profiles(d: str) -> None:
-    """Write profiles/<kernel>_<workload>.txt and profiles/traffic_<kernel>_<workload>.json from
-    the rocprofv3 runs under d (see PROFILE_COMMANDS)."""
+    """Write profiles/forward_<workload>.txt (kernel times and L2-to-memory bytes),
+    profiles/forward_counters_<workload>.txt (SQ counters) and profiles/traffic_<workload>.json
+    from the rocprofv3 runs under d (see PROFILE_COMMANDS)."""
     with open(os.path.join(d, "bench.json")) as f:
         bench = json.loads(f.read().strip().splitlines()[-1])
     workload = bench["config"]["workload"]
@@ -171,7 +199,7 @@ def summarize_profiles(d: str) -> None:
             stats[k] = (int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
                         float(r["MaxNs"]))
     counters = {}
-    for sub in ("prof_fetch", "prof_write"):
+    for sub in ("prof_fetch", "prof_write", *[f"prof_{n}" for n in SQ_PASSES]):
         for r in _csv_rows(os.path.join(d, sub, "*counter_collection.csv")):
             k = _short_kernel(r["Kernel_Name"])
             if k:
@@ -184,17 +212,21 @@ def summarize_profiles(d: str) -> None:
         raise SystemExit("no 1 GiB copy dispatch found in the counter runs (--copy-calibration)")
     fetch_scale, write_scale = gib / (cf * 1024), gib / (cw * 1024)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    alg_bytes = bench["roofline"]["achieved"] * 1e9 * bench["roofline"]["kernel_ms"] / 1e3
+    src = kernel_source_hash()
+    roof = bench["roofline"]
+    dom = bench["dominant_kernel_roofline"]
     lines = [
         f"rocprofv3 summary: libssd forward kernels, workload {workload} "
         f"({json.dumps(bench['config'])})",
-        f"kernel sources hash {kernel_source_hash()}",
+        f"kernel sources hash {src}; run {json.dumps(bench.get('run', {}))}",
         "",
         "commands (DIR = a scratch output folder; the last runs on any host):",
         *["  " + c for c in PROFILE_COMMANDS],
         "",
         f"copy calibration (1 GiB copy): FETCH_SIZE {cf:.0f} KiB -> x{fetch_scale:.3f}, "
         f"WRITE_SIZE {cw:.0f} KiB -> x{write_scale:.3f}",
+        "FETCH_SIZE / WRITE_SIZE count bytes between the L2s and the memory side, part of which "
+        "the Infinity Cache may serve: an upper bound on HBM bytes.",
         "",
         f"{'kernel':16s}{'calls':>7s}{'avg us':>10s}{'min us':>10s}{'max us':>10s}"
         f"{'bench us':>10s}{'fetch MB':>11s}{'write MB':>11s}",
@@ -206,28 +238,92 @@ def summarize_profiles(d: str) -> None:
         fb = (sum(fk) / len(fk)) * 1024 * fetch_scale if fk else float("nan")
         wb = (sum(wk) / len(wk)) * 1024 * write_scale if wk else float("nan")
         traffic[k] = (fb, wb)
-        bus = bench["kernel_ms"].get(k, float("nan")) * 1e3
+        name = next((t for t, o in _KERNEL_OBJ.items() if o == k), k)
+        bus = bench["kernel_ms"].get(name, float("nan")) * 1e3
         lines.append(f"{k:16s}{calls:7d}{avg / 1e3:10.1f}{mn / 1e3:10.1f}{mx / 1e3:10.1f}"
                      f"{bus:10.1f}{fb / 1e6:11.2f}{wb / 1e6:11.2f}")
-    dom = bench["roofline"]["kernel"]
-    fb, wb = traffic.get(dom, (float("nan"), float("nan")))
+    fwd = [_KERNEL_OBJ.get(k, k) for k in bench["kernel_ms"]]
+    tot = sum(sum(traffic.get(k, (float("nan"),) * 2)) for k in fwd)
+    dk = _KERNEL_OBJ.get(dom["kernel"], dom["kernel"])
+    dfb, dwb = traffic.get(dk, (float("nan"), float("nan")))
     lines += [
         "",
-        f"dominant kernel {dom}: algorithmic bytes per launch {alg_bytes / 1e6:.2f} MB, "
-        f"measured HBM bytes per launch {(fb + wb) / 1e6:.2f} MB "
-        f"(ratio {(fb + wb) / alg_bytes:.2f})",
-        f"bench line: {bench['ms_per_step'] * 1e3:.1f} us per forward, "
-        f"{bench['value'] / 1e6:.2f} M tokens/s, roofline frac {bench['roofline']['frac']:.3f}",
+        f"whole forward ({' + '.join(fwd)}): algorithmic bytes {roof['bytes'] / 1e6:.2f} MB, "
+        f"L2-to-memory bytes {tot / 1e6:.2f} MB (ratio {tot / roof['bytes']:.2f})",
+        f"dominant kernel {dk}: algorithmic bytes per launch {dom['bytes'] / 1e6:.2f} MB, "
+        f"L2-to-memory bytes per launch {(dfb + dwb) / 1e6:.2f} MB "
+        f"(ratio {(dfb + dwb) / dom['bytes']:.2f})",
+        f"bench line: {bench['ms_per_step'] * 1e3:.1f} us per forward (median "
+        f"{bench['ms_per_step_median'] * 1e3:.1f}), {bench['value'] / 1e6:.2f} M tokens/s, "
+        f"forward roofline frac {roof['frac']:.3f}, dominant kernel frac {dom['frac']:.3f}",
     ]
-    with open(os.path.join(ROOT, "profiles", f"{dom}_{workload}.txt"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"forward_{workload}.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    rec = {"kernel": dom, "workload": workload, "source_hash": kernel_source_hash(),
-           "hbm_bytes_per_launch": fb + wb, "fetch_bytes_per_launch": fb,
-           "write_bytes_per_launch": wb, "fetch_scale": fetch_scale, "write_scale": write_scale,
-           "commands": PROFILE_COMMANDS}
-    with open(os.path.join(ROOT, "profiles", f"traffic_{dom}_{workload}.json"), "w") as f:
+    rec = {"workload": workload, "source_hash": src, "fetch_scale": fetch_scale,
+           "write_scale": write_scale, "commands": PROFILE_COMMANDS,
+           "kernels": {_KERNEL_OBJ_REV.get(k, k): {"fetch_bytes": fb, "write_bytes": wb}
+                       for k, (fb, wb) in traffic.items()}}
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as f:
         json.dump(rec, f, indent=1)
     print("\n".join(lines))
+    clines = _sq_summary(counters, stats, workload, src)
+    if clines:
+        with open(os.path.join(ROOT, "profiles", f"forward_counters_{workload}.txt"), "w") as f:
+            f.write("\n".join(clines) + "\n")
+        print("\n".join(clines))
+
+
+_KERNEL_OBJ_REV = {o: t for t, o in _KERNEL_OBJ.items()}
+
+
+def _sq_summary(counters, stats, workload, src):
+    """Per-kernel SQ counter figures. Normalisation (MI355X: 8 XCDs, 256 CUs, 1024 SIMDs):
+    GRBM_GUI_ACTIVE sums the XCDs' busy cycles, so a SIMD's cycles are GUI_ACTIVE / 8;
+    SQ_VALU_MFMA_BUSY_CYCLES sums matrix-core busy cycles over SIMDs; SQ_ACTIVE_INST_VALU counts
+    issue quad-cycles (4 cycles each) summed over waves; SQ_WAVE_CYCLES and SQ_WAIT_* count
+    quad-cycles per wave, summed over waves."""
+    names = sorted({k for (k, c) in counters if c.startswith("SQ_") and k != "copy"})
+    if not names:
+        return []
+    out = [f"rocprofv3 SQ counters: libssd forward kernels, workload {workload}; kernel sources "
+           f"hash {src}", "commands: the two 'rocprofv3 --pmc SQ_...' lines of the forward "
+           f"summary (profiles/forward_{workload}.txt)", "",
+           _sq_summary.__doc__.split("Normalisation")[1].strip().replace("\n    ", "\n"), ""]
+    for k in names:
+        v = {c: sum(x) / len(x) for (kk, c), x in counters.items() if kk == k}
+        gui = v.get("GRBM_GUI_ACTIVE", 0.0)
+        waves = v.get("SQ_WAVES", 0.0)
+        simd_cycles = gui / 8 * 1024 if gui else 0.0
+        out.append(f"{k}: {stats.get(k, (0, float('nan')))[1] / 1e3:.1f} us average "
+                   f"(kernel trace), {waves:.0f} waves")
+        if waves:
+            per = ", ".join(f"{c[9:].lower()} {v[c] / waves:.0f}" for c in
+                            ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_LDS",
+                             "SQ_INSTS_VMEM") if c in v)
+            out.append(f"   instructions per wave: {per}")
+        if simd_cycles:
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+                out.append(f"   matrix cores busy: {v['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.3f}"
+                           " of SIMD cycles")
+            if "SQ_ACTIVE_INST_VALU" in v:
+                out.append(f"   vector ALU issuing: {4 * v['SQ_ACTIVE_INST_VALU'] / simd_cycles:.3f}"
+                           " of SIMD cycles")
+        if v.get("SQ_WAVE_CYCLES"):
+            wc = v["SQ_WAVE_CYCLES"]
+            for c, what in (("SQ_WAIT_INST_ANY", "waiting on a dependency (waitcnt)"),
+                            ("SQ_WAIT_ANY", "waiting on anything")):
+                if c in v:
+                    out.append(f"   wave time {what}: {v[c] / wc:.3f}")
+        if v.get("SQ_LDS_IDX_ACTIVE"):
+            out.append(f"   LDS bank-conflict cycles / LDS active cycles: "
+                       f"{v.get('SQ_LDS_BANK_CONFLICT', 0.0) / v['SQ_LDS_IDX_ACTIVE']:.3f}")
+        if "SQ_INSTS_VALU_MFMA_MOPS_F16" in v and gui:
+            t = stats.get(k, (0, 0.0))[1] * 1e-9
+            if t:
+                out.append(f"   fp16 matrix flops: {v['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512 / t / 1e12:.1f}"
+                           " TFLOP/s (MOPS x 512 over the kernel's average duration)")
+        out.append("")
+    return out
 
 
 def decode_bench(shape, dev, layers: int = 64, rounds: int = 5) -> dict:
@@ -385,6 +481,132 @@ def backward_bench(shape, d, flush, flush_out, steps: int = 3) -> dict:
                     "kernels"}
 
 
+def host_metadata() -> dict:
+    """What the numbers were measured with, from the host side: ROCm and compiler, GPU clocks
+    (rocm-smi), the library's revision (git, or the one recorded when it was built) and source
+    hash, and the host CPU. Runs its helper programs as child processes, so it is called before
+    this process touches the GPU (a child forked after that would inherit the initialised
+    device)."""
+    import platform
+
+    # Under a profiler whose preloaded library has already opened the device (rocprofv3 with
+    # counters does), even a child process would start from an initialised device: no children.
+    profiled = "rocprof" in os.environ.get("LD_PRELOAD", "") or any(
+        k.startswith("ROCPROF") for k in os.environ)
+
+    def cmd(args, timeout=20):
+        if profiled:
+            return ""
+        try:
+            return subprocess.run(args, capture_output=True, text=True, timeout=timeout).stdout
+        except (OSError, subprocess.SubprocessError):
+            return ""
+
+    info = {}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    info["hipcc"] = (cmd(["/opt/rocm/bin/hipcc", "--version"]).splitlines() or [None])[0]
+    clocks = {}
+    for line in cmd(["rocm-smi", "--showclocks"]).splitlines():
+        for key in ("sclk", "mclk", "fclk", "socclk"):
+            if f"{key} clock level" in line and "(" in line:
+                clocks[key] = line.split("(")[-1].split(")")[0]
+    info["clocks"] = clocks or None
+    rev = cmd(["git", "-C", ROOT, "rev-parse", "HEAD"]).strip()
+    build = {}
+    try:
+        with open(os.path.join(ROOT, "mamba_ssd_chunked_cumsum_amd", "_lib", "build_info.json")) as f:
+            build = json.load(f)
+    except (OSError, ValueError):
+        pass
+    info["git_rev"] = rev or build.get("git_rev")
+    info["library_built_from"] = build or None
+    info["kernel_sources_hash"] = kernel_source_hash()
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    info["cpu"] = cpu or platform.processor()
+    info["cpu_threads"] = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") \
+        else os.cpu_count()
+    return info
+
+
+def run_metadata(dev, host: dict) -> dict:
+    """host_metadata() plus the GPU's name, architecture and compute units, and torch."""
+    import torch
+
+    props = torch.cuda.get_device_properties(dev)
+    info = dict(host)
+    info["gpu"] = props.name
+    info["arch"] = getattr(props, "gcnArchName", None)
+    info["compute_units"] = props.multi_processor_count
+    info["torch"] = torch.__version__
+    return info
+
+
+def workload_bench(index: int, dev, flush, flush_out, steps: int = 5) -> dict:
+    """One more workload's whole forward (auto variant, cold cache before every step): mean and
+    median ms, tokens/s, per-kernel ms and its roofline fraction."""
+    import numpy as np
+    import torch
+
+    import mamba_ssd_chunked_cumsum_amd as ssd
+    from mamba_ssd_chunked_cumsum_amd import libssd, synth
+
+    shape = synth.CONFIGS[index]
+    inp = synth.make_inputs(shape, cfg_index=index)
+    io = torch.bfloat16 if shape.io == "bf16" else torch.float32
+    d = {k: (None if v is None else torch.from_numpy(v).to(dev)) for k, v in inp.items()}
+    del inp
+    for k in ("x", "B", "C"):
+        d[k] = d[k].to(io)
+    y = torch.empty_like(d["x"])
+    fin = torch.empty((shape.batch, shape.nheads, shape.headdim, shape.dstate),
+                      dtype=torch.float32, device=dev)
+
+    def call(timer=None):
+        ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], shape.chunk_size,
+                    d["initial_state"], out=y, final_out=fin, timer=timer)
+
+    call()
+    torch.cuda.synchronize()
+    ms, per = [], {}
+    for k in range(2 * steps):
+        if flush is not None:
+            torch.sum(flush, dim=0, dtype=torch.int64, out=flush_out)
+        tm = libssd.KernelTimer() if k >= steps else None
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call(tm)
+        e1.record()
+        torch.cuda.synchronize()
+        if tm is None:
+            ms.append(e0.elapsed_time(e1))
+        else:
+            for name, t in tm.times_ms().items():
+                per.setdefault(name, []).append(t)
+    alg = algorithmic(shape, d["initial_state"] is not None)
+    t = float(np.mean(ms))
+    t_roof = max(alg["bytes"] / (HBM_PEAK_GBS * 1e9),
+                 alg["flops"] / ((MFMA_F16_PEAK_TFLOPS if shape.io == "bf16"
+                                  else FP32_PEAK_TFLOPS) * 1e12))
+    return {"shape": {"batch": shape.batch, "seqlen": shape.seqlen, "nheads": shape.nheads,
+                      "headdim": shape.headdim, "dstate": shape.dstate,
+                      "ngroups": shape.ngroups, "chunk_size": shape.chunk_size,
+                      "initial_state": d["initial_state"] is not None},
+            "ms_per_forward": t, "ms_per_forward_median": float(np.median(ms)),
+            "tokens_per_s": alg["tokens"] / (t / 1e3),
+            "kernel_ms": {k: float(np.mean(v)) for k, v in per.items()},
+            "t_roofline_us": t_roof * 1e6, "frac": t_roof / (t / 1e3),
+            "bytes": alg["bytes"], "flops": alg["flops"]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -403,6 +625,8 @@ def main():
                     help="skip the timed ssd_backward calls reported under 'backward' and the "
                          "short-sequence forwards under 'short_sequence'")
     ap.add_argument("--cpu-seconds", type=float, default=30.0)
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other bf16 workloads reported under 'workloads'")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 output under DIR and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -418,6 +642,8 @@ def main():
         print(f"bench.py: libssd runs the SSD forward on one GPU; --gpus {args.gpus} "
               f"(WORLD_SIZE {world}) is not supported. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    host = host_metadata()  # before anything touches the GPU
 
     import numpy as np
     import torch
@@ -512,20 +738,30 @@ def main():
             per_kernel.setdefault(name, []).append(ms)
     kernel_ms = {k: float(np.mean(v)) for k, v in per_kernel.items()}
     ms_per_step = float(np.mean(step_ms))
+    ms_median = float(np.median(step_ms))
     alg = algorithmic(shape, d["initial_state"] is not None)
     tokens = alg["tokens"]
     value = tokens / (ms_per_step / 1e3)
-
+    t_roof = max(alg["bytes"] / (HBM_PEAK_GBS * 1e9),
+                 alg["flops"] / ((MFMA_F16_PEAK_TFLOPS if shape.io == "bf16"
+                                  else FP32_PEAK_TFLOPS) * 1e12))
+    fwd_kernels = list(kernel_ms)  # the timer's names, as the traffic record keys them
+    # The whole forward against the HBM roofline: its algorithmic bytes (inputs read once, y and
+    # the final state written once) over the measured time of a forward.
+    fwd_gbs = alg["bytes"] / (ms_per_step / 1e3) / 1e9
+    roofline = {
+        "bound": "hbm", "achieved": fwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": fwd_gbs / HBM_PEAK_GBS,
+        "traffic": measured_traffic(shape.name, fwd_kernels),
+        "scope": "whole forward (" + " + ".join(kernel_ms) + ")",
+        "bytes": alg["bytes"], "ms": ms_per_step,
+    }
     dominant = max(kernel_ms, key=kernel_ms.get)
     # Algorithmic bytes of the dominant kernel: the fused scan (or the unfused chunk scan) streams
     # every input token's x, B, C, dt and writes y -- the per-token stream figure times the
     # tokens of one launch. Other kernels are charged the same figure only if they dominate.
     kb = alg["stream_bytes_per_token"] * tokens
     achieved = kb / (kernel_ms[dominant] / 1e3) / 1e9
-    traffic = measured_traffic(dominant, shape.name, kb)
-    t_roof = max(alg["bytes"] / (HBM_PEAK_GBS * 1e9),
-                 alg["flops"] / ((MFMA_F16_PEAK_TFLOPS if shape.io == "bf16"
-                                  else FP32_PEAK_TFLOPS) * 1e12))
     out = {
         "metric": METRIC,
         "value": value,
@@ -546,29 +782,43 @@ def main():
             "variant": args.variant, "precision": args.precision,
             "cache_flush": flush is not None,
         },
-        "roofline": {
+        "roofline": roofline,
+        "dominant_kernel_roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,
-            "kernel_ms": kernel_ms[dominant],
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": measured_traffic(shape.name, [dominant]),
+            "kernel": dominant, "kernel_ms": kernel_ms[dominant], "bytes": kb,
         },
         "forward_roofline": {
             "bytes": alg["bytes"], "flops": alg["flops"], "t_roofline_us": t_roof * 1e6,
             "frac": t_roof / (ms_per_step / 1e3),
-            "gbs": alg["bytes"] / (ms_per_step / 1e3) / 1e9,
+            "frac_median": t_roof / (ms_median / 1e3),
+            "gbs": fwd_gbs,
             "tflops": alg["flops"] / (ms_per_step / 1e3) / 1e12,
         },
+        "ms_per_step_median": ms_median,
+        "value_median": tokens / (ms_median / 1e3),
         "kernel_ms": kernel_ms,
         "step_ms_min": float(np.min(step_ms)),
         "ms_per_step_with_kernel_events": float(np.mean(inst_ms)),
         "wall_s_timed_loop": wall,
         "cpu_baseline": cpu,
         "parity": parity,
+        "run": run_metadata(dev, host),
         "decode_step": decode_bench(shape, dev),
         "backward": None if args.no_backward else backward_bench(
             shape, d, flush, flush_out if flush is not None else None),
         "short_sequence": None if args.no_backward else short_sequence_bench(
             dev, flush, flush_out if flush is not None else None),
     }
+    if not args.no_workloads:
+        del d, y, fin
+        torch.cuda.empty_cache()
+        out["workloads"] = {
+            synth.CONFIGS[i].name: workload_bench(i, dev, flush,
+                                                  flush_out if flush is not None else None)
+            for i in range(1, len(synth.CONFIGS))
+            if i != args.config and synth.CONFIGS[i].io == "bf16"}
     print(json.dumps(out), flush=True)
 
 

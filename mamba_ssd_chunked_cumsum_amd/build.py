@@ -76,7 +76,33 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    write_build_info(cc)
     return LIB
+
+
+BUILD_INFO = os.path.join(LIBDIR, "build_info.json")
+
+
+def write_build_info(cc: str) -> None:
+    """Record what the library was built from (it travels with the library to hosts without the
+    git history): the git revision and whether the tree differed from it, and the compiler."""
+    import json
+
+    def run(args):
+        try:
+            return subprocess.run(args, cwd=ROOT, capture_output=True, text=True,
+                                  timeout=30).stdout.strip()
+        except (OSError, subprocess.SubprocessError):
+            return ""
+
+    info = {
+        "git_rev": run(["git", "rev-parse", "HEAD"]) or None,
+        "git_dirty": bool(run(["git", "status", "--porcelain", "--untracked-files=no"])),
+        "hipcc": (run([cc, "--version"]).splitlines() or [""])[0],
+        "arch": ARCH,
+    }
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f, indent=1)
 
 
 if __name__ == "__main__":
