@@ -138,6 +138,28 @@ def _problem_from(x, B) -> SSDProblem:
     return problem(Bt, L, H, P, B.shape[3], B.shape[2], DTYPES[x.dtype])
 
 
+def _check_shapes(named) -> None:
+    """named: (name, tensor or None, expected shape). The C ABI sees only pointers, so a tensor of
+    the wrong shape would be read or written out of bounds: every shape is checked here, before
+    anything is launched."""
+    for name, t, shp in named:
+        if t is not None and tuple(t.shape) != tuple(shp):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shp)}")
+
+
+def _sequence_shapes(x, B, C, dt, A, D, initial_state):
+    """The forward's and backward's shared inputs against x [Bt, L, H, P] and B [Bt, L, G, N]."""
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [batch, seqlen, nheads, headdim], B/C [batch, seqlen, "
+                         "ngroups, dstate]")
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _check_shapes((("B", B, (Bt, L, G, N)), ("C", C, (Bt, L, G, N)), ("dt", dt, (Bt, L, H)),
+                   ("A", A, (H,)), ("D", D, (H,)), ("initial_state", initial_state,
+                                                    (Bt, H, P, N))))
+    return Bt, L, H, P, G, N
+
+
 def _require(t, name, dtype=None, device=None):
     if t is None:
         return
@@ -199,6 +221,9 @@ def forward(x, dt, A, B, C, D, chunk_size, initial_state=None, *, variant="auto"
     dt + dt_bias, softplus, clamp to [lo, hi] (hi > 0), in that order. noalloc: call
     ssd_forward_noalloc (workspace from the library's static scratch; give out and final_out to
     keep torch from allocating too)."""
+    Bt, L, H, P, G, N = _sequence_shapes(x, B, C, dt, A, D, initial_state)
+    _check_shapes((("dt_bias", dt_bias, (H,)), ("out", out, x.shape),
+                   ("final_out", final_out if want_final else None, (Bt, H, P, N))))
     dev = x.device
     _require(x, "x", device=dev)
     for n, t in (("B", B), ("C", C)):
@@ -206,8 +231,6 @@ def forward(x, dt, A, B, C, D, chunk_size, initial_state=None, *, variant="auto"
     for n, t in (("dt", dt), ("A", A), ("D", D), ("initial_state", initial_state),
                  ("dt_bias", dt_bias)):
         _require(t, n, torch.float32, dev)
-    if dt_bias is not None and tuple(dt_bias.shape) != (x.shape[2],):
-        raise ValueError(f"dt_bias must have shape ({x.shape[2]},)")
     prob = _problem_from(x, B)
     y = out if out is not None else torch.empty_like(x)
     _require(y, "out", x.dtype, dev)
@@ -264,6 +287,8 @@ def backward(x, dt, A, B, C, D, dy, chunk_size, initial_state=None, dfinal=None,
     """Gradients of the forward for output gradient dy (x's dtype and shape) and final-state
     gradient dfinal ([Bt, H, P, N] f32, or None for zero). Returns a dict of float32 tensors:
     dx, ddt, dA, dB, dC, dD and dinitial_state (None unless want_initial_grad)."""
+    Bt, L, H, P, G, N = _sequence_shapes(x, B, C, dt, A, D, initial_state)
+    _check_shapes((("dy", dy, x.shape), ("dfinal", dfinal, (Bt, H, P, N))))
     dev = x.device
     _require(x, "x", device=dev)
     for n, t in (("B", B), ("C", C), ("dy", dy)):
@@ -271,11 +296,7 @@ def backward(x, dt, A, B, C, D, dy, chunk_size, initial_state=None, dfinal=None,
     for n, t in (("dt", dt), ("A", A), ("D", D), ("initial_state", initial_state),
                  ("dfinal", dfinal)):
         _require(t, n, torch.float32, dev)
-    if tuple(dy.shape) != tuple(x.shape):
-        raise ValueError(f"dy has shape {tuple(dy.shape)}, expected {tuple(x.shape)}")
     prob = _problem_from(x, B)
-    Bt, L, H, P = x.shape
-    G, N = B.shape[2], B.shape[3]
     f32 = dict(dtype=torch.float32, device=dev)
     out = dict(dx=torch.empty((Bt, L, H, P), **f32), ddt=torch.empty((Bt, L, H), **f32),
                dA=torch.empty((H,), **f32), dB=torch.empty((Bt, L, G, N), **f32),

@@ -3,13 +3,19 @@
 The GPU backward computes in fp32 throughout (its four chunked recurrences run the fp32 matrix
 cores; the inputs are exact in fp32, also for bf16 io), so each gradient is held to
 max |g - r| <= TOL * max|r| over the tensor: fp32 rounding (2^-24 per operation) accumulated over
-a few hundred terms of mixed sign leaves a few 1e-6; TOL = 1e-4 keeps a margin. dA is a sum over
-batch and time of dt_t dlog_t whose terms largely cancel (at L = 8192 their absolute sum is ~10^3
-times the result), so it is held to TOL times the absolute sum of its terms, the scale a
-floating-point sum's error is bounded by. At the full 8192-token sequence the decay gradients (ddt
-and dA) sum fp32 terms, each with the rounding of the recurrences that produced it, over
-thousands of tokens: they are held to TOL_LONG = 1e-3 there (still well inside the 2^-8 relative
-precision of the bf16 training these gradients serve).
+a few hundred terms of mixed sign leaves a few 1e-6; TOL = 1e-4 keeps a margin.
+
+dA is held per head: dA_h = sum over batch and time of dt_t dlog_t, terms that largely cancel, so
+its error is bounded by the per-term error times the absolute sum of the terms of that head,
+|g - r| <= TOL * sum_t |dt_t dlog_t| (the scale a floating-point sum's error is bounded by); the
+test prints each head's error relative to its own |dA| and to that sum. The relative error of dA
+itself is then about the per-term error times the head's condition number
+kappa_h = sum_t |dt_t dlog_t| / |dA_h|: heads whose dA cancels to a small fraction of its terms
+show large relative errors (at the full 8192-token sequence kappa reaches ~500, and fp32
+recurrence outputs carry per-term errors of a few 1e-4, which gives relative errors of ~10% on
+such heads) while their absolute error stays within the bound. At the full sequence the decay
+gradients (ddt and dA) sum fp32 terms, each with the rounding of the recurrences that produced
+it, over thousands of tokens: they are held to TOL_LONG = 1e-3 there.
 """
 
 import numpy as np
@@ -74,6 +80,19 @@ def _dev(a, io, io_tensor):
     return t.to(torch.bfloat16) if (io_tensor and io == "bf16") else t
 
 
+def _check_dA(got, ref, terms, tol, label):
+    """dA per head against its own scale: |g - r| <= tol * sum_t |dt dlog| of that head (the
+    absolute sum of the terms the head's dA sums, which bounds a floating-point sum's error).
+    Prints each head's error relative to its own |dA| and to that sum."""
+    err = np.abs(got - ref)
+    for h in range(len(ref)):
+        print(f"{label} dA head {h}: {ref[h]:+.5e}, |g - r| {err[h]:.2e}, relative "
+              f"{err[h] / max(abs(ref[h]), 1e-30):.2e}, sum|terms| {terms[h]:.3e}, "
+              f"|g - r| / sum|terms| {err[h] / max(terms[h], 1e-30):.2e} (bar {tol})")
+    assert np.all(err <= tol * np.maximum(terms, 1e-30)), (err, terms)
+    return err
+
+
 @pytest.mark.parametrize("case", CASES, ids=_case_id)
 def test_backward_matches_oracle(case):
     Bt, L, H, P, N, G, Q, io, h0, df = case
@@ -88,12 +107,13 @@ def test_backward_matches_oracle(case):
     dlog = ref.pop("dlog_decay")
     for k, r in ref.items():
         gk = g[k].cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(gk)), k
+        if k == "dA":
+            _check_dA(gk, r, np.sum(np.abs(inp["dt"] * dlog), axis=(0, 1)), TOL, _case_id(case))
+            continue
         err = float(np.max(np.abs(gk - r)))
         scale = float(np.max(np.abs(r)))
-        if k == "dA":
-            scale = max(scale, float(np.max(np.sum(np.abs(inp["dt"] * dlog), axis=(0, 1)))))
         print(f"{k}: max|g - r| = {err:.3e}, max|r| = {scale:.3e}, ratio {err / max(scale, 1e-30):.2e}")
-        assert np.all(np.isfinite(gk)), k
         assert err <= TOL * max(scale, 1e-30), f"{k}: {err:.3e} > {TOL} * {scale:.3e}"
 
 
@@ -151,10 +171,12 @@ def test_backward_full_size_sampled_heads():
                      dA=(got["dA"][h:h + 1], ref["dA"]), dD=(got["dD"][h:h + 1], ref["dD"]),
                      dinitial_state=(got["dinitial_state"][:, h:h + 1], ref["dinitial_state"]))
         for k, (gk, r) in pairs.items():
-            err = float(np.max(np.abs(gk - r)))
-            scale = float(np.max(np.abs(r))) if k != "dA" else max(float(np.max(np.abs(r))),
-                                                                      dA_scale)
             tol = TOL_LONG if k in ("ddt", "dA") else TOL
+            if k == "dA":
+                _check_dA(gk, r, np.array([dA_scale]), tol, f"full size, head {h}")
+                continue
+            err = float(np.max(np.abs(gk - r)))
+            scale = float(np.max(np.abs(r)))
             print(f"head {h} {k}: max|g - r| = {err:.3e}, scale = {scale:.3e}, "
                   f"ratio {err / max(scale, 1e-30):.2e} (bar {tol})")
             assert err <= tol * max(scale, 1e-30), f"head {h} {k}: {err:.3e} vs {scale:.3e}"
