@@ -211,19 +211,52 @@ class KernelTimer:
                 for k in range(len(names))}
 
 
+FP16_MAX = 65504.0
+
+
+def check_domain(x, dt, A, B, C, *, fp16_operands=True, dt_processed=False):
+    """Raise ValueError unless the inputs lie in the domain the kernels assume: A <= 0 and dt >= 0
+    (every decay at most 1; dt is not checked when the kernels pre-process it), no NaN or
+    infinity, and, with bf16 io at a precision with fp16 matrix-core operands, |x|, |B|, |C|
+    below fp16's largest finite value 65504. One reduction per tensor and a host
+    synchronisation: a check for callers that want it, not done by forward() unless asked."""
+    def bad(name, cond):
+        if bool(cond):
+            raise ValueError(f"{name} is outside the kernels' domain")
+    bad("A (positive or not finite)", ~torch.all(torch.isfinite(A) & (A <= 0)))
+    if not dt_processed:
+        bad("dt (negative or not finite)", ~torch.all(torch.isfinite(dt) & (dt >= 0)))
+    for name, t in (("x", x), ("B", B), ("C", C)):
+        bad(f"{name} (not finite)", ~torch.all(torch.isfinite(t)))
+        if fp16_operands and t.dtype == torch.bfloat16:
+            bad(f"{name} (beyond fp16's range, 65504)", torch.amax(torch.abs(t)) >= FP16_MAX)
+
+
 def forward(x, dt, A, B, C, D, chunk_size, initial_state=None, *, variant="auto",
             precision="auto", run_chunks=0, want_final=True, out=None, final_out=None,
             timer: KernelTimer | None = None, dt_bias=None, dt_softplus=False, dt_limit=None,
-            noalloc=False):
+            noalloc=False, check=False):
     """SSD chunked forward. Returns (y, final_state) (final_state None if not wanted).
 
     dt_bias [H], dt_softplus and dt_limit=(lo, hi) pre-process dt inside the kernels:
     dt + dt_bias, softplus, clamp to [lo, hi] (hi > 0), in that order. noalloc: call
     ssd_forward_noalloc (workspace from the library's static scratch; give out and final_out to
-    keep torch from allocating too)."""
+    keep torch from allocating too). check: run check_domain() on the inputs first.
+
+    Outside the domain (no check): a NaN or infinity in a head's inputs reaches that head's
+    outputs from the sub-chunk (fused: 32 tokens) or chunk (unfused) that holds it onwards and its
+    final state (in B or C: every head of the group), leaving the other heads and the earlier
+    tokens as they are; a bf16 x, B or C of magnitude 65504 or more is infinite in the fused
+    path's fp16 operands: the affected heads' outputs from its sub-chunk onwards are undefined
+    (so are the unfused kernels' at the default precision; the fp32 precision option has no such
+    limit); A > 0 or dt < 0 (decays above 1) give results the
+    kernels do not define."""
     Bt, L, H, P, G, N = _sequence_shapes(x, B, C, dt, A, D, initial_state)
     _check_shapes((("dt_bias", dt_bias, (H,)), ("out", out, x.shape),
                    ("final_out", final_out if want_final else None, (Bt, H, P, N))))
+    if check:
+        check_domain(x, dt, A, B, C, fp16_operands=precision != "fp32",
+                     dt_processed=dt_bias is not None or dt_softplus or dt_limit is not None)
     dev = x.device
     _require(x, "x", device=dev)
     for n, t in (("B", B), ("C", C)):
