@@ -102,8 +102,10 @@ typedef enum {
 typedef enum {
     SSD_PRECISION_AUTO = 0, /* bf16 io: fp16 operands, with the chunk-state operand split hi + lo
                                where a state is kept in fp32 (the unfused chunk states; the fused
-                               run state of a one-run sequence, which is its final state); the
-                               fused path hands run states to its chain in fp16. fp32 io: fp32 */
+                               path's last run state, which goes into the final state: over the
+                               run's last 128 tokens, or the whole run at one run per sequence);
+                               the fused path hands the other run states to its chain in fp16.
+                               fp32 io: fp32 */
     SSD_PRECISION_FP16 = 1, /* bf16 io: every fp32-carrying operand rounded once to fp16 */
     SSD_PRECISION_FP32 = 3  /* fp32 matrix-core instructions for every contraction */
 } ssd_precision;

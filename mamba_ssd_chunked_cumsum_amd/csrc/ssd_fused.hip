@@ -191,6 +191,7 @@ struct Fz {
   static constexpr int WA_BYTES = NW * NWA * T * 4;   // acs2, dt, w, cf, rdiag (phase A: per wave)
   static constexpr int WA_SCAN = HPB * NWA * T * 4;   // phase B: per head
   static constexpr int NSCAN = 2, NRUN = 3;           // stages
+  static constexpr int NSPLIT = 128 / T;              // phase A: split sub-chunks (final state)
   // phase B at one wave per head: the sub-chunk's C B^T blocks, fp32, computed once for the block's
   // heads (they share one B/C group)
   static constexpr bool SHARED_CB = WPH == 1 && NMB <= NW;
@@ -493,13 +494,23 @@ __device__ __forceinline__ f16x8 b_frag(const char* Bh, int js, int col0, int la
 // ---- phase A: run states ------------------------------------------------------------------------
 // state_r = sum_{t in run} exp(sum_{k in (t, end]} dt_k A) dt_t x_t B_t^T (zero entry state) and
 // logdecay_r = sum_{t in run} dt_t A. Walked backwards: per sub-chunk, S += B^T (w x) with the
-// weights anchored at the run end, the weighted x split into fp16 high and low parts. Leaves the
-// state in S (lane: p = p0 + 16 pt + c16, n = 16 nt + 4 g + 0..3) and returns the log-decay.
-template <class K, bool SPLIT>
+// weights anchored at the run end. The weighted x of the first `nsplit` sub-chunks walked (the
+// last tokens of the run) is split into fp16 high and low parts (two passes), the rest rounded
+// once: a token's rounding error scales with its weight, and the weights are largest at the run
+// end (dt itself there; a single such term can dominate an entry of the state), while earlier
+// tokens carry decayed weights or, in slowly decaying heads, many comparable terms whose
+// independent roundings average out. Leaves the state in S (lane: p = p0 + 16 pt + c16,
+// n = 16 nt + 4 g + 0..3) and returns the log-decay.
+template <bool V>
+struct Flag {
+  static constexpr bool value = V;
+};
+
+template <class K>
 __device__ __forceinline__ float run_state(char* smem, const Coord& c, const u16* __restrict__ x,
                                            const u16* __restrict__ Bm,
                                            const float* __restrict__ dt, float a_h, float dtb,
-                                           const Dims& d, int s_begin, int s_end,
+                                           const Dims& d, int s_begin, int s_end, int nsplit,
                                            f32x4 (&S)[K::NNT][K::NPT]) {
   using M = Mma<f16>;
   DmaLanes<K, false> dl;
@@ -524,7 +535,8 @@ __device__ __forceinline__ float run_state(char* smem, const Coord& c, const u16
   constexpr int NLO = K::RUN_NI / K::NW + 1;
   const bool hi = c.wave < K::RUN_NI % K::NW;
 
-  for (int s = s_end - 1; s >= s_begin; --s) {
+  auto body = [&](int s, auto split_c) {
+    constexpr bool SPL = decltype(split_c)::value;
     dl.pin();
     const int cur = (s_end - 1 - s) % K::NRUN;
     char* st = smem + cur * K::RUN_STAGE;
@@ -559,7 +571,7 @@ __device__ __forceinline__ float run_state(char* smem, const Coord& c, const u16
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= wj[e];
         xhi[pt] = cvt_f16x8(v);
-        if constexpr (SPLIT) {
+        if constexpr (SPL) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) lo[e] = v[e] - (float)xhi[pt][e];
           xlo[pt] = cvt_f16x8(lo);
@@ -571,11 +583,14 @@ __device__ __forceinline__ float run_state(char* smem, const Coord& c, const u16
 #pragma unroll
         for (int pt = 0; pt < K::NPT; ++pt) {
           S[nt][pt] = M::mma(bt, xhi[pt], S[nt][pt]);
-          if constexpr (SPLIT) S[nt][pt] = M::mma(bt, xlo[pt], S[nt][pt]);
+          if constexpr (SPL) S[nt][pt] = M::mma(bt, xlo[pt], S[nt][pt]);
         }
       }
     }
-  }
+  };
+  int s = s_end - 1;
+  for (const int s_lo = max(s_begin, s_end - nsplit); s >= s_lo; --s) body(s, Flag<true>{});
+  for (; s >= s_begin; --s) body(s, Flag<false>{});
   return rem;
 }
 
@@ -1087,14 +1102,14 @@ __device__ __forceinline__ void fused_scan(char* smem, Coord c, const u16* __res
 // ---- chain between runs -------------------------------------------------------------------------
 // One thread per 8 consecutive entries of one (batch, head) state: walk the runs,
 // h <- exp(logdecay_q) h + state_q starting from h0 (or 0), in fp32, writing the state entering
-// run q + 1 over slot q (fp16); after the last run (when a final state is wanted) h is the final
-// state. Only the multiply-adds depend on the run before: the loads of GS runs are issued
-// together.
+// run q + 1 over slot q (fp16). When a final state is wanted, the last run's state is already in
+// it (fp32, from phase A): final = exp(logdecay_last) h + that. Only the multiply-adds depend on
+// the run before: the loads of GS runs are issued together.
 struct ChainArgs {
-  u16* states;              // [Bt, nr, H, P, N] fp16
+  u16* states;              // [Bt, nr - 1, H, P, N] fp16
   const float* logdecay;    // [Bt, H, nr]
   const float* h0;          // [Bt, H, P, N] or null
-  float* fin;               // [Bt, H, P, N] or null
+  float* fin;               // [Bt, H, P, N] or null; holds the last run's state on entry
   int64_t pieces;           // Bt * H * P * N / 8
   int PN8, H, nr;
 };
@@ -1124,7 +1139,7 @@ __global__ __launch_bounds__(256) void k_state_chain(ChainArgs a) {
   const int64_t b = bh / a.H, h = bh % a.H;
   const int64_t PN = (int64_t)a.PN8 * 8;
   const int64_t slot = (int64_t)a.H * PN;  // elements between runs' slots
-  u16* sp = a.states + (b * a.nr * a.H + h) * PN + e;
+  u16* sp = a.states + (b * (a.nr - 1) * a.H + h) * PN + e;
   const float* ld = a.logdecay + bh * a.nr;
   float acc[8];
   if (a.h0) {
@@ -1136,7 +1151,7 @@ __global__ __launch_bounds__(256) void k_state_chain(ChainArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] = 0.f;
   }
-  const int nsteps = a.fin ? a.nr : a.nr - 1;
+  const int nsteps = a.nr - 1;
   for (int q0 = 0; q0 < nsteps; q0 += GS) {
     uint4 st[GS];
     float dec[GS];
@@ -1153,14 +1168,16 @@ __global__ __launch_bounds__(256) void k_state_chain(ChainArgs a) {
         unpack8(st[u], f);
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[k] = dec[u] * acc[k] + f[k];
-        if (q0 + u < a.nr - 1) *reinterpret_cast<uint4*>(sp + (q0 + u) * slot) = pack8(acc);
+        *reinterpret_cast<uint4*>(sp + (q0 + u) * slot) = pack8(acc);
       }
     }
   }
   if (a.fin) {
-    *reinterpret_cast<float4*>(a.fin + bh * PN + e) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    *reinterpret_cast<float4*>(a.fin + bh * PN + e + 4) =
-        make_float4(acc[4], acc[5], acc[6], acc[7]);
+    const float dl = __expf(ld[a.nr - 1]);
+    float4* fo = reinterpret_cast<float4*>(a.fin + bh * PN + e);
+    const float4 u = fo[0], v = fo[1];
+    fo[0] = make_float4(dl * acc[0] + u.x, dl * acc[1] + u.y, dl * acc[2] + u.z, dl * acc[3] + u.w);
+    fo[1] = make_float4(dl * acc[4] + v.x, dl * acc[5] + v.y, dl * acc[6] + v.z, dl * acc[7] + v.w);
   }
 }
 
@@ -1170,11 +1187,13 @@ struct FwdArgs {
   const float *dt, *A, *D, *h0;
   u16* y;
   float* fin;       // final state [Bt, H, P, N]; null: not written
-  u16* states;      // [Bt, nr, H, P, N] fp16: run states, then the state entering the next run
+  u16* states;      // [Bt, nr - 1, H, P, N] fp16: run states (all runs but the last), then the
+                    // state entering the next run
   float* logdecay;  // [Bt, H, nr]
   Dims d;
   int run_len, nr, hb;  // run length (tokens), runs per sequence, head blocks per batch entry
   int na;               // runs per sequence whose state phase A computes
+  int nsplit, nsplit_last;  // phase A sub-chunks with split operands, per run / in the last run
 };
 
 // A block's (batch, head block, run) and sub-chunk range from its item index: chains (batch,
@@ -1196,9 +1215,11 @@ __device__ __forceinline__ Item item_of(const FwdArgs& a, int item, int nper) {
 }
 
 // Phase A, one block per (chain, run) whose state is needed: the runs before the last (for the
-// chain) and, when a final state is wanted, the last one too. With one run per sequence the state
-// is completed into the final state here: S + exp(sum of dt A) h0.
-template <class K, bool SPLIT>
+// chain, stored fp16) and, when a final state is wanted, the last one too, stored fp32 into the
+// final state (the chain adds the decayed entry state to it). With one run per sequence the state
+// is completed into the final state here: S + exp(sum of dt A) h0. a.nsplit_last sub-chunks at the
+// end of the last run, and a.nsplit of every other, take the split operands.
+template <class K>
 __global__ __launch_bounds__(K::NT, 1) void k_run_states(FwdArgs a) {
   static_assert(K::RUN_LDS <= 160 * 1024, "LDS budget");
   __shared__ __align__(1024) char smem[K::RUN_LDS];
@@ -1207,14 +1228,17 @@ __global__ __launch_bounds__(K::NT, 1) void k_run_states(FwdArgs a) {
   const Coord c = coords<K>(d, it.r, it.chain % a.hb, it.b);
   const int64_t PN = (int64_t)K::P * K::N;
   f32x4 S[K::NNT][K::NPT];
-  const float ld = run_state<K, SPLIT>(smem, c, a.x, a.B, a.dt, a.A[c.h], dt_bias_of(d, c.h), d,
-                                       it.s_begin, it.s_end, S);
+  const bool last = it.r == a.nr - 1;
+  const float ld = run_state<K>(smem, c, a.x, a.B, a.dt, a.A[c.h], dt_bias_of(d, c.h), d,
+                                it.s_begin, it.s_end, last ? a.nsplit_last : a.nsplit, S);
   if (!c.active) return;
-  if (a.nr == 1) {
+  if (last) {  // only launched when a final state is wanted
     const int64_t o = ((int64_t)it.b * d.H + c.h) * PN;
-    store_state<K>(S, c, a.fin + o, a.h0 ? a.h0 + o : nullptr, __expf(ld));
+    store_state<K>(S, c, a.fin + o, a.nr == 1 && a.h0 ? a.h0 + o : nullptr, __expf(ld));
+    if (a.nr > 1 && c.lane == 0 && c.p0 == 0)
+      a.logdecay[((int64_t)it.b * d.H + c.h) * a.nr + it.r] = ld;
   } else {
-    store_state_h<K>(S, c, a.states + (((int64_t)it.b * a.nr + it.r) * d.H + c.h) * PN);
+    store_state_h<K>(S, c, a.states + (((int64_t)it.b * (a.nr - 1) + it.r) * d.H + c.h) * PN);
     if (c.lane == 0 && c.p0 == 0) a.logdecay[((int64_t)it.b * d.H + c.h) * a.nr + it.r] = ld;
   }
 }
@@ -1230,7 +1254,7 @@ __global__ __launch_bounds__(K::NT, 1) void k_fused_scan(FwdArgs a) {
   const int64_t PN = (int64_t)K::P * K::N;
   const float* h0 = it.r == 0 && a.h0 ? a.h0 + ((int64_t)it.b * d.H + c.h) * PN : nullptr;
   const u16* hin =
-      it.r > 0 ? a.states + (((int64_t)it.b * a.nr + (it.r - 1)) * d.H + c.h) * PN : nullptr;
+      it.r > 0 ? a.states + (((int64_t)it.b * (a.nr - 1) + (it.r - 1)) * d.H + c.h) * PN : nullptr;
   fused_scan<K>(smem, c, a.x, a.B, a.C, a.dt, a.A, a.D, h0, hin, a.y, d, it.s_begin, it.s_end);
 }
 
@@ -1289,7 +1313,7 @@ bool fused_plan(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp) {
 
 int64_t fused_workspace_bytes(const Dims& d, const FusedPlan& fp) {
   if (fp.nr <= 1) return 0;
-  const int64_t st = (int64_t)d.Bt * fp.nr * d.H * d.P * d.N * 2;
+  const int64_t st = (int64_t)d.Bt * (fp.nr - 1) * d.H * d.P * d.N * 2;
   const int64_t ld = (int64_t)d.Bt * d.H * fp.nr * 4;
   return ((st + 255) & ~int64_t(255)) + ld;
 }
@@ -1314,21 +1338,20 @@ static hipError_t launch_k(const Dims& d, const FusedPlan& fp, const void* x, co
   a.nr = fp.nr;
   a.hb = fp.head_blocks;
   a.na = fin ? fp.nr : fp.nr - 1;  // phase A: every run but the last, unless a final state
+  // split operands: where the run state is kept in fp32 (the final state), over the whole run at
+  // one run per sequence, else over its last K::NSPLIT sub-chunks; states handed on in fp16 are
+  // rounded anyway
+  a.nsplit = 0;
+  a.nsplit_last = !fp.split ? 0 : fp.nr == 1 ? fp.run_len / K::T : K::NSPLIT;
   if (fp.nr > 1) {
-    const int64_t st = (int64_t)d.Bt * fp.nr * d.H * d.P * d.N * 2;
+    const int64_t st = (int64_t)d.Bt * (fp.nr - 1) * d.H * d.P * d.N * 2;
     a.states = static_cast<u16*>(ws);
     a.logdecay = reinterpret_cast<float*>(static_cast<char*>(ws) + ((st + 255) & ~int64_t(255)));
   }
   const int chains = d.Bt * fp.head_blocks;
   hipError_t e = tm ? tm->mark(s) : hipSuccess;
   if (e == hipSuccess && a.na > 0) {
-    const dim3 grid(chains * a.na);
-    // the split pays only where the run state is the final state itself (one run per sequence):
-    // a state handed to the chain is rounded to fp16 anyway
-    if (fp.split && fp.nr == 1)
-      hipLaunchKernelGGL((k_run_states<K, true>), grid, dim3(K::NT), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_run_states<K, false>), grid, dim3(K::NT), 0, s, a);
+    hipLaunchKernelGGL((k_run_states<K>), dim3(chains * a.na), dim3(K::NT), 0, s, a);
     e = hipGetLastError();
     if (e == hipSuccess && tm) e = tm->mark(s);
   }

@@ -44,8 +44,9 @@ hipError_t launch_chunk_scan(const Dims& d, int io, int prec, const void* x, con
 // fused path (bf16 io)
 // Run plan of one fused forward: runs of run_len tokens (a multiple of 64), nr runs per sequence,
 // head_blocks blocks per (batch, run).
-// split: phase A feeds the weighted x to the matrix cores as fp16 high + low parts (else high
-// only).
+// split: where phase A keeps a run state in fp32 (the final state), it feeds the weighted x of the
+// run's last 128 tokens (of the whole run at one run per sequence) to the matrix cores as fp16
+// high + low parts; false: high parts only everywhere.
 struct FusedPlan {
   int run_len, nr, head_blocks;
   bool split = true;
@@ -64,8 +65,8 @@ using FusedTimer = KernelMarks;
 // many tokens (rounded up to 64); 0 lets the plan aim at about one block per compute unit (n_cu of
 // them).
 bool fused_plan(const Dims& d, int run_tokens, int n_cu, FusedPlan* fp);
-// Workspace bytes of a plan (0 for one run per sequence): run states [Bt, nr, H, P, N] f32 (256-byte
-// aligned), then run log-decays [Bt, H, nr] f32.
+// Workspace bytes of a plan (0 for one run per sequence): the states of every run but the last,
+// [Bt, nr - 1, H, P, N] fp16 (padded to 256 bytes), then run log-decays [Bt, H, nr] f32.
 int64_t fused_workspace_bytes(const Dims& d, const FusedPlan& fp);
 // The whole fused forward, up to three kernels: run states (skipped with one run per sequence and
 // no final state), the chain over runs (nr > 1) and the fused scan. h0 and fin nullable;

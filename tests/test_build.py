@@ -59,8 +59,8 @@ def test_fused_kernels_use_no_scratch():
     kernels = _kernel_descriptors()
     fused = {k: v for k, v in kernels.items()
              if any(n in k for n in ("k_run_states", "k_state_chain", "k_fused_scan"))}
-    # 6 (headdim, dstate) shapes: run states (split or not) and the fused scan; one chain kernel
-    assert len(fused) == 19, sorted(kernels)
+    # 6 (headdim, dstate) shapes: run states and the fused scan; one chain kernel
+    assert len(fused) == 13, sorted(kernels)
     bad = {k: v for k, v in fused.items()
            if v.get("private_segment_fixed_size", 0) or v.get("vgpr_spill_count", 0)}
     assert not bad, f"fused kernels spilling to scratch: {bad}"

@@ -3,7 +3,8 @@
 Bars: fp32 workloads max |g - r| / max(|r|, RMS(r)) <= 1e-4 for y and final_state; bf16 workloads
 y within 2e-2 of RMS beyond the half-ulp of bf16 output rounding, final_state max |g - r| / RMS
 <= 2e-2. Full-size workloads are compared on a spread sample of (batch, head) units, every token
-of each; RMS is over the sampled units.
+of each (RMS over the sampled units), and, on the fused path, the three large bf16 workloads on
+every unit.
 """
 
 import numpy as np
@@ -38,6 +39,16 @@ def test_workloads(cfg, variant):
     skip_unfusable(shape, variant)
     rep = check_shape(shape, cfg_index=cfg, variant=variant, max_units=8)
     print(cfg, variant, rep)
+    assert rep["pass"], rep
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_fused_workloads_every_unit(cfg):
+    """The fused path (auto's choice for every bf16 workload) on every (batch, head) unit of the
+    three large bf16 workloads; the float64 C oracle takes a few seconds for each."""
+    shape = synth.CONFIGS[cfg]
+    rep = check_shape(shape, cfg_index=cfg, variant="fused")
+    print(cfg, "fused, every unit", rep)
     assert rep["pass"], rep
 
 

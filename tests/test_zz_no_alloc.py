@@ -47,10 +47,11 @@ def test_two_calls_in_a_row_match_the_allocating_forward():
 
 
 def test_plan_fitted_to_the_scratch():
-    # headdim 128, dstate 256, runs of one 128-token chunk: 32 runs per sequence would need 64 MiB
-    # of fp16 run states plus the decays; the no-allocation plan doubles the run length, so the
-    # numbers differ from the allocating forward's only by rounding
-    shape = synth.SSDShape("noalloc_fitted", 1, 4096, 32, 128, 256, 1, 128, init_state=True)
+    # headdim 128, dstate 256, runs of one 128-token chunk: 32 runs per sequence, two sequences,
+    # would need 2 x 31 x 2 MiB of fp16 run states (all but the last run's) plus the decays; the
+    # no-allocation plan doubles the run length, so the numbers differ from the allocating
+    # forward's only by rounding
+    shape = synth.SSDShape("noalloc_fitted", 2, 4096, 32, 128, 256, 1, 128, init_state=True)
     note(f"noalloc fitted {shape}")
     y0, f0, _ = _run(shape, 9, noalloc=False, run_chunks=1)
     y1, f1, _ = _run(shape, 9, noalloc=True, run_chunks=1)
@@ -58,7 +59,7 @@ def test_plan_fitted_to_the_scratch():
     # both held to the parity bar against the oracle (two bf16 outputs of different plans may
     # differ by a rounding of each, which the bar's half-ulp allowance covers only once)
     inp = synth.make_inputs(shape, seed=9)
-    units = [0, 13, 31]
+    units = [0, 13, 31, 50, 63]
     y_ref, f_ref = native.forward(**inp, units=units)
     for y, f in ((y0, f0), (y1, f1)):
         rep = score(as64(y), as64(f), y_ref, f_ref, "bf16", units, shape.nheads)
