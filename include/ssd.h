@@ -26,7 +26,7 @@
  * Ownership: the caller owns every buffer; the library keeps no pointer after a call returns.
  * Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null stream):
  * device faults surface at the caller's next synchronisation. Workspace (unfused path, and the
- * run states and chain counters of the fused path) is allocated stream-ordered on `stream` and
+ * run states and run decays of the fused path) is allocated stream-ordered on `stream` and
  * released the same way.
  *
  * Errors: every argument check runs on the host before any HIP call; on failure nothing is

@@ -220,10 +220,10 @@ int compute_units() {
   return n;
 }
 
-// Fused forward: one kernel (after a reset of its chain counters when a sequence has several
-// runs). Runs are run_chunks chunks long when run_chunks > 0, else planned to give about one block
-// per compute unit (each run boundary costs one fp32 state write and read). ws: the workspace
-// (run states, decays, counters; none with one run per sequence), or null to allocate it
+// Fused forward: run states, the chain over runs (several runs per sequence) and the fused scan.
+// Runs are run_chunks chunks long when run_chunks > 0, else planned to give about one block per
+// compute unit (each run boundary costs one fp16 state write and read, twice). ws: the workspace
+// (fp16 run states and decays; none with one run per sequence), or null to allocate it
 // stream-ordered.
 ssd_status run_fused(const Dims& d, const ssd::FusedPlan& fp, const void* x, const float* dt,
                      const float* A, const void* B, const void* C, const float* D,
@@ -283,8 +283,8 @@ ssd_status forward_impl(const ssd_problem* prob, const void* x, const float* dt,
                        ssd::fused_plan(d, (int)(run_tokens < (1 << 30) ? run_tokens : (1 << 30)),
                                        compute_units(), &fp);
   if (variant == SSD_VARIANT_FUSED && !fusable) return SSD_ERR_UNSUPPORTED;
-  // auto: the run states chained over the sequence keep near-fp32 accuracy (hi + lo); fp16:
-  // every operand rounded once
+  // auto: the last run's state, which goes into the final state, takes the hi + lo split over
+  // the sequence's last 128 tokens; fp16: every operand rounded once
   fp.split = prec != ssd::kPrecFp16;
   Timer t;
   if (opts && opts->n_events > 0) {

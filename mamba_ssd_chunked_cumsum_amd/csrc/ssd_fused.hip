@@ -1,44 +1,44 @@
-// Fused SSD chunked forward (bf16 io): one kernel for the whole forward.
+// Fused SSD chunked forward (bf16 io): three kernels for the whole forward.
 //
 // The chunked algorithm ("nitter.gq/da_be19" thread, post 5/6; stage order as in "Mamba-2 in
 // NVIDIA cuTile: Faster Forward Kernels and What the Benchmark Means", section "Why Mamba-2 is a
 // useful kernel example") needs the state entering every chunk. A (batch, head)'s fp32 state
 // (P x N) is as large as its bf16 x tile of 256 tokens, so materialising one per chunk would
 // double the HBM traffic. Here each sequence is cut into a few runs of consecutive tokens (about
-// one block per compute unit in total), and one block per (batch, head block, run) does, in one
-// launch:
+// one block per compute unit in total; a chain is the runs of one batch entry and head block):
 //
-//   phase A   its run's own end state (zero entry state) and total log-decay, kept in registers
-//             and published to a workspace slot;
-//   chain     once every run of its chain (batch, head block) has published, the block walks the
-//             runs for 1 / nr of the chain's state entries, h_in(r+1) = exp(logdecay_r) h_in(r)
-//             + state_r, overwriting each run's slot with the state entering the next run, and
-//             writes the final state;
-//   phase B   once every part of the chain is written, its run sub-chunk by sub-chunk:
-//             cumulative decay, C B^T, the masked intra-sub-chunk product, the readout of the
-//             carried state, the skip term and the state update, all on chip; only y leaves.
+//   k_run_states  one block per (chain, run) whose state is needed: the run's own end state
+//                 (zero entry state) and total log-decay. States handed to the chain are stored
+//                 in fp16; the last run's state, computed only when a final state is wanted, is
+//                 stored in fp32 straight into the final state.
+//   k_state_chain one thread per 8 entries of a (batch, head) state walks its runs in fp32,
+//                 h_in(r+1) = exp(logdecay_r) h_in(r) + state_r from h0 (or zero), overwriting
+//                 each run's slot with the state entering the next run (fp16), and completes the
+//                 final state.
+//   k_fused_scan  one block per (chain, run), sub-chunk by sub-chunk from the state entering the
+//                 run: cumulative decay, C B^T, the masked intra-sub-chunk product, the readout
+//                 of the carried state, the skip term and the state update, all on chip; only y
+//                 leaves.
 //
-// Blocks take their (chain, run) from a ticket counter in start order, chains one after another,
-// so a block only ever waits for blocks of its own chain, and every such block has started or
-// will start as soon as a compute unit is free: with at most one run per compute unit in a
-// sequence, the waits always end. With one run per sequence there is no chain: phase A completes
-// its state into the final state (S + exp(sum of dt A) h0; skipped when no final state is
-// wanted) and phase B starts from the initial state itself.
+// With one run per sequence there is no chain: k_run_states completes its state into the final
+// state (S + exp(sum of dt A) h0; skipped when no final state is wanted) and k_fused_scan starts
+// from the initial state itself.
 //
-// Inside the phases the run is walked in sub-chunks of T = 32 tokens, whatever the caller's chunk
+// Inside the kernels a run is walked in sub-chunks of T = 32 tokens, whatever the caller's chunk
 // length: the exact result does not depend on where the sequence is cut (the chunk length cancels
-// out of the recurrence), so the kernel picks the cut that suits the chip's registers and LDS.
+// out of the recurrence), so the kernels pick the cut that suits the chip's registers and LDS.
 // The caller's chunk length still fixes the stage entry points' outputs.
 //
 // Work split (one 512-thread block per compute unit, two waves per SIMD): a wave owns one head's
 // p-slice of PS columns (PS * N <= 8192, so its fp32 state is at most 128 registers per lane; at
 // headdim 64 the whole head) and keeps that state in registers across the whole run. The HPB
 // heads of a block belong to one B/C group, so B and C are staged once per block; each head's
-// decay-masked C B^T blocks are built by that head's waves.
+// decay-masked C B^T blocks are built from C B^T products shared by the block's heads (one wave
+// per head) or computed by that head's waves.
 //
 // Staging: x, B and C tiles are copied global -> LDS by the gfx950 LDS DMA (global_load_lds
 // dwordx4), which needs no registers, so a whole sub-chunk is in flight while the previous one is
-// computed (phase B: two stages, phase A: three). The DMA writes each wave instruction's 64 pieces
+// computed (scan: two stages, run states: three). The DMA writes each wave instruction's 64 pieces
 // of 16 bytes contiguously; the swizzle (16-byte piece c of row t stored at position c ^ key(t))
 // is applied by choosing which global piece each lane fetches. B and C are converted to fp16 in
 // place after arrival; x stays raw bf16 (the skip term D x uses it exactly) and is converted while
@@ -47,9 +47,9 @@
 //
 // Matrix-core operand precision: x, B, C enter as exact fp16 copies of the bf16 inputs (inputs
 // are assumed to lie in fp16's range); the decay-masked C B^T block, the carried state (for the
-// readout) and the decay-weighted x (for the state update) are rounded to fp16; phase A splits
-// the weighted x into fp16 high and low parts (two passes), so the run states that are chained
-// over the sequence, and the final state, carry near-fp32 accuracy. All accumulation is fp32.
+// readout) and the decay-weighted x (for the state update) are rounded to fp16; k_run_states
+// splits the weighted x of the sequence's last 128 tokens into fp16 high and low parts (two
+// passes) where the state is kept in fp32 (the final state). All accumulation is fp32.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 

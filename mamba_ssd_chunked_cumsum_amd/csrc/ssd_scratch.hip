@@ -1,5 +1,5 @@
 // Static device scratch for the no-allocation forward (ssd_forward_noalloc): its workspace (run
-// states, decays and chain counters of the fused path; the unfused path's intermediates when they
+// states and decays of the fused path; the unfused path's intermediates when they
 // fit) lives in this file-scope array instead of stream-ordered allocations. Each device the
 // library runs on holds its own copy from the module's load until the process ends.
 //
