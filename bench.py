@@ -509,11 +509,30 @@ def host_metadata() -> dict:
     except OSError:
         info["rocm"] = None
     info["hipcc"] = (cmd(["/opt/rocm/bin/hipcc", "--version"]).splitlines() or [None])[0]
+    # Clocks: the highest supported level of each clock (rocm-smi --showclkfrq), and the level at
+    # the moment of the query, which on an idle GPU is its low-power state (sclk ~95 MHz), not
+    # the clock the kernels run at.
     clocks = {}
     for line in cmd(["rocm-smi", "--showclocks"]).splitlines():
         for key in ("sclk", "mclk", "fclk", "socclk"):
             if f"{key} clock level" in line and "(" in line:
-                clocks[key] = line.split("(")[-1].split(")")[0]
+                clocks[key + "_at_query"] = line.split("(")[-1].split(")")[0]
+    section = None
+    for line in cmd(["rocm-smi", "--showclkfrq"]).splitlines():
+        text = line.split(":", 1)[-1].strip() if line.startswith("GPU[") else line.strip()
+        if text.startswith("Supported ") and " frequencies" in text:
+            section = text.split()[1]
+            continue
+        head, _, val = text.partition(":")
+        val = val.replace("*", "").strip()
+        if section and head.strip() and val.lower().endswith("mhz"):
+            try:
+                mhz = float(val[:-3])
+            except ValueError:
+                continue
+            key = section + "_max"
+            if mhz > float(str(clocks.get(key, "0Mhz"))[:-3] or 0):
+                clocks[key] = f"{mhz:g}Mhz"
     info["clocks"] = clocks or None
     rev = cmd(["git", "-C", ROOT, "rev-parse", "HEAD"]).strip()
     build = {}
