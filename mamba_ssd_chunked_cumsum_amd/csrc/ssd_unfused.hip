@@ -429,10 +429,11 @@ __host__ __device__ inline bool scan_state_in_lds(const Dims& d) {
 }
 
 // =============================================================================================
-// Stage 5: y = intra + exp(Acs_i) * (C_i . h_in) + D x.
+// Stage 5: y = intra + exp(Acs_i) * (C_i . h_in) + D x, fp16 operands (bf16 io; fp32 arithmetic
+// is k_chunk_scan_f32 below).
 // Grid (nc * ceil(Q/64) * ceil(P/64), H, batch), 256 threads; a block takes 64 rows and 64
 // columns of headdim (wave w 16 rows of them: four 16x16 accumulator tiles for each of the
-// intra and inter parts, few enough registers for three waves per SIMD in fp32).
+// intra and inter parts).
 // intra: for each K step over j <= i, the A fragment M[i][j] = CB[i][j] exp(Acs_i - Acs_j) dt_j
 // (selected to 0 for j > i) is formed in registers straight from CB; X^T slabs [p][j] are staged
 // in LDS. inter: C rows and h_in rows are read from global memory (both contiguous along n).
@@ -496,36 +497,12 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
       for (int k = 0; k < 8; ++k) Xs[(p8 + k) * LD + jj] = (T)v[k];
     }
     __syncthreads();
-    if constexpr (sizeof(T) == 4) {
-      // fp32: the slab's A fragments (one masked, decayed C B^T value per K step) are computed
-      // before its matrix-core steps, from clamped addresses, so their loads are in flight
-      // together instead of one per step
-      if (active) {
-        constexpr int NKS = SX / M::KSTEP;
-        float av[NKS];
-        const float acs_i = acs[ia];
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-          const int j = j0 + s * M::KSTEP + kg, jc = min(j, d.Q - 1);
-          const float cv = cb[(int64_t)ia * d.Q + jc];
-          av[s] = (j <= ia && j < d.Q) ? cv * __expf(acs_i - acs[jc]) * dts[jc] : 0.f;
-        }
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-          const int k0 = s * M::KSTEP;
-          if (k0 < sx && j0 + k0 <= i0 + 15) {
-#pragma unroll
-            for (int pt = 0; pt < NPT; ++pt)
-              if (pt < npt)
-                acc[pt] = M::mma(av[s], M::lds(Xs + (pt * 16 + col) * LD + k0 + kg), acc[pt]);
-          }
-        }
-      }
-    } else if (active) {
+    static_assert(sizeof(T) == 2, "fp32 arithmetic: k_chunk_scan_f32");
+    if (active) {
       for (int k0 = 0; k0 < sx && j0 + k0 <= i0 + 15; k0 += M::KSTEP) {
         const int jb = j0 + k0 + M::KPL * kg;  // first j of this lane's K slice
         typename M::Frag a;
-        if constexpr (sizeof(T) == 2) {
+        {
           float cv[8];
           if (jb < d.Q) {
             load8(cb + (int64_t)ia * d.Q + jb, cv);
@@ -539,10 +516,6 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
             const float m = cv[qq] * __expf(acs[ia] - acs[j]) * dts[j];
             a[qq] = (T)((j <= ia) ? m : 0.f);
           }
-        } else {
-          const int j = jb;
-          const float m = cb[(int64_t)ia * d.Q + j] * __expf(acs[ia] - acs[j]) * dts[j];
-          a = (j <= ia) ? m : 0.f;
         }
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt)
@@ -578,37 +551,6 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   }
   if (!active) return;
   const int64_t crow = (((int64_t)b * d.L + t0 + ia) * d.G + g) * d.N;
-  if constexpr (sizeof(T) == 4) {
-    // fp32: C fragments of 8 K steps loaded together (row clamped to the chunk, zero past it)
-    constexpr int GK = 8;
-    const int64_t crow_c = (((int64_t)b * d.L + t0 + min(ia, q - 1)) * d.G + g) * d.N;
-    // the state operand from LDS or (too large a state) global memory: one loop each, so that
-    // every access has a fixed address space
-    auto readout = [&](const float* hs, int ldr) {
-      for (int k00 = 0; k00 < d.N; k00 += GK * M::KSTEP) {
-        float av[GK];
-#pragma unroll
-        for (int s = 0; s < GK; ++s) {
-          const int n = k00 + s * M::KSTEP + kg;
-          const float v = Io<IO>::load(Cm, crow_c + min(n, d.N - 1));
-          av[s] = (ia < q && n < d.N) ? v : 0.f;
-        }
-#pragma unroll
-        for (int s = 0; s < GK; ++s) {
-          const int n = k00 + s * M::KSTEP + kg;
-          if (k00 + s * M::KSTEP < d.N) {
-#pragma unroll
-            for (int pt = 0; pt < NPT; ++pt)
-              if (pt < npt) inter[pt] = M::mma(av[s], hs[(pt * 16 + col) * ldr + n], inter[pt]);
-          }
-        }
-      }
-    };
-    if (hlds)
-      readout(Hs, ldh);
-    else
-      readout(hb, d.N);
-  } else
   for (int k0 = 0; k0 < d.N; k0 += M::KSTEP) {
     const int n = k0 + M::KPL * kg;
     const bool nvalid = n < d.N;  // the fp16 K step is 32 wide, N only a multiple of 16
@@ -619,7 +561,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
         typename M::Frag bf;
         const float* hp = hlds ? Hs + (pt * 16 + col) * ldh + n
                                : hb + (int64_t)(pt * 16 + col) * d.N + n;
-        if constexpr (sizeof(T) == 2) {
+        {
           float hv[8];
           if (nvalid) {
             load8(hp, hv);
@@ -629,13 +571,179 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
           }
 #pragma unroll
           for (int qq = 0; qq < 8; ++qq) bf[qq] = (T)hv[qq];
-        } else {
-          bf = *hp;
         }
         inter[pt] = M::mma(a, bf, inter[pt]);
       }
     }
   }
+  const float dh = Dv[h];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = i0 + 4 * kg + r;
+    if (i >= q) continue;
+    const float e = __expf(acs[i]);
+    const int64_t row = (((int64_t)b * d.L + t0 + i) * d.H + h) * d.P;
+    const int64_t xrow = (((int64_t)b * d.L + t0 + i) * xh.n + xh.row) * d.P;
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt) {
+      if (pt < npt) {
+        const int p = p0 + pt * 16 + col;
+        const float xv = Io<IO>::load(x, xrow + p);
+        Io<IO>::store(y, row + p, acc[pt][r] + e * inter[pt][r] + dh * xv);
+      }
+    }
+  }
+}
+
+// Four consecutive io values as floats (16 bytes of fp32 or 8 of bf16, aligned).
+__device__ __forceinline__ float4 load4f(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4f(const u16* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+}
+__device__ __forceinline__ float at4(const float4& v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+// Stage 5 in fp32 (fp32 matrix cores, 16 x 16 x 4): the same grid and tiles as k_chunk_scan, with
+// the K index of every group of four matrix-core steps running over 16 consecutive positions, lane
+// group kg taking positions 4 kg .. 4 kg + 3 (one per step): every operand a lane feeds is then 16
+// contiguous bytes, one 16-byte load per group of four steps (C and C B^T rows from global memory,
+// the decay arrays, the X^T slab and the entering state from LDS) instead of four scalar loads.
+// The X slab is staged transposed ([p][j]) through registers, 4 tokens x 4 columns per thread.
+template <typename IO>
+__global__ __launch_bounds__(256) void k_chunk_scan_f32(
+    const IO* __restrict__ x, const IO* __restrict__ Cm, const float* __restrict__ CB,
+    const float* __restrict__ Acs, const float* __restrict__ dtc,
+    const float* __restrict__ h_in, const float* __restrict__ Dv, IO* __restrict__ y, Dims d) {
+  using M = Mma<float>;
+  constexpr int SX = 32, LDX = SX + 4;  // tokens per staged X slab; its rows [p][j], 16-byte aligned
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* acs = reinterpret_cast<float*>(smem);
+  float* dts = acs + 256;
+  float* Xs = dts + 256;
+
+  constexpr int NPT = 4;
+  const int nib = (d.Q + 63) / 64, npb = (d.P + 63) / 64;
+  const int c = blockIdx.x / (nib * npb), ib = (blockIdx.x / npb) % nib, pb = blockIdx.x % npb;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (d.H / d.G);
+  const XRow xh(d, h);
+  const int p0 = pb * 64, np = min(64, d.P - p0), npt = np / 16;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, kg = lane >> 4;
+  const int t0 = c * d.Q, q = min(d.Q, d.L - t0);
+  const int i0 = ib * 64 + wave * 16;
+  const bool active = i0 < d.Q;
+  const int rowmax_blk = min(ib * 64 + 63, d.Q - 1);
+  const int64_t abase = (((int64_t)b * d.H + h) * d.nc + c) * d.Q;
+  for (int i = threadIdx.x; i < d.Q; i += 256) {
+    acs[i] = Acs[abase + i];
+    dts[i] = dtc[abase + i];
+  }
+  f32x4 acc[NPT], inter[NPT];
+#pragma unroll
+  for (int pt = 0; pt < NPT; ++pt) { acc[pt] = zero4(); inter[pt] = zero4(); }
+  const float* cb = CB + (((int64_t)b * d.nc + c) * d.G + g) * d.Q * d.Q;
+  const int ia = i0 + col;
+  __syncthreads();
+
+  for (int j0 = 0; j0 <= rowmax_blk; j0 += SX) {
+    // stage X^T: thread e takes columns 4 (e % (np/4)) .. + 3 of tokens 4 (e / (np/4)) .. + 3
+    // (zeros past the chunk)
+    {
+      const int e = threadIdx.x, nc4 = np / 4;
+      if (e < nc4 * (SX / 4)) {
+        const int pc = 4 * (e % nc4), jj = 4 * (e / nc4);
+        float4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int j = j0 + jj + k;
+          v[k] = j < q ? load4f(x + (((int64_t)b * d.L + t0 + j) * xh.n + xh.row) * d.P + p0 + pc)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<float4*>(Xs + (pc + r) * LDX + jj) =
+              make_float4(at4(v[0], r), at4(v[1], r), at4(v[2], r), at4(v[3], r));
+      }
+    }
+    __syncthreads();
+    if (active) {
+      const float acs_i = acs[ia];
+#pragma unroll
+      for (int u = 0; u < SX / 16; ++u) {
+        const int jb = j0 + 16 * u;  // first position of the group (wave-uniform)
+        if (jb > i0 + 15 || jb >= d.Q) break;
+        const int j = jb + 4 * kg;   // this lane's four positions j .. j + 3
+        float m[4];
+        if (j < d.Q) {
+          const float4 cv = *reinterpret_cast<const float4*>(cb + (int64_t)ia * d.Q + j);
+          const float4 av = *reinterpret_cast<const float4*>(acs + j);
+          const float4 dv = *reinterpret_cast<const float4*>(dts + j);
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            m[v] = (j + v <= ia) ? at4(cv, v) * __expf(acs_i - at4(av, v)) * at4(dv, v) : 0.f;
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) m[v] = 0.f;
+        }
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) {
+          if (pt < npt) {
+            const float4 xb =
+                *reinterpret_cast<const float4*>(Xs + (pt * 16 + col) * LDX + 16 * u + 4 * kg);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[pt] = M::mma(m[v], at4(xb, v), acc[pt]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // inter-chunk readout: C_i . h_in[p, :], the state staged in LDS (rows padded by 4 floats) when
+  // it fits the budget, else read from global memory
+  const float* hb = h_in + ((((int64_t)b * d.nc + c) * d.H + h) * d.P + p0) * d.N;
+  const bool hlds = scan_state_in_lds(d);
+  const int ldh = d.N + 4;
+  float* Hs = Xs;
+  if (hlds) {
+    const int nv = np * d.N / 4;
+    for (int e0 = threadIdx.x; e0 < nv; e0 += 256 * 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = *reinterpret_cast<const float4*>(hb + 4 * min(e0 + 256 * u, nv - 1));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = 4 * (e0 + 256 * u);
+        if (e0 + 256 * u < nv) *reinterpret_cast<float4*>(Hs + (e / d.N) * ldh + e % d.N) = v[u];
+      }
+    }
+    __syncthreads();
+  }
+  if (!active) return;
+  const bool iv = ia < q;
+  const IO* crow = Cm + (((int64_t)b * d.L + t0 + min(ia, q - 1)) * d.G + g) * d.N;
+  auto readout = [&](const float* hs, int ldr) {
+    for (int n0 = 0; n0 < d.N; n0 += 16) {
+      const int n = n0 + 4 * kg;
+      const float4 cv = iv ? load4f(crow + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) {
+        if (pt < npt) {
+          const float4 hv = *reinterpret_cast<const float4*>(hs + (pt * 16 + col) * ldr + n);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) inter[pt] = M::mma(at4(cv, v), at4(hv, v), inter[pt]);
+        }
+      }
+    }
+  };
+  if (hlds)
+    readout(Hs, ldh);
+  else
+    readout(hb, d.N);
   const float dh = Dv[h];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -750,11 +858,31 @@ static hipError_t scan_impl(const Dims& d, const void* x, const void* C, const f
   return hipGetLastError();
 }
 
+template <typename IO>
+static hipError_t scan_f32_impl(const Dims& d, const void* x, const void* C, const float* CB,
+                                const float* Acs, const float* dtc, const float* h_in,
+                                const float* D, void* y, hipStream_t s) {
+  const int rows = std::min(d.P, 64);
+  size_t slab = (size_t)rows * (32 + 4) * 4;
+  if (scan_state_in_lds(d)) slab = std::max(slab, (size_t)rows * (d.N + 4) * 4);
+  const size_t shm = 512 * 4 + slab;
+  auto kern = k_chunk_scan_f32<IO>;
+  if (shm > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(d.nc * ((d.Q + 63) / 64) * ((d.P + 63) / 64), d.H, d.Bt);
+  hipLaunchKernelGGL(kern, grid, dim3(256), shm, s, (const IO*)x, (const IO*)C, CB, Acs, dtc,
+                     h_in, D, (IO*)y, d);
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk_scan(const Dims& d, int io, int prec, const void* x, const void* C,
                              const float* CB, const float* Acs, const float* dtc,
                              const float* h_in, const float* D, void* y, hipStream_t s) {
-  if (io == kIoF32) return scan_impl<float, float>(d, x, C, CB, Acs, dtc, h_in, D, y, s);
-  if (prec == kPrecFp32) return scan_impl<u16, float>(d, x, C, CB, Acs, dtc, h_in, D, y, s);
+  if (io == kIoF32) return scan_f32_impl<float>(d, x, C, CB, Acs, dtc, h_in, D, y, s);
+  if (prec == kPrecFp32) return scan_f32_impl<u16>(d, x, C, CB, Acs, dtc, h_in, D, y, s);
   return scan_impl<u16, f16>(d, x, C, CB, Acs, dtc, h_in, D, y, s);
 }
 
