@@ -120,17 +120,22 @@ __device__ __forceinline__ int swz(int t, int c) {
 // treats any such DMA as possibly aliasing every LDS access); the kernels wait for them
 // explicitly (wait_vm_*) and publish the data with a barrier. M0 holds the LDS address; the
 // compiler reserves M0 and sets it right before its own uses, so it holds no live value here.
+// No memory clobber: a DMA writes a stage that no LDS access between two barriers touches (every
+// access of that stage lies before the barrier that precedes the DMA, or after the wait and the
+// barrier that follow it, and the waits, being volatile with a memory clobber, and the barriers
+// keep their order), and it reads only kernel inputs; so the compiler may move the block's other
+// LDS accesses across it (measured: -0.7%).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_x4(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
                "s"(sbase), "s"(lds)
-               : "memory", "m0");
+               : "m0");
 }
 __device__ __forceinline__ void dma_x1(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff),
                "s"(sbase), "s"(lds)
-               : "memory", "m0");
+               : "m0");
 }
 #pragma clang diagnostic pop
 // 32-bit LDS address of a pointer into shared memory.
@@ -961,15 +966,39 @@ __device__ __forceinline__ void fused_scan(char* smem, Coord c, const u16* __res
     bool fast;
     const float acs_end = decay_terms<K>(dv, a_h, wa, c, &fast);
     __syncthreads();  // A: stage and token arrays visible; every wave is done with sub-chunk s - 1
-    // the next stage's DMA (into the stage every wave is done with), spread over the K steps of
-    // the M blocks (slots 0 .. NKN - 1) and of the readout (slots NKN .. 2 NKN - 1)
+    // the next stage's DMA (into the stage every wave is done with), spread over the work: slots
+    // 0 .. NKN - 1 are the K steps of the C B^T / M blocks, slot NKN follows the M blocks, slots
+    // NKN + 1 .. 2 NKN are the readout's K steps (the dt goes with the last). With the C B^T
+    // blocks shared (one wave per head) one round goes into the C B^T step, one after the M blocks
+    // and the rest over the readout (a wave issuing several rounds back to back waits for the
+    // memory pipeline; measured -1% at the headline shape, -1.6% at 65536 tokens); otherwise the
+    // rounds are spread evenly over the C B^T and readout steps (at headdim 128, dstate 256 the
+    // other spread measured 1.7% slower).
     const bool more = s + 1 < s_end;
-    constexpr int NSLOT = 2 * K::NKN;
-    constexpr int NRND = (K::SCAN_NI + K::NW - 1) / K::NW, RPS = (NRND + NSLOT - 1) / NSLOT;
+    constexpr int NSLOT = 2 * K::NKN + 1;
+    constexpr int NRND = (K::SCAN_NI + K::NW - 1) / K::NW;
+    constexpr int RR = NRND > 2 ? (NRND - 2 + K::NKN - 1) / K::NKN : 0;  // rounds per readout step
+    constexpr int RPS = (NRND + 2 * K::NKN - 1) / (2 * K::NKN);          // even spread
     auto dma = [&](int slot) {
-      if (more)
+      int r0 = 0, r1 = 0;
+      if constexpr (K::SHARED_CB) {
+        if (slot == 0) {
+          r1 = 1;
+        } else if (slot == K::NKN) {
+          r0 = 1;
+          r1 = 2;
+        } else if (slot > K::NKN) {
+          r0 = 2 + (slot - K::NKN - 1) * RR;
+          r1 = r0 + RR;
+        }
+      } else if (slot != K::NKN) {
+        const int k = slot < K::NKN ? slot : slot - 1;
+        r0 = k * RPS;
+        r1 = r0 + RPS;
+      }
+      if (more && (r1 > r0 || slot == NSLOT - 1))
         issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, dt, d, c, dl,
-                             (s + 1) * T, slot * RPS, (slot + 1) * RPS, slot == NSLOT - 1);
+                             (s + 1) * T, r0, r1, slot == NSLOT - 1);
     };
 
     f32x4 Y[NPT][NIT];
@@ -984,6 +1013,7 @@ __device__ __forceinline__ void fused_scan(char* smem, Coord c, const u16* __res
       for (int slot = K::SHARED_CB ? K::NKN : 0; slot < NSLOT; ++slot) dma(slot);
     } else {
       if constexpr (!K::SHARED_CB) build_m<K>(Bh, Ch, wa, d_h, fast, mh, sl, c, dma);
+      dma(K::NKN);
 
       // readout of the carried state: Y^T = S C^T (K index n in accumulator order)
 #pragma unroll
@@ -992,7 +1022,7 @@ __device__ __forceinline__ void fused_scan(char* smem, Coord c, const u16* __res
         for (int it = 0; it < NIT; ++it) Y[pt][it] = zero4();
 #pragma unroll
       for (int kn = 0; kn < K::NKN; ++kn) {
-        dma(K::NKN + kn);
+        dma(K::NKN + 1 + kn);
         f16x8 sa[NPT];
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
