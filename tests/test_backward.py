@@ -1,21 +1,29 @@
 """ssd_backward on the GPU against the float64 backward oracle, element by element.
 
 The GPU backward computes in fp32 throughout (its four chunked recurrences run the fp32 matrix
-cores; the inputs are exact in fp32, also for bf16 io), so each gradient is held to
-max |g - r| <= TOL * max|r| over the tensor: fp32 rounding (2^-24 per operation) accumulated over
-a few hundred terms of mixed sign leaves a few 1e-6; TOL = 1e-4 keeps a margin.
+cores; the inputs are exact in fp32, also for bf16 io), so dx, dB, dC, dD and the initial-state
+gradient are held to max |g - r| <= TOL * max|r| over the tensor: fp32 rounding (2^-24 per
+operation) accumulated over a few hundred terms of mixed sign leaves a few 1e-6; TOL = 1e-4 keeps
+a margin.
 
-dA is held per head: dA_h = sum over batch and time of dt_t dlog_t, terms that largely cancel, so
-its error is bounded by the per-term error times the absolute sum of the terms of that head,
-|g - r| <= TOL * sum_t |dt_t dlog_t| (the scale a floating-point sum's error is bounded by); the
-test prints each head's error relative to its own |dA| and to that sum. The relative error of dA
-itself is then about the per-term error times the head's condition number
-kappa_h = sum_t |dt_t dlog_t| / |dA_h|: heads whose dA cancels to a small fraction of its terms
-show large relative errors (at the full 8192-token sequence kappa reaches ~500, and fp32
-recurrence outputs carry per-term errors of a few 1e-4, which gives relative errors of ~10% on
-such heads) while their absolute error stays within the bound. At the full sequence the decay
-gradients (ddt and dA) sum fp32 terms, each with the rounding of the recurrences that produced
-it, over thousands of tokens: they are held to TOL_LONG = 1e-3 there.
+The decay gradients are held to a bound derived from how the GPU forms them. It sums, in double,
+the per-token terms q_s = dy_s . ys_s - dt_s x_s . u_s (ys the state part of y, u = G B, both
+outputs of fp32 recurrences, dotted over headdim in fp32) from the sequence end back to t, plus
+<dfinal, final state>; that suffix sum is dlog_t, ddt_t = A dlog_t + x_t . u_t, and
+dA = sum over batch and time of dt_t dlog_t. If every fp32 product entering those dots carries a
+relative error of at most EPS, the errors are bounded by
+
+    |ddt_t error| <= EPS (|A| R_t + X_t) + 2^-24 |ddt_t|,   |dA error| <= EPS sum_t dt_t R_t,
+
+with R_t = sum_{s >= t} (sum_p |dy_sp ys_sp| + |dt_s x_sp u_sp|) + sum |dfinal * final| and
+X_t = sum_p |x_tp u_tp|, the absolute values of the terms summed (computed here from the oracle's
+y, final state and dx = D dy + dt u). EPS = 2^-24 (Q + N + P) with Q = 64, the backward's own
+chunk length, is the rounding bound of a sum of that many fp32 terms (a recurrence output sums at
+most a chunk of Q tokens and a state row of N entries, and the dot over headdim adds P): it
+covers the fp32 work between the inputs and the double sums. The tests print each element's
+error as a multiple of 2^-24 (|A| R_t + X_t) and each head's dA error relative to its own |dA|:
+the suffix sums R_t grow with the tokens after t while dlog_t does not (the terms telescope), so
+relative errors are largest on heads whose dA cancels.
 """
 
 import numpy as np
@@ -23,6 +31,7 @@ import pytest
 import torch
 
 import mamba_ssd_chunked_cumsum_amd as ssd
+from oracle import ssd_recurrence
 from oracle.backward import ssd_backward as oracle_backward
 
 from gpu_util import DEV, note
@@ -30,7 +39,12 @@ from gpu_util import DEV, note
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-4
-TOL_LONG = 1e-3
+U32 = 2.0 ** -24
+BWD_CHUNK = 64  # the chunk length the backward's recurrences run at, whatever the caller's
+
+
+def _eps(N, P):
+    return U32 * (BWD_CHUNK + N + P)
 
 # Bt, L, H, P, N, G, chunk, io, h0, dfinal
 CASES = [
@@ -80,17 +94,40 @@ def _dev(a, io, io_tensor):
     return t.to(torch.bfloat16) if (io_tensor and io == "bf16") else t
 
 
-def _check_dA(got, ref, terms, tol, label):
-    """dA per head against its own scale: |g - r| <= tol * sum_t |dt dlog| of that head (the
-    absolute sum of the terms the head's dA sums, which bounds a floating-point sum's error).
-    Prints each head's error relative to its own |dA| and to that sum."""
-    err = np.abs(got - ref)
-    for h in range(len(ref)):
-        print(f"{label} dA head {h}: {ref[h]:+.5e}, |g - r| {err[h]:.2e}, relative "
-              f"{err[h] / max(abs(ref[h]), 1e-30):.2e}, sum|terms| {terms[h]:.3e}, "
-              f"|g - r| / sum|terms| {err[h] / max(terms[h], 1e-30):.2e} (bar {tol})")
-    assert np.all(err <= tol * np.maximum(terms, 1e-30)), (err, terms)
-    return err
+def _decay_scales(inp, dy, dfinal, ref):
+    """R [Bt, L, H] and X [Bt, L, H] of the decay-gradient bound, from oracle quantities."""
+    y, fin = ssd_recurrence(**inp)
+    x = inp["x"].astype(np.float64)
+    dy64 = dy.astype(np.float64)
+    D = inp["D"].astype(np.float64)[None, None, :, None]
+    ys = y - D * x
+    dtu = ref["dx"] - D * dy64                                   # dt_t u_t
+    q_abs = np.sum(np.abs(dy64 * ys), axis=3) + np.sum(np.abs(x * dtu), axis=3)
+    R = np.flip(np.cumsum(np.flip(q_abs, axis=1), axis=1), axis=1)
+    if dfinal is not None:
+        R = R + np.sum(np.abs(dfinal.astype(np.float64) * fin), axis=(2, 3))[:, None, :]
+    X = np.sum(np.abs(x * dtu), axis=3) / inp["dt"].astype(np.float64)
+    return R, X
+
+
+def _check_decay(got_ddt, got_dA, ref, inp, R, X, eps, label):
+    """ddt element by element and dA per head against the derived bound; prints the errors as
+    multiples of the bound's fp32 scale and each head's dA error relative to its own |dA|."""
+    A = np.abs(inp["A"].astype(np.float64))[None, None, :]
+    scale = A * R + X
+    err = np.abs(got_ddt - ref["ddt"])
+    bound = eps * scale + U32 * np.abs(ref["ddt"])
+    print(f"{label} ddt: max|g - r| {err.max():.3e}, max err / (2^-24 (|A| R + X)) "
+          f"{np.max(err / np.maximum(U32 * scale, 1e-300)):.2f} (bar {eps / U32:.0f}), "
+          f"max|r| {np.abs(ref['ddt']).max():.3e}")
+    assert np.all(err <= bound), float(np.max(err / np.maximum(bound, 1e-300)))
+    dscale = np.sum(inp["dt"].astype(np.float64) * R, axis=(0, 1))
+    derr = np.abs(got_dA - ref["dA"])
+    for h in range(len(derr)):
+        print(f"{label} dA head {h}: {ref['dA'][h]:+.5e}, |g - r| {derr[h]:.2e}, relative "
+              f"{derr[h] / max(abs(ref['dA'][h]), 1e-30):.2e}, err / (2^-24 sum dt R) "
+              f"{derr[h] / max(U32 * dscale[h], 1e-300):.2f} (bar {eps / U32:.0f})")
+    assert np.all(derr <= eps * dscale), (derr, dscale)
 
 
 @pytest.mark.parametrize("case", CASES, ids=_case_id)
@@ -104,13 +141,16 @@ def test_backward_matches_oracle(case):
                      d["initial_state"], _dev(dfinal, io, False))
     torch.cuda.synchronize()
     ref = oracle_backward(**inp, dy=dy, dfinal=dfinal)
-    dlog = ref.pop("dlog_decay")
-    for k, r in ref.items():
-        gk = g[k].cpu().numpy().astype(np.float64)
+    ref.pop("dlog_decay")
+    got = {k: g[k].cpu().numpy().astype(np.float64) for k in ref}
+    for k, gk in got.items():
         assert np.all(np.isfinite(gk)), k
-        if k == "dA":
-            _check_dA(gk, r, np.sum(np.abs(inp["dt"] * dlog), axis=(0, 1)), TOL, _case_id(case))
+    R, X = _decay_scales(inp, dy, dfinal, ref)
+    _check_decay(got["ddt"], got["dA"], ref, inp, R, X, _eps(N, P), _case_id(case))
+    for k, r in ref.items():
+        if k in ("ddt", "dA"):
             continue
+        gk = got[k]
         err = float(np.max(np.abs(gk - r)))
         scale = float(np.max(np.abs(r)))
         print(f"{k}: max|g - r| = {err:.3e}, max|r| = {scale:.3e}, ratio {err / max(scale, 1e-30):.2e}")
@@ -165,18 +205,15 @@ def test_backward_full_size_sampled_heads():
         sub = dict(x=inp["x"][:, :, h:h + 1], dt=inp["dt"][:, :, h:h + 1], A=inp["A"][h:h + 1],
                    B=inp["B"], C=inp["C"], D=inp["D"][h:h + 1], initial_state=None)
         ref = oracle_backward(**sub, dy=dy[:, :, h:h + 1], dfinal=dfinal[:, h:h + 1])
-        dA_scale = float(np.sum(np.abs(sub["dt"] * ref["dlog_decay"])))
-        pairs = dict(dx=(got["dx"][:, :, h:h + 1], ref["dx"]),
-                     ddt=(got["ddt"][:, :, h:h + 1], ref["ddt"]),
-                     dA=(got["dA"][h:h + 1], ref["dA"]), dD=(got["dD"][h:h + 1], ref["dD"]),
+        R, X = _decay_scales(sub, dy[:, :, h:h + 1], dfinal[:, h:h + 1], ref)
+        _check_decay(got["ddt"][:, :, h:h + 1], got["dA"][h:h + 1], ref, sub, R, X,
+                     _eps(shape.dstate, shape.headdim),
+                     f"full size, head {h}")
+        pairs = dict(dx=(got["dx"][:, :, h:h + 1], ref["dx"]), dD=(got["dD"][h:h + 1], ref["dD"]),
                      dinitial_state=(got["dinitial_state"][:, h:h + 1], ref["dinitial_state"]))
         for k, (gk, r) in pairs.items():
-            tol = TOL_LONG if k in ("ddt", "dA") else TOL
-            if k == "dA":
-                _check_dA(gk, r, np.array([dA_scale]), tol, f"full size, head {h}")
-                continue
             err = float(np.max(np.abs(gk - r)))
             scale = float(np.max(np.abs(r)))
             print(f"head {h} {k}: max|g - r| = {err:.3e}, scale = {scale:.3e}, "
-                  f"ratio {err / max(scale, 1e-30):.2e} (bar {tol})")
-            assert err <= tol * max(scale, 1e-30), f"head {h} {k}: {err:.3e} vs {scale:.3e}"
+                  f"ratio {err / max(scale, 1e-30):.2e} (bar {TOL})")
+            assert err <= TOL * max(scale, 1e-30), f"head {h} {k}: {err:.3e} vs {scale:.3e}"
