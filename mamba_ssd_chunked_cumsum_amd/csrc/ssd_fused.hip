@@ -158,19 +158,6 @@ __device__ __forceinline__ s16x4 tr4(const char* p) {
       (__attribute__((address_space(3))) s16x4*)(p));
 }
 
-// K fragment of a staged swizzled tile whose rows are the K index (tokens): lane (g, j) gets
-// column col0 + j and rows r0 + 8 g + 0..7 as eight 16-bit values (raw bits).
-template <int ROW>
-__device__ __forceinline__ s16x8 frag_tr(const char* tile, int r0, int col0, int lane) {
-  const int j = lane & 15, g = lane >> 4;
-  const int t = r0 + 8 * g + (j >> 2);
-  const int c = (col0 >> 3) + ((j & 3) >> 1);
-  const int half = (j & 1) << 3;
-  const s16x4 lo = tr4(tile + swz<ROW>(t, c) + half);
-  const s16x4 hi = tr4(tile + swz<ROW>(t + 4, c) + half);
-  return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
 // ---- configuration ----------------------------------------------------------------------------
 template <int P_, int N_, int NW_ = 4, int PSMAX_ = 64, int T_ = (N_ >= 256 ? 32 : 64)>
 struct Fz {
@@ -201,6 +188,10 @@ struct Fz {
   // heads (they share one B/C group)
   static constexpr bool SHARED_CB = WPH == 1 && NMB <= NW;
   static constexpr int CB_SHARED = SHARED_CB ? NMB * 1024 : 0;
+  // phase B runs two sub-chunks per loop pass with the stage buffer fixed at compile time (no
+  // stage-base additions on LDS addresses) where that fits in the registers: dstate <= 128 at one
+  // wave per head
+  static constexpr bool UNROLL2 = SHARED_CB && N <= 128;
   static constexpr int SCAN_LDS = NSCAN * SCAN_STAGE + HPB * MT_HEAD + WA_SCAN + CB_SHARED;
   static constexpr int RUN_LDS = NRUN * RUN_STAGE + WA_BYTES;
   static_assert(P % PS == 0 && NW % WPH == 0, "whole waves per head");
@@ -482,19 +473,62 @@ __device__ __forceinline__ float decay_terms(float dv, float a_h, float* wa, con
   return acs_end;
 }
 
-// x K fragment of p columns col0 .. col0 + 15: raw bf16 -> 8 floats (tokens 32 js + 8 g + 0..7).
+// Lane-constant byte offsets of the LDS fragment accesses of both phases, relative to the tile they read,
+// computed once per kernel. The swizzle key sees only a row's low 4 bits and a piece's low bits,
+// so the unrolled loop indices it does not see (token-tile rows, high piece bits) enter as
+// immediates on top of these.
+
 template <class K>
-__device__ __forceinline__ void x_frag(const char* xt, int js, int col0, int lane, float (&v)[8]) {
-  const s16x8 r = frag_tr<K::ROW_P>(xt, 32 * js, col0, lane);
+struct ScanLane {
+  static constexpr int PPR_N = K::N / 8;
+  static constexpr int KP = PPR_N >= 16 ? 4 : 2;   // K steps over n with distinct patterns
+  static constexpr int NP = PPR_N >= 16 ? 8 : 4;   // n tiles with distinct patterns
+  uint32_t cro[KP][2];      // readout C^T fragment: row c16, piece 4 kn + 2 h + g/2, half g&1
+  // B^T fragment (transposing read) of n tile 0: rows 8 g + j/4 (+4), pieces 0..1; n tile b < NP
+  // reads at btr0 ^ (b << 5) (its pieces 2 b, 2 b + 1: the swizzle key flips bits of the piece
+  // index, and the row's own offset has no bits in 5..7 below the NP tiles)
+  uint32_t btr0[2];
+  uint32_t xtr[K::NPT][2];  // x fragment (transposing read)
+  uint32_t cbr[KP];         // C B^T inputs: row c16, piece 4 kn + g
+  uint32_t epi[K::NPT];     // y write into the x tile: row c16, piece (p0 + 16 pt) / 8 + g/2
+  uint32_t mwr;             // M block write: row c16, columns 4 g .. 4 g + 3
+  uint32_t mrd;             // M fragment read: block + g/2, row c16, columns 8 (g&1) .. + 7
+  __device__ __forceinline__ void init(const Coord& c) {
+    const int g = c.g, c16 = c.c16, j = c.lane & 15;
+    const int sw = (c16 >> 3) & 1;  // M rows 8..15 of a block hold their two pieces swapped
+    mwr = c16 * 32 + (((g >> 1) ^ sw) << 4) + ((g & 1) << 3);
+    mrd = (g >> 1) * 512 + c16 * 32 + (((g & 1) ^ sw) << 4);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = __uint_as_float((uint32_t)(uint16_t)r[e] << 16);
+    for (int b = 0; b < KP; ++b) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        cro[b][h] = swz<K::ROW_N>(c16, 4 * b + 2 * h + (g >> 1)) + ((g & 1) << 3);
+      cbr[b] = swz<K::ROW_N>(c16, 4 * b + g);
+    }
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int t = 8 * g + (j >> 2) + 4 * hi;
+      btr0[hi] = swz<K::ROW_N>(t, (j & 3) >> 1) + ((j & 1) << 3);
+#pragma unroll
+      for (int pt = 0; pt < K::NPT; ++pt)
+        xtr[pt][hi] = swz<K::ROW_P>(t, ((c.p0 + 16 * pt) >> 3) + ((j & 3) >> 1)) + ((j & 1) << 3);
+    }
+#pragma unroll
+    for (int pt = 0; pt < K::NPT; ++pt)
+      epi[pt] = swz<K::ROW_P>(c16, ((c.p0 + 16 * pt) >> 3) + (g >> 1)) + ((g & 1) << 3);
+  }
+};
+
+// Two transposing reads at precomputed lane offsets -> one 8-value K fragment.
+__device__ __forceinline__ s16x8 tr8(const char* base, uint32_t lo, uint32_t hi) {
+  const s16x4 a = tr4(base + lo), b = tr4(base + hi);
+  return s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// B^T K fragment (rows n = col0 .. col0 + 15, K = tokens) of a converted fp16 B tile.
-template <class K>
-__device__ __forceinline__ f16x8 b_frag(const char* Bh, int js, int col0, int lane) {
-  return __builtin_bit_cast(f16x8, frag_tr<K::ROW_N>(Bh, 32 * js, col0, lane));
-}
+template <bool V>
+struct Flag {
+  static constexpr bool value = V;
+};
 
 // ---- phase A: run states ------------------------------------------------------------------------
 // state_r = sum_{t in run} exp(sum_{k in (t, end]} dt_k A) dt_t x_t B_t^T (zero entry state) and
@@ -506,11 +540,6 @@ __device__ __forceinline__ f16x8 b_frag(const char* Bh, int js, int col0, int la
 // tokens carry decayed weights or, in slowly decaying heads, many comparable terms whose
 // independent roundings average out. Leaves the state in S (lane: p = p0 + 16 pt + c16,
 // n = 16 nt + 4 g + 0..3) and returns the log-decay.
-template <bool V>
-struct Flag {
-  static constexpr bool value = V;
-};
-
 template <class K>
 __device__ __forceinline__ float run_state(char* smem, const Coord& c, const u16* __restrict__ x,
                                            const u16* __restrict__ Bm,
@@ -520,6 +549,9 @@ __device__ __forceinline__ float run_state(char* smem, const Coord& c, const u16
   using M = Mma<f16>;
   DmaLanes<K, false> dl;
   dl.init(d, c);
+  ScanLane<K> sl;
+  sl.init(c);
+  using SL = ScanLane<K>;
   constexpr int T = K::T;
   float* wa = reinterpret_cast<float*>(smem + K::NRUN * K::RUN_STAGE) + c.wave * K::NWA * T;
   const int xoff = K::BC_BYTES + (c.wave / K::WPH) * (T * K::ROW_P);
@@ -559,6 +591,7 @@ __device__ __forceinline__ float run_state(char* smem, const Coord& c, const u16
     // the DMA of sub-chunk s - 2 (into the stage of s + 1), spread over the K steps below
     const bool more = s - 2 >= s_begin;
     constexpr int NRND = (K::RUN_NI + K::NW - 1) / K::NW, RPJ = (NRND + K::NJS - 1) / K::NJS;
+    const uint32_t bt0 = sl.btr0[0], bt1 = sl.btr0[1];
     rem += decay_terms<K, true>(dv, a_h, wa, c, nullptr, rem);
 #pragma unroll
     for (int js = 0; js < K::NJS; ++js) {
@@ -572,7 +605,9 @@ __device__ __forceinline__ float run_state(char* smem, const Coord& c, const u16
 #pragma unroll
       for (int pt = 0; pt < K::NPT; ++pt) {
         float v[8], lo[8];
-        x_frag<K>(st + xoff, js, c.p0 + 16 * pt, c.lane, v);
+        const s16x8 r = tr8(st + xoff + 32 * js * K::ROW_P, sl.xtr[pt][0], sl.xtr[pt][1]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = __uint_as_float((uint32_t)(uint16_t)r[e] << 16);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= wj[e];
         xhi[pt] = cvt_f16x8(v);
@@ -584,7 +619,9 @@ __device__ __forceinline__ float run_state(char* smem, const Coord& c, const u16
       }
 #pragma unroll
       for (int nt = 0; nt < K::NNT; ++nt) {
-        const f16x8 bt = b_frag<K>(st, js, 16 * nt, c.lane);
+        const char* bb = st + 32 * js * K::ROW_N + (nt / SL::NP) * (16 * 2 * SL::NP);
+        const f16x8 bt = __builtin_bit_cast(
+            f16x8, tr8(bb, bt0 ^ ((nt % SL::NP) << 5), bt1 ^ ((nt % SL::NP) << 5)));
 #pragma unroll
         for (int pt = 0; pt < K::NPT; ++pt) {
           S[nt][pt] = M::mma(bt, xhi[pt], S[nt][pt]);
@@ -667,57 +704,6 @@ __device__ __forceinline__ void store_y(const char* xt, u16* y, const Dims& d, c
                                   reinterpret_cast<u32x4*>(yb + (int64_t)row0 * ld));
     }
   }
-}
-
-// Lane-constant byte offsets of phase B's LDS fragment accesses, relative to the tile they read,
-// computed once per kernel. The swizzle key sees only a row's low 4 bits and a piece's low bits,
-// so the unrolled loop indices it does not see (token-tile rows, high piece bits) enter as
-// immediates on top of these.
-template <class K>
-struct ScanLane {
-  static constexpr int PPR_N = K::N / 8;
-  static constexpr int KP = PPR_N >= 16 ? 4 : 2;   // K steps over n with distinct patterns
-  static constexpr int NP = PPR_N >= 16 ? 8 : 4;   // n tiles with distinct patterns
-  uint32_t cro[KP][2];      // readout C^T fragment: row c16, piece 4 kn + 2 h + g/2, half g&1
-  // B^T fragment (transposing read) of n tile 0: rows 8 g + j/4 (+4), pieces 0..1; n tile b < NP
-  // reads at btr0 ^ (b << 5) (its pieces 2 b, 2 b + 1: the swizzle key flips bits of the piece
-  // index, and the row's own offset has no bits in 5..7 below the NP tiles)
-  uint32_t btr0[2];
-  uint32_t xtr[K::NPT][2];  // x fragment (transposing read)
-  uint32_t cbr[KP];         // C B^T inputs: row c16, piece 4 kn + g
-  uint32_t epi[K::NPT];     // y write into the x tile: row c16, piece (p0 + 16 pt) / 8 + g/2
-  uint32_t mwr;             // M block write: row c16, columns 4 g .. 4 g + 3
-  uint32_t mrd;             // M fragment read: block + g/2, row c16, columns 8 (g&1) .. + 7
-  __device__ __forceinline__ void init(const Coord& c) {
-    const int g = c.g, c16 = c.c16, j = c.lane & 15;
-    const int sw = (c16 >> 3) & 1;  // M rows 8..15 of a block hold their two pieces swapped
-    mwr = c16 * 32 + (((g >> 1) ^ sw) << 4) + ((g & 1) << 3);
-    mrd = (g >> 1) * 512 + c16 * 32 + (((g & 1) ^ sw) << 4);
-#pragma unroll
-    for (int b = 0; b < KP; ++b) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        cro[b][h] = swz<K::ROW_N>(c16, 4 * b + 2 * h + (g >> 1)) + ((g & 1) << 3);
-      cbr[b] = swz<K::ROW_N>(c16, 4 * b + g);
-    }
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-      const int t = 8 * g + (j >> 2) + 4 * hi;
-      btr0[hi] = swz<K::ROW_N>(t, (j & 3) >> 1) + ((j & 1) << 3);
-#pragma unroll
-      for (int pt = 0; pt < K::NPT; ++pt)
-        xtr[pt][hi] = swz<K::ROW_P>(t, ((c.p0 + 16 * pt) >> 3) + ((j & 3) >> 1)) + ((j & 1) << 3);
-    }
-#pragma unroll
-    for (int pt = 0; pt < K::NPT; ++pt)
-      epi[pt] = swz<K::ROW_P>(c16, ((c.p0 + 16 * pt) >> 3) + (g >> 1)) + ((g & 1) << 3);
-  }
-};
-
-// Two transposing reads at precomputed lane offsets -> one 8-value K fragment.
-__device__ __forceinline__ s16x8 tr8(const char* base, uint32_t lo, uint32_t hi) {
-  const s16x4 a = tr4(base + lo), b = tr4(base + hi);
-  return s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 // ---- phase B helpers: the fused scan -------------------------------------------------------------
@@ -950,177 +936,192 @@ __device__ __forceinline__ void fused_scan(char* smem, Coord c, const u16* __res
 
   int ytok = -1;  // first token of the sub-chunk whose y waits in the previous stage's x tile
 
-  for (int s = s_begin; s < s_end; ++s) {
-    refresh_lane(c);
-    dl.pin();
-    const int cur = (s - s_begin) & 1;
-    char* st = smem + cur * K::SCAN_STAGE;
-    const char* Bh = st;
-    const char* Ch = st + K::BC_BYTES;
-    const char* xt = st + xoff;
-    wait_vm_all();  // this stage's DMA and the y stores of the previous round
-    if (ytok >= 0) store_y<K>(smem + (cur ^ 1) * K::SCAN_STAGE + xoff, y, d, c, ytok);
-    const float dv = stage_dt<K>(st + K::SCAN_DT, d, c, s * T, dtb);
-    convert_stage<K, true>(st, c);
-    // the head's decay bookkeeping needs only its dt: done while other waves finish converting
-    bool fast;
-    const float acs_end = decay_terms<K>(dv, a_h, wa, c, &fast);
-    __syncthreads();  // A: stage and token arrays visible; every wave is done with sub-chunk s - 1
-    // the next stage's DMA (into the stage every wave is done with), spread over the work: slots
-    // 0 .. NKN - 1 are the K steps of the C B^T / M blocks, slot NKN follows the M blocks, slots
-    // NKN + 1 .. 2 NKN are the readout's K steps (the dt goes with the last). With the C B^T
-    // blocks shared (one wave per head) one round goes into the C B^T step, one after the M blocks
-    // and the rest over the readout (a wave issuing several rounds back to back waits for the
-    // memory pipeline; measured -1% at the headline shape, -1.6% at 65536 tokens); otherwise the
-    // rounds are spread evenly over the C B^T and readout steps (at headdim 128, dstate 256 the
-    // other spread measured 1.7% slower).
-    const bool more = s + 1 < s_end;
-    constexpr int NSLOT = 2 * K::NKN + 1;
-    constexpr int NRND = (K::SCAN_NI + K::NW - 1) / K::NW;
-    constexpr int RR = NRND > 2 ? (NRND - 2 + K::NKN - 1) / K::NKN : 0;  // rounds per readout step
-    constexpr int RPS = (NRND + 2 * K::NKN - 1) / (2 * K::NKN);          // even spread
-    auto dma = [&](int slot) {
-      int r0 = 0, r1 = 0;
-      if constexpr (K::SHARED_CB) {
-        if (slot == 0) {
-          r1 = 1;
-        } else if (slot == K::NKN) {
-          r0 = 1;
-          r1 = 2;
-        } else if (slot > K::NKN) {
-          r0 = 2 + (slot - K::NKN - 1) * RR;
-          r1 = r0 + RR;
+  // Sub-chunks in pairs where that fits in the registers: two unrolled copies, one per stage
+  // buffer, so that in each the stage is a compile-time constant and every LDS address a lane
+  // offset plus an immediate.
+  constexpr int UN = K::UNROLL2 ? 2 : 1;
+  for (int s0 = s_begin; s0 < s_end; s0 += UN) {
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int s = s0 + u;
+      if (UN > 1 && s >= s_end) break;
+      const int cur = UN > 1 ? u : (s - s_begin) & 1;
+      refresh_lane(c);
+      dl.pin();
+      char* st = smem + cur * K::SCAN_STAGE;
+      const char* Bh = st;
+      const char* Ch = st + K::BC_BYTES;
+      const char* xt = st + xoff;
+      wait_vm_all();  // this stage's DMA and the y stores of the previous round
+      if (ytok >= 0) store_y<K>(smem + (cur ^ 1) * K::SCAN_STAGE + xoff, y, d, c, ytok);
+      const float dv = stage_dt<K>(st + K::SCAN_DT, d, c, s * T, dtb);
+      convert_stage<K, true>(st, c);
+      // the head's decay bookkeeping needs only its dt: done while other waves finish converting
+      bool fast;
+      const float acs_end = decay_terms<K>(dv, a_h, wa, c, &fast);
+      // A: stage and token arrays visible; every wave is done with sub-chunk s - 1
+      __syncthreads();
+      // the next stage's DMA (into the stage every wave is done with), spread over the work:
+      // slots 0 .. NKN - 1 are the K steps of the C B^T / M blocks, slot NKN follows the M
+      // blocks, slots NKN + 1 .. 2 NKN are the readout's K steps (the dt goes with the last).
+      // With the C B^T blocks shared (one wave per head) one round goes into the C B^T step, one
+      // after the M blocks and the rest over the readout (a wave issuing several rounds back to
+      // back waits for the memory pipeline; measured -1% at the headline shape, -1.6% at 65536
+      // tokens); otherwise the rounds are spread evenly over the C B^T and readout steps (at
+      // headdim 128, dstate 256 the other spread measured 1.7% slower).
+      const bool more = s + 1 < s_end;
+      constexpr int NSLOT = 2 * K::NKN + 1;
+      constexpr int NRND = (K::SCAN_NI + K::NW - 1) / K::NW;
+      constexpr int RR = NRND > 2 ? (NRND - 2 + K::NKN - 1) / K::NKN : 0;  // per readout step
+      constexpr int RPS = (NRND + 2 * K::NKN - 1) / (2 * K::NKN);         // even spread
+      auto dma = [&](int slot) {
+        int r0 = 0, r1 = 0;
+        if constexpr (K::SHARED_CB) {
+          if (slot == 0) {
+            r1 = 1;
+          } else if (slot == K::NKN) {
+            r0 = 1;
+            r1 = 2;
+          } else if (slot > K::NKN) {
+            r0 = 2 + (slot - K::NKN - 1) * RR;
+            r1 = r0 + RR;
+          }
+        } else if (slot != K::NKN) {
+          const int k = slot < K::NKN ? slot : slot - 1;
+          r0 = k * RPS;
+          r1 = r0 + RPS;
         }
-      } else if (slot != K::NKN) {
-        const int k = slot < K::NKN ? slot : slot - 1;
-        r0 = k * RPS;
-        r1 = r0 + RPS;
+        if (more && (r1 > r0 || slot == NSLOT - 1))
+          issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, dt, d, c, dl,
+                               (s + 1) * T, r0, r1, slot == NSLOT - 1);
+      };
+
+      f32x4 Y[NPT][NIT];
+      f16x8 w16[K::NJS];  // state weights of the lane's 8 tokens per K step
+      if constexpr (K::SHARED_CB) {
+        shared_cb<K>(Bh, Ch, cbs, sl, c, dma);
+        __syncthreads();  // the shared C B^T blocks visible to every wave
+        if (c.active) m_from_shared<K>(cbs, wa, d_h, fast, mh, sl, c);
       }
-      if (more && (r1 > r0 || slot == NSLOT - 1))
-        issue_stage<K, true>(smem + (cur ^ 1) * K::SCAN_STAGE, x, Bm, Cm, dt, d, c, dl,
-                             (s + 1) * T, r0, r1, slot == NSLOT - 1);
-    };
+      if (!c.active) {
+#pragma unroll
+        for (int slot = K::SHARED_CB ? K::NKN : 0; slot < NSLOT; ++slot) dma(slot);
+      } else {
+        if constexpr (!K::SHARED_CB) build_m<K>(Bh, Ch, wa, d_h, fast, mh, sl, c, dma);
+        dma(K::NKN);
 
-    f32x4 Y[NPT][NIT];
-    f16x8 w16[K::NJS];  // state weights of the lane's 8 tokens per K step
-    if constexpr (K::SHARED_CB) {
-      shared_cb<K>(Bh, Ch, cbs, sl, c, dma);
-      __syncthreads();  // the shared C B^T blocks visible to every wave
-      if (c.active) m_from_shared<K>(cbs, wa, d_h, fast, mh, sl, c);
-    }
-    if (!c.active) {
+        // readout of the carried state: Y^T = S C^T (K index n in accumulator order)
 #pragma unroll
-      for (int slot = K::SHARED_CB ? K::NKN : 0; slot < NSLOT; ++slot) dma(slot);
-    } else {
-      if constexpr (!K::SHARED_CB) build_m<K>(Bh, Ch, wa, d_h, fast, mh, sl, c, dma);
-      dma(K::NKN);
-
-      // readout of the carried state: Y^T = S C^T (K index n in accumulator order)
+        for (int pt = 0; pt < NPT; ++pt)
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt)
+          for (int it = 0; it < NIT; ++it) Y[pt][it] = zero4();
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) Y[pt][it] = zero4();
+        for (int kn = 0; kn < K::NKN; ++kn) {
+          dma(K::NKN + 1 + kn);
+          f16x8 sa[NPT];
 #pragma unroll
-      for (int kn = 0; kn < K::NKN; ++kn) {
-        dma(K::NKN + 1 + kn);
-        f16x8 sa[NPT];
+          for (int pt = 0; pt < NPT; ++pt) {
+            const float v[8] = {S[2 * kn][pt][0],     S[2 * kn][pt][1],     S[2 * kn][pt][2],
+                                S[2 * kn][pt][3],     S[2 * kn + 1][pt][0], S[2 * kn + 1][pt][1],
+                                S[2 * kn + 1][pt][2], S[2 * kn + 1][pt][3]};
+            sa[pt] = cvt_f16x8(v);
+          }
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) {
-          const float v[8] = {S[2 * kn][pt][0],     S[2 * kn][pt][1],     S[2 * kn][pt][2],
-                              S[2 * kn][pt][3],     S[2 * kn + 1][pt][0], S[2 * kn + 1][pt][1],
-                              S[2 * kn + 1][pt][2], S[2 * kn + 1][pt][3]};
-          sa[pt] = cvt_f16x8(v);
+          for (int it = 0; it < NIT; ++it) {
+            const char* crow = Ch + 16 * it * K::ROW_N + (kn / SL::KP) * (16 * SL::KP * 4);
+            const uint2 lo = *reinterpret_cast<const uint2*>(crow + sl.cro[kn % SL::KP][0]);
+            const uint2 hi = *reinterpret_cast<const uint2*>(crow + sl.cro[kn % SL::KP][1]);
+            const f16x8 cf = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(sa[pt], cf, Y[pt][it]);
+          }
         }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-          const char* crow = Ch + 16 * it * K::ROW_N + (kn / SL::KP) * (16 * SL::KP * 4);
-          const uint2 lo = *reinterpret_cast<const uint2*>(crow + sl.cro[kn % SL::KP][0]);
-          const uint2 hi = *reinterpret_cast<const uint2*>(crow + sl.cro[kn % SL::KP][1]);
-          const f16x8 cf = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          const float e = __builtin_amdgcn_exp2f(wa[16 * it + c.c16]);
 #pragma unroll
-          for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(sa[pt], cf, Y[pt][it]);
+          for (int pt = 0; pt < NPT; ++pt) Y[pt][it] *= e;
+        }
+#pragma unroll
+        for (int js = 0; js < K::NJS; ++js) {
+          const float4 w0 = *reinterpret_cast<const float4*>(wa + 2 * T + 32 * js + 8 * c.g);
+          const float4 w1 = *reinterpret_cast<const float4*>(wa + 2 * T + 32 * js + 8 * c.g + 4);
+          const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+          w16[js] = cvt_f16x8(wv);
         }
       }
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const float e = __builtin_amdgcn_exp2f(wa[16 * it + c.c16]);
-#pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) Y[pt][it] *= e;
+      if constexpr (K::WPH > 1) {
+        __syncthreads();  // B: every M block of the head visible to both of its waves
+      } else {
+        // one wave per head: it alone writes and reads its M blocks and token arrays (the shared
+        // C B^T blocks were published by the barrier before them), and a wave's LDS accesses
+        // complete in order, so only the compiler must keep them in program order
+        asm volatile("" ::: "memory");
       }
+      if (!c.active) continue;
+
+      // Raised wave priority from here to the y tile: the SIMD's other wave is then usually in
+      // its readout or bookkeeping, and the state update's matrix-core chain is the longer one
+      // (measured: fused scan -2.5%).
+      __builtin_amdgcn_s_setprio(1);
+      // with two sub-chunks per pass the B^T fragment offsets of the n tiles are formed here, per
+      // sub-chunk (held across the loop they would take 16 registers, more than are left; with one
+      // per pass they are held: measured faster there)
+      uint32_t bt0 = sl.btr0[0], bt1 = sl.btr0[1];
+      if constexpr (K::UNROLL2) asm volatile("" : "+v"(bt0), "+v"(bt1));
+      // state decay (the readout above used the entry state)
+      const float dec = __expf(acs_end);
+#pragma unroll
+      for (int nt = 0; nt < K::NNT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) S[nt][pt] *= dec;
+
 #pragma unroll
       for (int js = 0; js < K::NJS; ++js) {
-        const float4 w0 = *reinterpret_cast<const float4*>(wa + 2 * T + 32 * js + 8 * c.g);
-        const float4 w1 = *reinterpret_cast<const float4*>(wa + 2 * T + 32 * js + 8 * c.g + 4);
-        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        w16[js] = cvt_f16x8(wv);
+        f16x8 xh[NPT], xs[NPT];
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) {
+          const s16x8 r = tr8(xt + 32 * js * K::ROW_P, sl.xtr[pt][0], sl.xtr[pt][1]);
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = __uint_as_float((uint32_t)(uint16_t)r[e] << 16);
+          xh[pt] = cvt_f16x8(v);
+          xs[pt] = xh[pt] * w16[js];  // packed fp16 multiply
+        }
+        // intra-sub-chunk product: Y^T += x^T M^T over the K step's 32 tokens; in the block row
+        // on the diagonal, lanes g >= 2 hold tokens after the row block (zero)
+#pragma unroll
+        for (int it = 2 * js; it < NIT; ++it) {
+          f16x8 mf = *reinterpret_cast<const f16x8*>(mh + mblk(it, 2 * js) + sl.mrd);
+          if (it == 2 * js) mf = c.g >= 2 ? f16x8{} : mf;
+#pragma unroll
+          for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(xh[pt], mf, Y[pt][it]);
+        }
+        // state update: S^T += B^T (w x)
+#pragma unroll
+        for (int nt = 0; nt < K::NNT; ++nt) {
+          const char* bb = Bh + 32 * js * K::ROW_N + (nt / SL::NP) * (16 * 2 * SL::NP);
+          const f16x8 bt = __builtin_bit_cast(
+              f16x8, tr8(bb, bt0 ^ ((nt % SL::NP) << 5), bt1 ^ ((nt % SL::NP) << 5)));
+#pragma unroll
+          for (int pt = 0; pt < NPT; ++pt) S[nt][pt] = M::mma(bt, xs[pt], S[nt][pt]);
+        }
       }
-    }
-    if constexpr (K::WPH > 1) {
-      __syncthreads();  // B: every M block of the head visible to both of its waves
-    } else {
-      // one wave per head: it alone writes and reads its M blocks and token arrays (the shared
-      // C B^T blocks were published by the barrier before them), and a wave's LDS accesses
-      // complete in order, so only the compiler must keep them in program order
-      asm volatile("" ::: "memory");
-    }
-    if (!c.active) continue;
 
-    // Raised wave priority from here to the y tile: the SIMD's other wave is then usually in
-    // its readout or bookkeeping, and the state update's matrix-core chain is the longer one
-    // (measured: fused scan -2.5%).
-    __builtin_amdgcn_s_setprio(1);
-    // state decay (the readout above used the entry state)
-    const float dec = __expf(acs_end);
+      __builtin_amdgcn_s_setprio(0);
+      // y = Y, written over x in the stage (each lane's 8-byte pieces are its own and x is no
+      // longer needed); stored to memory after the next wait
 #pragma unroll
-    for (int nt = 0; nt < K::NNT; ++nt)
+      for (int it = 0; it < NIT; ++it) {
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) S[nt][pt] *= dec;
-
-#pragma unroll
-    for (int js = 0; js < K::NJS; ++js) {
-      f16x8 xh[NPT], xs[NPT];
-#pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) {
-        const s16x8 r = tr8(xt + 32 * js * K::ROW_P, sl.xtr[pt][0], sl.xtr[pt][1]);
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = __uint_as_float((uint32_t)(uint16_t)r[e] << 16);
-        xh[pt] = cvt_f16x8(v);
-        xs[pt] = xh[pt] * w16[js];  // packed fp16 multiply
+        for (int pt = 0; pt < NPT; ++pt) {
+          const f32x4 v = Y[pt][it];
+          *reinterpret_cast<uint2*>(st + xoff + 16 * it * K::ROW_P + sl.epi[pt]) =
+              make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
+        }
       }
-      // intra-sub-chunk product: Y^T += x^T M^T over the K step's 32 tokens; in the block row
-      // on the diagonal, lanes g >= 2 hold tokens after the row block (zero)
-#pragma unroll
-      for (int it = 2 * js; it < NIT; ++it) {
-        f16x8 mf = *reinterpret_cast<const f16x8*>(mh + mblk(it, 2 * js) + sl.mrd);
-        if (it == 2 * js) mf = c.g >= 2 ? f16x8{} : mf;
-#pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(xh[pt], mf, Y[pt][it]);
-      }
-      // state update: S^T += B^T (w x)
-#pragma unroll
-      for (int nt = 0; nt < K::NNT; ++nt) {
-        const char* bb = Bh + 32 * js * K::ROW_N + (nt / SL::NP) * (16 * 2 * SL::NP);
-        const f16x8 bt = __builtin_bit_cast(
-            f16x8, tr8(bb, sl.btr0[0] ^ ((nt % SL::NP) << 5), sl.btr0[1] ^ ((nt % SL::NP) << 5)));
-#pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) S[nt][pt] = M::mma(bt, xs[pt], S[nt][pt]);
-      }
+      ytok = s * T;
     }
-
-    __builtin_amdgcn_s_setprio(0);
-    // y = Y, written over x in the stage (each lane's 8-byte pieces are its own and x is no
-    // longer needed); stored to memory after the next wait
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-#pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) {
-        const f32x4 v = Y[pt][it];
-        *reinterpret_cast<uint2*>(st + xoff + 16 * it * K::ROW_P + sl.epi[pt]) =
-            make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
-      }
-    }
-    ytok = s * T;
   }
   if (ytok >= 0) {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's y tile writes have landed
