@@ -1029,8 +1029,13 @@ __device__ __forceinline__ void fused_scan(char* smem, Coord c, const u16* __res
 #pragma unroll
           for (int it = 0; it < NIT; ++it) {
             const char* crow = Ch + 16 * it * K::ROW_N + (kn / SL::KP) * (16 * SL::KP * 4);
-            const uint2 lo = *reinterpret_cast<const uint2*>(crow + sl.cro[kn % SL::KP][0]);
-            const uint2 hi = *reinterpret_cast<const uint2*>(crow + sl.cro[kn % SL::KP][1]);
+            uint32_t o0 = sl.cro[kn % SL::KP][0], o1 = sl.cro[kn % SL::KP][1];
+            // later row blocks read at offsets the compiler cannot relate to the first's: it
+            // would merge the row blocks' reads at one offset into one instruction whose halves
+            // then need register moves into the fragments
+            if (it > 0) asm volatile("" : "+v"(o0), "+v"(o1));
+            const uint2 lo = *reinterpret_cast<const uint2*>(crow + o0);
+            const uint2 hi = *reinterpret_cast<const uint2*>(crow + o1);
             const f16x8 cf = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
             for (int pt = 0; pt < NPT; ++pt) Y[pt][it] = M::mma(sa[pt], cf, Y[pt][it]);
