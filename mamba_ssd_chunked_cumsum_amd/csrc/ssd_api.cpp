@@ -444,6 +444,18 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   tp.io_dtype = SSD_DTYPE_F32;
   st = check_problem(&tp, kBackwardChunk);
   if (st != SSD_OK) return st;
+  // The reversed-time recurrences run over pad leading tokens of no input and no decay, so that
+  // their chunk boundaries fall on the forward recurrence's (Lp % Q == 0): the states both hold
+  // there give the decay gradient's exact value at the first token of every 256-token tile.
+  const int64_t pad = (kBackwardChunk - prob->seqlen % kBackwardChunk) % kBackwardChunk;
+  const int64_t Lp = prob->seqlen + pad;
+  ssd_problem pp = *prob, tpp = tp;
+  pp.seqlen = Lp;
+  pp.io_dtype = SSD_DTYPE_F32;
+  tpp.seqlen = Lp;
+  st = check_problem(&pp, kBackwardChunk);
+  if (st == SSD_OK) st = check_problem(&tpp, kBackwardChunk);
+  if (st != SSD_OK) return st;
   if (!x || !dt || !A || !B || !C || !D || !dy || !dx || !ddt || !dA || !dB || !dC || !dD)
     return SSD_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {x,  dt, A,  B,  C,  D,  initial_state, dy, dfinal,
@@ -473,11 +485,29 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   if (st != SSD_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
-  // workspace (fp32): see the steps below for what each holds
-  enum { X32, DY32, B32, C32, Y0, FIN0, XR, BR, CR, DTR, UR, G0, YT, H0T, CTR, YTR, DFT,
-         Q, XU, DYX, FT, PA, PD, ZD, NBUF };
-  const int64_t el[NBUF] = {nx, nx, nb, nb, nx, ns, nx, nb, nb, nd, nx, ns, nt, ns,
-                            nx, nt, ns, nd, nd, nd, Bt * H, 2 * Bt * H, 2 * Bt * H, H};
+  ssd_problem p32 = *prob;
+  p32.io_dtype = SSD_DTYPE_F32;
+  const Dims d = make_dims(&p32, kBackwardChunk);
+  Dims dup = make_dims(&pp, kBackwardChunk);  // the adjoint: reversed, padded, unit input weight
+  dup.unit_input = 1;
+  // the transposed problems' input is B (or C) per head: read in place, shared by each group
+  Dims dT = make_dims(&tp, kBackwardChunk);
+  dT.x_groups = (int)G;
+  Dims dTup = make_dims(&tpp, kBackwardChunk);
+  dTup.x_groups = (int)G;
+  dTup.unit_input = 1;
+  int64_t off1[5], off2[5];
+  const int64_t ws1 = unfused_workspace_bytes(d, off1), ws2 = unfused_workspace_bytes(dup, off2);
+  const int64_t ntile = (L + 255) / 256;
+  const int64_t nxp = Bt * Lp * H * P, nbp = Bt * Lp * G * N, ntp = Bt * Lp * H * N,
+                ndp = Bt * Lp * H;
+  // workspace (fp32): see the steps below for what each holds; WS1 and WS2 are the unfused
+  // workspaces of steps 1 and 2 (kept for their chunk-entry states), ANCH doubles
+  enum { X32, DY32, B32, C32, Y0, XR, BR, CR, DTR, UR, G0, YT, H0T, CTR, YTR, DFT,
+         Q, XU, DYX, PA, PD, ZD, WS1, WS2, ANCH, NBUF };
+  const int64_t el[NBUF] = {nx,  nx,  nb,  nb,  nx,  nxp, nbp, nbp, ndp,        nxp,
+                            ns,  nt,  ns,  nxp, ntp, ns,  nd,  nd,  nd,         2 * Bt * H,
+                            2 * Bt * H, H, (ws1 + 3) / 4, (ws2 + 3) / 4, 2 * Bt * H * ntile};
   int64_t off[NBUF], total = 0;
   for (int i = 0; i < NBUF; ++i) {
     off[i] = total;
@@ -489,63 +519,60 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   for (int i = 0; i < NBUF; ++i) w[i] = reinterpret_cast<float*>(static_cast<char*>(base) + off[i]);
 
   const int io = prob->io_dtype;
-  const int iBt = (int)Bt, iL = (int)L, iH = (int)H, iP = (int)P, iN = (int)N, iG = (int)G;
-  ssd_problem p32 = *prob;
-  p32.io_dtype = SSD_DTYPE_F32;
-  const Dims d = make_dims(&p32, kBackwardChunk);
-  Dims du = d;
-  du.unit_input = 1;
-  // the transposed problems' input is B (or C) per head: read in place, shared by each group
-  Dims dT = make_dims(&tp, kBackwardChunk);
-  dT.x_groups = (int)G;
-  Dims dTu = dT;
-  dTu.unit_input = 1;
+  const int iBt = (int)Bt, iL = (int)L, iH = (int)H, iP = (int)P, iN = (int)N, iG = (int)G,
+            ipad = (int)pad;
   Timer none;
   ssd_status r = SSD_OK;
   auto hip = [&](hipError_t e) {
     if (r == SSD_OK && e != hipSuccess) r = from_hip(e);
   };
-  auto fwd = [&](const ssd_problem* pp, const Dims& dd, const float* xx, const float* dtt,
-                 const float* bb, const float* cc, const float* h0, float* yy, float* fin) {
+  auto fwd = [&](const ssd_problem* pr, const Dims& dd, const float* xx, const float* dtt,
+                 const float* bb, const float* cc, const float* h0, float* yy, float* fin,
+                 float* ws) {
     if (r == SSD_OK)
-      r = run_unfused(pp, dd, ssd::kPrecFp32, xx, dtt, A, bb, cc, w[ZD], h0, yy, fin, hs, none,
-                      nullptr);
+      r = run_unfused(pr, dd, ssd::kPrecFp32, xx, dtt, A, bb, cc, w[ZD], h0, yy, fin, hs, none, ws);
   };
   // fp32 copies of the inputs and a zero skip term (the forwards below compute state terms only)
-  hip(ssd::launch_gather(io, x, w[X32], iBt, iL, iH, 1, iP, false, hs));
-  hip(ssd::launch_gather(io, dy, w[DY32], iBt, iL, iH, 1, iP, false, hs));
-  hip(ssd::launch_gather(io, B, w[B32], iBt, iL, iG, 1, iN, false, hs));
-  hip(ssd::launch_gather(io, C, w[C32], iBt, iL, iG, 1, iN, false, hs));
+  hip(ssd::launch_gather(io, x, w[X32], iBt, iL, iH, 1, iP, false, 0, hs));
+  hip(ssd::launch_gather(io, dy, w[DY32], iBt, iL, iH, 1, iP, false, 0, hs));
+  hip(ssd::launch_gather(io, B, w[B32], iBt, iL, iG, 1, iN, false, 0, hs));
+  hip(ssd::launch_gather(io, C, w[C32], iBt, iL, iG, 1, iN, false, 0, hs));
   if (r == SSD_OK) hip(hipMemsetAsync(w[ZD], 0, (size_t)H * 4, hs));
-  // 1. forward: the state part of y (ys = y - D x) and the final state
-  fwd(&p32, d, w[X32], dt, w[B32], w[C32], initial_state, w[Y0], dfinal ? w[FIN0] : nullptr);
+  // 1. forward: the state part of y (ys = y - D x); its chunk-entry states stay in WS1
+  fwd(&p32, d, w[X32], dt, w[B32], w[C32], initial_state, w[Y0], nullptr, w[WS1]);
   // 2. adjoint G_t = dy_t C_t^T + exp(dt_{t+1} A) G_{t+1} as a forward recurrence in reversed
-  //    time (decay of the next token, unit input weight) from dfinal; its readout with B gives
-  //    u_t = G_t B_t, its final state G_0
-  hip(ssd::launch_gather(ssd::kIoF32, w[DY32], w[XR], iBt, iL, iH, 1, iP, true, hs));
-  hip(ssd::launch_gather(ssd::kIoF32, w[C32], w[BR], iBt, iL, iG, 1, iN, true, hs));
-  hip(ssd::launch_gather(ssd::kIoF32, w[B32], w[CR], iBt, iL, iG, 1, iN, true, hs));
-  hip(ssd::launch_dt_shift_rev(dt, w[DTR], iBt, iL, iH, hs));
-  fwd(&p32, du, w[XR], w[DTR], w[BR], w[CR], dfinal, w[UR], dinitial_state ? w[G0] : nullptr);
+  //    time (decay of the next token, unit input weight) from dfinal, after pad tokens of zero
+  //    input and zero dt (the state passes them unchanged); its readout with B gives u_t = G_t B_t,
+  //    its final state G_0, its chunk-entry states (in WS2) G_t at the forward chunks' starts
+  hip(ssd::launch_gather(ssd::kIoF32, w[DY32], w[XR], iBt, iL, iH, 1, iP, true, ipad, hs));
+  hip(ssd::launch_gather(ssd::kIoF32, w[C32], w[BR], iBt, iL, iG, 1, iN, true, ipad, hs));
+  hip(ssd::launch_gather(ssd::kIoF32, w[B32], w[CR], iBt, iL, iG, 1, iN, true, ipad, hs));
+  hip(ssd::launch_dt_shift_rev(dt, w[DTR], iBt, iL, iH, ipad, hs));
+  fwd(&pp, dup, w[XR], w[DTR], w[BR], w[CR], dfinal, w[UR], w[G0], w[WS2]);
   // 3. dC: the transposed state S_t^T (state dim N, head dim P) read out with dy; its input is
   //    B of the head's group
   if (initial_state) hip(ssd::launch_transpose_state(initial_state, w[H0T], iBt, iH, iP, iN, hs));
-  fwd(&tp, dT, w[B32], dt, w[X32], w[DY32], initial_state ? w[H0T] : nullptr, w[YT], nullptr);
-  // 4. dB: the transposed adjoint G_t^T in reversed time, read out with x; its input is C of the
-  //    head's group in reversed time (step 2's BR)
-  hip(ssd::launch_gather(ssd::kIoF32, w[X32], w[CTR], iBt, iL, iH, 1, iP, true, hs));
+  fwd(&tp, dT, w[B32], dt, w[X32], w[DY32], initial_state ? w[H0T] : nullptr, w[YT], nullptr,
+      nullptr);
+  // 4. dB: the transposed adjoint G_t^T in reversed time (padded as step 2), read out with x; its
+  //    input is C of the head's group in reversed time (step 2's BR)
+  hip(ssd::launch_gather(ssd::kIoF32, w[X32], w[CTR], iBt, iL, iH, 1, iP, true, ipad, hs));
   if (dfinal) hip(ssd::launch_transpose_state(dfinal, w[DFT], iBt, iH, iP, iN, hs));
-  fwd(&tp, dTu, w[BR], w[DTR], w[XR], w[CTR], dfinal ? w[DFT] : nullptr, w[YTR], nullptr);
+  fwd(&tpp, dTup, w[BR], w[DTR], w[XR], w[CTR], dfinal ? w[DFT] : nullptr, w[YTR], nullptr,
+      nullptr);
   // 5. the gradients
   hip(ssd::launch_bwd_pointwise(io, x, dy, w[UR], w[Y0], dt, D, dx, w[Q], w[XU], w[DYX], iBt, iL,
-                                iH, iP, hs));
-  if (dfinal) hip(ssd::launch_state_dot(dfinal, w[FIN0], w[FT], iBt, iH, iP * iN, hs));
+                                iH, iP, ipad, hs));
   double* pa = reinterpret_cast<double*>(w[PA]);
   double* pd = reinterpret_cast<double*>(w[PD]);
-  hip(ssd::launch_bwd_scan(w[Q], w[XU], w[DYX], dt, A, dfinal ? w[FT] : nullptr, ddt, pa, pd, iBt,
-                           iL, iH, hs));
+  double* anch = reinterpret_cast<double*>(w[ANCH]);
+  const float* hf = reinterpret_cast<const float*>(reinterpret_cast<const char*>(w[WS1]) + off1[4]);
+  const float* hg = reinterpret_cast<const float*>(reinterpret_cast<const char*>(w[WS2]) + off2[4]);
+  hip(ssd::launch_anchor_dot(hf, hg, w[G0], anch, iBt, iH, iP * iN, (int)kBackwardChunk, d.nc,
+                             dup.nc, iL, (int)Lp, hs));
+  hip(ssd::launch_bwd_scan(w[Q], w[XU], w[DYX], dt, A, anch, ddt, pa, pd, iBt, iL, iH, hs));
   hip(ssd::launch_sum_batch(pa, pd, dA, dD, iBt, iH, hs));
-  hip(ssd::launch_group_sums(w[YTR], w[YT], dt, dB, dC, iBt, iL, iH, iG, iN, hs));
+  hip(ssd::launch_group_sums(w[YTR], w[YT], dt, dB, dC, iBt, iL, iH, iG, iN, ipad, hs));
   if (dinitial_state)
     hip(ssd::launch_scale_state(w[G0], dt, A, dinitial_state, iBt, iL, iH, iP * iN, hs));
   const hipError_t ef = hipFreeAsync(base, hs);

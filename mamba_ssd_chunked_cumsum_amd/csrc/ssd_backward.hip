@@ -12,14 +12,22 @@ namespace ssd {
 
 namespace {
 
-// One block per output row (b, t): K * E values, four per thread step (E is a multiple of 16).
+// One block per output row (b, t) of L + pad rows per batch entry: K * E values, four per thread
+// step (E is a multiple of 16); the first pad rows of each batch entry are zero.
 template <typename IO>
 __global__ __launch_bounds__(256) void k_gather(const IO* __restrict__ in, float* __restrict__ out,
-                                                int L, int K, int rep, int E, int rev) {
-  const int row = blockIdx.x, t = row % L, b = row / L;
+                                                int L, int K, int rep, int E, int rev, int pad) {
+  const int Lo = L + pad;
+  const int row = blockIdx.x, tp = row % Lo, b = row / Lo;
+  float* o = out + (int64_t)row * K * E;
+  if (tp < pad) {
+    for (int f = threadIdx.x * 4; f < K * E; f += 1024)
+      *reinterpret_cast<float4*>(o + f) = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int t = tp - pad;
   const int ts = rev ? L - 1 - t : t;
   const int Kin = K / rep;
-  float* o = out + (int64_t)row * K * E;
   const IO* src = in + ((int64_t)b * L + ts) * Kin * E;
   for (int f = threadIdx.x * 4; f < K * E; f += 1024) {
     const int k = f / E, e = f % E;
@@ -38,14 +46,15 @@ __global__ __launch_bounds__(256) void k_gather(const IO* __restrict__ in, float
 
 __global__ __launch_bounds__(256) void k_dt_shift_rev(const float* __restrict__ dt,
                                                       float* __restrict__ dtr, int Bt, int L,
-                                                      int H) {
-  const int64_t total = (int64_t)Bt * L * H;
+                                                      int H, int pad) {
+  const int Lo = L + pad;
+  const int64_t total = (int64_t)Bt * Lo * H;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * 256) {
     const int h = (int)(i % H);
-    const int t = (int)((i / H) % L);
-    const int b = (int)(i / ((int64_t)H * L));
-    dtr[i] = t == 0 ? 0.f : dt[((int64_t)b * L + (L - t)) * H + h];
+    const int t = (int)((i / H) % Lo) - pad;
+    const int b = (int)(i / ((int64_t)H * Lo));
+    dtr[i] = t <= 0 ? 0.f : dt[((int64_t)b * L + (L - t)) * H + h];
   }
 }
 
@@ -87,7 +96,7 @@ __global__ __launch_bounds__(256) void k_bwd_pointwise(
     const IO* __restrict__ x, const IO* __restrict__ dy, const float* __restrict__ ur,
     const float* __restrict__ ys, const float* __restrict__ dt, const float* __restrict__ D,
     float* __restrict__ dx, float* __restrict__ q, float* __restrict__ xu,
-    float* __restrict__ dyx, int Bt, int L, int H, int P) {
+    float* __restrict__ dyx, int Bt, int L, int H, int P, int pad) {
   // 16 lanes per (b, t, h) unit, four units per wave: lane k of a unit takes p = 4 k + 64 m
   // (16-byte accesses); headdim is a multiple of 16. Lanes of a unit past the last one compute on
   // a clamped unit and store nothing (all lanes take part in the reductions).
@@ -101,7 +110,8 @@ __global__ __launch_bounds__(256) void k_bwd_pointwise(
   const int b = (int)(unit / ((int64_t)H * L));
   const float dtv = dt[unit], dh = D[h];
   const int64_t row = unit * P;                                          // [b, t, h, :]
-  const int64_t rrow = (((int64_t)b * L + (L - 1 - t)) * H + h) * P;    // reversed time
+  // reversed time, pad leading rows per batch entry
+  const int64_t rrow = (((int64_t)b * (L + pad) + pad + (L - 1 - t)) * H + h) * P;
   float s_dyys = 0.f, s_xu = 0.f, s_dyx = 0.f;
   for (int p = 4 * sl; p < P; p += 64) {
     float xv[4], dyv[4];
@@ -136,30 +146,42 @@ __global__ __launch_bounds__(256) void k_bwd_pointwise(
   }
 }
 
-// One 256-thread block per (b, h).
-__global__ __launch_bounds__(256) void k_state_dot(const float* __restrict__ a,
-                                                   const float* __restrict__ c,
-                                                   float* __restrict__ out, int PN) {
-  __shared__ float part[4];
-  const int64_t base = (int64_t)blockIdx.x * PN;
-  float s = 0.f;
-  for (int i = threadIdx.x; i < PN; i += 256) s += a[base + i] * c[base + i];
-  s = wave_sum(s);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+// One 256-thread block per (b, h, tile k): the anchor <G_t, S_{t-1}> of the tile's first token
+// t = 256 k, in double, from the state that the forward recurrence has entering its chunk t / Q
+// (hf: [Bt, ncf, H, P, N]) and the adjoint G_t, which the adjoint recurrence, run in reversed
+// time over Lp = L + pad tokens (Lp % Q == 0), has entering its chunk (Lp - t) / Q (hg:
+// [Bt, ncg, H, P, N]) or, for t = 0, leaves as its final state (g0: [Bt, H, P, N]).
+__global__ __launch_bounds__(256) void k_anchor_dot(const float* __restrict__ hf,
+                                                    const float* __restrict__ hg,
+                                                    const float* __restrict__ g0,
+                                                    double* __restrict__ anch, int H, int PN,
+                                                    int Q, int ncf, int ncg, int Lp, int ntile) {
+  __shared__ double part[4];
+  const int k = blockIdx.x % ntile, bh = blockIdx.x / ntile, h = bh % H, b = bh / H;
+  const int t = 256 * k;
+  const float* S = hf + (((int64_t)b * ncf + t / Q) * H + h) * PN;
+  const float* G = k == 0 ? g0 + (int64_t)bh * PN
+                          : hg + (((int64_t)b * ncg + (Lp - t) / Q) * H + h) * PN;
+  double v = 0.0;
+  for (int i = threadIdx.x; i < PN; i += 256) v += (double)S[i] * (double)G[i];
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
   __syncthreads();
-  if (threadIdx.x == 0) out[blockIdx.x] = (part[0] + part[1]) + (part[2] + part[3]);
+  if (threadIdx.x == 0) anch[blockIdx.x] = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
-// One 256-thread block per (b, h): the sequence walked backwards in tiles of 256 tokens, each
-// tile's suffix sums by a block scan, plus the running total of the tiles after it. The sums run
-// in double: da_t sums up to L terms of mixed sign and dA sums dt_t da_t over batch and time, so
-// fp32 accumulation would lose digits that the gradients keep.
+// One 256-thread block per (b, h): tiles of 256 tokens, each tile's suffix sums by a block
+// scan. Every tile starts from the exact value at its first token t0,
+// da_t0 = exp(dt_t0 A) <G_t0, S_t0-1> (anch, per (b, h, tile)), and forms
+// da_t = da_t0 - sum_{t0 <= s < t} q_s: a sum over the rest of the sequence instead would carry
+// the terms' fp32 rounding, which grows with its length while da_t does not. The sums run in
+// double: dA sums dt_t da_t over batch and time.
 __global__ __launch_bounds__(256) void k_bwd_scan(const float* __restrict__ q,
                                                   const float* __restrict__ xu,
                                                   const float* __restrict__ dyx,
                                                   const float* __restrict__ dt,
                                                   const float* __restrict__ A,
-                                                  const float* __restrict__ fterm,
+                                                  const double* __restrict__ anch,
                                                   float* __restrict__ ddt, double* __restrict__ pa,
                                                   double* __restrict__ pd, int L, int H) {
   __shared__ double wtot[4];
@@ -167,7 +189,6 @@ __global__ __launch_bounds__(256) void k_bwd_scan(const float* __restrict__ q,
   const int bh = blockIdx.x, h = bh % H, b = bh / H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const double a = A[h];
-  double carry = fterm ? (double)fterm[bh] : 0.0;  // sum of q over the tokens after the tile
   double sa = 0.0, sd = 0.0;
   const int ntile = (L + 255) / 256;
   for (int k = ntile - 1; k >= 0; --k) {
@@ -182,14 +203,16 @@ __global__ __launch_bounds__(256) void k_bwd_scan(const float* __restrict__ q,
     __syncthreads();
     double before = 0.0;
     for (int w = 0; w < wave; ++w) before += wtot[w];
+    // before + incl = sum_{t <= s <= tile end} q_s; less the tile's total: -sum_{t0 <= s < t} q_s
     const double tile_total = (wtot[0] + wtot[1]) + (wtot[2] + wtot[3]);
-    const double da = carry + before + incl;
+    const double da0 = exp((double)dt[((int64_t)b * L + 256 * k) * H + h] * a) *
+                       anch[(int64_t)bh * ntile + k];
+    const double da = da0 - tile_total + before + incl;
     if (ok) {
       ddt[i] = (float)(a * da + (double)xu[i]);
       sa += (double)dt[i] * da;
       sd += (double)dyx[i];
     }
-    carry += tile_total;
     __syncthreads();  // wtot is rewritten by the next tile
   }
   sa = wave_sum(sa);
@@ -224,7 +247,8 @@ __global__ __launch_bounds__(256) void k_group_sums(const float* __restrict__ vb
                                                     const float* __restrict__ vc,
                                                     const float* __restrict__ dt,
                                                     float* __restrict__ dB, float* __restrict__ dC,
-                                                    int Bt, int L, int H, int G, int N) {
+                                                    int Bt, int L, int H, int G, int N,
+                                                    int pad) {
   const int64_t total = (int64_t)Bt * L * G * N;
   const int hpg = H / G;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
@@ -237,7 +261,7 @@ __global__ __launch_bounds__(256) void k_group_sums(const float* __restrict__ vb
     for (int k = 0; k < hpg; ++k) {
       const int h = g * hpg + k;
       const int64_t f = ((int64_t)b * L + t) * H + h;
-      const int64_t r = ((int64_t)b * L + (L - 1 - t)) * H + h;
+      const int64_t r = ((int64_t)b * (L + pad) + pad + (L - 1 - t)) * H + h;
       sb += dt[f] * vb[r * N + n];
       sc += vc[f * N + n];
     }
@@ -269,20 +293,21 @@ int grid_for(int64_t total) {
 }  // namespace
 
 hipError_t launch_gather(int io, const void* in, float* out, int Bt, int L, int K, int rep, int E,
-                         bool rev, hipStream_t s) {
-  const dim3 g((unsigned)Bt * (unsigned)L);
+                         bool rev, int pad, hipStream_t s) {
+  const dim3 g((unsigned)Bt * (unsigned)(L + pad));
   if (io == kIoBf16)
     hipLaunchKernelGGL(k_gather<u16>, g, dim3(256), 0, s, (const u16*)in, out, L, K, rep, E,
-                       (int)rev);
+                       (int)rev, pad);
   else
     hipLaunchKernelGGL(k_gather<float>, g, dim3(256), 0, s, (const float*)in, out, L, K, rep, E,
-                       (int)rev);
+                       (int)rev, pad);
   return hipGetLastError();
 }
 
-hipError_t launch_dt_shift_rev(const float* dt, float* dtr, int Bt, int L, int H, hipStream_t s) {
-  hipLaunchKernelGGL(k_dt_shift_rev, dim3(grid_for((int64_t)Bt * L * H)), dim3(256), 0, s, dt,
-                     dtr, Bt, L, H);
+hipError_t launch_dt_shift_rev(const float* dt, float* dtr, int Bt, int L, int H, int pad,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(k_dt_shift_rev, dim3(grid_for((int64_t)Bt * (L + pad) * H)), dim3(256), 0, s,
+                     dt, dtr, Bt, L, H, pad);
   return hipGetLastError();
 }
 
@@ -296,28 +321,31 @@ hipError_t launch_transpose_state(const float* in, float* out, int Bt, int H, in
 hipError_t launch_bwd_pointwise(int io, const void* x, const void* dy, const float* ur,
                                 const float* ys, const float* dt, const float* D, float* dx,
                                 float* q, float* xu, float* dyx, int Bt, int L, int H, int P,
-                                hipStream_t s) {
+                                int pad, hipStream_t s) {
   const int64_t units = (int64_t)Bt * L * H;
   const dim3 grid((unsigned)((units + 15) / 16));  // 16 units per block
   if (io == kIoBf16)
     hipLaunchKernelGGL(k_bwd_pointwise<u16>, grid, dim3(256), 0, s, (const u16*)x,
-                       (const u16*)dy, ur, ys, dt, D, dx, q, xu, dyx, Bt, L, H, P);
+                       (const u16*)dy, ur, ys, dt, D, dx, q, xu, dyx, Bt, L, H, P, pad);
   else
     hipLaunchKernelGGL(k_bwd_pointwise<float>, grid, dim3(256), 0, s, (const float*)x,
-                       (const float*)dy, ur, ys, dt, D, dx, q, xu, dyx, Bt, L, H, P);
+                       (const float*)dy, ur, ys, dt, D, dx, q, xu, dyx, Bt, L, H, P, pad);
   return hipGetLastError();
 }
 
-hipError_t launch_state_dot(const float* dfinal, const float* fin, float* fterm, int Bt, int H,
-                            int PN, hipStream_t s) {
-  hipLaunchKernelGGL(k_state_dot, dim3(Bt * H), dim3(256), 0, s, dfinal, fin, fterm, PN);
+hipError_t launch_anchor_dot(const float* hf, const float* hg, const float* g0, double* anch,
+                             int Bt, int H, int PN, int Q, int ncf, int ncg, int L, int Lp,
+                             hipStream_t s) {
+  const int ntile = (L + 255) / 256;
+  hipLaunchKernelGGL(k_anchor_dot, dim3((unsigned)(Bt * H * ntile)), dim3(256), 0, s, hf, hg, g0,
+                     anch, H, PN, Q, ncf, ncg, Lp, ntile);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_scan(const float* q, const float* xu, const float* dyx, const float* dt,
-                           const float* A, const float* fterm, float* ddt, double* pa, double* pd,
+                           const float* A, const double* anch, float* ddt, double* pa, double* pd,
                            int Bt, int L, int H, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_scan, dim3(Bt * H), dim3(256), 0, s, q, xu, dyx, dt, A, fterm, ddt, pa,
+  hipLaunchKernelGGL(k_bwd_scan, dim3(Bt * H), dim3(256), 0, s, q, xu, dyx, dt, A, anch, ddt, pa,
                      pd, L, H);
   return hipGetLastError();
 }
@@ -329,9 +357,10 @@ hipError_t launch_sum_batch(const double* pa, const double* pd, float* dA, float
 }
 
 hipError_t launch_group_sums(const float* vb, const float* vc, const float* dt, float* dB,
-                             float* dC, int Bt, int L, int H, int G, int N, hipStream_t s) {
+                             float* dC, int Bt, int L, int H, int G, int N, int pad,
+                             hipStream_t s) {
   hipLaunchKernelGGL(k_group_sums, dim3(grid_for((int64_t)Bt * L * G * N)), dim3(256), 0, s, vb,
-                     vc, dt, dB, dC, Bt, L, H, G, N);
+                     vc, dt, dB, dC, Bt, L, H, G, N, pad);
   return hipGetLastError();
 }
 

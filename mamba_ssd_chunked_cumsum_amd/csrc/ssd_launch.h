@@ -91,36 +91,43 @@ constexpr int64_t kScratchBytes = int64_t(64) << 20;
 hipError_t scratch_address(void** out);
 
 // backward helpers (ssd_backward.hip); all outputs fp32, layouts row-major.
-// out[b, t, k, e] = in[b, rev ? L - 1 - t : t, k / rep, e]   (in: [Bt, L, K / rep, E], io dtype)
+// out[b, pad + t, k, e] = in[b, rev ? L - 1 - t : t, k / rep, e], out[b, 0 .. pad - 1] = 0
+// (in: [Bt, L, K / rep, E], io dtype; out: [Bt, L + pad, K, E])
 hipError_t launch_gather(int io, const void* in, float* out, int Bt, int L, int K, int rep, int E,
-                         bool rev, hipStream_t s);
-// dtr[b, t, h] = t == 0 ? 0 : dt[b, L - t, h]
-hipError_t launch_dt_shift_rev(const float* dt, float* dtr, int Bt, int L, int H, hipStream_t s);
+                         bool rev, int pad, hipStream_t s);
+// dtr[b, pad + t, h] = t == 0 ? 0 : dt[b, L - t, h], dtr[b, 0 .. pad - 1] = 0
+hipError_t launch_dt_shift_rev(const float* dt, float* dtr, int Bt, int L, int H, int pad,
+                               hipStream_t s);
 // out[b, h, n, p] = in[b, h, p, n]
 hipError_t launch_transpose_state(const float* in, float* out, int Bt, int H, int P, int N,
                                   hipStream_t s);
 // per (b, t, h): dx = D dy + dt u; q = dy . ys - dt x . u; xu = x . u; dyx = dy . x, where
-// u = ur[b, L - 1 - t, h, :] (the adjoint readout, stored in reversed time)
+// u = ur[b, pad + L - 1 - t, h, :] (the adjoint readout, stored in reversed time after pad rows)
 hipError_t launch_bwd_pointwise(int io, const void* x, const void* dy, const float* ur,
                                 const float* ys, const float* dt, const float* D, float* dx,
                                 float* q, float* xu, float* dyx, int Bt, int L, int H, int P,
-                                hipStream_t s);
-// fterm[b, h] = <dfinal[b, h], fin[b, h]> (0 when dfinal is null)
-hipError_t launch_state_dot(const float* dfinal, const float* fin, float* fterm, int Bt, int H,
-                            int PN, hipStream_t s);
-// per (b, h): da_t = sum_{s >= t} q_s + fterm; ddt = A da + xu; per-(b, h) partial sums of
-// dt da (for dA) and of dyx (for dD)
-// (sums in double)
+                                int pad, hipStream_t s);
+// anch[b, h, k] = <G_t, S_{t-1}> at t = 256 k, k < ceil(L / 256), from the forward recurrence's
+// chunk-entry states hf [Bt, ncf, H, P, N] (chunk t / Q) and the reversed-time adjoint's hg
+// [Bt, ncg, H, P, N] over Lp tokens (chunk (Lp - t) / Q; Lp = L + pad, Lp % Q == 0), or its final
+// state g0 [Bt, H, P, N] for t = 0; double
+hipError_t launch_anchor_dot(const float* hf, const float* hg, const float* g0, double* anch,
+                             int Bt, int H, int PN, int Q, int ncf, int ncg, int L, int Lp,
+                             hipStream_t s);
+// per (b, h): da_t = exp(dt_t0 A) anch[b, h, k] - sum_{t0 <= s < t} q_s over each 256-token tile k
+// (first token t0); ddt = A da + xu; per-(b, h) partial sums of dt da (for dA) and of dyx (for
+// dD) (sums in double)
 hipError_t launch_bwd_scan(const float* q, const float* xu, const float* dyx, const float* dt,
-                           const float* A, const float* fterm, float* ddt, double* pa, double* pd,
+                           const float* A, const double* anch, float* ddt, double* pa, double* pd,
                            int Bt, int L, int H, hipStream_t s);
 // dA[h] = sum_b pa[b, h]; dD[h] = sum_b pd[b, h]
 hipError_t launch_sum_batch(const double* pa, const double* pd, float* dA, float* dD, int Bt,
                             int H, hipStream_t s);
-// dB[b, t, g, n] = sum_{h in g} dt[b, t, h] vb[b, L - 1 - t, h, n];
+// dB[b, t, g, n] = sum_{h in g} dt[b, t, h] vb[b, pad + L - 1 - t, h, n];
 // dC[b, t, g, n] = sum_{h in g} vc[b, t, h, n]
 hipError_t launch_group_sums(const float* vb, const float* vc, const float* dt, float* dB,
-                             float* dC, int Bt, int L, int H, int G, int N, hipStream_t s);
+                             float* dC, int Bt, int L, int H, int G, int N, int pad,
+                             hipStream_t s);
 // dh0[b, h] = exp(dt[b, 0, h] A[h]) g0[b, h]
 hipError_t launch_scale_state(const float* g0, const float* dt, const float* A, float* dh0,
                               int Bt, int L, int H, int PN, hipStream_t s);

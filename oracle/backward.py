@@ -26,8 +26,10 @@ def ssd_backward(x, dt, A, B, C, D, dy, initial_state=None, dfinal=None):
     """Gradients of sum(dy * y) + sum(dfinal * final_state) with respect to every input.
 
     Shapes as in ``ssd_recurrence``; dy [Bt, L, H, P], dfinal [Bt, H, P, N] or None.
-    Returns a dict of float64 arrays: dx, ddt, dA, dB, dC, dD, dinitial_state, and dlog_decay
-    [Bt, L, H] = dL/d(dt_t A), the per-token terms that dA and ddt are built from.
+    Returns a dict of float64 arrays: dx, ddt, dA, dB, dC, dD, dinitial_state, dlog_decay
+    [Bt, L, H] = dL/d(dt_t A), the per-token terms that dA and ddt are built from, and
+    dlog_decay_abs [Bt, L, H], the sum of the absolute values of the products that dlog_decay
+    sums (a scale for rounding-error bounds; no gradient).
     """
     x, dt, A, B, C, D, dy = (_as64(v) for v in (x, dt, A, B, C, D, dy))
     Bt, L, H, P = x.shape
@@ -47,6 +49,7 @@ def ssd_backward(x, dt, A, B, C, D, dy, initial_state=None, dfinal=None):
     dx = np.empty_like(x)
     ddt = np.empty_like(dt)
     dlog = np.empty_like(dt)
+    dlog_abs = np.empty_like(dt)
     dA = np.zeros(H)
     dBh = np.zeros((Bt, L, H, N))
     dCh = np.zeros((Bt, L, H, N))
@@ -62,6 +65,8 @@ def ssd_backward(x, dt, A, B, C, D, dy, initial_state=None, dfinal=None):
         dCh[:, t] = (np.swapaxes(states[t + 1], 2, 3) @ dy[:, t][..., None])[..., 0]
         dloga = np.einsum("bhpn,bhpn->bh", Gs, a[:, t, :, None, None] * states[t])
         dlog[:, t] = dloga
+        dlog_abs[:, t] = np.einsum("bhpn,bhpn->bh", np.abs(Gs),
+                                   a[:, t, :, None, None] * np.abs(states[t]))
         ddt[:, t] = A[None, :] * dloga + np.einsum("bhp,bhp->bh", x[:, t], GB)
         dA += np.sum(dt[:, t] * dloga, axis=0)
         Gs = a[:, t, :, None, None] * Gs                            # into dL/dS_{t-1}
@@ -71,4 +76,5 @@ def ssd_backward(x, dt, A, B, C, D, dy, initial_state=None, dfinal=None):
         dB[:, :, grp[h]] += dBh[:, :, h]
         dC[:, :, grp[h]] += dCh[:, :, h]
     dD = np.einsum("blhp,blhp->h", dy, x)
-    return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD, dinitial_state=Gs, dlog_decay=dlog)
+    return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD, dinitial_state=Gs, dlog_decay=dlog,
+                dlog_decay_abs=dlog_abs)

@@ -6,24 +6,26 @@ gradient are held to max |g - r| <= TOL * max|r| over the tensor: fp32 rounding 
 operation) accumulated over a few hundred terms of mixed sign leaves a few 1e-6; TOL = 1e-4 keeps
 a margin.
 
-The decay gradients are held to a bound derived from how the GPU forms them. It sums, in double,
-the per-token terms q_s = dy_s . ys_s - dt_s x_s . u_s (ys the state part of y, u = G B, both
-outputs of fp32 recurrences, dotted over headdim in fp32) from the sequence end back to t, plus
-<dfinal, final state>; that suffix sum is dlog_t, ddt_t = A dlog_t + x_t . u_t, and
-dA = sum over batch and time of dt_t dlog_t. If every fp32 product entering those dots carries a
-relative error of at most EPS, the errors are bounded by
+The decay gradients are held to a bound derived from how the GPU forms them. dlog_t (the
+gradient with respect to dt_t A) is <G_t, exp(dt_t A) S_{t-1}>, and the difference of two
+tokens' values is a sum of per-token terms q_s = dy_s . ys_s - dt_s x_s . u_s (ys the state part
+of y, u = G B, both outputs of fp32 recurrences, dotted over headdim in fp32). The GPU forms
+dlog at the first token t0 of every 256-token tile from the product itself (in double, from the
+fp32 states the forward and adjoint recurrences hold there) and within the tile as
+dlog_t0 - sum_{t0 <= s < t} q_s (in double). Then ddt_t = A dlog_t + x_t . u_t and
+dA = sum over batch and time of dt_t dlog_t. If every fp32 quantity entering those sums carries
+a relative error of at most EPS,
 
     |ddt_t error| <= EPS (|A| R_t + X_t) + 2^-24 |ddt_t|,   |dA error| <= EPS sum_t dt_t R_t,
 
-with R_t = sum_{s >= t} (sum_p |dy_sp ys_sp| + |dt_s x_sp u_sp|) + sum |dfinal * final| and
-X_t = sum_p |x_tp u_tp|, the absolute values of the terms summed (computed here from the oracle's
-y, final state and dx = D dy + dt u). EPS = 2^-24 (Q + N + P) with Q = 64, the backward's own
-chunk length, is the rounding bound of a sum of that many fp32 terms (a recurrence output sums at
-most a chunk of Q tokens and a state row of N entries, and the dot over headdim adds P): it
-covers the fp32 work between the inputs and the double sums. The tests print each element's
-error as a multiple of 2^-24 (|A| R_t + X_t) and each head's dA error relative to its own |dA|:
-the suffix sums R_t grow with the tokens after t while dlog_t does not (the terms telescope), so
-relative errors are largest on heads whose dA cancels.
+with R_t = sum_{t0 <= s < t} (sum_p |dy_sp ys_sp| + |dt_s x_sp u_sp|) + dlog_abs_t0 (the
+absolute values of the products dlog_t0 sums) and X_t = sum_p |x_tp u_tp| (computed here from
+the oracle's y, dx = D dy + dt u and dlog_decay_abs). EPS = 2^-24 (Q + N + P) with Q = 64, the
+backward's own chunk length, is the rounding bound of a sum of that many fp32 terms (a
+recurrence output sums at most a chunk of Q tokens and a state row of N entries, and the dot
+over headdim adds P). The tests print each element's error as a multiple of
+2^-24 (|A| R_t + X_t) and each head's dA error relative to its own |dA| (large only on heads
+whose dA cancels to a small fraction of its terms).
 """
 
 import numpy as np
@@ -94,19 +96,26 @@ def _dev(a, io, io_tensor):
     return t.to(torch.bfloat16) if (io_tensor and io == "bf16") else t
 
 
-def _decay_scales(inp, dy, dfinal, ref):
+TILE = 256  # the GPU's decay-gradient tiles
+
+
+def _decay_scales(inp, dy, ref):
     """R [Bt, L, H] and X [Bt, L, H] of the decay-gradient bound, from oracle quantities."""
-    y, fin = ssd_recurrence(**inp)
+    y, _ = ssd_recurrence(**inp)
     x = inp["x"].astype(np.float64)
+    dt = inp["dt"].astype(np.float64)
     dy64 = dy.astype(np.float64)
     D = inp["D"].astype(np.float64)[None, None, :, None]
     ys = y - D * x
     dtu = ref["dx"] - D * dy64                                   # dt_t u_t
     q_abs = np.sum(np.abs(dy64 * ys), axis=3) + np.sum(np.abs(x * dtu), axis=3)
-    R = np.flip(np.cumsum(np.flip(q_abs, axis=1), axis=1), axis=1)
-    if dfinal is not None:
-        R = R + np.sum(np.abs(dfinal.astype(np.float64) * fin), axis=(2, 3))[:, None, :]
-    X = np.sum(np.abs(x * dtu), axis=3) / inp["dt"].astype(np.float64)
+    X = np.sum(np.abs(x * dtu), axis=3) / dt
+    R = np.empty_like(q_abs)
+    L = q_abs.shape[1]
+    for t0 in range(0, L, TILE):  # exclusive prefix sums within the tile, plus its anchor's scale
+        seg = q_abs[:, t0:t0 + TILE]
+        R[:, t0:t0 + TILE] = (np.cumsum(seg, axis=1) - seg
+                              + ref["dlog_decay_abs"][:, t0][:, None, :])
     return R, X
 
 
@@ -142,13 +151,13 @@ def test_backward_matches_oracle(case):
     torch.cuda.synchronize()
     ref = oracle_backward(**inp, dy=dy, dfinal=dfinal)
     ref.pop("dlog_decay")
-    got = {k: g[k].cpu().numpy().astype(np.float64) for k in ref}
+    got = {k: g[k].cpu().numpy().astype(np.float64) for k in ref if k != "dlog_decay_abs"}
     for k, gk in got.items():
         assert np.all(np.isfinite(gk)), k
-    R, X = _decay_scales(inp, dy, dfinal, ref)
+    R, X = _decay_scales(inp, dy, ref)
     _check_decay(got["ddt"], got["dA"], ref, inp, R, X, _eps(N, P), _case_id(case))
     for k, r in ref.items():
-        if k in ("ddt", "dA"):
+        if k in ("ddt", "dA", "dlog_decay_abs"):
             continue
         gk = got[k]
         err = float(np.max(np.abs(gk - r)))
@@ -205,7 +214,7 @@ def test_backward_full_size_sampled_heads():
         sub = dict(x=inp["x"][:, :, h:h + 1], dt=inp["dt"][:, :, h:h + 1], A=inp["A"][h:h + 1],
                    B=inp["B"], C=inp["C"], D=inp["D"][h:h + 1], initial_state=None)
         ref = oracle_backward(**sub, dy=dy[:, :, h:h + 1], dfinal=dfinal[:, h:h + 1])
-        R, X = _decay_scales(sub, dy[:, :, h:h + 1], dfinal[:, h:h + 1], ref)
+        R, X = _decay_scales(sub, dy[:, :, h:h + 1], ref)
         _check_decay(got["ddt"][:, :, h:h + 1], got["dA"][h:h + 1], ref, sub, R, X,
                      _eps(shape.dstate, shape.headdim),
                      f"full size, head {h}")

@@ -93,3 +93,21 @@ def test_backward_closed_form_no_decay():
     K = np.tril(Cm @ Bm.T)                              # K[t, s] = C_t . B_s for s <= t
     dx = inp["D"][0] * dy[0, :, 0] + dt[:, None] * (K.T @ dy[0, :, 0])
     np.testing.assert_allclose(g["dx"][0, :, 0], dx, rtol=1e-12, atol=1e-12)
+
+
+def test_dlog_decay_abs_bounds_the_decay_gradient():
+    """dlog_decay_abs_t = sum |G_t a_t S_{t-1}| bounds |dlog_t| = |<G_t, a_t S_{t-1}>|, and equals it
+    when every product is >= 0 (nonnegative inputs and initial state)."""
+    rng = np.random.default_rng(11)
+    Bt, L, H, P, N, G = 1, 12, 2, 3, 4, 1
+    inp = dict(x=rng.standard_normal((Bt, L, H, P)), dt=rng.uniform(0.1, 0.5, (Bt, L, H)),
+               A=-rng.uniform(0.5, 2.0, H), B=rng.standard_normal((Bt, L, G, N)),
+               C=rng.standard_normal((Bt, L, G, N)), D=np.ones(H),
+               initial_state=rng.standard_normal((Bt, H, P, N)))
+    dy = rng.standard_normal((Bt, L, H, P))
+    g = ssd_backward(**inp, dy=dy)
+    assert np.all(g["dlog_decay_abs"] >= np.abs(g["dlog_decay"]) * (1 - 1e-12))
+    assert np.any(g["dlog_decay_abs"] > 1.01 * np.abs(g["dlog_decay"]))  # cancellation occurs
+    pos = {k: (np.abs(v) if k in ("x", "B", "C", "initial_state") else v) for k, v in inp.items()}
+    gp = ssd_backward(**pos, dy=np.abs(dy))
+    assert np.allclose(gp["dlog_decay_abs"], gp["dlog_decay"], rtol=1e-12)
