@@ -57,6 +57,8 @@ CASES = [
     (2, 130, 8, 64, 64, 2, 64, "bf16", False, True),
     (1, 1, 2, 16, 16, 1, 16, "f32", True, True),       # a single token
     (1, 1024, 4, 64, 128, 1, 256, "bf16", True, True),  # longer runs of chunks
+    (1, 600, 2, 32, 64, 1, 64, "f32", True, True),      # several 256-token tiles, ragged end
+    (2, 520, 4, 64, 128, 2, 64, "bf16", False, True),   # ... with groups, no initial state
 ]
 
 
