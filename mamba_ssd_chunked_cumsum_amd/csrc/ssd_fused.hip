@@ -43,7 +43,10 @@
 // is applied by choosing which global piece each lane fetches. B and C are converted to fp16 in
 // place after arrival; x stays raw bf16 (the skip term D x uses it exactly) and is converted while
 // its fragments are built. Fragments whose K index is the token are read with the gfx950
-// transposing LDS load (ds_read_b64_tr_b16).
+// transposing LDS load (ds_read_b64_tr_b16). Every fragment access reads at a lane offset
+// computed once per kernel; where the registers allow, the fused scan's loop runs two
+// sub-chunks per pass, one per stage buffer, so each LDS address is that offset plus an
+// immediate.
 //
 // Matrix-core operand precision: x, B, C enter as exact fp16 copies of the bf16 inputs (inputs
 // are assumed to lie in fp16's range); the decay-masked C B^T block, the carried state (for the
