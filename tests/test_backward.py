@@ -143,8 +143,27 @@ def _check_decay(got_ddt, got_dA, ref, inp, R, X, eps, label):
 
 @pytest.mark.parametrize("case", CASES, ids=_case_id)
 def test_backward_matches_oracle(case):
+    _check_case(case, np.random.default_rng(100 + case[1] + 7 * case[2] + case[4]))
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(500 + seed)
+    G = int(rng.integers(1, 3))
+    return (int(rng.integers(1, 3)), int(rng.integers(1, 700)), G * int(rng.integers(1, 4)),
+            int(rng.choice([16, 32, 64, 128])), int(rng.choice([16, 32, 64, 128])), G,
+            int(rng.choice([16, 32, 64, 128, 256])), str(rng.choice(["f32", "bf16"])),
+            bool(rng.random() < 0.5), bool(rng.random() < 0.5))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_backward_random_problems(seed):
+    """Seeded random shapes (lengths across several 256-token tiles and none, groups, io,
+    initial state and final-state gradient present or not) to the same bars."""
+    _check_case(_random_case(seed), np.random.default_rng(seed))
+
+
+def _check_case(case, rng):
     Bt, L, H, P, N, G, Q, io, h0, df = case
-    rng = np.random.default_rng(100 + L + 7 * H + N)
     inp, dy, dfinal = _inputs(rng, Bt, L, H, P, N, G, io, h0, df)
     note(f"backward {_case_id(case)}")
     d = {k: _dev(v, io, k in ("x", "B", "C")) for k, v in inp.items()}
