@@ -254,15 +254,19 @@ ssd_status ssd_step(const ssd_problem* prob, const void* x, const float* dt, con
  *     dinitial_state = exp(dt_0 A) G_0.
  * It runs the chunked forward machinery four times in fp32 (the state part of y and the final
  * state; the adjoint G in reversed time; the transposed state for dC; the transposed adjoint for
- * dB) plus elementwise and reduction kernels. Inputs as for ssd_forward (io dtype for x, B, C and
+ * dB) plus elementwise and reduction kernels; dlog is formed from the product of the forward's
+ * and the adjoint's states at the first token of every 256-token tile and from per-token terms
+ * within the tile (sums in double). Inputs as for ssd_forward (io dtype for x, B, C and
  * dy; initial_state and dfinal [batch, nheads, headdim, dstate] f32, both nullable). Outputs, all
  * f32 and overwritten (not accumulated into): dx [batch, seqlen, nheads, headdim], ddt [batch,
  * seqlen, nheads], dA and dD [nheads], dB and dC [batch, seqlen, ngroups, dstate],
  * dinitial_state [batch, nheads, headdim, dstate] (nullable: not computed). No output may overlap
  * an input or another output; every pointer 16-byte aligned. Shapes as for the forward, and the
  * transposed problem (headdim and dstate swapped, one group per head) must pass the same checks.
- * Workspace: about 6 fp32 copies of x-sized tensors and 4 of [batch, seqlen, nheads, dstate],
- * allocated and released stream-ordered on `stream`. Errors as for ssd_forward. */
+ * Workspace: about 6 fp32 copies of x-sized tensors, 4 of [batch, seqlen, nheads, dstate] and
+ * the chunk states of two recurrences (4 fp32 tensors of [batch, ceil(seqlen / 64), nheads,
+ * headdim, dstate]), allocated and released stream-ordered on `stream`. Errors as for
+ * ssd_forward. */
 ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt, const float* A,
                         const void* B, const void* C, const float* D, int64_t chunk_size,
                         const float* initial_state, const void* dy, const float* dfinal,
