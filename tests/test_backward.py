@@ -247,3 +247,21 @@ def test_backward_full_size_sampled_heads():
             print(f"head {h} {k}: max|g - r| = {err:.3e}, scale = {scale:.3e}, "
                   f"ratio {err / max(scale, 1e-30):.2e} (bar {TOL})")
             assert err <= TOL * max(scale, 1e-30), f"head {h} {k}: {err:.3e} vs {scale:.3e}"
+
+
+def test_backward_deterministic():
+    """Two calls on the same inputs give bitwise equal gradients (no atomics, fixed reduction
+    orders)."""
+    rng = np.random.default_rng(9)
+    Bt, L, H, P, N, G, Q = 2, 700, 4, 64, 128, 2, 64
+    inp, dy, dfinal = _inputs(rng, Bt, L, H, P, N, G, "bf16", True, True)
+    d = {k: _dev(v, "bf16", k in ("x", "B", "C")) for k, v in inp.items()}
+    note("backward determinism")
+    args = (d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], _dev(dy, "bf16", True), Q,
+            d["initial_state"], _dev(dfinal, "bf16", False))
+    ga = ssd.backward(*args)
+    gb = ssd.backward(*args)
+    torch.cuda.synchronize()
+    for k in ga:
+        if ga[k] is not None:
+            assert torch.equal(ga[k], gb[k]), k
