@@ -143,19 +143,29 @@ SQ_PASSES = {
            "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_LDS SQ_INSTS_VALU_MFMA_MOPS_F16 "
            "GRBM_GUI_ACTIVE",
 }
-_PROF_RUN = "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-backward --no-workloads"
-PROFILE_COMMANDS = [
-    "python3 bench.py --steps 20 --warmup 3 > DIR/bench.json",
-    "rocprofv3 --kernel-trace --stats -d DIR/prof_kt -o kt --output-format csv -- "
-    "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-backward --no-workloads",
-    "rocprofv3 --pmc FETCH_SIZE -d DIR/prof_fetch -o fetch --output-format csv -- "
-    f"{_PROF_RUN} --copy-calibration",
-    "rocprofv3 --pmc WRITE_SIZE -d DIR/prof_write -o write --output-format csv -- "
-    f"{_PROF_RUN} --copy-calibration",
-    *[f"rocprofv3 --pmc {c} -d DIR/prof_{n} -o {n} --output-format csv -- {_PROF_RUN}"
-      for n, c in SQ_PASSES.items()],
-    "python3 bench.py --summarize-profiles DIR",
-]
+
+
+def profile_commands(cfg: int = 2) -> list:
+    """The commands whose output --summarize-profiles reads, for workload index cfg (the headline
+    workload's commands carry no --config)."""
+    c = "" if cfg == 2 else f" --config {cfg}"
+    run = ("python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-backward --no-workloads"
+           + c)
+    return [
+        f"python3 bench.py --steps 20 --warmup 3{c} > DIR/bench.json",
+        "rocprofv3 --kernel-trace --stats -d DIR/prof_kt -o kt --output-format csv -- "
+        f"python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-backward --no-workloads{c}",
+        "rocprofv3 --pmc FETCH_SIZE -d DIR/prof_fetch -o fetch --output-format csv -- "
+        f"{run} --copy-calibration",
+        "rocprofv3 --pmc WRITE_SIZE -d DIR/prof_write -o write --output-format csv -- "
+        f"{run} --copy-calibration",
+        *[f"rocprofv3 --pmc {q} -d DIR/prof_{n} -o {n} --output-format csv -- {run}"
+          for n, q in SQ_PASSES.items()],
+        "python3 bench.py --summarize-profiles DIR",
+    ]
+
+
+PROFILE_COMMANDS = profile_commands()
 
 
 def _short_kernel(name: str):
@@ -192,6 +202,9 @@ def summarize_profiles(d: str) -> None:
     with open(os.path.join(d, "bench.json")) as f:
         bench = json.loads(f.read().strip().splitlines()[-1])
     workload = bench["config"]["workload"]
+    from mamba_ssd_chunked_cumsum_amd import synth
+    cfg = next(i for i, sh in enumerate(synth.CONFIGS) if sh.name == workload)
+    commands = profile_commands(cfg)
     stats = {}
     for r in _csv_rows(os.path.join(d, "prof_kt", "*kernel_stats.csv")):
         k = _short_kernel(r["Name"])
@@ -221,7 +234,7 @@ def summarize_profiles(d: str) -> None:
         f"kernel sources hash {src}; run {json.dumps(bench.get('run', {}))}",
         "",
         "commands (DIR = a scratch output folder; the last runs on any host):",
-        *["  " + c for c in PROFILE_COMMANDS],
+        *["  " + c for c in commands],
         "",
         f"copy calibration (1 GiB copy): FETCH_SIZE {cf:.0f} KiB -> x{fetch_scale:.3f}, "
         f"WRITE_SIZE {cw:.0f} KiB -> x{write_scale:.3f}",
@@ -260,7 +273,7 @@ def summarize_profiles(d: str) -> None:
     with open(os.path.join(ROOT, "profiles", f"forward_{workload}.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     rec = {"workload": workload, "source_hash": src, "fetch_scale": fetch_scale,
-           "write_scale": write_scale, "commands": PROFILE_COMMANDS,
+           "write_scale": write_scale, "commands": commands,
            "kernels": {_KERNEL_OBJ_REV.get(k, k): {"fetch_bytes": fb, "write_bytes": wb}
                        for k, (fb, wb) in traffic.items()}}
     with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as f:
