@@ -544,9 +544,10 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   //    time (decay of the next token, unit input weight) from dfinal, after pad tokens of zero
   //    input and zero dt (the state passes them unchanged); its readout with B gives u_t = G_t B_t,
   //    its final state G_0, its chunk-entry states (in WS2) G_t at the forward chunks' starts
-  hip(ssd::launch_gather(ssd::kIoF32, w[DY32], w[XR], iBt, iL, iH, 1, iP, true, ipad, hs));
-  hip(ssd::launch_gather(ssd::kIoF32, w[C32], w[BR], iBt, iL, iG, 1, iN, true, ipad, hs));
-  hip(ssd::launch_gather(ssd::kIoF32, w[B32], w[CR], iBt, iL, iG, 1, iN, true, ipad, hs));
+  // (reversed copies straight from the caller's tensors: half the bytes read for bf16 io)
+  hip(ssd::launch_gather(io, dy, w[XR], iBt, iL, iH, 1, iP, true, ipad, hs));
+  hip(ssd::launch_gather(io, C, w[BR], iBt, iL, iG, 1, iN, true, ipad, hs));
+  hip(ssd::launch_gather(io, B, w[CR], iBt, iL, iG, 1, iN, true, ipad, hs));
   hip(ssd::launch_dt_shift_rev(dt, w[DTR], iBt, iL, iH, ipad, hs));
   fwd(&pp, dup, w[XR], w[DTR], w[BR], w[CR], dfinal, w[UR], w[G0], w[WS2]);
   // 3. dC: the transposed state S_t^T (state dim N, head dim P) read out with dy; its input is
@@ -556,7 +557,7 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
       nullptr);
   // 4. dB: the transposed adjoint G_t^T in reversed time (padded as step 2), read out with x; its
   //    input is C of the head's group in reversed time (step 2's BR)
-  hip(ssd::launch_gather(ssd::kIoF32, w[X32], w[CTR], iBt, iL, iH, 1, iP, true, ipad, hs));
+  hip(ssd::launch_gather(io, x, w[CTR], iBt, iL, iH, 1, iP, true, ipad, hs));
   if (dfinal) hip(ssd::launch_transpose_state(dfinal, w[DFT], iBt, iH, iP, iN, hs));
   fwd(&tpp, dTup, w[BR], w[DTR], w[XR], w[CTR], dfinal ? w[DFT] : nullptr, w[YTR], nullptr,
       nullptr);
