@@ -207,6 +207,30 @@ ssd_status run_unfused(const ssd_problem* prob, const Dims& d, int prec, const v
   return from_hip(ef);
 }
 
+// The unfused path's S1, S2 and S5 only, with the entering state of every chunk read from h_in
+// (the backward's transposed recurrences read, transposed, those of the untransposed ones: see
+// Dims::hin_transposed); fp32 arithmetic.
+ssd_status run_unfused_scan(const ssd_problem* prob, const Dims& d, const void* x,
+                            const float* dt, const float* A, const void* B, const void* C,
+                            const float* D, const float* h_in, void* y, hipStream_t s) {
+  int64_t sz[5];
+  workspace_sizes(d, sz);
+  const int64_t od = (sz[0] + 255) & ~int64_t(255), oc = od + ((sz[1] + 255) & ~int64_t(255));
+  void* base = nullptr;
+  if (hipMallocAsync(&base, (size_t)(oc + sz[2]), s) != hipSuccess) return SSD_ERR_OUT_OF_MEMORY;
+  char* b = static_cast<char*>(base);
+  float *Acs = reinterpret_cast<float*>(b), *dtc = reinterpret_cast<float*>(b + od),
+        *CB = reinterpret_cast<float*>(b + oc);
+  const int io = prob->io_dtype;
+  hipError_t e = ssd::launch_chunk_cumsum(d, dt, A, Acs, dtc, s);
+  if (e == hipSuccess) e = ssd::launch_bmm_chunk(d, io, B, C, CB, s);
+  if (e == hipSuccess)
+    e = ssd::launch_chunk_scan(d, io, ssd::kPrecFp32, x, C, CB, Acs, dtc, h_in, D, y, s);
+  const hipError_t ef = hipFreeAsync(base, s);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(ef);
+}
+
 // Compute units of the current device (cached per device).
 int compute_units() {
   static int cached[64] = {0};
@@ -503,11 +527,11 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
                 ndp = Bt * Lp * H;
   // workspace (fp32): see the steps below for what each holds; WS1 and WS2 are the unfused
   // workspaces of steps 1 and 2 (kept for their chunk-entry states), ANCH doubles
-  enum { X32, DY32, B32, C32, Y0, XR, BR, CR, DTR, UR, G0, YT, H0T, CTR, YTR, DFT,
+  enum { X32, DY32, B32, C32, Y0, XR, BR, CR, DTR, UR, G0, YT, CTR, YTR,
          Q, XU, DYX, PA, PD, ZD, WS1, WS2, ANCH, NBUF };
-  const int64_t el[NBUF] = {nx,  nx,  nb,  nb,  nx,  nxp, nbp, nbp, ndp,        nxp,
-                            ns,  nt,  ns,  nxp, ntp, ns,  nd,  nd,  nd,         2 * Bt * H,
-                            2 * Bt * H, H, (ws1 + 3) / 4, (ws2 + 3) / 4, 2 * Bt * H * ntile};
+  const int64_t el[NBUF] = {nx,  nx,  nb,  nb,  nx,  nxp, nbp, nbp, ndp, nxp, ns,  nt,
+                            nxp, ntp, nd,  nd,  nd,  2 * Bt * H, 2 * Bt * H, H,
+                            (ws1 + 3) / 4, (ws2 + 3) / 4, 2 * Bt * H * ntile};
   int64_t off[NBUF], total = 0;
   for (int i = 0; i < NBUF; ++i) {
     off[i] = total;
@@ -550,25 +574,32 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   hip(ssd::launch_gather(io, B, w[CR], iBt, iL, iG, 1, iN, true, ipad, hs));
   hip(ssd::launch_dt_shift_rev(dt, w[DTR], iBt, iL, iH, ipad, hs));
   fwd(&pp, dup, w[XR], w[DTR], w[BR], w[CR], dfinal, w[UR], w[G0], w[WS2]);
+  // chunk-entry states of steps 1 and 2 ([Bt, nc, H, P, N]): the anchors of the decay gradient,
+  // and, transposed, the entering states of steps 3 and 4
+  const float* hf = reinterpret_cast<const float*>(reinterpret_cast<const char*>(w[WS1]) + off1[4]);
+  const float* hg = reinterpret_cast<const float*>(reinterpret_cast<const char*>(w[WS2]) + off2[4]);
+  auto scan = [&](const ssd_problem* pr, const Dims& dd, const float* xx, const float* dtt,
+                  const float* bb, const float* cc, const float* h_in, float* yy) {
+    if (r == SSD_OK)
+      r = run_unfused_scan(pr, dd, xx, dtt, A, bb, cc, w[ZD], h_in, yy, hs);
+  };
   // 3. dC: the transposed state S_t^T (state dim N, head dim P) read out with dy; its input is
-  //    B of the head's group
-  if (initial_state) hip(ssd::launch_transpose_state(initial_state, w[H0T], iBt, iH, iP, iN, hs));
-  fwd(&tp, dT, w[B32], dt, w[X32], w[DY32], initial_state ? w[H0T] : nullptr, w[YT], nullptr,
-      nullptr);
+  //    B of the head's group. Its chunk-entry states are those of step 1, transposed (the same
+  //    chunks), so only its cumulative decay, C B^T and chunk scan run.
+  dT.hin_transposed = 1;
+  scan(&tp, dT, w[B32], dt, w[X32], w[DY32], hf, w[YT]);
   // 4. dB: the transposed adjoint G_t^T in reversed time (padded as step 2), read out with x; its
-  //    input is C of the head's group in reversed time (step 2's BR)
+  //    input is C of the head's group in reversed time (step 2's BR); entering states: step 2's,
+  //    transposed
   hip(ssd::launch_gather(io, x, w[CTR], iBt, iL, iH, 1, iP, true, ipad, hs));
-  if (dfinal) hip(ssd::launch_transpose_state(dfinal, w[DFT], iBt, iH, iP, iN, hs));
-  fwd(&tpp, dTup, w[BR], w[DTR], w[XR], w[CTR], dfinal ? w[DFT] : nullptr, w[YTR], nullptr,
-      nullptr);
+  dTup.hin_transposed = 1;
+  scan(&tpp, dTup, w[BR], w[DTR], w[XR], w[CTR], hg, w[YTR]);
   // 5. the gradients
   hip(ssd::launch_bwd_pointwise(io, x, dy, w[UR], w[Y0], dt, D, dx, w[Q], w[XU], w[DYX], iBt, iL,
                                 iH, iP, ipad, hs));
   double* pa = reinterpret_cast<double*>(w[PA]);
   double* pd = reinterpret_cast<double*>(w[PD]);
   double* anch = reinterpret_cast<double*>(w[ANCH]);
-  const float* hf = reinterpret_cast<const float*>(reinterpret_cast<const char*>(w[WS1]) + off1[4]);
-  const float* hg = reinterpret_cast<const float*>(reinterpret_cast<const char*>(w[WS2]) + off2[4]);
   hip(ssd::launch_anchor_dot(hf, hg, w[G0], anch, iBt, iH, iP * iN, (int)kBackwardChunk, d.nc,
                              dup.nc, iL, (int)Lp, hs));
   hip(ssd::launch_bwd_scan(w[Q], w[XU], w[DYX], dt, A, anch, ddt, pa, pd, iBt, iL, iH, hs));

@@ -58,19 +58,6 @@ __global__ __launch_bounds__(256) void k_dt_shift_rev(const float* __restrict__ 
   }
 }
 
-__global__ __launch_bounds__(256) void k_transpose_state(const float* __restrict__ in,
-                                                         float* __restrict__ out, int BH, int P,
-                                                         int N) {
-  const int64_t total = (int64_t)BH * P * N;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * 256) {
-    const int p = (int)(i % P);  // output index [bh, n, p]
-    const int n = (int)((i / P) % N);
-    const int64_t bh = i / ((int64_t)P * N);
-    out[i] = in[(bh * P + p) * N + n];
-  }
-}
-
 // Sum over the 64 lanes of a wave (every lane gets the total).
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
@@ -308,13 +295,6 @@ hipError_t launch_dt_shift_rev(const float* dt, float* dtr, int Bt, int L, int H
                                hipStream_t s) {
   hipLaunchKernelGGL(k_dt_shift_rev, dim3(grid_for((int64_t)Bt * (L + pad) * H)), dim3(256), 0, s,
                      dt, dtr, Bt, L, H, pad);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_state(const float* in, float* out, int Bt, int H, int P, int N,
-                                  hipStream_t s) {
-  hipLaunchKernelGGL(k_transpose_state, dim3(grid_for((int64_t)Bt * H * P * N)), dim3(256), 0, s,
-                     in, out, Bt * H, P, N);
   return hipGetLastError();
 }
 

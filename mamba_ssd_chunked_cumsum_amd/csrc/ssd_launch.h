@@ -20,6 +20,9 @@ struct Dims {
   // unfused path only (the backward's transposed recurrences): 0 = x has one row per head; else x
   // has x_groups rows per token and head h reads row h / (H / x_groups) (x shared like B and C)
   int x_groups = 0;
+  // fp32 chunk scan only (the backward's transposed recurrences): h_in holds, per (batch, chunk,
+  // head), the transposed states [N][P] that the untransposed problem left, read transposed
+  int hin_transposed = 0;
 };
 
 constexpr int kIoF32 = 0, kIoBf16 = 1;
@@ -98,9 +101,6 @@ hipError_t launch_gather(int io, const void* in, float* out, int Bt, int L, int 
 // dtr[b, pad + t, h] = t == 0 ? 0 : dt[b, L - t, h], dtr[b, 0 .. pad - 1] = 0
 hipError_t launch_dt_shift_rev(const float* dt, float* dtr, int Bt, int L, int H, int pad,
                                hipStream_t s);
-// out[b, h, n, p] = in[b, h, p, n]
-hipError_t launch_transpose_state(const float* in, float* out, int Bt, int H, int P, int N,
-                                  hipStream_t s);
 // per (b, t, h): dx = D dy + dt u; q = dy . ys - dt x . u; xu = x . u; dyx = dy . x, where
 // u = ur[b, pad + L - 1 - t, h, :] (the adjoint readout, stored in reversed time after pad rows)
 hipError_t launch_bwd_pointwise(int io, const void* x, const void* dy, const float* ur,

@@ -708,7 +708,32 @@ __global__ __launch_bounds__(256) void k_chunk_scan_f32(
   const bool hlds = scan_state_in_lds(d);
   const int ldh = d.N + 4;
   float* Hs = Xs;
-  if (hlds) {
+  if (d.hin_transposed) {
+    // rows p0 .. p0 + np - 1 of the state from its transpose [N][P]: 16-byte loads along p,
+    // four rows' entries per load (the host guarantees the LDS staging)
+    const float* ht = h_in + (((int64_t)b * d.nc + c) * d.H + h) * d.P * d.N;
+    const int nq = np / 4, nv = nq * d.N;
+    for (int e0 = threadIdx.x; e0 < nv; e0 += 256 * 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = min(e0 + 256 * u, nv - 1);
+        v[u] = *reinterpret_cast<const float4*>(ht + (int64_t)(e / nq) * d.P + p0 + 4 * (e % nq));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + 256 * u;
+        if (e < nv) {
+          float* o = Hs + (4 * (e % nq)) * ldh + e / nq;
+          o[0] = v[u].x;
+          o[ldh] = v[u].y;
+          o[2 * ldh] = v[u].z;
+          o[3 * ldh] = v[u].w;
+        }
+      }
+    }
+    __syncthreads();
+  } else if (hlds) {
     const int nv = np * d.N / 4;
     for (int e0 = threadIdx.x; e0 < nv; e0 += 256 * 8) {
       float4 v[8];
@@ -740,7 +765,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_f32(
       }
     }
   };
-  if (hlds)
+  if (hlds || d.hin_transposed)
     readout(Hs, ldh);
   else
     readout(hb, d.N);
@@ -864,6 +889,7 @@ static hipError_t scan_f32_impl(const Dims& d, const void* x, const void* C, con
                                 const float* D, void* y, hipStream_t s) {
   const int rows = std::min(d.P, 64);
   size_t slab = (size_t)rows * (32 + 4) * 4;
+  if (d.hin_transposed && !scan_state_in_lds(d)) return hipErrorInvalidValue;  // staged only
   if (scan_state_in_lds(d)) slab = std::max(slab, (size_t)rows * (d.N + 4) * 4);
   const size_t shm = 512 * 4 + slab;
   auto kern = k_chunk_scan_f32<IO>;
@@ -881,6 +907,7 @@ static hipError_t scan_f32_impl(const Dims& d, const void* x, const void* C, con
 hipError_t launch_chunk_scan(const Dims& d, int io, int prec, const void* x, const void* C,
                              const float* CB, const float* Acs, const float* dtc,
                              const float* h_in, const float* D, void* y, hipStream_t s) {
+  if (d.hin_transposed && io != kIoF32 && prec != kPrecFp32) return hipErrorInvalidValue;
   if (io == kIoF32) return scan_f32_impl<float>(d, x, C, CB, Acs, dtc, h_in, D, y, s);
   if (prec == kPrecFp32) return scan_f32_impl<u16>(d, x, C, CB, Acs, dtc, h_in, D, y, s);
   return scan_impl<u16, f16>(d, x, C, CB, Acs, dtc, h_in, D, y, s);
