@@ -528,9 +528,9 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   // workspace (fp32): see the steps below for what each holds; WS1 and WS2 are the unfused
   // workspaces of steps 1 and 2 (kept for their chunk-entry states), ANCH doubles
   enum { X32, DY32, B32, C32, Y0, XR, BR, CR, DTR, UR, G0, YT, CTR, YTR,
-         Q, XU, DYX, PA, PD, ZD, WS1, WS2, ANCH, NBUF };
+         Q, XU, DYX, PA, PD, WS1, WS2, ANCH, NBUF };
   const int64_t el[NBUF] = {nx,  nx,  nb,  nb,  nx,  nxp, nbp, nbp, ndp, nxp, ns,  nt,
-                            nxp, ntp, nd,  nd,  nd,  2 * Bt * H, 2 * Bt * H, H,
+                            nxp, ntp, nd,  nd,  nd,  2 * Bt * H, 2 * Bt * H,
                             (ws1 + 3) / 4, (ws2 + 3) / 4, 2 * Bt * H * ntile};
   int64_t off[NBUF], total = 0;
   for (int i = 0; i < NBUF; ++i) {
@@ -554,14 +554,14 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
                  const float* bb, const float* cc, const float* h0, float* yy, float* fin,
                  float* ws) {
     if (r == SSD_OK)
-      r = run_unfused(pr, dd, ssd::kPrecFp32, xx, dtt, A, bb, cc, w[ZD], h0, yy, fin, hs, none, ws);
+      r = run_unfused(pr, dd, ssd::kPrecFp32, xx, dtt, A, bb, cc, nullptr, h0, yy, fin, hs, none,
+                      ws);
   };
-  // fp32 copies of the inputs and a zero skip term (the forwards below compute state terms only)
+  // fp32 copies of the inputs (the recurrences below compute state terms only: no skip term D)
   hip(ssd::launch_gather(io, x, w[X32], iBt, iL, iH, 1, iP, false, 0, hs));
   hip(ssd::launch_gather(io, dy, w[DY32], iBt, iL, iH, 1, iP, false, 0, hs));
   hip(ssd::launch_gather(io, B, w[B32], iBt, iL, iG, 1, iN, false, 0, hs));
   hip(ssd::launch_gather(io, C, w[C32], iBt, iL, iG, 1, iN, false, 0, hs));
-  if (r == SSD_OK) hip(hipMemsetAsync(w[ZD], 0, (size_t)H * 4, hs));
   // 1. forward: the state part of y (ys = y - D x); its chunk-entry states stay in WS1
   fwd(&p32, d, w[X32], dt, w[B32], w[C32], initial_state, w[Y0], nullptr, w[WS1]);
   // 2. adjoint G_t = dy_t C_t^T + exp(dt_{t+1} A) G_{t+1} as a forward recurrence in reversed
@@ -581,7 +581,7 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   auto scan = [&](const ssd_problem* pr, const Dims& dd, const float* xx, const float* dtt,
                   const float* bb, const float* cc, const float* h_in, float* yy) {
     if (r == SSD_OK)
-      r = run_unfused_scan(pr, dd, xx, dtt, A, bb, cc, w[ZD], h_in, yy, hs);
+      r = run_unfused_scan(pr, dd, xx, dtt, A, bb, cc, nullptr, h_in, yy, hs);
   };
   // 3. dC: the transposed state S_t^T (state dim N, head dim P) read out with dy; its input is
   //    B of the head's group. Its chunk-entry states are those of step 1, transposed (the same

@@ -769,7 +769,9 @@ __global__ __launch_bounds__(256) void k_chunk_scan_f32(
     readout(Hs, ldh);
   else
     readout(hb, d.N);
-  const float dh = Dv[h];
+  // the skip term D x (none when Dv is null: x is then not read again)
+  const bool skip = Dv != nullptr;
+  const float dh = skip ? Dv[h] : 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = i0 + 4 * kg + r;
@@ -781,8 +783,9 @@ __global__ __launch_bounds__(256) void k_chunk_scan_f32(
     for (int pt = 0; pt < NPT; ++pt) {
       if (pt < npt) {
         const int p = p0 + pt * 16 + col;
-        const float xv = Io<IO>::load(x, xrow + p);
-        Io<IO>::store(y, row + p, acc[pt][r] + e * inter[pt][r] + dh * xv);
+        float v = acc[pt][r] + e * inter[pt][r];
+        if (skip) v += dh * Io<IO>::load(x, xrow + p);
+        Io<IO>::store(y, row + p, v);
       }
     }
   }
@@ -907,7 +910,8 @@ static hipError_t scan_f32_impl(const Dims& d, const void* x, const void* C, con
 hipError_t launch_chunk_scan(const Dims& d, int io, int prec, const void* x, const void* C,
                              const float* CB, const float* Acs, const float* dtc,
                              const float* h_in, const float* D, void* y, hipStream_t s) {
-  if (d.hin_transposed && io != kIoF32 && prec != kPrecFp32) return hipErrorInvalidValue;
+  // a null D (no skip term) and the transposed entering state: fp32 arithmetic only
+  if ((d.hin_transposed || !D) && io != kIoF32 && prec != kPrecFp32) return hipErrorInvalidValue;
   if (io == kIoF32) return scan_f32_impl<float>(d, x, C, CB, Acs, dtc, h_in, D, y, s);
   if (prec == kPrecFp32) return scan_f32_impl<u16>(d, x, C, CB, Acs, dtc, h_in, D, y, s);
   return scan_impl<u16, f16>(d, x, C, CB, Acs, dtc, h_in, D, y, s);
