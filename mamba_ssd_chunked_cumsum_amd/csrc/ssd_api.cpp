@@ -509,14 +509,18 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   if (st != SSD_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
-  ssd_problem p32 = *prob;
-  p32.io_dtype = SSD_DTYPE_F32;
-  const Dims d = make_dims(&p32, kBackwardChunk);
+  // the forward-time recurrences (1, 3) read the caller's x, B, C and dy in place, bf16 ones
+  // widened exactly and computed in fp32 (f32_math)
+  Dims d = make_dims(prob, kBackwardChunk);
+  d.f32_math = 1;
   Dims dup = make_dims(&pp, kBackwardChunk);  // the adjoint: reversed, padded, unit input weight
   dup.unit_input = 1;
   // the transposed problems' input is B (or C) per head: read in place, shared by each group
+  ssd_problem tpio = tp;
+  tpio.io_dtype = prob->io_dtype;
   Dims dT = make_dims(&tp, kBackwardChunk);
   dT.x_groups = (int)G;
+  dT.f32_math = 1;
   Dims dTup = make_dims(&tpp, kBackwardChunk);
   dTup.x_groups = (int)G;
   dTup.unit_input = 1;
@@ -527,11 +531,10 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
                 ndp = Bt * Lp * H;
   // workspace (fp32): see the steps below for what each holds; WS1 and WS2 are the unfused
   // workspaces of steps 1 and 2 (kept for their chunk-entry states), ANCH doubles
-  enum { X32, DY32, B32, C32, Y0, XR, BR, CR, DTR, UR, G0, YT, CTR, YTR,
-         Q, XU, DYX, PA, PD, WS1, WS2, ANCH, NBUF };
-  const int64_t el[NBUF] = {nx,  nx,  nb,  nb,  nx,  nxp, nbp, nbp, ndp, nxp, ns,  nt,
-                            nxp, ntp, nd,  nd,  nd,  2 * Bt * H, 2 * Bt * H,
-                            (ws1 + 3) / 4, (ws2 + 3) / 4, 2 * Bt * H * ntile};
+  enum { Y0, XR, BR, CR, DTR, UR, G0, YT, CTR, YTR, Q, XU, DYX, PA, PD, WS1, WS2, ANCH, NBUF };
+  const int64_t el[NBUF] = {nx, nxp, nbp, nbp, ndp, nxp, ns, nt, nxp, ntp, nd, nd, nd,
+                            2 * Bt * H, 2 * Bt * H, (ws1 + 3) / 4, (ws2 + 3) / 4,
+                            2 * Bt * H * ntile};
   int64_t off[NBUF], total = 0;
   for (int i = 0; i < NBUF; ++i) {
     off[i] = total;
@@ -550,20 +553,16 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   auto hip = [&](hipError_t e) {
     if (r == SSD_OK && e != hipSuccess) r = from_hip(e);
   };
-  auto fwd = [&](const ssd_problem* pr, const Dims& dd, const float* xx, const float* dtt,
-                 const float* bb, const float* cc, const float* h0, float* yy, float* fin,
+  auto fwd = [&](const ssd_problem* pr, const Dims& dd, const void* xx, const float* dtt,
+                 const void* bb, const void* cc, const float* h0, float* yy, float* fin,
                  float* ws) {
     if (r == SSD_OK)
       r = run_unfused(pr, dd, ssd::kPrecFp32, xx, dtt, A, bb, cc, nullptr, h0, yy, fin, hs, none,
                       ws);
   };
-  // fp32 copies of the inputs (the recurrences below compute state terms only: no skip term D)
-  hip(ssd::launch_gather(io, x, w[X32], iBt, iL, iH, 1, iP, false, 0, hs));
-  hip(ssd::launch_gather(io, dy, w[DY32], iBt, iL, iH, 1, iP, false, 0, hs));
-  hip(ssd::launch_gather(io, B, w[B32], iBt, iL, iG, 1, iN, false, 0, hs));
-  hip(ssd::launch_gather(io, C, w[C32], iBt, iL, iG, 1, iN, false, 0, hs));
+  // (the recurrences below compute state terms only: no skip term D)
   // 1. forward: the state part of y (ys = y - D x); its chunk-entry states stay in WS1
-  fwd(&p32, d, w[X32], dt, w[B32], w[C32], initial_state, w[Y0], nullptr, w[WS1]);
+  fwd(prob, d, x, dt, B, C, initial_state, w[Y0], nullptr, w[WS1]);
   // 2. adjoint G_t = dy_t C_t^T + exp(dt_{t+1} A) G_{t+1} as a forward recurrence in reversed
   //    time (decay of the next token, unit input weight) from dfinal, after pad tokens of zero
   //    input and zero dt (the state passes them unchanged); its readout with B gives u_t = G_t B_t,
@@ -578,8 +577,8 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   // and, transposed, the entering states of steps 3 and 4
   const float* hf = reinterpret_cast<const float*>(reinterpret_cast<const char*>(w[WS1]) + off1[4]);
   const float* hg = reinterpret_cast<const float*>(reinterpret_cast<const char*>(w[WS2]) + off2[4]);
-  auto scan = [&](const ssd_problem* pr, const Dims& dd, const float* xx, const float* dtt,
-                  const float* bb, const float* cc, const float* h_in, float* yy) {
+  auto scan = [&](const ssd_problem* pr, const Dims& dd, const void* xx, const float* dtt,
+                  const void* bb, const void* cc, const float* h_in, float* yy) {
     if (r == SSD_OK)
       r = run_unfused_scan(pr, dd, xx, dtt, A, bb, cc, nullptr, h_in, yy, hs);
   };
@@ -587,7 +586,7 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   //    B of the head's group. Its chunk-entry states are those of step 1, transposed (the same
   //    chunks), so only its cumulative decay, C B^T and chunk scan run.
   dT.hin_transposed = 1;
-  scan(&tp, dT, w[B32], dt, w[X32], w[DY32], hf, w[YT]);
+  scan(&tpio, dT, B, dt, x, dy, hf, w[YT]);
   // 4. dB: the transposed adjoint G_t^T in reversed time (padded as step 2), read out with x; its
   //    input is C of the head's group in reversed time (step 2's BR); entering states: step 2's,
   //    transposed

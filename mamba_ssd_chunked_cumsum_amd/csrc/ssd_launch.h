@@ -23,6 +23,9 @@ struct Dims {
   // fp32 chunk scan only (the backward's transposed recurrences): h_in holds, per (batch, chunk,
   // head), the transposed states [N][P] that the untransposed problem left, read transposed
   int hin_transposed = 0;
+  // unfused path, bf16 io (the backward's recurrences): every stage computes in fp32 (C B^T
+  // included) and the chunk scan stores y in fp32
+  int f32_math = 0;
 };
 
 constexpr int kIoF32 = 0, kIoBf16 = 1;

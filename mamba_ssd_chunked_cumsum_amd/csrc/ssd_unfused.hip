@@ -170,8 +170,9 @@ __global__ __launch_bounds__(256) void k_bmm_chunk(const IO* __restrict__ Bm,
 // of a fragment fall in distinct banks; rows past the sequence are zero), then every 16x16 block
 // is computed from LDS. Each row serves up to four blocks of the lower triangle, which the
 // global-memory version reads once per block.
-__global__ __launch_bounds__(256) void k_bmm_chunk_lds(const float* __restrict__ Bm,
-                                                       const float* __restrict__ Cm,
+template <typename IO>
+__global__ __launch_bounds__(256) void k_bmm_chunk_lds(const IO* __restrict__ Bm,
+                                                       const IO* __restrict__ Cm,
                                                        float* __restrict__ CB, Dims d) {
   using M = Mma<float>;
   extern __shared__ __align__(16) float sm_bmm[];
@@ -193,8 +194,17 @@ __global__ __launch_bounds__(256) void k_bmm_chunk_lds(const float* __restrict__
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int64_t o = gbase + (int64_t)min(r0 + 8 * u, q - 1) * rowstride + 4 * c4c;
-      vc[u] = *reinterpret_cast<const float4*>(Cm + o);
-      vb[u] = *reinterpret_cast<const float4*>(Bm + o);
+      if constexpr (sizeof(IO) == 2) {  // bf16: four values in 8 bytes, widened exactly
+        const uint2 c2 = *reinterpret_cast<const uint2*>(Cm + o);
+        const uint2 b2 = *reinterpret_cast<const uint2*>(Bm + o);
+        vc[u] = make_float4(__uint_as_float(c2.x << 16), __uint_as_float(c2.x & 0xffff0000u),
+                            __uint_as_float(c2.y << 16), __uint_as_float(c2.y & 0xffff0000u));
+        vb[u] = make_float4(__uint_as_float(b2.x << 16), __uint_as_float(b2.x & 0xffff0000u),
+                            __uint_as_float(b2.y << 16), __uint_as_float(b2.y & 0xffff0000u));
+      } else {
+        vc[u] = *reinterpret_cast<const float4*>(Cm + o);
+        vb[u] = *reinterpret_cast<const float4*>(Bm + o);
+      }
     }
     // rows past the sequence are zeroed component by component (a select between two float4
     // values would become a load through a selected pointer, which puts the arrays in scratch)
@@ -785,7 +795,10 @@ __global__ __launch_bounds__(256) void k_chunk_scan_f32(
         const int p = p0 + pt * 16 + col;
         float v = acc[pt][r] + e * inter[pt][r];
         if (skip) v += dh * Io<IO>::load(x, xrow + p);
-        Io<IO>::store(y, row + p, v);
+        if (d.f32_math)
+          reinterpret_cast<float*>(y)[row + p] = v;
+        else
+          Io<IO>::store(y, row + p, v);
       }
     }
   }
@@ -804,21 +817,30 @@ hipError_t launch_chunk_cumsum(const Dims& d, const float* dt, const float* A, f
 hipError_t launch_bmm_chunk(const Dims& d, int io, const void* B, const void* C, float* CB,
                             hipStream_t s) {
   dim3 grid(d.nc, d.G, d.Bt);
-  if (io == kIoBf16) {
+  if (io == kIoBf16 && !d.f32_math) {
     hipLaunchKernelGGL((k_bmm_chunk<u16, f16>), grid, dim3(256), 0, s, (const u16*)B,
                        (const u16*)C, CB, d);
   } else if (d.Q <= 64 && d.N <= 128) {
     const size_t shm = (size_t)2 * d.Q * (d.N + 4) * 4;
+    auto kern = io == kIoBf16 ? (const void*)k_bmm_chunk_lds<u16> : (const void*)k_bmm_chunk_lds<float>;
     if (shm > 64 * 1024) {
-      hipError_t e = hipFuncSetAttribute((const void*)k_bmm_chunk_lds,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+      hipError_t e =
+          hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_bmm_chunk_lds, grid, dim3(256), shm, s, (const float*)B, (const float*)C,
-                       CB, d);
-  } else
+    if (io == kIoBf16)
+      hipLaunchKernelGGL(k_bmm_chunk_lds<u16>, grid, dim3(256), shm, s, (const u16*)B,
+                         (const u16*)C, CB, d);
+    else
+      hipLaunchKernelGGL(k_bmm_chunk_lds<float>, grid, dim3(256), shm, s, (const float*)B,
+                         (const float*)C, CB, d);
+  } else if (io == kIoBf16) {
+    hipLaunchKernelGGL((k_bmm_chunk<u16, float>), grid, dim3(256), 0, s, (const u16*)B,
+                       (const u16*)C, CB, d);
+  } else {
     hipLaunchKernelGGL((k_bmm_chunk<float, float>), grid, dim3(256), 0, s, (const float*)B,
                        (const float*)C, CB, d);
+  }
   return hipGetLastError();
 }
 
