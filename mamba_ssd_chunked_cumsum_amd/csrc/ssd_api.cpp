@@ -475,7 +475,6 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   const int64_t Lp = prob->seqlen + pad;
   ssd_problem pp = *prob, tpp = tp;
   pp.seqlen = Lp;
-  pp.io_dtype = SSD_DTYPE_F32;
   tpp.seqlen = Lp;
   st = check_problem(&pp, kBackwardChunk);
   if (st == SSD_OK) st = check_problem(&tpp, kBackwardChunk);
@@ -515,15 +514,19 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   d.f32_math = 1;
   Dims dup = make_dims(&pp, kBackwardChunk);  // the adjoint: reversed, padded, unit input weight
   dup.unit_input = 1;
+  dup.f32_math = 1;
   // the transposed problems' input is B (or C) per head: read in place, shared by each group
   ssd_problem tpio = tp;
   tpio.io_dtype = prob->io_dtype;
   Dims dT = make_dims(&tp, kBackwardChunk);
   dT.x_groups = (int)G;
   dT.f32_math = 1;
+  ssd_problem tppio = tpp;
+  tppio.io_dtype = prob->io_dtype;
   Dims dTup = make_dims(&tpp, kBackwardChunk);
   dTup.x_groups = (int)G;
   dTup.unit_input = 1;
+  dTup.f32_math = 1;
   int64_t off1[5], off2[5];
   const int64_t ws1 = unfused_workspace_bytes(d, off1), ws2 = unfused_workspace_bytes(dup, off2);
   const int64_t ntile = (L + 255) / 256;
@@ -532,7 +535,10 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   // workspace (fp32): see the steps below for what each holds; WS1 and WS2 are the unfused
   // workspaces of steps 1 and 2 (kept for their chunk-entry states), ANCH doubles
   enum { Y0, XR, BR, CR, DTR, UR, G0, YT, CTR, YTR, Q, XU, DYX, PA, PD, WS1, WS2, ANCH, NBUF };
-  const int64_t el[NBUF] = {nx, nxp, nbp, nbp, ndp, nxp, ns, nt, nxp, ntp, nd, nd, nd,
+  // (XR, BR, CR and CTR hold reversed copies in the io type)
+  const int64_t eb = io_bytes(prob);
+  const int64_t rx = (nxp * eb + 3) / 4, rb = (nbp * eb + 3) / 4;
+  const int64_t el[NBUF] = {nx, rx, rb, rb, ndp, nxp, ns, nt, rx, ntp, nd, nd, nd,
                             2 * Bt * H, 2 * Bt * H, (ws1 + 3) / 4, (ws2 + 3) / 4,
                             2 * Bt * H * ntile};
   int64_t off[NBUF], total = 0;
@@ -567,10 +573,10 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   //    time (decay of the next token, unit input weight) from dfinal, after pad tokens of zero
   //    input and zero dt (the state passes them unchanged); its readout with B gives u_t = G_t B_t,
   //    its final state G_0, its chunk-entry states (in WS2) G_t at the forward chunks' starts
-  // (reversed copies straight from the caller's tensors: half the bytes read for bf16 io)
-  hip(ssd::launch_gather(io, dy, w[XR], iBt, iL, iH, 1, iP, true, ipad, hs));
-  hip(ssd::launch_gather(io, C, w[BR], iBt, iL, iG, 1, iN, true, ipad, hs));
-  hip(ssd::launch_gather(io, B, w[CR], iBt, iL, iG, 1, iN, true, ipad, hs));
+  // (reversed copies of the caller's tensors in their own type, widened to fp32 where read)
+  hip(ssd::launch_reverse_rows(io, dy, w[XR], iBt, iL, iH * iP, ipad, hs));
+  hip(ssd::launch_reverse_rows(io, C, w[BR], iBt, iL, iG * iN, ipad, hs));
+  hip(ssd::launch_reverse_rows(io, B, w[CR], iBt, iL, iG * iN, ipad, hs));
   hip(ssd::launch_dt_shift_rev(dt, w[DTR], iBt, iL, iH, ipad, hs));
   fwd(&pp, dup, w[XR], w[DTR], w[BR], w[CR], dfinal, w[UR], w[G0], w[WS2]);
   // chunk-entry states of steps 1 and 2 ([Bt, nc, H, P, N]): the anchors of the decay gradient,
@@ -590,9 +596,9 @@ ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt,
   // 4. dB: the transposed adjoint G_t^T in reversed time (padded as step 2), read out with x; its
   //    input is C of the head's group in reversed time (step 2's BR); entering states: step 2's,
   //    transposed
-  hip(ssd::launch_gather(io, x, w[CTR], iBt, iL, iH, 1, iP, true, ipad, hs));
+  hip(ssd::launch_reverse_rows(io, x, w[CTR], iBt, iL, iH * iP, ipad, hs));
   dTup.hin_transposed = 1;
-  scan(&tpp, dTup, w[BR], w[DTR], w[XR], w[CTR], hg, w[YTR]);
+  scan(&tppio, dTup, w[BR], w[DTR], w[XR], w[CTR], hg, w[YTR]);
   // 5. the gradients
   hip(ssd::launch_bwd_pointwise(io, x, dy, w[UR], w[Y0], dt, D, dx, w[Q], w[XU], w[DYX], iBt, iL,
                                 iH, iP, ipad, hs));

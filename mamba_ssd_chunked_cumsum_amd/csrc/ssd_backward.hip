@@ -12,38 +12,6 @@ namespace ssd {
 
 namespace {
 
-// One block per output row (b, t) of L + pad rows per batch entry: K * E values, four per thread
-// step (E is a multiple of 16); the first pad rows of each batch entry are zero.
-template <typename IO>
-__global__ __launch_bounds__(256) void k_gather(const IO* __restrict__ in, float* __restrict__ out,
-                                                int L, int K, int rep, int E, int rev, int pad) {
-  const int Lo = L + pad;
-  const int row = blockIdx.x, tp = row % Lo, b = row / Lo;
-  float* o = out + (int64_t)row * K * E;
-  if (tp < pad) {
-    for (int f = threadIdx.x * 4; f < K * E; f += 1024)
-      *reinterpret_cast<float4*>(o + f) = make_float4(0.f, 0.f, 0.f, 0.f);
-    return;
-  }
-  const int t = tp - pad;
-  const int ts = rev ? L - 1 - t : t;
-  const int Kin = K / rep;
-  const IO* src = in + ((int64_t)b * L + ts) * Kin * E;
-  for (int f = threadIdx.x * 4; f < K * E; f += 1024) {
-    const int k = f / E, e = f % E;
-    const int64_t si = (int64_t)(k / rep) * E + e;
-    float4 v;
-    if constexpr (sizeof(IO) == 4) {
-      v = *reinterpret_cast<const float4*>(src + si);
-    } else {
-      const uint2 r = *reinterpret_cast<const uint2*>(src + si);
-      v = make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
-                      __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
-    }
-    *reinterpret_cast<float4*>(o + f) = v;
-  }
-}
-
 __global__ __launch_bounds__(256) void k_dt_shift_rev(const float* __restrict__ dt,
                                                       float* __restrict__ dtr, int Bt, int L,
                                                       int H, int pad) {
@@ -279,15 +247,34 @@ int grid_for(int64_t total) {
 
 }  // namespace
 
-hipError_t launch_gather(int io, const void* in, float* out, int Bt, int L, int K, int rep, int E,
-                         bool rev, int pad, hipStream_t s) {
+// out[b, pad + t] = in[b, L - 1 - t] (rows of E elements of type T), out[b, 0 .. pad - 1] = 0:
+// a copy reversed in time, in the input's own type. One block per output row, 16-byte pieces
+// (E * sizeof(T) is a multiple of 16).
+template <typename T>
+__global__ __launch_bounds__(256) void k_reverse_rows(const T* __restrict__ in, T* __restrict__ out,
+                                                     int L, int E, int pad) {
+  const int Lo = L + pad;
+  const int row = blockIdx.x, tp = row % Lo, b = row / Lo;
+  uint4* o = reinterpret_cast<uint4*>(out + (int64_t)row * E);
+  const int n16 = E * (int)sizeof(T) / 16;
+  if (tp < pad) {
+    for (int f = threadIdx.x; f < n16; f += 256) o[f] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
+  const uint4* src =
+      reinterpret_cast<const uint4*>(in + ((int64_t)b * L + (L - 1 - (tp - pad))) * E);
+  for (int f = threadIdx.x; f < n16; f += 256) o[f] = src[f];
+}
+
+hipError_t launch_reverse_rows(int io, const void* in, void* out, int Bt, int L, int E, int pad,
+                               hipStream_t s) {
   const dim3 g((unsigned)Bt * (unsigned)(L + pad));
   if (io == kIoBf16)
-    hipLaunchKernelGGL(k_gather<u16>, g, dim3(256), 0, s, (const u16*)in, out, L, K, rep, E,
-                       (int)rev, pad);
+    hipLaunchKernelGGL(k_reverse_rows<u16>, g, dim3(256), 0, s, (const u16*)in, (u16*)out, L, E,
+                       pad);
   else
-    hipLaunchKernelGGL(k_gather<float>, g, dim3(256), 0, s, (const float*)in, out, L, K, rep, E,
-                       (int)rev, pad);
+    hipLaunchKernelGGL(k_reverse_rows<float>, g, dim3(256), 0, s, (const float*)in, (float*)out,
+                       L, E, pad);
   return hipGetLastError();
 }
 

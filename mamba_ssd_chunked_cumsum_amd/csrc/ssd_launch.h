@@ -96,11 +96,11 @@ hipError_t launch_quadratic(const Dims& d, int io, const void* x, const float* d
 constexpr int64_t kScratchBytes = int64_t(64) << 20;
 hipError_t scratch_address(void** out);
 
-// backward helpers (ssd_backward.hip); all outputs fp32, layouts row-major.
-// out[b, pad + t, k, e] = in[b, rev ? L - 1 - t : t, k / rep, e], out[b, 0 .. pad - 1] = 0
-// (in: [Bt, L, K / rep, E], io dtype; out: [Bt, L + pad, K, E])
-hipError_t launch_gather(int io, const void* in, float* out, int Bt, int L, int K, int rep, int E,
-                         bool rev, int pad, hipStream_t s);
+// backward helpers (ssd_backward.hip); outputs fp32 unless stated, layouts row-major.
+// out[b, pad + t, :] = in[b, L - 1 - t, :] (rows of E elements of the io type), out[b, 0 .. pad - 1]
+// = 0; E times the element size a multiple of 16 bytes
+hipError_t launch_reverse_rows(int io, const void* in, void* out, int Bt, int L, int E, int pad,
+                               hipStream_t s);
 // dtr[b, pad + t, h] = t == 0 ? 0 : dt[b, L - t, h], dtr[b, 0 .. pad - 1] = 0
 hipError_t launch_dt_shift_rev(const float* dt, float* dtr, int Bt, int L, int H, int pad,
                                hipStream_t s);
