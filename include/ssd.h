@@ -263,9 +263,9 @@ ssd_status ssd_step(const ssd_problem* prob, const void* x, const float* dt, con
  * dinitial_state [batch, nheads, headdim, dstate] (nullable: not computed). No output may overlap
  * an input or another output; every pointer 16-byte aligned. Shapes as for the forward, and the
  * transposed problem (headdim and dstate swapped, one group per head) must pass the same checks.
- * Workspace: about 6 fp32 copies of x-sized tensors, 4 of [batch, seqlen, nheads, dstate] and
- * the chunk states of two recurrences (4 fp32 tensors of [batch, ceil(seqlen / 64), nheads,
- * headdim, dstate]), allocated and released stream-ordered on `stream`. Errors as for
+ * Workspace: 2 fp32 and 2 io-typed x-sized tensors, 2 fp32 tensors of [batch, seqlen, nheads,
+ * dstate] and the chunk states of two recurrences (4 fp32 tensors of [batch, ceil(seqlen / 64),
+ * nheads, headdim, dstate]), allocated and released stream-ordered on `stream`. Errors as for
  * ssd_forward. */
 ssd_status ssd_backward(const ssd_problem* prob, const void* x, const float* dt, const float* A,
                         const void* B, const void* C, const float* D, int64_t chunk_size,
