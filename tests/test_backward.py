@@ -59,6 +59,8 @@ CASES = [
     (1, 1024, 4, 64, 128, 1, 256, "bf16", True, True),  # longer runs of chunks
     (1, 600, 2, 32, 64, 1, 64, "f32", True, True),      # several 256-token tiles, ragged end
     (2, 520, 4, 64, 128, 2, 64, "bf16", False, True),   # ... with groups, no initial state
+    (1, 300, 2, 128, 256, 1, 128, "bf16", True, True),  # dstate 256: the general C B^T kernel
+    (1, 130, 2, 32, 256, 2, 64, "f32", False, True),    # ... with fp32 inputs
 ]
 
 
